@@ -1,0 +1,324 @@
+#!/usr/bin/env python3
+"""Benchmark: one NVFP4 linear-layer training step (Fprop, Dgrad, Wgrad with
+all their quantizations) at the 12B hybrid's FFN down-projection shape,
+8192 tokens x 20480 (FFN) -> 5120 (hidden), on one MI355X.
+
+A step is the whole hot path over one batch of seeded synthetic inputs that
+are resident in HBM before timing starts:
+  Q(X)   rowwise 1D RTN          (amax + encode)
+  Q(W)   2D 16x16 RTN + codes_t  (amax + encode)
+  Fprop  Y  = Q(X) Q(W)^T        M=8192  N=5120  K=20480
+  Q(dY)  rowwise 1D SR           (amax + encode)
+  Dgrad  dX = Q(dY) Q(W)         M=8192  N=20480 K=5120
+  Q(RHT(dY)^T) SR, Q(RHT(X)^T) RTN (RHT amax + transpose-encode each)
+  Wgrad  dW = dY^T X             M=5120  N=20480 K=8192
+Outputs are preallocated; nothing is allocated inside the timed region.
+
+Prints ONE JSON line.  `value` is whole-step NVFP4-linear throughput
+(3 * 2MNK GEMM FLOP per step / step time, quantization included); per-kernel
+GB/s and TFLOP/s (HIP events on the launch stream) are reported beside it, with
+the roofline of the dominant kernel and the CPU oracle's rate on a bounded
+sample of the same workload.
+"""
+from __future__ import annotations
+
+import argparse
+import json
+import os
+import sys
+import time
+
+import numpy as np
+import torch
+
+ROOT = os.path.dirname(os.path.abspath(__file__))
+sys.path.insert(0, ROOT)
+
+import bit_microscaled_numerics_amd as nv  # noqa: E402
+from bit_microscaled_numerics_amd import inputs  # noqa: E402
+
+METRIC = "NVFP4 quantize GB/s + NVFP4-linear GEMM TFLOP/s at 8192×5120×20480"
+HBM_PEAK_GBS = 8000.0          # MI355X HBM3E
+MFMA_F16_PEAK_TFLOPS = 2500.0  # MI355X dense FP16/BF16 matrix peak
+
+TOKENS, HIDDEN, FFN = 8192, 5120, 20480
+RHT_SEED, SR_SEED = 1, 1
+
+
+def log(*a):
+    print("[bench]", *a, file=sys.stderr, flush=True)
+
+
+class Step:
+    """Preallocated buffers and the ordered list of launches of one step."""
+
+    def __init__(self, x, w, dy):
+        dev = x.device
+        T, F = x.shape          # tokens, in-features (FFN)
+        H = w.shape[0]          # out-features (hidden)
+        self.x, self.w, self.dy = x, w, dy
+        e = lambda *s, dt=torch.uint8: torch.empty(*s, dtype=dt, device=dev)  # noqa: E731
+        f1 = lambda: torch.empty(1, dtype=torch.float32, device=dev)  # noqa: E731
+        self.qx = nv.NVFP4Tensor(e(T, F // 2), e(T, F // 16), f1(), f1(), T, F, 1, F // 16, 1)
+        self.qw = nv.NVFP4Tensor(e(H, F // 2), e(H // 16, F // 16), f1(), f1(), H, F, 16,
+                                 F // 16, 1, e(F, H // 2))
+        self.qdy = nv.NVFP4Tensor(e(T, H // 2), e(T, H // 16), f1(), f1(), T, H, 1, H // 16, 1)
+        self.qdy_t = nv.NVFP4Tensor(e(H, T // 2), e(H, T // 16), f1(), f1(), H, T, 1, T // 16, 1)
+        self.qx_t = nv.NVFP4Tensor(e(F, T // 2), e(F, T // 16), f1(), f1(), F, T, 1, T // 16, 1)
+        self.y = e(T, H, dt=torch.float32)
+        self.dx = e(T, F, dt=torch.float32)
+        self.dw = e(H, F, dt=torch.float32)
+        C, G = nv.NVFP4_AMAX_COMPUTE, nv.NVFP4_AMAX_GIVEN
+        q = self
+        n_x, n_w, n_dy = x.numel(), w.numel(), dy.numel()
+        # (name, kind, algorithmic bytes or flops, callable); amax passes are
+        # separate launches so each kernel is timed on its own.
+        self.ops = [
+            ("amax X", "hbm", 2 * n_x, lambda: nv.nvfp4_amax(x, q.qx.amax)),
+            ("quant X rowwise RTN", "hbm", 2.5625 * n_x,
+             lambda: nv.nvfp4_quantize1d_rtn(x, 0, q.qx.amax, G, q.qx.codes, q.qx.scales,
+                                             q.qx.tensor_scale)),
+            ("amax W", "hbm", 2 * n_w, lambda: nv.nvfp4_amax(w, q.qw.amax)),
+            ("quant W 2D RTN +codes_t", "hbm", 3.00390625 * n_w,
+             lambda: nv.nvfp4_quantize2d_rtn(w, q.qw.amax, G, q.qw.codes, q.qw.codes_t,
+                                             q.qw.scales, q.qw.tensor_scale)),
+            ("gemm Fprop", "mfma", 2.0 * T * H * F, lambda: nv.gemm(q.qx, q.qw, q.y)),
+            ("amax dY", "hbm", 2 * n_dy, lambda: nv.nvfp4_amax(dy, q.qdy.amax)),
+            ("quant dY rowwise SR", "hbm", 2.5625 * n_dy,
+             lambda: nv.nvfp4_quantize1d_sr(dy, 0, q.qdy.amax, G, SR_SEED, 0, q.qdy.codes,
+                                            q.qdy.scales, q.qdy.tensor_scale)),
+            ("gemm Dgrad", "mfma", 2.0 * T * F * H, lambda: nv.gemm(q.qdy, q.qw.t(), q.dx)),
+            ("amax RHT dY", "hbm", 2 * n_dy, lambda: nv.nvfp4_amax_rht(dy, RHT_SEED, q.qdy_t.amax)),
+            ("quant dY^T RHT SR", "hbm", 2.5625 * n_dy,
+             lambda: nv.nvfp4_rht_quantize(dy, RHT_SEED, 1, SR_SEED, 1, q.qdy_t.amax, G,
+                                           q.qdy_t.codes, q.qdy_t.scales, q.qdy_t.tensor_scale)),
+            ("amax RHT X", "hbm", 2 * n_x, lambda: nv.nvfp4_amax_rht(x, RHT_SEED, q.qx_t.amax)),
+            ("quant X^T RHT RTN", "hbm", 2.5625 * n_x,
+             lambda: nv.nvfp4_rht_quantize(x, RHT_SEED, 0, 0, 0, q.qx_t.amax, G, q.qx_t.codes,
+                                           q.qx_t.scales, q.qx_t.tensor_scale)),
+            ("gemm Wgrad", "mfma", 2.0 * H * F * T, lambda: nv.gemm(q.qdy_t, q.qx_t, q.dw)),
+        ]
+        del C
+
+    def run(self, events=None):
+        for i, (_, _, _, fn) in enumerate(self.ops):
+            if events is not None:
+                events[i].record()
+            fn()
+        if events is not None:
+            events[len(self.ops)].record()
+
+
+def cpu_baseline(x, w, dy, budget_s: float = 15.0):
+    """The oracle, as it stands, on a bounded sample of the same step: a slice
+    of rows of every quantization and a set of entries of every GEMM, timed
+    and extrapolated linearly to the full step."""
+    import oracle
+    T, F = x.shape
+    H = w.shape[0]
+    rows = 64   # sampled rows / columns of each quantized tensor
+    t_quant = 0.0
+    full_quant = 0.0
+    for name, t, mode, kw in [("X", x, oracle.ROWWISE, {}), ("W", w, oracle.TWO_D, {}),
+                              ("dY", dy, oracle.ROWWISE, {"sr_seed": SR_SEED}),
+                              ("dY^T", dy, oracle.COLWISE, {"rht_seed": RHT_SEED, "sr_seed": 1}),
+                              ("X^T", x, oracle.COLWISE, {"rht_seed": RHT_SEED})]:
+        if mode == oracle.COLWISE:
+            sl = t[:, :rows].contiguous()       # `rows` output rows of the transpose
+            frac = rows / t.shape[1]
+        else:
+            sl = t[:rows].contiguous()
+            frac = rows / t.shape[0]
+        extra = {"with_codes_t": True} if mode == oracle.TWO_D else {}
+        t0 = time.perf_counter()
+        oracle.quantize(sl, mode, **kw, **extra)
+        dt = time.perf_counter() - t0
+        t_quant += dt
+        full_quant += dt / frac
+    # GEMM entries: pick n entries per GEMM so the sample is ~budget seconds
+    ox = oracle.quantize(x[:256].contiguous(), oracle.ROWWISE)
+    ow = oracle.quantize(w[:256].contiguous(), oracle.TWO_D)
+    rng = np.random.default_rng(0)
+    n = 2048
+    ms = rng.integers(0, 256, n)
+    ns = rng.integers(0, 256, n)
+    t0 = time.perf_counter()
+    oracle.gemm_entries(ox, ow, ms, ns)
+    dt = time.perf_counter() - t0
+    per_mac = dt / (n * F)
+    # scale the sample up until it costs about the budget, then re-time
+    n2 = int(min(2_000_000, max(n, n * (budget_s - t_quant) / max(dt, 1e-6) * 0.8)))
+    ms = rng.integers(0, 256, n2)
+    ns = rng.integers(0, 256, n2)
+    t0 = time.perf_counter()
+    oracle.gemm_entries(ox, ow, ms, ns)
+    dt = time.perf_counter() - t0
+    per_mac = dt / (n2 * F)
+    macs_step = 3.0 * T * H * F
+    full = full_quant + per_mac * macs_step
+    flops = 2.0 * macs_step
+    return {"value": flops / full / 1e12, "unit": "TFLOP/s", "cores": oracle.num_threads(),
+            "kind": "oracle",
+            "sample": (f"oracle quantize of {rows} rows/cols of each of the 5 operands "
+                       f"({t_quant:.2f} s) + {n2} exact GEMM entries at K={F} ({dt:.2f} s), "
+                       f"extrapolated to one full step ({full:.0f} s)")}
+
+
+def quant_sweep(steps: int = 10):
+    """Quantize-only bandwidth on 32768x8192 tensors (N(0,1) and Student-t):
+    1D / 2D x RTN / SR, RHT on / off.  Returns GB/s per variant."""
+    dev = torch.device("cuda")
+    g = torch.Generator(device=dev).manual_seed(0)
+    R, C = 32768, 8192
+    out = {}
+    for dist in ["normal", "t3"]:
+        if dist == "normal":
+            x = torch.randn(R, C, generator=g, device=dev).to(torch.bfloat16)
+        else:
+            z = torch.randn(4, R, C, generator=g, device=dev)
+            x = (z[0] / torch.sqrt((z[1] ** 2 + z[2] ** 2 + z[3] ** 2) / 3)).to(torch.bfloat16)
+            del z
+        n = x.numel()
+        q1 = nv.quantize_1d(x)
+        q2 = nv.quantize_2d(x)
+        qc = nv.quantize_1d(x, nv.NVFP4_COLWISE)
+        G = nv.NVFP4_AMAX_GIVEN
+        variants = [
+            ("amax", 2 * n, lambda: nv.nvfp4_amax(x, q1.amax)),
+            ("1d RTN encode", 2.5625 * n, lambda: nv.nvfp4_quantize1d_rtn(
+                x, 0, q1.amax, G, q1.codes, q1.scales, q1.tensor_scale)),
+            ("1d SR encode", 2.5625 * n, lambda: nv.nvfp4_quantize1d_sr(
+                x, 0, q1.amax, G, 7, 0, q1.codes, q1.scales, q1.tensor_scale)),
+            ("2d RTN encode", 2.50390625 * n, lambda: nv.nvfp4_quantize2d_rtn(
+                x, q2.amax, G, q2.codes, None, q2.scales, q2.tensor_scale)),
+            ("2d RTN encode +codes_t", 3.00390625 * n, lambda: nv.nvfp4_quantize2d_rtn(
+                x, q2.amax, G, q2.codes, q2.codes_t, q2.scales, q2.tensor_scale)),
+            ("col RTN encode", 2.5625 * n, lambda: nv.nvfp4_quantize1d_rtn(
+                x, 1, qc.amax, G, qc.codes, qc.scales, qc.tensor_scale)),
+            ("amax RHT", 2 * n, lambda: nv.nvfp4_amax_rht(x, 1, qc.amax)),
+            ("col RHT SR encode", 2.5625 * n, lambda: nv.nvfp4_rht_quantize(
+                x, 1, 1, 7, 0, qc.amax, G, qc.codes, qc.scales, qc.tensor_scale)),
+            ("1d RTN incl. amax", 4.5625 * n, lambda: nv.nvfp4_quantize1d_rtn(
+                x, 0, q1.amax, nv.NVFP4_AMAX_COMPUTE, q1.codes, q1.scales, q1.tensor_scale)),
+            ("RHT SR incl. amax", 4.5625 * n, lambda: nv.nvfp4_rht_quantize(
+                x, 1, 1, 7, 0, qc.amax, nv.NVFP4_AMAX_COMPUTE, qc.codes, qc.scales,
+                qc.tensor_scale)),
+        ]
+        s = torch.cuda.current_stream()
+        for name, nbytes, fn in variants:
+            fn()
+            ev = [torch.cuda.Event(enable_timing=True) for _ in range(steps + 1)]
+            s.synchronize()
+            for i in range(steps):
+                ev[i].record(s)
+                fn()
+            ev[steps].record(s)
+            s.synchronize()
+            ms = float(np.median([ev[i].elapsed_time(ev[i + 1]) for i in range(steps)]))
+            out[f"{dist} {name}"] = {"us": round(ms * 1e3, 1),
+                                     "GB/s": round(nbytes / (ms * 1e-3) / 1e9, 1),
+                                     "frac": round(nbytes / (ms * 1e-3) / 1e9 / HBM_PEAK_GBS, 3)}
+        del x, q1, q2, qc
+        torch.cuda.empty_cache()
+    return out
+
+
+def main():
+    ap = argparse.ArgumentParser(description=__doc__.split("\n")[0])
+    ap.add_argument("--gpus", type=int, default=1)
+    ap.add_argument("--steps", type=int, default=20)
+    ap.add_argument("--warmup", type=int, default=3)
+    ap.add_argument("--no-cpu-baseline", action="store_true")
+    ap.add_argument("--no-sweep", action="store_true")
+    ap.add_argument("--seed", type=int, default=0)
+    args = ap.parse_args()
+    if args.gpus != 1 or int(os.environ.get("WORLD_SIZE", "1")) != 1:
+        print("bench.py measures one GPU: this build has no multi-GPU path "
+              "(rerun with --gpus 1)", file=sys.stderr)
+        sys.exit(2)
+    if not torch.cuda.is_available():
+        print("bench.py needs a GPU", file=sys.stderr)
+        sys.exit(2)
+    nv.load_library()
+
+    log("generating inputs (host, seeded)")
+    wl = inputs.ffn_down(args.seed, TOKENS, HIDDEN, FFN)
+    xh, wh, dyh = wl.tensors["X"], wl.tensors["W"], wl.tensors["dY"]
+    dev = torch.device("cuda")
+    x, w, dy = xh.to(dev), wh.to(dev), dyh.to(dev)
+    step = Step(x, w, dy)
+    stream = torch.cuda.current_stream()
+
+    log(f"warmup {args.warmup}")
+    for _ in range(args.warmup):
+        step.run()
+    torch.cuda.synchronize()
+
+    nops = len(step.ops)
+    evs = [[torch.cuda.Event(enable_timing=True) for _ in range(nops + 1)]
+           for _ in range(args.steps)]
+    log(f"timing {args.steps} steps")
+    torch.cuda.synchronize()
+    t0 = time.perf_counter()
+    for k in range(args.steps):
+        step.run(evs[k])
+    torch.cuda.synchronize()
+    wall = time.perf_counter() - t0
+    per_op = np.array([[evs[k][i].elapsed_time(evs[k][i + 1]) for i in range(nops)]
+                       for k in range(args.steps)])  # ms
+    step_ms = float(np.mean([evs[k][0].elapsed_time(evs[k][nops]) for k in range(args.steps)]))
+    gemm_flops = sum(a for (_, kind, a, _) in step.ops if kind == "mfma")
+    value = gemm_flops / (step_ms * 1e-3) / 1e12
+
+    kernels = {}
+    for i, (name, kind, amount, _) in enumerate(step.ops):
+        ms = float(per_op[:, i].mean())
+        if kind == "hbm":
+            gbs = amount / (ms * 1e-3) / 1e9
+            kernels[name] = {"us": round(ms * 1e3, 1), "GB/s": round(gbs, 1),
+                             "frac_hbm": round(gbs / HBM_PEAK_GBS, 3)}
+        else:
+            tf = amount / (ms * 1e-3) / 1e12
+            kernels[name] = {"us": round(ms * 1e3, 1), "TFLOP/s": round(tf, 1),
+                             "frac_mfma": round(tf / MFMA_F16_PEAK_TFLOPS, 3)}
+    gemm_idx = [i for i, o in enumerate(step.ops) if o[1] == "mfma"]
+    gemm_ms = float(per_op[:, gemm_idx].mean())
+    gemm_flops_launch = gemm_flops / len(gemm_idx)
+    achieved = gemm_flops_launch / (gemm_ms * 1e-3) / 1e12
+    roofline = {"bound": "mfma", "kernel": "k_gemm (Fprop, Dgrad, Wgrad launches)",
+                "achieved": round(achieved, 1), "peak": MFMA_F16_PEAK_TFLOPS,
+                "unit": "TFLOP/s", "frac": round(achieved / MFMA_F16_PEAK_TFLOPS, 4),
+                "traffic": None}
+    quant_ms = float(per_op[:, [i for i in range(nops) if i not in gemm_idx]].sum(axis=1).mean())
+    quant_bytes = sum(a for (_, kind, a, _) in step.ops if kind == "hbm")
+
+    result = {
+        "metric": METRIC, "value": round(value, 2), "unit": "TFLOP/s", "n_gpus": 1,
+        "steps": args.steps, "warmup": args.warmup, "ms_per_step": round(step_ms, 4),
+        "higher_is_better": True, "scaling": "weak", "vs_baseline": None,
+        "dtype": "nvfp4 operands, fp16 mfma, fp32 accumulate", "data": "synthetic",
+        "config": {"workload": "NVFP4 linear fwd+bwd triple, FFN down-projection: "
+                               "X 8192x20480, W 5120x20480, dY 8192x5120 (bf16, seed 0)",
+                   "tokens": TOKENS, "in_features": FFN, "out_features": HIDDEN,
+                   "gemms": "Fprop 8192x5120x20480, Dgrad 8192x20480x5120, "
+                            "Wgrad 5120x20480x8192",
+                   "quantization": "X 1D RTN, W 2D RTN, dY 1D SR, Wgrad inputs RHT16 "
+                                   "(dY SR, X RTN)"},
+        "gemm_tflops": round(achieved, 1),
+        "quantize_gbs": round(quant_bytes / (quant_ms * 1e-3) / 1e9, 1),
+        "quantize_ms_per_step": round(quant_ms, 4),
+        "kernels": kernels,
+        "roofline": roofline,
+        "wall_s_timed": round(wall, 4),
+    }
+    if not args.no_sweep:
+        log("quantize sweep 32768x8192")
+        result["quantize_sweep_32768x8192"] = quant_sweep()
+    if not args.no_cpu_baseline:
+        log("cpu baseline (oracle) on a bounded sample")
+        result["cpu_baseline"] = cpu_baseline(xh, wh, dyh)
+    print(json.dumps(result), flush=True)
+
+
+if __name__ == "__main__":
+    main()

@@ -1,0 +1,283 @@
+"""NVFP4 quantization and the NVFP4-linear GEMM on MI355X (gfx950).
+
+A thin ctypes binding over ``libnvfp4.so`` (C ABI in ``include/nvfp4.h``).
+PyTorch provides device memory and the current HIP stream; every step of the
+path runs in the library's HIP kernels.  There is no CPU fallback: if the
+library is missing or no GPU is present, calls raise.
+
+Two layers:
+  * ``nvfp4_*`` functions with the C names and arguments (torch tensors in
+    place of pointers), for callers that manage their own buffers;
+  * ``quantize_1d`` / ``quantize_2d`` / ``rht_quantize`` / ``dequantize`` /
+    ``gemm``, which allocate outputs with ``torch.empty`` and return
+    :class:`NVFP4Tensor` operands.
+"""
+from __future__ import annotations
+
+import ctypes
+import os
+from dataclasses import dataclass
+from typing import Optional
+
+import torch
+
+_HERE = os.path.dirname(os.path.abspath(__file__))
+LIB_PATH = os.path.join(_HERE, "libnvfp4.so")
+
+NVFP4_OK, NVFP4_ERR_NULL, NVFP4_ERR_SHAPE, NVFP4_ERR_ALIGN, NVFP4_ERR_ARG, NVFP4_ERR_LAUNCH = (
+    0, -1, -2, -3, -4, -5)
+NVFP4_AMAX_COMPUTE, NVFP4_AMAX_GIVEN = 0, 1
+NVFP4_ROWWISE, NVFP4_COLWISE = 0, 1
+
+EXPORTED = ("nvfp4_amax", "nvfp4_amax_rht", "nvfp4_quantize1d_rtn", "nvfp4_quantize1d_sr",
+            "nvfp4_quantize2d_rtn", "nvfp4_quantize2d_sr", "nvfp4_rht_quantize",
+            "nvfp4_dequantize", "nvfp4_gemm", "nvfp4_status_string", "nvfp4_last_error")
+
+
+class NVFP4Error(RuntimeError):
+    def __init__(self, status: int, msg: str):
+        super().__init__(f"{msg} ({status})")
+        self.status = status
+
+
+class c_operand(ctypes.Structure):
+    """Mirror of ``nvfp4_operand``."""
+    _fields_ = [("codes", ctypes.c_void_p), ("ld_codes", ctypes.c_int64),
+                ("scales", ctypes.c_void_p), ("ss_row", ctypes.c_int64),
+                ("ss_k", ctypes.c_int64), ("blk_rows", ctypes.c_int32),
+                ("tensor_scale", ctypes.c_void_p), ("rows", ctypes.c_int64),
+                ("k", ctypes.c_int64)]
+
+
+_lib = None
+
+
+def load_library(path: str = LIB_PATH) -> ctypes.CDLL:
+    """Load libnvfp4.so (raises if it has not been built)."""
+    global _lib
+    if _lib is not None:
+        return _lib
+    if not os.path.exists(path):
+        raise RuntimeError(f"{path} is missing: build it with "
+                           f"`python -m bit_microscaled_numerics_amd.build`")
+    lib = ctypes.CDLL(path)
+    vp, i64, u64, u32, i32 = (ctypes.c_void_p, ctypes.c_int64, ctypes.c_uint64,
+                              ctypes.c_uint32, ctypes.c_int)
+    sigs = {
+        "nvfp4_amax": [vp, i64, i64, vp, vp],
+        "nvfp4_amax_rht": [vp, i64, i64, u64, vp, vp],
+        "nvfp4_quantize1d_rtn": [vp, i64, i64, i32, vp, i32, vp, vp, vp, vp],
+        "nvfp4_quantize1d_sr": [vp, i64, i64, i32, vp, i32, u64, u32, vp, vp, vp, vp],
+        "nvfp4_quantize2d_rtn": [vp, i64, i64, vp, i32, vp, vp, vp, vp, vp],
+        "nvfp4_quantize2d_sr": [vp, i64, i64, vp, i32, u64, u32, vp, vp, vp, vp, vp],
+        "nvfp4_rht_quantize": [vp, i64, i64, u64, i32, u64, u32, vp, i32, vp, vp, vp, vp],
+        "nvfp4_dequantize": [ctypes.POINTER(c_operand), vp, vp],
+        "nvfp4_gemm": [ctypes.POINTER(c_operand), ctypes.POINTER(c_operand), vp, i64, vp],
+    }
+    for name, args in sigs.items():
+        fn = getattr(lib, name)
+        fn.argtypes = args
+        fn.restype = ctypes.c_int
+    lib.nvfp4_status_string.argtypes = [ctypes.c_int]
+    lib.nvfp4_status_string.restype = ctypes.c_char_p
+    lib.nvfp4_last_error.argtypes = []
+    lib.nvfp4_last_error.restype = ctypes.c_char_p
+    _lib = lib
+    return lib
+
+
+def _check(status: int) -> None:
+    if status != NVFP4_OK:
+        lib = load_library()
+        raise NVFP4Error(status, f"{lib.nvfp4_status_string(status).decode()}: "
+                                 f"{lib.nvfp4_last_error().decode()}")
+
+
+def _p(t: Optional[torch.Tensor]):
+    return None if t is None else t.data_ptr()
+
+
+def _stream(stream=None):
+    s = torch.cuda.current_stream() if stream is None else stream
+    return s.cuda_stream
+
+
+def _dev_bf16(x: torch.Tensor, name: str):
+    if not x.is_cuda or x.dtype != torch.bfloat16 or x.dim() != 2 or not x.is_contiguous():
+        raise ValueError(f"{name} must be a contiguous 2-D bf16 CUDA tensor")
+
+
+# --------------------------------------------------------------------------- C names
+def nvfp4_amax(x, amax_out, stream=None):
+    _dev_bf16(x, "x")
+    _check(load_library().nvfp4_amax(_p(x), x.shape[0], x.shape[1], _p(amax_out), _stream(stream)))
+
+
+def nvfp4_amax_rht(x, rht_seed, amax_out, stream=None):
+    _dev_bf16(x, "x")
+    _check(load_library().nvfp4_amax_rht(_p(x), x.shape[0], x.shape[1], rht_seed, _p(amax_out),
+                                         _stream(stream)))
+
+
+def nvfp4_quantize1d_rtn(x, axis, amax_io, amax_mode, codes, scales, ts_out, stream=None):
+    _dev_bf16(x, "x")
+    _check(load_library().nvfp4_quantize1d_rtn(_p(x), x.shape[0], x.shape[1], axis, _p(amax_io),
+                                               amax_mode, _p(codes), _p(scales), _p(ts_out),
+                                               _stream(stream)))
+
+
+def nvfp4_quantize1d_sr(x, axis, amax_io, amax_mode, seed, stream_id, codes, scales, ts_out,
+                        stream=None):
+    _dev_bf16(x, "x")
+    _check(load_library().nvfp4_quantize1d_sr(_p(x), x.shape[0], x.shape[1], axis, _p(amax_io),
+                                              amax_mode, seed, stream_id, _p(codes), _p(scales),
+                                              _p(ts_out), _stream(stream)))
+
+
+def nvfp4_quantize2d_rtn(w, amax_io, amax_mode, codes, codes_t, scales, ts_out, stream=None):
+    _dev_bf16(w, "w")
+    _check(load_library().nvfp4_quantize2d_rtn(_p(w), w.shape[0], w.shape[1], _p(amax_io),
+                                               amax_mode, _p(codes), _p(codes_t), _p(scales),
+                                               _p(ts_out), _stream(stream)))
+
+
+def nvfp4_quantize2d_sr(w, amax_io, amax_mode, seed, stream_id, codes, codes_t, scales, ts_out,
+                        stream=None):
+    _dev_bf16(w, "w")
+    _check(load_library().nvfp4_quantize2d_sr(_p(w), w.shape[0], w.shape[1], _p(amax_io),
+                                              amax_mode, seed, stream_id, _p(codes), _p(codes_t),
+                                              _p(scales), _p(ts_out), _stream(stream)))
+
+
+def nvfp4_rht_quantize(x, rht_seed, use_sr, sr_seed, stream_id, amax_io, amax_mode, codes,
+                       scales, ts_out, stream=None):
+    _dev_bf16(x, "x")
+    _check(load_library().nvfp4_rht_quantize(_p(x), x.shape[0], x.shape[1], rht_seed,
+                                             int(use_sr), sr_seed, stream_id, _p(amax_io),
+                                             amax_mode, _p(codes), _p(scales), _p(ts_out),
+                                             _stream(stream)))
+
+
+def nvfp4_dequantize(q: "NVFP4Tensor", out, stream=None):
+    op = q.c_struct()
+    _check(load_library().nvfp4_dequantize(ctypes.byref(op), _p(out), _stream(stream)))
+
+
+def nvfp4_gemm(a: "NVFP4Tensor", b: "NVFP4Tensor", c, ldc: int, stream=None):
+    oa, ob = a.c_struct(), b.c_struct()
+    _check(load_library().nvfp4_gemm(ctypes.byref(oa), ctypes.byref(ob), _p(c), ldc,
+                                     _stream(stream)))
+
+
+# --------------------------------------------------------------------------- operands
+@dataclass
+class NVFP4Tensor:
+    """A quantized operand, logically [rows][k], K-contiguous (device tensors)."""
+    codes: torch.Tensor          # uint8 [rows][ld_codes]
+    scales: torch.Tensor         # uint8 E4M3 codes
+    tensor_scale: torch.Tensor   # float32 [1]
+    amax: torch.Tensor           # float32 [1]
+    rows: int
+    k: int
+    blk_rows: int = 1
+    ss_row: int = 0
+    ss_k: int = 1
+    codes_t: Optional[torch.Tensor] = None   # 2D weights: the same codes transposed
+
+    def c_struct(self) -> c_operand:
+        return c_operand(self.codes.data_ptr(), self.codes.shape[1], self.scales.data_ptr(),
+                         self.ss_row, self.ss_k, self.blk_rows, self.tensor_scale.data_ptr(),
+                         self.rows, self.k)
+
+    def t(self) -> "NVFP4Tensor":
+        """A 2D-quantized weight read as its transpose (the Dgrad operand)."""
+        if self.blk_rows != 16 or self.codes_t is None:
+            raise ValueError("only 2D operands quantized with codes_t can be transposed")
+        return NVFP4Tensor(self.codes_t, self.scales, self.tensor_scale, self.amax, self.k,
+                           self.rows, 16, self.ss_k, self.ss_row, self.codes)
+
+    def nbytes(self) -> int:
+        return self.codes.numel() + self.scales.numel()
+
+
+def _outputs(I, K, dev, scale_shape):
+    codes = torch.empty(I, K // 2, dtype=torch.uint8, device=dev)
+    scales = torch.empty(*scale_shape, dtype=torch.uint8, device=dev)
+    ts = torch.empty(1, dtype=torch.float32, device=dev)
+    return codes, scales, ts
+
+
+def _amax_arg(x, amax):
+    if amax is None:
+        return torch.empty(1, dtype=torch.float32, device=x.device), NVFP4_AMAX_COMPUTE
+    if isinstance(amax, torch.Tensor):
+        return amax, NVFP4_AMAX_GIVEN
+    return torch.tensor([float(amax)], dtype=torch.float32, device=x.device), NVFP4_AMAX_GIVEN
+
+
+def amax(x: torch.Tensor) -> torch.Tensor:
+    out = torch.empty(1, dtype=torch.float32, device=x.device)
+    nvfp4_amax(x, out)
+    return out
+
+
+def amax_rht(x: torch.Tensor, rht_seed: int) -> torch.Tensor:
+    out = torch.empty(1, dtype=torch.float32, device=x.device)
+    nvfp4_amax_rht(x, rht_seed, out)
+    return out
+
+
+def quantize_1d(x: torch.Tensor, axis: int = NVFP4_ROWWISE, sr_seed: Optional[int] = None,
+                stream_id: int = 0, amax=None) -> NVFP4Tensor:
+    """1D (16 along K) quantization; COLWISE gives the quantized transpose."""
+    _dev_bf16(x, "x")
+    R, C = x.shape
+    I, K = (C, R) if axis == NVFP4_COLWISE else (R, C)
+    codes, scales, ts = _outputs(I, K, x.device, (I, K // 16))
+    am, mode = _amax_arg(x, amax)
+    if sr_seed is None:
+        nvfp4_quantize1d_rtn(x, axis, am, mode, codes, scales, ts)
+    else:
+        nvfp4_quantize1d_sr(x, axis, am, mode, sr_seed, stream_id, codes, scales, ts)
+    return NVFP4Tensor(codes, scales, ts, am, I, K, 1, K // 16, 1)
+
+
+def quantize_2d(w: torch.Tensor, sr_seed: Optional[int] = None, stream_id: int = 0,
+                with_codes_t: bool = True, amax=None) -> NVFP4Tensor:
+    """2D (16x16 tile) quantization of a weight [rows][cols]."""
+    _dev_bf16(w, "w")
+    R, C = w.shape
+    codes, scales, ts = _outputs(R, C, w.device, (R // 16, C // 16))
+    codes_t = torch.empty(C, R // 2, dtype=torch.uint8, device=w.device) if with_codes_t else None
+    am, mode = _amax_arg(w, amax)
+    if sr_seed is None:
+        nvfp4_quantize2d_rtn(w, am, mode, codes, codes_t, scales, ts)
+    else:
+        nvfp4_quantize2d_sr(w, am, mode, sr_seed, stream_id, codes, codes_t, scales, ts)
+    return NVFP4Tensor(codes, scales, ts, am, R, C, 16, C // 16, 1, codes_t)
+
+
+def rht_quantize(x: torch.Tensor, rht_seed: int, sr_seed: Optional[int] = None,
+                 stream_id: int = 0, amax=None) -> NVFP4Tensor:
+    """Wgrad operand: quantized transpose of RHT(x) along the rows (tokens)."""
+    _dev_bf16(x, "x")
+    R, C = x.shape
+    codes, scales, ts = _outputs(C, R, x.device, (C, R // 16))
+    am, mode = _amax_arg(x, amax)
+    nvfp4_rht_quantize(x, rht_seed, sr_seed is not None, 0 if sr_seed is None else sr_seed,
+                       stream_id, am, mode, codes, scales, ts)
+    return NVFP4Tensor(codes, scales, ts, am, C, R, 1, R // 16, 1)
+
+
+def dequantize(q: NVFP4Tensor) -> torch.Tensor:
+    out = torch.empty(q.rows, q.k, dtype=torch.float32, device=q.codes.device)
+    nvfp4_dequantize(q, out)
+    return out
+
+
+def gemm(a: NVFP4Tensor, b: NVFP4Tensor, out: Optional[torch.Tensor] = None) -> torch.Tensor:
+    """C = s_a s_b A B^T in FP32, A [M][K], B [N][K]."""
+    if out is None:
+        out = torch.empty(a.rows, b.rows, dtype=torch.float32, device=a.codes.device)
+    nvfp4_gemm(a, b, out, out.stride(0))
+    return out

@@ -1,0 +1,253 @@
+// nvfp4_api.cpp -- the C ABI of libnvfp4.so (declared in include/nvfp4.h):
+// argument validation, then kernel launches on the caller's stream.  Nothing
+// here allocates, frees or synchronises.
+#include "../../include/nvfp4.h"
+
+#include <hip/hip_runtime.h>
+
+#include <atomic>
+#include <cstdarg>
+#include <cstdio>
+#include <cstdlib>
+#include <cstring>
+
+#include "nvfp4_kernels.h"
+
+namespace {
+
+thread_local char g_last_error[256] = "";
+
+int fail(int status, const char* fmt, ...) {
+  va_list ap;
+  va_start(ap, fmt);
+  vsnprintf(g_last_error, sizeof g_last_error, fmt, ap);
+  va_end(ap);
+  return status;
+}
+
+bool aligned(const void* p, uintptr_t a) { return (reinterpret_cast<uintptr_t>(p) % a) == 0; }
+
+int check_tensor(const void* x, int64_t rows, int64_t cols, const char* name) {
+  if (x == nullptr) return fail(NVFP4_ERR_NULL, "%s is NULL", name);
+  if (rows <= 0 || cols <= 0 || rows % 16 || cols % 16)
+    return fail(NVFP4_ERR_SHAPE, "%s: rows=%lld cols=%lld must be positive multiples of 16", name,
+                (long long)rows, (long long)cols);
+  if (!aligned(x, 16)) return fail(NVFP4_ERR_ALIGN, "%s must be 16-byte aligned", name);
+  return NVFP4_OK;
+}
+
+int check_outputs(const void* codes, const void* scales, const float* amax_io,
+                  const float* ts_out) {
+  if (codes == nullptr) return fail(NVFP4_ERR_NULL, "codes is NULL");
+  if (scales == nullptr) return fail(NVFP4_ERR_NULL, "scales_e4m3 is NULL");
+  if (amax_io == nullptr) return fail(NVFP4_ERR_NULL, "amax_io is NULL");
+  if (ts_out == nullptr) return fail(NVFP4_ERR_NULL, "tensor_scale_out is NULL");
+  if (!aligned(codes, 16)) return fail(NVFP4_ERR_ALIGN, "codes must be 16-byte aligned");
+  if (!aligned(amax_io, 4) || !aligned(ts_out, 4))
+    return fail(NVFP4_ERR_ALIGN, "amax_io / tensor_scale_out must be 4-byte aligned");
+  return NVFP4_OK;
+}
+
+int launched(hipError_t e) {
+  if (e != hipSuccess) return fail(NVFP4_ERR_LAUNCH, "launch failed: %s", hipGetErrorString(e));
+  g_last_error[0] = '\0';
+  return NVFP4_OK;
+}
+
+hipStream_t as_stream(void* s) { return reinterpret_cast<hipStream_t>(s); }
+
+// GEMM operand decode: the hardware FP4 convert (exponent) + FP16 mantissa
+// multiply by default; NVFP4_GEMM_DECODE=perm selects the byte-permute decode.
+int gemm_decode_mode() {
+  const char* e = std::getenv("NVFP4_GEMM_DECODE");
+  return (e != nullptr && std::strcmp(e, "perm") == 0) ? 1 : 0;
+}
+
+int check_operand(const nvfp4_operand* q, const char* name) {
+  if (q == nullptr) return fail(NVFP4_ERR_NULL, "%s is NULL", name);
+  if (q->codes == nullptr || q->scales == nullptr || q->tensor_scale == nullptr)
+    return fail(NVFP4_ERR_NULL, "%s: codes, scales and tensor_scale are required", name);
+  if (q->rows <= 0 || q->k <= 0 || q->rows % 16 || q->k % 16)
+    return fail(NVFP4_ERR_SHAPE, "%s: rows=%lld k=%lld must be positive multiples of 16", name,
+                (long long)q->rows, (long long)q->k);
+  if (q->ld_codes < q->k / 2)
+    return fail(NVFP4_ERR_SHAPE, "%s: ld_codes=%lld < k/2", name, (long long)q->ld_codes);
+  if (q->ld_codes % 8)
+    return fail(NVFP4_ERR_ALIGN, "%s: ld_codes=%lld must be a multiple of 8", name,
+                (long long)q->ld_codes);
+  if (!aligned(q->codes, 16)) return fail(NVFP4_ERR_ALIGN, "%s: codes must be 16-byte aligned", name);
+  if (q->blk_rows != 1 && q->blk_rows != 16)
+    return fail(NVFP4_ERR_ARG, "%s: blk_rows must be 1 or 16", name);
+  if (q->ss_row < 0 || q->ss_k < 0) return fail(NVFP4_ERR_ARG, "%s: negative scale stride", name);
+  return NVFP4_OK;
+}
+
+nvfp4::GemmOperand to_kernel(const nvfp4_operand* q) {
+  return nvfp4::GemmOperand{q->codes, q->ld_codes, q->scales, q->ss_row, q->ss_k,
+                            q->blk_rows, q->tensor_scale, q->rows};
+}
+
+}  // namespace
+
+namespace nvfp4 {
+int num_cus() {
+  static std::atomic<int> cache[64];
+  int dev = 0;
+  if (hipGetDevice(&dev) != hipSuccess || dev < 0 || dev >= 64) return 256;
+  int n = cache[dev].load(std::memory_order_relaxed);
+  if (n <= 0) {
+    if (hipDeviceGetAttribute(&n, hipDeviceAttributeMultiprocessorCount, dev) != hipSuccess ||
+        n <= 0)
+      n = 256;
+    cache[dev].store(n, std::memory_order_relaxed);
+  }
+  return n;
+}
+}  // namespace nvfp4
+
+extern "C" {
+
+const char* nvfp4_status_string(int status) {
+  switch (status) {
+    case NVFP4_OK: return "NVFP4_OK";
+    case NVFP4_ERR_NULL: return "NVFP4_ERR_NULL";
+    case NVFP4_ERR_SHAPE: return "NVFP4_ERR_SHAPE";
+    case NVFP4_ERR_ALIGN: return "NVFP4_ERR_ALIGN";
+    case NVFP4_ERR_ARG: return "NVFP4_ERR_ARG";
+    case NVFP4_ERR_LAUNCH: return "NVFP4_ERR_LAUNCH";
+    default: return "NVFP4_ERR_UNKNOWN";
+  }
+}
+
+const char* nvfp4_last_error(void) { return g_last_error; }
+
+int nvfp4_amax(const void* x, int64_t rows, int64_t cols, float* amax_out, void* stream) {
+  int st = check_tensor(x, rows, cols, "x");
+  if (st) return st;
+  if (amax_out == nullptr) return fail(NVFP4_ERR_NULL, "amax_out is NULL");
+  if (!aligned(amax_out, 4)) return fail(NVFP4_ERR_ALIGN, "amax_out must be 4-byte aligned");
+  return launched(nvfp4::launch_amax(x, rows * cols, amax_out, as_stream(stream)));
+}
+
+int nvfp4_amax_rht(const void* x, int64_t rows, int64_t cols, uint64_t rht_seed, float* amax_out,
+                   void* stream) {
+  int st = check_tensor(x, rows, cols, "x");
+  if (st) return st;
+  if (amax_out == nullptr) return fail(NVFP4_ERR_NULL, "amax_out is NULL");
+  if (!aligned(amax_out, 4)) return fail(NVFP4_ERR_ALIGN, "amax_out must be 4-byte aligned");
+  return launched(nvfp4::launch_amax_rht(x, rows, cols, rht_seed, amax_out, as_stream(stream)));
+}
+
+static int quantize1d(const void* x, int64_t rows, int64_t cols, int axis, float* amax_io,
+                      int amax_mode, bool sr, uint64_t seed, uint32_t stream_id, uint8_t* codes,
+                      uint8_t* scales, float* ts_out, void* stream) {
+  int st = check_tensor(x, rows, cols, "x");
+  if (st) return st;
+  if ((st = check_outputs(codes, scales, amax_io, ts_out))) return st;
+  if (axis != NVFP4_ROWWISE && axis != NVFP4_COLWISE)
+    return fail(NVFP4_ERR_ARG, "axis=%d is neither NVFP4_ROWWISE nor NVFP4_COLWISE", axis);
+  if (amax_mode != NVFP4_AMAX_COMPUTE && amax_mode != NVFP4_AMAX_GIVEN)
+    return fail(NVFP4_ERR_ARG, "amax_mode=%d out of range", amax_mode);
+  hipStream_t s = as_stream(stream);
+  if (amax_mode == NVFP4_AMAX_COMPUTE) {
+    hipError_t e = nvfp4::launch_amax(x, rows * cols, amax_io, s);
+    if (e != hipSuccess) return launched(e);
+  }
+  if (axis == NVFP4_ROWWISE)
+    return launched(nvfp4::launch_quant_row(x, rows, cols, amax_io, sr, seed, stream_id, codes,
+                                            scales, ts_out, s));
+  return launched(nvfp4::launch_quant_col(x, rows, cols, amax_io, false, 0, sr, seed, stream_id,
+                                          codes, scales, ts_out, s));
+}
+
+int nvfp4_quantize1d_rtn(const void* x, int64_t rows, int64_t cols, int axis, float* amax_io,
+                         int amax_mode, uint8_t* codes, uint8_t* scales, float* ts_out,
+                         void* stream) {
+  return quantize1d(x, rows, cols, axis, amax_io, amax_mode, false, 0, 0, codes, scales, ts_out,
+                    stream);
+}
+
+int nvfp4_quantize1d_sr(const void* x, int64_t rows, int64_t cols, int axis, float* amax_io,
+                        int amax_mode, uint64_t seed, uint32_t stream_id, uint8_t* codes,
+                        uint8_t* scales, float* ts_out, void* stream) {
+  return quantize1d(x, rows, cols, axis, amax_io, amax_mode, true, seed, stream_id, codes, scales,
+                    ts_out, stream);
+}
+
+static int quantize2d(const void* w, int64_t rows, int64_t cols, float* amax_io, int amax_mode,
+                      bool sr, uint64_t seed, uint32_t stream_id, uint8_t* codes,
+                      uint8_t* codes_t, uint8_t* scales, float* ts_out, void* stream) {
+  int st = check_tensor(w, rows, cols, "w");
+  if (st) return st;
+  if ((st = check_outputs(codes, scales, amax_io, ts_out))) return st;
+  if (codes_t != nullptr && !aligned(codes_t, 16))
+    return fail(NVFP4_ERR_ALIGN, "codes_t must be 16-byte aligned");
+  if (amax_mode != NVFP4_AMAX_COMPUTE && amax_mode != NVFP4_AMAX_GIVEN)
+    return fail(NVFP4_ERR_ARG, "amax_mode=%d out of range", amax_mode);
+  hipStream_t s = as_stream(stream);
+  if (amax_mode == NVFP4_AMAX_COMPUTE) {
+    hipError_t e = nvfp4::launch_amax(w, rows * cols, amax_io, s);
+    if (e != hipSuccess) return launched(e);
+  }
+  return launched(nvfp4::launch_quant_2d(w, rows, cols, amax_io, sr, seed, stream_id, codes,
+                                         codes_t, scales, ts_out, s));
+}
+
+int nvfp4_quantize2d_rtn(const void* w, int64_t rows, int64_t cols, float* amax_io, int amax_mode,
+                         uint8_t* codes, uint8_t* codes_t, uint8_t* scales, float* ts_out,
+                         void* stream) {
+  return quantize2d(w, rows, cols, amax_io, amax_mode, false, 0, 0, codes, codes_t, scales,
+                    ts_out, stream);
+}
+
+int nvfp4_quantize2d_sr(const void* w, int64_t rows, int64_t cols, float* amax_io, int amax_mode,
+                        uint64_t seed, uint32_t stream_id, uint8_t* codes, uint8_t* codes_t,
+                        uint8_t* scales, float* ts_out, void* stream) {
+  return quantize2d(w, rows, cols, amax_io, amax_mode, true, seed, stream_id, codes, codes_t,
+                    scales, ts_out, stream);
+}
+
+int nvfp4_rht_quantize(const void* x, int64_t rows, int64_t cols, uint64_t rht_seed, int use_sr,
+                       uint64_t sr_seed, uint32_t stream_id, float* amax_io, int amax_mode,
+                       uint8_t* codes, uint8_t* scales, float* ts_out, void* stream) {
+  int st = check_tensor(x, rows, cols, "x");
+  if (st) return st;
+  if ((st = check_outputs(codes, scales, amax_io, ts_out))) return st;
+  if (use_sr != 0 && use_sr != 1) return fail(NVFP4_ERR_ARG, "use_sr=%d must be 0 or 1", use_sr);
+  if (amax_mode != NVFP4_AMAX_COMPUTE && amax_mode != NVFP4_AMAX_GIVEN)
+    return fail(NVFP4_ERR_ARG, "amax_mode=%d out of range", amax_mode);
+  hipStream_t s = as_stream(stream);
+  if (amax_mode == NVFP4_AMAX_COMPUTE) {
+    hipError_t e = nvfp4::launch_amax_rht(x, rows, cols, rht_seed, amax_io, s);
+    if (e != hipSuccess) return launched(e);
+  }
+  return launched(nvfp4::launch_quant_col(x, rows, cols, amax_io, true, rht_seed, use_sr == 1,
+                                          sr_seed, stream_id, codes, scales, ts_out, s));
+}
+
+int nvfp4_dequantize(const nvfp4_operand* q, float* out, void* stream) {
+  int st = check_operand(q, "q");
+  if (st) return st;
+  if (out == nullptr) return fail(NVFP4_ERR_NULL, "out is NULL");
+  if (!aligned(out, 16)) return fail(NVFP4_ERR_ALIGN, "out must be 16-byte aligned");
+  return launched(nvfp4::launch_dequant(q->codes, q->ld_codes, q->scales, q->ss_row, q->ss_k,
+                                        q->blk_rows, q->tensor_scale, q->rows, q->k, out,
+                                        as_stream(stream)));
+}
+
+int nvfp4_gemm(const nvfp4_operand* a, const nvfp4_operand* b, float* c, int64_t ldc,
+               void* stream) {
+  int st = check_operand(a, "a");
+  if (st) return st;
+  if ((st = check_operand(b, "b"))) return st;
+  if (a->k != b->k)
+    return fail(NVFP4_ERR_SHAPE, "a.k=%lld != b.k=%lld", (long long)a->k, (long long)b->k);
+  if (c == nullptr) return fail(NVFP4_ERR_NULL, "c is NULL");
+  if (!aligned(c, 4)) return fail(NVFP4_ERR_ALIGN, "c must be 4-byte aligned");
+  if (ldc < b->rows) return fail(NVFP4_ERR_SHAPE, "ldc=%lld < N=%lld", (long long)ldc,
+                                 (long long)b->rows);
+  return launched(nvfp4::launch_gemm(to_kernel(a), to_kernel(b), a->k, c, ldc,
+                                     gemm_decode_mode(), as_stream(stream)));
+}
+
+}  // extern "C"

@@ -1,0 +1,228 @@
+// nvfp4_device.h -- gfx950 device helpers for the NVFP4 kernels: bf16
+// unpacking, E4M3 and E2M1 codecs, Philox4x32-10 and the 16-point Hadamard
+// butterfly.  Every routine is IEEE binary32 with round-to-nearest-even; the
+// kernels are built with -ffp-contract=off so no multiply-add is fused.
+//
+// Sources (web pages, cited by title and section):
+//  [PAPER] "Pretraining Large Language Models with NVFP4", summary page:
+//          format paragraph (E2M1 elements, E4M3 per 16, FP32 tensor scale).
+//  [BLOG]  "NVFP4 Trains with Precision of 16-Bit and Speed and Efficiency of
+//          4-Bit": E4M3 scale factors; Hadamard transforms; stochastic
+//          rounding.
+//  [SC11]  Salmon et al., "Parallel random numbers: as easy as 1, 2, 3".
+#pragma once
+
+#include <hip/hip_runtime.h>
+#include <stdint.h>
+
+namespace nvfp4 {
+
+// Plain clang vector types (HIP's uint4 & co. are structs, which the memory
+// builtins do not take).
+typedef uint32_t v4u __attribute__((ext_vector_type(4)));
+typedef uint32_t v2u __attribute__((ext_vector_type(2)));
+typedef float v4f __attribute__((ext_vector_type(4)));
+
+// Global memory access points of the streaming kernels (one place to change
+// cache policy).
+template <class T>
+__device__ __forceinline__ T ld_(const T* p) { return *p; }
+template <class T>
+__device__ __forceinline__ void st_(T v, T* p) { *p = v; }
+
+// Tensor scale maps the tensor amax onto the largest block scale:
+// 6 (largest E2M1 magnitude) * 448 (largest E4M3 value).
+constexpr float kScaleDen = 2688.0f;
+
+__device__ __forceinline__ float bf16_lo(uint32_t w) { return __uint_as_float(w << 16); }
+__device__ __forceinline__ float bf16_hi(uint32_t w) { return __uint_as_float(w & 0xFFFF0000u); }
+
+// ---------------------------------------------------------------------------
+// E4M3 (OCP E4M3FN) -- [BLOG] E4M3 scale factors
+// ---------------------------------------------------------------------------
+// Non-negative binary32 -> E4M3FN code, round-to-nearest-even, saturating at
+// 448 (code 0x7E).  Subnormal range (x < 2^-6): the code is rint(x * 2^9),
+// an exact scaling; 8 there is the smallest normal.  Normal range: round the
+// binary32 mantissa to 3 bits (add half-ulp-minus-one plus the kept lsb) and
+// rebias the exponent from 127 to 7.
+__device__ __forceinline__ uint32_t e4m3_from_float(float x) {
+  if (!(x > 0.0f)) return 0u;
+  if (x >= 448.0f) return 0x7Eu;
+  if (x < 0.015625f) return (uint32_t)__builtin_rintf(x * 512.0f);
+  uint32_t u = __float_as_uint(x);
+  u += 0x7FFFFu + ((u >> 20) & 1u);
+  uint32_t e = (u >> 23) - 120u;  // 127 - 7
+  uint32_t m = (u >> 20) & 7u;
+  uint32_t c = (e << 3) | m;
+  return c > 0x7Eu ? 0x7Eu : c;
+}
+
+// E4M3FN code (0..0x7E) -> binary32 (branch-free: both forms are computed
+// and the exponent field selects; the subnormal form is m * 2^-9, exact).
+__device__ __forceinline__ float e4m3_to_float(uint32_t c) {
+  const uint32_t e = (c >> 3) & 15u, m = c & 7u;
+  const float sub = (float)m * 0.001953125f;
+  const float nrm = __uint_as_float(((e + 120u) << 23) | (m << 20));
+  return e == 0u ? sub : nrm;
+}
+
+// ---------------------------------------------------------------------------
+// E2M1 -- [PAPER] format paragraph: magnitudes 0, .5, 1, 1.5, 2, 3, 4, 6
+// ---------------------------------------------------------------------------
+// Round-to-nearest-even magnitude index of a >= 0, saturating at 6.  The
+// decision points are the midpoints between grid values; at a midpoint the
+// even index wins, so the comparison is >= where the upper neighbour has an
+// even index and > where it has an odd one.
+__device__ __forceinline__ uint32_t e2m1_rtn_index(float a) {
+  uint32_t i = 0;
+  i += (a > 0.25f);
+  i += (a >= 0.75f);
+  i += (a > 1.25f);
+  i += (a >= 1.75f);
+  i += (a > 2.5f);
+  i += (a >= 3.5f);
+  i += (a > 5.0f);
+  return i;
+}
+
+// Stochastic rounding of a >= 0 with 16 random bits u.  With lo <= a < hi the
+// neighbouring grid values and p = (a - lo)/(hi - lo), round up iff
+// u < p * 65536.  lo - a is exact (Sterbenz) and the gaps are powers of two,
+// so p and p * 65536 are exact.  a >= 6 gives index 7.
+__device__ __forceinline__ uint32_t e2m1_sr_index(float a, uint32_t u) {
+  a = a < 6.0f ? a : 6.0f;
+  uint32_t i = 0;
+  i += (a >= 0.5f);
+  i += (a >= 1.0f);
+  i += (a >= 1.5f);
+  i += (a >= 2.0f);
+  i += (a >= 3.0f);
+  i += (a >= 4.0f);
+  i += (a >= 6.0f);
+  // grid value of index i and the reciprocal of the gap above it
+  float lo = i < 4u ? 0.5f * (float)i : (i < 7u ? (float)i - 2.0f : 6.0f);
+  float inv_gap = i < 4u ? 2.0f : (i < 6u ? 1.0f : 0.5f);
+  float p65536 = (a - lo) * inv_gap * 65536.0f;
+  return i + (((float)u < p65536) ? 1u : 0u);
+}
+
+// ---------------------------------------------------------------------------
+// Philox4x32-10 -- [SC11]
+// ---------------------------------------------------------------------------
+struct u32x4 { uint32_t x, y, z, w; };
+
+__device__ __forceinline__ u32x4 philox4x32_10(u32x4 c, uint32_t k0, uint32_t k1) {
+#pragma unroll
+  for (int r = 0; r < 10; ++r) {
+    uint64_t p0 = (uint64_t)0xD2511F53u * c.x;
+    uint64_t p1 = (uint64_t)0xCD9E8D57u * c.z;
+    u32x4 n;
+    n.x = (uint32_t)(p1 >> 32) ^ c.y ^ k0;
+    n.y = (uint32_t)p1;
+    n.z = (uint32_t)(p0 >> 32) ^ c.w ^ k1;
+    n.w = (uint32_t)p0;
+    c = n;
+    k0 += 0x9E3779B9u;
+    k1 += 0xBB67AE85u;
+  }
+  return c;
+}
+
+// The four words for the 8 elements n0 .. n0+7 (n0 a multiple of 8).
+__device__ __forceinline__ u32x4 sr_words(uint64_t seed, uint32_t stream_id, uint64_t n0) {
+  uint64_t g = n0 >> 3;
+  u32x4 c = {(uint32_t)g, (uint32_t)(g >> 32), stream_id, 0u};
+  return philox4x32_10(c, (uint32_t)seed, (uint32_t)(seed >> 32));
+}
+
+__device__ __forceinline__ uint32_t rht_sign_bits(uint64_t rht_seed) {
+  u32x4 c = {0u, 0u, 0u, 1u};
+  return philox4x32_10(c, (uint32_t)rht_seed, (uint32_t)(rht_seed >> 32)).x & 0xFFFFu;
+}
+
+// ---------------------------------------------------------------------------
+// 16-point Hadamard -- [BLOG] Hadamard transforms
+// ---------------------------------------------------------------------------
+// v <- 1/4 * H16 * D * v: sign flips, then butterflies over index bits
+// 0, 1, 2, 3 (pairs j, j + h with bit h of j clear), then the exact * 1/4.
+__device__ __forceinline__ void rht16(float (&v)[16], uint32_t signs) {
+#pragma unroll
+  for (int j = 0; j < 16; ++j)
+    v[j] = __uint_as_float(__float_as_uint(v[j]) ^ (((signs >> j) & 1u) << 31));
+#pragma unroll
+  for (int h = 1; h < 16; h <<= 1) {
+#pragma unroll
+    for (int j = 0; j < 16; ++j) {
+      if (j & h) continue;
+      float a = v[j], b = v[j + h];
+      v[j] = a + b;
+      v[j + h] = a - b;
+    }
+  }
+#pragma unroll
+  for (int j = 0; j < 16; ++j) v[j] *= 0.25f;
+}
+
+// ---------------------------------------------------------------------------
+// Encoding one group of 8 elements given the block's reciprocal scale
+// ---------------------------------------------------------------------------
+// Codes of z[0..7] (element j in nibble j), round-to-nearest-even.
+__device__ __forceinline__ uint32_t encode8_rtn(const float* z, float r) {
+  uint32_t out = 0;
+#pragma unroll
+  for (int j = 0; j < 8; ++j) {
+    float v = z[j] * r;
+    uint32_t s = (__float_as_uint(v) >> 31) << 3;
+    out |= (s | e2m1_rtn_index(__builtin_fabsf(v))) << (4 * j);
+  }
+  return out;
+}
+
+// Stochastic rounding with the 8 16-bit halves of w (element j takes word
+// j/2, low half for even j).
+__device__ __forceinline__ uint32_t encode8_sr(const float* z, float r, u32x4 w) {
+  uint32_t words[4] = {w.x, w.y, w.z, w.w};
+  uint32_t out = 0;
+#pragma unroll
+  for (int j = 0; j < 8; ++j) {
+    float v = z[j] * r;
+    uint32_t s = (__float_as_uint(v) >> 31) << 3;
+    uint32_t u = (j & 1) ? (words[j >> 1] >> 16) : (words[j >> 1] & 0xFFFFu);
+    out |= (s | e2m1_sr_index(__builtin_fabsf(v), u)) << (4 * j);
+  }
+  return out;
+}
+
+// Sign-only codes for a block whose scale is zero.
+__device__ __forceinline__ uint32_t encode8_zero(const float* z) {
+  uint32_t out = 0;
+#pragma unroll
+  for (int j = 0; j < 8; ++j) out |= ((__float_as_uint(z[j]) >> 31) << 3) << (4 * j);
+  return out;
+}
+
+// Block scale code and reciprocal element scale from a block amax.
+struct BlockScale { uint32_t code; float r; };
+
+__device__ __forceinline__ BlockScale block_scale(float amax_b, float s_t, float t6) {
+  BlockScale b;
+  b.code = e4m3_from_float(amax_b / t6);
+  float d = e4m3_to_float(b.code) * s_t;
+  b.r = 1.0f / d;
+  return b;
+}
+
+__device__ __forceinline__ float tensor_scale_from_amax(float amax_t) {
+  return amax_t > 0.0f ? amax_t / kScaleDen : 1.0f;
+}
+
+// ---------------------------------------------------------------------------
+// Wave reductions (max of non-negative floats)
+// ---------------------------------------------------------------------------
+__device__ __forceinline__ float wave_max(float v) {
+#pragma unroll
+  for (int off = 32; off > 0; off >>= 1) v = fmaxf(v, __shfl_xor(v, off, 64));
+  return v;
+}
+
+}  // namespace nvfp4

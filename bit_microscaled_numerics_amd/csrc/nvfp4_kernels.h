@@ -1,0 +1,44 @@
+// nvfp4_kernels.h -- launch functions of the gfx950 kernels (internal to
+// libnvfp4.so; the public interface is include/nvfp4.h).
+#pragma once
+
+#include <hip/hip_runtime.h>
+#include <stdint.h>
+
+namespace nvfp4 {
+
+int num_cus();  // compute units of the current device (cached per device)
+
+hipError_t launch_amax(const void* x, int64_t n_elems, float* out, hipStream_t s);
+hipError_t launch_amax_rht(const void* x, int64_t rows, int64_t cols, uint64_t rht_seed,
+                           float* out, hipStream_t s);
+hipError_t launch_quant_row(const void* x, int64_t rows, int64_t cols, const float* amax,
+                            bool sr, uint64_t seed, uint32_t stream_id, uint8_t* codes,
+                            uint8_t* scales, float* ts_out, hipStream_t s);
+hipError_t launch_quant_col(const void* x, int64_t rows, int64_t cols, const float* amax,
+                            bool rht, uint64_t rht_seed, bool sr, uint64_t seed,
+                            uint32_t stream_id, uint8_t* codes, uint8_t* scales, float* ts_out,
+                            hipStream_t s);
+hipError_t launch_quant_2d(const void* x, int64_t rows, int64_t cols, const float* amax, bool sr,
+                           uint64_t seed, uint32_t stream_id, uint8_t* codes, uint8_t* codes_t,
+                           uint8_t* scales, float* ts_out, hipStream_t s);
+hipError_t launch_dequant(const uint8_t* codes, int64_t ld_codes, const uint8_t* scales,
+                          int64_t ss_row, int64_t ss_k, int32_t blk_rows, const float* ts,
+                          int64_t rows, int64_t k, float* out, hipStream_t s);
+
+// One GEMM operand as the kernels see it.
+struct GemmOperand {
+  const uint8_t* codes;
+  int64_t ld;  // bytes per row
+  const uint8_t* scales;
+  int64_t ss_row, ss_k;
+  int32_t blk_rows;
+  const float* ts;
+  int64_t rows;
+};
+
+// decode: 0 = hardware FP4 convert with FP32 scale, 1 = byte-permute decode
+hipError_t launch_gemm(const GemmOperand& a, const GemmOperand& b, int64_t K, float* c,
+                       int64_t ldc, int decode, hipStream_t s);
+
+}  // namespace nvfp4

@@ -1,0 +1,424 @@
+// nvfp4_quant.hip -- gfx950 kernels for NVFP4 quantization: tensor amax (plain
+// and under the 16-point RHT), 1D rowwise, 1D colwise (transpose-quantize,
+// optional RHT), 2D 16x16 tiles (optional transposed codes) and dequantize.
+//
+// All are HBM-bound: 16-byte loads (8 bf16 per lane), lanes of a wave on
+// consecutive 16-byte chunks, packed 4-bit stores, no re-reads inside a pass.
+// The tensor scale is re-derived from the device amax by every workgroup, so
+// no host round trip separates the amax pass from the encode pass.
+//
+// Sources: "Pretraining Large Language Models with NVFP4" (summary page,
+// format and limitations paragraphs); "NVFP4 Trains with Precision of 16-Bit
+// and Speed and Efficiency of 4-Bit" (micro-block scaling, E4M3 scales,
+// Hadamard transforms, 2D block quantization, stochastic rounding); news item
+// "Soumith Chintala 发布 NVFP4 训练详解文章", section 三 (1D blocks for
+// activations and gradients, 2D for weights, RHT on Wgrad inputs).
+#include "nvfp4_device.h"
+#include "nvfp4_kernels.h"
+
+namespace nvfp4 {
+
+constexpr int kThreads = 256;
+
+// ---------------------------------------------------------------------------
+// amax
+// ---------------------------------------------------------------------------
+__global__ void k_zero_u32(uint32_t* p) { *p = 0u; }
+
+// Block-wide max of non-negative float bit patterns, then one atomic per
+// workgroup.  Non-negative binary32 values order like their bit patterns.
+__device__ __forceinline__ void block_max_atomic(uint32_t m, uint32_t* out) {
+  __shared__ uint32_t red[kThreads / 64];
+#pragma unroll
+  for (int off = 32; off > 0; off >>= 1) {
+    uint32_t o = (uint32_t)__shfl_xor((int)m, off, 64);
+    m = m > o ? m : o;
+  }
+  const int wave = threadIdx.x >> 6;
+  if ((threadIdx.x & 63) == 0) red[wave] = m;
+  __syncthreads();
+  if (threadIdx.x == 0) {
+    uint32_t r = red[0];
+#pragma unroll
+    for (int w = 1; w < kThreads / 64; ++w) r = r > red[w] ? r : red[w];
+    atomicMax(out, r);
+  }
+}
+
+// |x| of bf16 is its bit pattern with the sign cleared, and non-negative bf16
+// patterns order like their values: the amax runs on packed 16-bit integer
+// maxima (two elements per 32-bit lane op).
+__device__ __forceinline__ uint32_t pk_max_u16(uint32_t a, uint32_t b) {
+  uint32_t lo = (a & 0xFFFFu) > (b & 0xFFFFu) ? (a & 0xFFFFu) : (b & 0xFFFFu);
+  uint32_t hi = (a >> 16) > (b >> 16) ? (a >> 16) : (b >> 16);
+  return lo | (hi << 16);
+}
+
+__global__ __launch_bounds__(kThreads) void k_amax(const v4u* __restrict__ x, int64_t nvec,
+                                                     uint32_t* __restrict__ out) {
+  uint32_t m = 0;
+  const int64_t stride = (int64_t)gridDim.x * kThreads;
+  int64_t i = (int64_t)blockIdx.x * kThreads + threadIdx.x;
+  for (; i + 3 * stride < nvec; i += 4 * stride) {
+    v4u v[4];
+#pragma unroll
+    for (int u = 0; u < 4; ++u) v[u] = ld_(&x[i + u * stride]);
+#pragma unroll
+    for (int u = 0; u < 4; ++u) {
+      m = pk_max_u16(m, v[u].x & 0x7FFF7FFFu);
+      m = pk_max_u16(m, v[u].y & 0x7FFF7FFFu);
+      m = pk_max_u16(m, v[u].z & 0x7FFF7FFFu);
+      m = pk_max_u16(m, v[u].w & 0x7FFF7FFFu);
+    }
+  }
+  for (; i < nvec; i += stride) {
+    v4u v = ld_(&x[i]);
+    m = pk_max_u16(m, v.x & 0x7FFF7FFFu);
+    m = pk_max_u16(m, v.y & 0x7FFF7FFFu);
+    m = pk_max_u16(m, v.z & 0x7FFF7FFFu);
+    m = pk_max_u16(m, v.w & 0x7FFF7FFFu);
+  }
+  uint32_t lo = m & 0xFFFFu, hi = m >> 16;
+  uint32_t bf = lo > hi ? lo : hi;
+  block_max_atomic(bf << 16, out);
+}
+
+// Load a 16-row x 8-column bf16 micro-tile (one 16-byte chunk per row) and
+// return column j's 16 values as binary32.
+struct Tile16x8 { v4u row[16]; };
+
+__device__ __forceinline__ void tile_load(Tile16x8& t, const uint16_t* __restrict__ x,
+                                          int64_t cols, int64_t r0, int64_t c0) {
+#pragma unroll
+  for (int j = 0; j < 16; ++j)
+    t.row[j] = ld_(
+        reinterpret_cast<const v4u*>(x + (r0 + j) * cols + c0));
+}
+
+__device__ __forceinline__ void tile_column(const Tile16x8& t, int c, float (&v)[16]) {
+#pragma unroll
+  for (int j = 0; j < 16; ++j) {
+    uint32_t w = (c >> 1) == 0 ? t.row[j].x : (c >> 1) == 1 ? t.row[j].y
+               : (c >> 1) == 2 ? t.row[j].z : t.row[j].w;
+    v[j] = (c & 1) ? bf16_hi(w) : bf16_lo(w);
+  }
+}
+
+// amax of RHT(x^T): each work item is 16 consecutive rows x 8 columns.
+__global__ __launch_bounds__(kThreads) void k_amax_rht(const uint16_t* __restrict__ x,
+                                                         int64_t rows, int64_t cols,
+                                                         uint64_t rht_seed,
+                                                         uint32_t* __restrict__ out) {
+  const uint32_t signs = rht_sign_bits(rht_seed);
+  const int64_t cg_n = cols / 8, items = (rows / 16) * cg_n;
+  float m = 0.0f;
+  for (int64_t it = (int64_t)blockIdx.x * kThreads + threadIdx.x; it < items;
+       it += (int64_t)gridDim.x * kThreads) {
+    const int64_t rg = it / cg_n, cg = it - rg * cg_n;
+    Tile16x8 t;
+    tile_load(t, x, cols, rg * 16, cg * 8);
+#pragma unroll
+    for (int c = 0; c < 8; ++c) {
+      float v[16];
+      tile_column(t, c, v);
+      rht16(v, signs);
+#pragma unroll
+      for (int j = 0; j < 16; ++j) m = fmaxf(m, __builtin_fabsf(v[j]));
+    }
+  }
+  block_max_atomic(__float_as_uint(m), out);
+}
+
+// ---------------------------------------------------------------------------
+// 1D rowwise: blocks of 16 along cols, two lanes per block
+// ---------------------------------------------------------------------------
+template <bool SR>
+__global__ __launch_bounds__(kThreads) void k_quant_row(
+    const v4u* __restrict__ x, int64_t nvec, const float* __restrict__ amax,
+    uint64_t seed, uint32_t stream_id, uint32_t* __restrict__ codes,
+    uint8_t* __restrict__ scales, float* __restrict__ ts_out) {
+  const float s_t = tensor_scale_from_amax(*amax);
+  const float t6 = 6.0f * s_t;
+  if (blockIdx.x == 0 && threadIdx.x == 0) *ts_out = s_t;
+  const int64_t stride = (int64_t)gridDim.x * kThreads;  // even: lane pairs stay together
+  for (int64_t i = (int64_t)blockIdx.x * kThreads + threadIdx.x; i < nvec; i += stride) {
+    const v4u v = ld_(&x[i]);
+    float z[8] = {bf16_lo(v.x), bf16_hi(v.x), bf16_lo(v.y), bf16_hi(v.y),
+                  bf16_lo(v.z), bf16_hi(v.z), bf16_lo(v.w), bf16_hi(v.w)};
+    float m = 0.0f;
+#pragma unroll
+    for (int j = 0; j < 8; ++j) m = fmaxf(m, __builtin_fabsf(z[j]));
+    m = fmaxf(m, __shfl_xor(m, 1, 64));
+    const BlockScale b = block_scale(m, s_t, t6);
+    uint32_t q;
+    if (b.code == 0u) q = encode8_zero(z);
+    else if (SR) q = encode8_sr(z, b.r, sr_words(seed, stream_id, (uint64_t)i * 8u));
+    else q = encode8_rtn(z, b.r);
+    st_(q, &codes[i]);
+    if ((i & 1) == 0) scales[i >> 1] = (uint8_t)b.code;
+  }
+}
+
+// ---------------------------------------------------------------------------
+// 1D colwise (transpose-quantize), optional RHT along the rows
+// ---------------------------------------------------------------------------
+// Workgroup tile: 256 rows (K) x 128 columns.  Thread t owns 16 rows x 8
+// columns (cg = t % 16, rg = t / 16); a wave's loads cover 4 rows x 256
+// contiguous bytes each.  Codes are staged in LDS as [column][row/2] so the
+// stores run along the output's contiguous dimension.
+constexpr int kColTileR = 256, kColTileC = 128;
+
+template <bool SR, bool RHT>
+__global__ __launch_bounds__(kThreads) void k_quant_col(
+    const uint16_t* __restrict__ x, int64_t rows, int64_t cols,
+    const float* __restrict__ amax, uint64_t rht_seed, uint64_t seed, uint32_t stream_id,
+    uint8_t* __restrict__ codes, uint8_t* __restrict__ scales, float* __restrict__ ts_out) {
+  __shared__ v2u lds_codes[kColTileC][kColTileR / 16];   // 8 bytes = 16 codes per block
+  __shared__ uint8_t lds_scales[kColTileC][kColTileR / 16];
+  const float s_t = tensor_scale_from_amax(*amax);
+  const float t6 = 6.0f * s_t;
+  if (blockIdx.x == 0 && blockIdx.y == 0 && threadIdx.x == 0) *ts_out = s_t;
+  const uint32_t signs = RHT ? rht_sign_bits(rht_seed) : 0u;
+  const int64_t r0 = (int64_t)blockIdx.y * kColTileR, c0 = (int64_t)blockIdx.x * kColTileC;
+  const int cg = threadIdx.x & 15, rg = threadIdx.x >> 4;
+  const int64_t rr = r0 + 16 * rg, cc = c0 + 8 * cg;
+  if (rr < rows && cc < cols) {
+    Tile16x8 t;
+    tile_load(t, x, cols, rr, cc);
+#pragma unroll
+    for (int c = 0; c < 8; ++c) {
+      float v[16];
+      tile_column(t, c, v);
+      if (RHT) rht16(v, signs);
+      float m = 0.0f;
+#pragma unroll
+      for (int j = 0; j < 16; ++j) m = fmaxf(m, __builtin_fabsf(v[j]));
+      const BlockScale b = block_scale(m, s_t, t6);
+      uint32_t q0, q1;
+      if (b.code == 0u) {
+        q0 = encode8_zero(v);
+        q1 = encode8_zero(v + 8);
+      } else if (SR) {
+        const uint64_t n0 = (uint64_t)(cc + c) * (uint64_t)rows + (uint64_t)rr;
+        q0 = encode8_sr(v, b.r, sr_words(seed, stream_id, n0));
+        q1 = encode8_sr(v + 8, b.r, sr_words(seed, stream_id, n0 + 8));
+      } else {
+        q0 = encode8_rtn(v, b.r);
+        q1 = encode8_rtn(v + 8, b.r);
+      }
+      lds_codes[8 * cg + c][rg] = v2u{q0, q1};
+      lds_scales[8 * cg + c][rg] = (uint8_t)b.code;
+    }
+  }
+  __syncthreads();
+  // 2048 (column, row-group) pieces per tile; 16 consecutive threads write one
+  // column's 128 contiguous code bytes and 16 contiguous scale bytes.
+  const int64_t ld_codes = rows / 2, ld_scales = rows / 16;
+#pragma unroll
+  for (int j = 0; j < (kColTileC * kColTileR / 16) / kThreads; ++j) {
+    const int p = threadIdx.x + kThreads * j;
+    const int col = p >> 4, g = p & 15;
+    const int64_t oc = c0 + col, orow = r0 + 16 * g;
+    if (oc < cols && orow < rows) {
+      st_(lds_codes[col][g],
+                                  reinterpret_cast<v2u*>(codes + oc * ld_codes + orow / 2));
+      scales[oc * ld_scales + orow / 16] = lds_scales[col][g];
+    }
+  }
+}
+
+// ---------------------------------------------------------------------------
+// 2D: 16x16 tiles, one lane per tile row (16 lanes per tile)
+// ---------------------------------------------------------------------------
+// Workgroup: 64 rows x 64 columns (4 x 4 tiles); wave w holds tile row w,
+// lane = r + 16 * tc.  The tile amax is a 16-lane xor reduction.  The
+// transposed codes go through LDS as bytes [column][row] and are packed by
+// columns.
+template <bool SR>
+__global__ __launch_bounds__(kThreads) void k_quant_2d(
+    const uint16_t* __restrict__ x, int64_t rows, int64_t cols,
+    const float* __restrict__ amax, uint64_t seed, uint32_t stream_id,
+    uint8_t* __restrict__ codes, uint8_t* __restrict__ codes_t, uint8_t* __restrict__ scales,
+    float* __restrict__ ts_out) {
+  __shared__ uint8_t lds_t[64][64 + 16];  // [column][row]; padded rows
+  const float s_t = tensor_scale_from_amax(*amax);
+  const float t6 = 6.0f * s_t;
+  if (blockIdx.x == 0 && blockIdx.y == 0 && threadIdx.x == 0) *ts_out = s_t;
+  const int lane = threadIdx.x & 63, w = threadIdx.x >> 6;
+  const int r = lane & 15, tc = lane >> 4;
+  const int64_t row = (int64_t)blockIdx.y * 64 + 16 * w + r;
+  const int64_t col0 = (int64_t)blockIdx.x * 64 + 16 * tc;
+  const bool valid = row < rows && col0 < cols;  // whole tiles are in or out
+  float z[16];
+  if (valid) {
+    const v4u* p = reinterpret_cast<const v4u*>(x + row * cols + col0);
+    const v4u a = ld_(p), b = ld_(p + 1);
+    const uint32_t wds[8] = {a.x, a.y, a.z, a.w, b.x, b.y, b.z, b.w};
+#pragma unroll
+    for (int j = 0; j < 8; ++j) { z[2 * j] = bf16_lo(wds[j]); z[2 * j + 1] = bf16_hi(wds[j]); }
+  } else {
+#pragma unroll
+    for (int j = 0; j < 16; ++j) z[j] = 0.0f;
+  }
+  float m = 0.0f;
+#pragma unroll
+  for (int j = 0; j < 16; ++j) m = fmaxf(m, __builtin_fabsf(z[j]));
+#pragma unroll
+  for (int off = 1; off < 16; off <<= 1) m = fmaxf(m, __shfl_xor(m, off, 64));
+  const BlockScale bs = block_scale(m, s_t, t6);
+  uint32_t q0, q1;
+  if (bs.code == 0u) {
+    q0 = encode8_zero(z);
+    q1 = encode8_zero(z + 8);
+  } else if (SR) {
+    const uint64_t n0 = (uint64_t)row * (uint64_t)cols + (uint64_t)col0;
+    q0 = encode8_sr(z, bs.r, sr_words(seed, stream_id, n0));
+    q1 = encode8_sr(z + 8, bs.r, sr_words(seed, stream_id, n0 + 8));
+  } else {
+    q0 = encode8_rtn(z, bs.r);
+    q1 = encode8_rtn(z + 8, bs.r);
+  }
+  if (valid) {
+    st_(v2u{q0, q1},
+                                reinterpret_cast<v2u*>(codes + row * (cols / 2) + col0 / 2));
+    if (r == 0) scales[(row / 16) * (cols / 16) + col0 / 16] = (uint8_t)bs.code;
+  }
+  if (codes_t == nullptr) return;  // uniform across the grid
+#pragma unroll
+  for (int j = 0; j < 16; ++j) {
+    const uint32_t q = j < 8 ? q0 : q1;
+    lds_t[16 * tc + j][16 * w + r] = (uint8_t)((q >> (4 * (j & 7))) & 0xFu);
+  }
+  __syncthreads();
+  // thread t packs column t/4, rows 16*(t%4) .. +15 -> 8 bytes of codes_t
+  const int c = threadIdx.x >> 2, qd = threadIdx.x & 3;
+  const int64_t oc = (int64_t)blockIdx.x * 64 + c;
+  const int64_t orow = (int64_t)blockIdx.y * 64 + 16 * qd;
+  if (oc < cols && orow < rows) {
+    uint32_t lo = 0, hi = 0;
+#pragma unroll
+    for (int j = 0; j < 8; ++j) {
+      lo |= (uint32_t)lds_t[c][16 * qd + j] << (4 * j);
+      hi |= (uint32_t)lds_t[c][16 * qd + 8 + j] << (4 * j);
+    }
+    st_(v2u{lo, hi},
+                                reinterpret_cast<v2u*>(codes_t + oc * (rows / 2) + orow / 2));
+  }
+}
+
+// ---------------------------------------------------------------------------
+// dequantize: out = (E2M1 * E4M3) * s_t
+// ---------------------------------------------------------------------------
+__global__ __launch_bounds__(kThreads) void k_dequant(
+    const uint8_t* __restrict__ codes, int64_t ld_codes, const uint8_t* __restrict__ scales,
+    int64_t ss_row, int64_t ss_k, int32_t blk_rows, const float* __restrict__ ts,
+    int64_t rows, int64_t k, float* __restrict__ out) {
+  const float s_t = *ts;
+  const int64_t kv = k / 8, items = rows * kv;
+  for (int64_t it = (int64_t)blockIdx.x * kThreads + threadIdx.x; it < items;
+       it += (int64_t)gridDim.x * kThreads) {
+    const int64_t r = it / kv, c8 = (it - r * kv) * 8;
+    const uint32_t q = *reinterpret_cast<const uint32_t*>(codes + r * ld_codes + c8 / 2);
+    const float E = e4m3_to_float(scales[(r / blk_rows) * ss_row + (c8 / 16) * ss_k]);
+    float o[8];
+#pragma unroll
+    for (int j = 0; j < 8; ++j) {
+      const uint32_t c = (q >> (4 * j)) & 0xFu;
+      const uint32_t i = c & 7u;
+      float mag = i < 4u ? 0.5f * (float)i : (i < 7u ? (float)i - 2.0f : 6.0f);
+      float v = (c & 8u) ? -mag : mag;
+      o[j] = (v * E) * s_t;
+    }
+    v4f* dst = reinterpret_cast<v4f*>(out + r * k + c8);
+    st_(v4f{o[0], o[1], o[2], o[3]}, dst);
+    st_(v4f{o[4], o[5], o[6], o[7]}, dst + 1);
+  }
+}
+
+// ---------------------------------------------------------------------------
+// launchers
+// ---------------------------------------------------------------------------
+static int grid_for(int64_t items, int per_cu) {
+  int64_t g = (items + kThreads - 1) / kThreads;
+  int64_t cap = (int64_t)num_cus() * per_cu;
+  if (g > cap) g = cap;
+  return (int)(g < 1 ? 1 : g);
+}
+
+hipError_t launch_amax(const void* x, int64_t n_elems, float* out, hipStream_t s) {
+  uint32_t* o = reinterpret_cast<uint32_t*>(out);
+  hipLaunchKernelGGL(k_zero_u32, dim3(1), dim3(1), 0, s, o);
+  const int64_t nvec = n_elems / 8;
+  hipLaunchKernelGGL(k_amax, dim3(grid_for(nvec / 4, 8)), dim3(kThreads), 0, s,
+                     reinterpret_cast<const v4u*>(x), nvec, o);
+  return hipGetLastError();
+}
+
+hipError_t launch_amax_rht(const void* x, int64_t rows, int64_t cols, uint64_t rht_seed,
+                           float* out, hipStream_t s) {
+  uint32_t* o = reinterpret_cast<uint32_t*>(out);
+  hipLaunchKernelGGL(k_zero_u32, dim3(1), dim3(1), 0, s, o);
+  const int64_t items = (rows / 16) * (cols / 8);
+  hipLaunchKernelGGL(k_amax_rht, dim3(grid_for(items, 8)), dim3(kThreads), 0, s,
+                     reinterpret_cast<const uint16_t*>(x), rows, cols, rht_seed, o);
+  return hipGetLastError();
+}
+
+hipError_t launch_quant_row(const void* x, int64_t rows, int64_t cols, const float* amax,
+                            bool sr, uint64_t seed, uint32_t stream_id, uint8_t* codes,
+                            uint8_t* scales, float* ts_out, hipStream_t s) {
+  const int64_t nvec = rows * cols / 8;
+  const dim3 g(grid_for(nvec, 16)), b(kThreads);
+  const v4u* xv = reinterpret_cast<const v4u*>(x);
+  uint32_t* cv = reinterpret_cast<uint32_t*>(codes);
+  if (sr)
+    hipLaunchKernelGGL(k_quant_row<true>, g, b, 0, s, xv, nvec, amax, seed, stream_id, cv,
+                       scales, ts_out);
+  else
+    hipLaunchKernelGGL(k_quant_row<false>, g, b, 0, s, xv, nvec, amax, seed, stream_id, cv,
+                       scales, ts_out);
+  return hipGetLastError();
+}
+
+hipError_t launch_quant_col(const void* x, int64_t rows, int64_t cols, const float* amax,
+                            bool rht, uint64_t rht_seed, bool sr, uint64_t seed,
+                            uint32_t stream_id, uint8_t* codes, uint8_t* scales, float* ts_out,
+                            hipStream_t s) {
+  const dim3 g((unsigned)((cols + kColTileC - 1) / kColTileC),
+               (unsigned)((rows + kColTileR - 1) / kColTileR)), b(kThreads);
+  const uint16_t* xp = reinterpret_cast<const uint16_t*>(x);
+#define NVFP4_COL(SRV, RHTV)                                                                  \
+  hipLaunchKernelGGL((k_quant_col<SRV, RHTV>), g, b, 0, s, xp, rows, cols, amax, rht_seed,   \
+                     seed, stream_id, codes, scales, ts_out)
+  if (sr && rht) NVFP4_COL(true, true);
+  else if (sr) NVFP4_COL(true, false);
+  else if (rht) NVFP4_COL(false, true);
+  else NVFP4_COL(false, false);
+#undef NVFP4_COL
+  return hipGetLastError();
+}
+
+hipError_t launch_quant_2d(const void* x, int64_t rows, int64_t cols, const float* amax, bool sr,
+                           uint64_t seed, uint32_t stream_id, uint8_t* codes, uint8_t* codes_t,
+                           uint8_t* scales, float* ts_out, hipStream_t s) {
+  const dim3 g((unsigned)((cols + 63) / 64), (unsigned)((rows + 63) / 64)), b(kThreads);
+  const uint16_t* xp = reinterpret_cast<const uint16_t*>(x);
+  if (sr)
+    hipLaunchKernelGGL(k_quant_2d<true>, g, b, 0, s, xp, rows, cols, amax, seed, stream_id,
+                       codes, codes_t, scales, ts_out);
+  else
+    hipLaunchKernelGGL(k_quant_2d<false>, g, b, 0, s, xp, rows, cols, amax, seed, stream_id,
+                       codes, codes_t, scales, ts_out);
+  return hipGetLastError();
+}
+
+hipError_t launch_dequant(const uint8_t* codes, int64_t ld_codes, const uint8_t* scales,
+                          int64_t ss_row, int64_t ss_k, int32_t blk_rows, const float* ts,
+                          int64_t rows, int64_t k, float* out, hipStream_t s) {
+  const int64_t items = rows * (k / 8);
+  hipLaunchKernelGGL(k_dequant, dim3(grid_for(items, 16)), dim3(kThreads), 0, s, codes,
+                     ld_codes, scales, ss_row, ss_k, blk_rows, ts, rows, k, out);
+  return hipGetLastError();
+}
+
+}  // namespace nvfp4

@@ -1,0 +1,176 @@
+/*
+ * nvfp4.h -- C ABI of the MI355X (gfx950) NVFP4 quantize + NVFP4-linear GEMM
+ * library (libnvfp4.so).
+ *
+ * NVFP4 stores a tensor as 4-bit E2M1 elements (values 0, +-0.5, +-1, +-1.5,
+ * +-2, +-3, +-4, +-6), one E4M3 scale per 16 consecutive elements, and one
+ * FP32 scale for the whole tensor ("Pretraining Large Language Models with
+ * NVFP4", summary page, format paragraph; "NVFP4 Trains with Precision of
+ * 16-Bit and Speed and Efficiency of 4-Bit", micro-block scaling and E4M3
+ * scale-factor sections).  Activations and gradients are scaled in 1D blocks
+ * of 16 along the contraction dimension K, weights in 2D 16x16 tiles; the
+ * weight-gradient GEMM inputs get a 16-point random Hadamard transform; the
+ * gradients are stochastically rounded (news item "Soumith Chintala 发布
+ * NVFP4 训练详解文章", section 三; NVIDIA blog, Hadamard, 2D block and
+ * stochastic-rounding sections).
+ *
+ * Quantization of an operand z (K-contiguous, [I][K]) runs in six steps:
+ *   1. amax_t = max |z| over the tensor            (a full read of the input)
+ *   2. s_t    = amax_t / (6*448)  (1 when amax_t == 0)
+ *   3. amax_b = max |z| over each block (1x16, or 16x16 for weights)
+ *   4. E_b    = E4M3(amax_b / (6*s_t)), round-to-nearest-even, saturating
+ *   5. code   = E2M1(z * (1/(E_b*s_t))), round-to-nearest-even or stochastic
+ *               (16 bits of Philox4x32-10 per element: key = seed, counter =
+ *               (n/8, stream_id, 0), n = element index in the K-contiguous
+ *               output operand)
+ *   6. (optional) z = 1/4 * H16 * D * x along K before step 1, D = +-1 signs
+ *               from Philox(key = rht_seed, counter = (0,0,0,1)), word 0
+ * The GPU output is bit-identical to the CPU reference for every finite
+ * input with amax_t >= 2^-100 (outputs for NaN/Inf inputs are unspecified,
+ * and never out of bounds).
+ *
+ * Conventions (all entry points):
+ *  - Every pointer is DEVICE memory owned by the caller; the library never
+ *    allocates, frees or synchronises.  `stream` is a hipStream_t (NULL = the
+ *    default stream); all work is enqueued on it, in order.
+ *  - bf16 inputs are row-major [rows][cols] with 16-byte aligned base
+ *    pointers; rows and cols are positive multiples of 16.
+ *  - Packed codes hold two elements per byte, the even-k element in the low
+ *    nibble; code = sign << 3 | magnitude index (0, .5, 1, 1.5, 2, 3, 4, 6).
+ *  - Arguments are validated before anything is enqueued; on error nothing
+ *    is launched and a negative NVFP4_ERR_* status is returned.  A launch
+ *    failure returns NVFP4_ERR_LAUNCH.  nvfp4_last_error() describes the most
+ *    recent error of the calling thread.
+ *  - amax_io / tensor_scale_out point to one device float each.  With
+ *    NVFP4_AMAX_COMPUTE the library computes amax_t into *amax_io; with
+ *    NVFP4_AMAX_GIVEN *amax_io must already hold it (e.g. from nvfp4_amax),
+ *    which saves the extra full read of the input.
+ */
+#ifndef NVFP4_H
+#define NVFP4_H
+
+#include <stdint.h>
+
+#ifdef __cplusplus
+extern "C" {
+#endif
+
+enum {
+  NVFP4_OK = 0,
+  NVFP4_ERR_NULL = -1,   /* a required pointer is NULL */
+  NVFP4_ERR_SHAPE = -2,  /* a dimension is not a positive multiple of 16, or mismatched */
+  NVFP4_ERR_ALIGN = -3,  /* a base pointer or leading dimension is misaligned */
+  NVFP4_ERR_ARG = -4,    /* an enum argument is out of range */
+  NVFP4_ERR_LAUNCH = -5  /* the HIP runtime refused a launch */
+};
+
+enum { NVFP4_AMAX_COMPUTE = 0, NVFP4_AMAX_GIVEN = 1 };
+
+enum {
+  NVFP4_ROWWISE = 0, /* blocks run along cols: codes [rows][cols/2], scales [rows][cols/16] */
+  NVFP4_COLWISE = 1  /* blocks run along rows: the quantized transpose,
+                        codes [cols][rows/2], scales [cols][rows/16] */
+};
+
+/* Step 1 alone: *amax_out = max |x| over the bf16 tensor [rows][cols]
+ * (NVFP4 format paragraph: the tensor-level FP32 scale needs this full-tensor
+ * scan).  rows*cols must be a multiple of 256. */
+int nvfp4_amax(const void* x_bf16, int64_t rows, int64_t cols, float* amax_out, void* stream);
+
+/* Step 1 under the transform: *amax_out = max |RHT(x^T)|, the RHT taken over
+ * every 16 consecutive rows of each column, signs from rht_seed.  This is
+ * the tensor statistic nvfp4_rht_quantize scales by. */
+int nvfp4_amax_rht(const void* x_bf16, int64_t rows, int64_t cols, uint64_t rht_seed,
+                   float* amax_out, void* stream);
+
+/* 1D quantization (activations, gradients), round-to-nearest-even.
+ * axis NVFP4_ROWWISE: operand = x,   I = rows, K = cols.
+ * axis NVFP4_COLWISE: operand = x^T, I = cols, K = rows (Wgrad layout).
+ * Outputs: codes [I][K/2], scales_e4m3 [I][K/16], *tensor_scale_out = s_t. */
+int nvfp4_quantize1d_rtn(const void* x_bf16, int64_t rows, int64_t cols, int axis,
+                         float* amax_io, int amax_mode,
+                         uint8_t* codes, uint8_t* scales_e4m3, float* tensor_scale_out,
+                         void* stream);
+
+/* As nvfp4_quantize1d_rtn with stochastic rounding: the larger neighbouring
+ * E2M1 magnitude is taken with probability (|v|-lo)/(hi-lo) (NVIDIA blog,
+ * stochastic-rounding section), decided by 16 bits of
+ * Philox4x32-10(key = seed, counter = (n/8, stream_id, 0)). */
+int nvfp4_quantize1d_sr(const void* x_bf16, int64_t rows, int64_t cols, int axis,
+                        float* amax_io, int amax_mode, uint64_t seed, uint32_t stream_id,
+                        uint8_t* codes, uint8_t* scales_e4m3, float* tensor_scale_out,
+                        void* stream);
+
+/* 2D quantization (weights): one E4M3 scale per 16x16 tile (NVIDIA blog, 2D
+ * block quantization: the forward and backward passes see the same
+ * quantized weight).  Operand = w, I = rows, K = cols.
+ * Outputs: codes [rows][cols/2]; codes_t [cols][rows/2] (nullable: the same
+ * codes transposed, the Dgrad operand); scales_e4m3 [rows/16][cols/16]. */
+int nvfp4_quantize2d_rtn(const void* w_bf16, int64_t rows, int64_t cols,
+                         float* amax_io, int amax_mode,
+                         uint8_t* codes, uint8_t* codes_t, uint8_t* scales_e4m3,
+                         float* tensor_scale_out, void* stream);
+
+int nvfp4_quantize2d_sr(const void* w_bf16, int64_t rows, int64_t cols,
+                        float* amax_io, int amax_mode, uint64_t seed, uint32_t stream_id,
+                        uint8_t* codes, uint8_t* codes_t, uint8_t* scales_e4m3,
+                        float* tensor_scale_out, void* stream);
+
+/* Weight-gradient operand: the quantized transpose of RHT-transformed x
+ * (news item, section 三: RHT on the weight-gradient GEMM inputs; summary
+ * page, limitations paragraph: only Wgrad, to stay compatible with 2D weight
+ * scaling).  x is [rows = K tokens][cols]; the transform runs over every 16
+ * consecutive tokens of each column.  Give both Wgrad operands the same
+ * rht_seed so the transforms cancel in the product.  use_sr selects
+ * stochastic rounding (seed, stream_id) or RTN.  *amax_io is max |RHT(x^T)|.
+ * Outputs: codes [cols][rows/2], scales_e4m3 [cols][rows/16]. */
+int nvfp4_rht_quantize(const void* x_bf16, int64_t rows, int64_t cols, uint64_t rht_seed,
+                       int use_sr, uint64_t sr_seed, uint32_t stream_id,
+                       float* amax_io, int amax_mode,
+                       uint8_t* codes, uint8_t* scales_e4m3, float* tensor_scale_out,
+                       void* stream);
+
+/* A quantized GEMM operand, logically [rows][k], K-contiguous.  The scale of
+ * element (r, k) is scales[(r / blk_rows) * ss_row + (k / 16) * ss_k].
+ *  1D rowwise operand: blk_rows 1,  ss_row = k/16, ss_k = 1.
+ *  2D operand:         blk_rows 16, ss_row = k/16, ss_k = 1.
+ *  2D transposed (codes_t of a [R][C] weight, read as [C][R]):
+ *                      blk_rows 16, ss_row = 1,    ss_k = C/16. */
+typedef struct {
+  const uint8_t* codes;      /* [rows][ld_codes] bytes, 16-byte aligned base; ld_codes >= k/2,
+                                a multiple of 8 (a multiple of 16 takes the faster path) */
+  int64_t ld_codes;
+  const uint8_t* scales;     /* E4M3 codes */
+  int64_t ss_row, ss_k;
+  int32_t blk_rows;          /* 1 or 16 */
+  const float* tensor_scale; /* device pointer to s_t */
+  int64_t rows, k;
+} nvfp4_operand;
+
+/* out[r][c] = (E2M1(code) * E4M3(scale)) * s_t as FP32 [rows][k]: the real
+ * value a 4-bit element stands for (blog essay "NVFP4：让大模型从零预训练跑在4位
+ * 浮点上", section 2.2: multiply the element by its block scale). */
+int nvfp4_dequantize(const nvfp4_operand* q, float* out, void* stream);
+
+/* C[m][n] = s_a * s_b * sum_k A[m,k] * B[n,k] in FP32, A = [M][K], B = [N][K],
+ * C row-major with leading dimension ldc >= N (floats, multiple of 4).
+ * Fprop  Y  = X W^T : A = rowwise Q(X),  B = 2D Q(W)
+ * Dgrad  dX = dY W  : A = rowwise Q(dY), B = 2D Q(W) read through codes_t
+ * Wgrad  dW = dY^T X: A = RHT-quantized dY, B = RHT-quantized X (same seed)
+ * The decoded E2M1 x E4M3 products are exact in FP16; the contraction runs
+ * on the matrix cores with FP32 accumulation (NVIDIA blog: the linear-layer
+ * GEMMs are the core compute of pretraining).  M, N, K multiples of 16. */
+int nvfp4_gemm(const nvfp4_operand* a, const nvfp4_operand* b, float* c, int64_t ldc,
+               void* stream);
+
+/* Human-readable name of a status code (static storage). */
+const char* nvfp4_status_string(int status);
+
+/* Description of the calling thread's most recent error ("" if none). */
+const char* nvfp4_last_error(void);
+
+#ifdef __cplusplus
+}
+#endif
+
+#endif /* NVFP4_H */

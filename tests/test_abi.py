@@ -1,0 +1,112 @@
+"""The C-ABI library loads, exports every symbol include/nvfp4.h declares,
+and rejects bad arguments before touching the GPU.  CPU only: every call
+here fails validation, which returns before any HIP call."""
+import ctypes
+import os
+import re
+
+import pytest
+
+import bit_microscaled_numerics_amd as nv
+
+ROOT = os.path.dirname(os.path.dirname(os.path.abspath(__file__)))
+HEADER = os.path.join(ROOT, "include", "nvfp4.h")
+
+
+@pytest.fixture(scope="module")
+def lib():
+    if not os.path.exists(nv.LIB_PATH):
+        from bit_microscaled_numerics_amd import build
+        build.build()
+    return nv.load_library()
+
+
+def declared():
+    text = open(HEADER).read()
+    return sorted(set(re.findall(r"^\s*(?:int|const char\*)\s+(nvfp4_\w+)\s*\(", text, re.M)))
+
+
+def test_header_and_binding_agree():
+    assert declared() == sorted(nv.EXPORTED)
+
+
+def test_every_declared_symbol_is_exported(lib):
+    for name in declared():
+        assert hasattr(lib, name), name
+
+
+def test_status_strings(lib):
+    for code, name in [(0, "NVFP4_OK"), (-1, "NVFP4_ERR_NULL"), (-2, "NVFP4_ERR_SHAPE"),
+                       (-3, "NVFP4_ERR_ALIGN"), (-4, "NVFP4_ERR_ARG"), (-5, "NVFP4_ERR_LAUNCH")]:
+        assert lib.nvfp4_status_string(code).decode() == name
+
+
+FAKE = 0x10000          # aligned, never dereferenced: validation fails first
+MIS = 0x10001
+
+
+def test_amax_validation(lib):
+    assert lib.nvfp4_amax(None, 16, 16, FAKE, None) == nv.NVFP4_ERR_NULL
+    assert lib.nvfp4_amax(FAKE, 16, 24, FAKE, None) == nv.NVFP4_ERR_SHAPE
+    assert lib.nvfp4_amax(FAKE, 0, 16, FAKE, None) == nv.NVFP4_ERR_SHAPE
+    assert lib.nvfp4_amax(FAKE, -16, 16, FAKE, None) == nv.NVFP4_ERR_SHAPE
+    assert lib.nvfp4_amax(MIS, 16, 16, FAKE, None) == nv.NVFP4_ERR_ALIGN
+    assert lib.nvfp4_amax(FAKE, 16, 16, None, None) == nv.NVFP4_ERR_NULL
+    assert "16" in lib.nvfp4_last_error().decode() or lib.nvfp4_last_error()
+
+
+def test_quantize_validation(lib):
+    q1 = lib.nvfp4_quantize1d_rtn
+    assert q1(FAKE, 16, 16, 0, FAKE, 0, None, FAKE, FAKE, None) == nv.NVFP4_ERR_NULL
+    assert q1(FAKE, 16, 16, 0, FAKE, 0, FAKE, None, FAKE, None) == nv.NVFP4_ERR_NULL
+    assert q1(FAKE, 16, 16, 0, None, 0, FAKE, FAKE, FAKE, None) == nv.NVFP4_ERR_NULL
+    assert q1(FAKE, 16, 16, 0, FAKE, 0, FAKE, FAKE, None, None) == nv.NVFP4_ERR_NULL
+    assert q1(FAKE, 16, 16, 0, FAKE, 0, MIS, FAKE, FAKE, None) == nv.NVFP4_ERR_ALIGN
+    assert q1(FAKE, 16, 16, 2, FAKE, 0, FAKE, FAKE, FAKE, None) == nv.NVFP4_ERR_ARG
+    assert q1(FAKE, 16, 16, 0, FAKE, 2, FAKE, FAKE, FAKE, None) == nv.NVFP4_ERR_ARG
+    assert q1(FAKE, 17, 16, 0, FAKE, 0, FAKE, FAKE, FAKE, None) == nv.NVFP4_ERR_SHAPE
+    qs = lib.nvfp4_quantize1d_sr
+    assert qs(FAKE, 16, 16, 5, FAKE, 0, 1, 0, FAKE, FAKE, FAKE, None) == nv.NVFP4_ERR_ARG
+    q2 = lib.nvfp4_quantize2d_rtn
+    assert q2(FAKE, 16, 8, FAKE, 0, FAKE, None, FAKE, FAKE, None) == nv.NVFP4_ERR_SHAPE
+    assert q2(FAKE, 16, 16, FAKE, 0, FAKE, MIS, FAKE, FAKE, None) == nv.NVFP4_ERR_ALIGN
+    assert q2(FAKE, 16, 16, FAKE, 3, FAKE, None, FAKE, FAKE, None) == nv.NVFP4_ERR_ARG
+    q2s = lib.nvfp4_quantize2d_sr
+    assert q2s(None, 16, 16, FAKE, 0, 1, 0, FAKE, None, FAKE, FAKE, None) == nv.NVFP4_ERR_NULL
+    r = lib.nvfp4_rht_quantize
+    assert r(FAKE, 16, 16, 1, 2, 1, 0, FAKE, 0, FAKE, FAKE, FAKE, None) == nv.NVFP4_ERR_ARG
+    assert r(FAKE, 8, 16, 1, 0, 1, 0, FAKE, 0, FAKE, FAKE, FAKE, None) == nv.NVFP4_ERR_SHAPE
+    assert lib.nvfp4_amax_rht(FAKE, 16, 16, 1, None, None) == nv.NVFP4_ERR_NULL
+
+
+def _op(**kw):
+    base = dict(codes=FAKE, ld_codes=16, scales=FAKE, ss_row=2, ss_k=1, blk_rows=1,
+                tensor_scale=FAKE, rows=16, k=32)
+    base.update(kw)
+    return nv.c_operand(**base)
+
+
+def test_gemm_validation(lib):
+    g = lib.nvfp4_gemm
+    ok = _op()
+    assert g(None, ctypes.byref(ok), FAKE, 16, None) == nv.NVFP4_ERR_NULL
+    assert g(ctypes.byref(ok), ctypes.byref(_op(k=48)), FAKE, 16, None) == nv.NVFP4_ERR_SHAPE
+    assert g(ctypes.byref(ok), ctypes.byref(_op(ld_codes=20)), FAKE, 16, None) == nv.NVFP4_ERR_ALIGN
+    assert g(ctypes.byref(ok), ctypes.byref(_op(k=48, ld_codes=32)), FAKE, 16,
+             None) == nv.NVFP4_ERR_SHAPE
+    assert g(ctypes.byref(ok), ctypes.byref(_op(rows=24)), FAKE, 24, None) == nv.NVFP4_ERR_SHAPE
+    assert g(ctypes.byref(ok), ctypes.byref(_op(codes=MIS)), FAKE, 16, None) == nv.NVFP4_ERR_ALIGN
+    assert g(ctypes.byref(ok), ctypes.byref(_op(blk_rows=4)), FAKE, 16, None) == nv.NVFP4_ERR_ARG
+    assert g(ctypes.byref(ok), ctypes.byref(_op(scales=None)), FAKE, 16, None) == nv.NVFP4_ERR_NULL
+    assert g(ctypes.byref(ok), ctypes.byref(ok), None, 16, None) == nv.NVFP4_ERR_NULL
+    assert g(ctypes.byref(ok), ctypes.byref(ok), FAKE, 8, None) == nv.NVFP4_ERR_SHAPE
+    assert g(ctypes.byref(ok), ctypes.byref(_op(ss_k=-1)), FAKE, 16, None) == nv.NVFP4_ERR_ARG
+    assert lib.nvfp4_dequantize(ctypes.byref(ok), None, None) == nv.NVFP4_ERR_NULL
+    assert lib.nvfp4_dequantize(ctypes.byref(ok), MIS, None) == nv.NVFP4_ERR_ALIGN
+
+
+def test_python_layer_refuses_cpu_tensors():
+    import torch
+    x = torch.zeros(16, 16, dtype=torch.bfloat16)
+    with pytest.raises(ValueError):
+        nv.quantize_1d(x)

@@ -1,0 +1,234 @@
+"""HIP path vs CPU oracle on the same seeded inputs, through the C ABI.
+
+Quantization (amax, tensor scale, E4M3 scales, codes, transposed codes) must
+be bit-exact; the GEMM must be within 1e-5 * sum_k |a_dec * b_dec| of the
+exact product for every entry.  Sizes span several workgroup tiles with
+ragged tails; the degenerate cases (all-zero tensors, negative zeros, blocks
+whose scale underflows, saturating blocks, K = 16) are included."""
+import numpy as np
+import pytest
+import torch
+
+import oracle
+import bit_microscaled_numerics_amd as nv
+from bit_microscaled_numerics_amd import inputs
+from parity import assert_gemm_close, assert_operand_equal, say
+
+pytestmark = pytest.mark.gpu
+
+SHAPES = [(16, 16), (48, 80), (256, 512), (272, 144), (528, 400)]
+
+
+def _tensor(kind: str, rows: int, cols: int, seed: int = 0) -> torch.Tensor:
+    g = torch.Generator().manual_seed(seed)
+    if kind == "normal":
+        return inputs.normal(g, rows, cols)
+    if kind == "outliers":
+        return inputs.normal(g, rows, cols, 1.0, 0.001, 50.0)
+    if kind == "t3":
+        return inputs.student_t3(g, rows, cols, 1e-3)
+    if kind == "zeros":
+        return torch.zeros(rows, cols, dtype=torch.bfloat16)
+    if kind == "negzeros":
+        return -torch.zeros(rows, cols, dtype=torch.bfloat16)
+    if kind == "mixed":
+        # all-zero blocks, blocks far below the tensor amax (their scale
+        # underflows to zero), one large outlier, exact E2M1 midpoints
+        x = inputs.normal(g, rows, cols, 1.0).float()
+        x[:, :16] = 0.0
+        x[0, -1] = 3.0e4
+        if cols >= 64:
+            x[1::3, 32:48] *= 1e-6
+            ties = torch.tensor([0.25, 0.75, 1.25, 1.75, 2.5, 3.5, 5.0, -5.0] * 2)
+            x[2::5, 48:64] = ties
+        return x.to(torch.bfloat16)
+    raise ValueError(kind)
+
+
+KINDS = ["normal", "outliers", "t3", "zeros", "negzeros", "mixed"]
+
+
+@pytest.mark.parametrize("shape", SHAPES)
+@pytest.mark.parametrize("kind", ["normal", "t3", "mixed"])
+def test_amax(shape, kind):
+    x = _tensor(kind, *shape)
+    say("amax", shape, kind)
+    got = nv.amax(x.cuda())
+    torch.cuda.synchronize()
+    assert float(got.cpu()[0]) == oracle.amax(x)
+    say("amax_rht", shape, kind)
+    got = nv.amax_rht(x.cuda(), 1234)
+    torch.cuda.synchronize()
+    assert float(got.cpu()[0]) == oracle.amax_rht(x, 1234)
+
+
+@pytest.mark.parametrize("shape", SHAPES)
+@pytest.mark.parametrize("kind", KINDS)
+@pytest.mark.parametrize("axis", [nv.NVFP4_ROWWISE, nv.NVFP4_COLWISE])
+@pytest.mark.parametrize("sr", [False, True])
+def test_quantize_1d(shape, kind, axis, sr):
+    x = _tensor(kind, *shape, seed=1)
+    kw = {"sr_seed": 0xC0FFEE_0000_0001, "stream_id": 3} if sr else {}
+    say("quantize_1d", shape, kind, axis, sr)
+    g = nv.quantize_1d(x.cuda(), axis, **kw)
+    torch.cuda.synchronize()
+    o = oracle.quantize(x, oracle.COLWISE if axis else oracle.ROWWISE, **kw)
+    assert_operand_equal(g, o, f"1d {shape} {kind} axis={axis} sr={sr}")
+
+
+@pytest.mark.parametrize("shape", SHAPES)
+@pytest.mark.parametrize("kind", KINDS)
+@pytest.mark.parametrize("sr", [False, True])
+def test_rht_quantize(shape, kind, sr):
+    x = _tensor(kind, *shape, seed=2)
+    kw = {"sr_seed": 77, "stream_id": 1} if sr else {}
+    say("rht_quantize", shape, kind, sr)
+    g = nv.rht_quantize(x.cuda(), 99, **kw)
+    torch.cuda.synchronize()
+    o = oracle.quantize(x, oracle.COLWISE, rht_seed=99, **kw)
+    assert_operand_equal(g, o, f"rht {shape} {kind} sr={sr}")
+
+
+@pytest.mark.parametrize("shape", SHAPES)
+@pytest.mark.parametrize("kind", KINDS)
+@pytest.mark.parametrize("sr", [False, True])
+def test_quantize_2d(shape, kind, sr):
+    x = _tensor(kind, *shape, seed=3)
+    kw = {"sr_seed": 5, "stream_id": 2} if sr else {}
+    say("quantize_2d", shape, kind, sr)
+    g = nv.quantize_2d(x.cuda(), **kw)
+    torch.cuda.synchronize()
+    o = oracle.quantize(x, oracle.TWO_D, with_codes_t=True, **kw)
+    assert_operand_equal(g, o, f"2d {shape} {kind} sr={sr}")
+
+
+def test_amax_given_skips_the_scan():
+    x = _tensor("normal", 272, 144)
+    xd = x.cuda()
+    say("amax_given")
+    a = nv.amax(xd)
+    g1 = nv.quantize_1d(xd, amax=a)
+    g2 = nv.quantize_2d(xd, amax=a)
+    g3 = nv.rht_quantize(xd, 5, amax=nv.amax_rht(xd, 5))
+    torch.cuda.synchronize()
+    assert_operand_equal(g1, oracle.quantize(x, oracle.ROWWISE))
+    assert_operand_equal(g2, oracle.quantize(x, oracle.TWO_D, with_codes_t=True))
+    assert_operand_equal(g3, oracle.quantize(x, oracle.COLWISE, rht_seed=5))
+    # a given amax that is not the tensor's own is used as is
+    g4 = nv.quantize_1d(xd, amax=float(a.cpu()[0]) * 4)
+    torch.cuda.synchronize()
+    assert_operand_equal(g4, oracle.quantize(x, oracle.ROWWISE,
+                                             amax_given=float(a.cpu()[0]) * 4))
+
+
+def test_sr_is_deterministic_and_seeded():
+    x = _tensor("normal", 256, 512)
+    xd = x.cuda()
+    say("sr determinism")
+    a = nv.quantize_1d(xd, sr_seed=1)
+    b = nv.quantize_1d(xd, sr_seed=1)
+    c = nv.quantize_1d(xd, sr_seed=2)
+    d = nv.quantize_1d(xd, sr_seed=1, stream_id=1)
+    torch.cuda.synchronize()
+    assert torch.equal(a.codes, b.codes)
+    assert not torch.equal(a.codes, c.codes) and not torch.equal(a.codes, d.codes)
+
+
+@pytest.mark.parametrize("kind", ["normal", "mixed", "zeros"])
+def test_dequantize(kind):
+    x = _tensor(kind, 272, 144, seed=4)
+    say("dequantize", kind)
+    for gq, oq in [(nv.quantize_1d(x.cuda()), oracle.quantize(x, oracle.ROWWISE)),
+                   (nv.quantize_2d(x.cuda()), oracle.quantize(x, oracle.TWO_D, with_codes_t=True))]:
+        got = nv.dequantize(gq).cpu().numpy()
+        assert np.array_equal(got.view(np.uint32), oracle.dequantize(oq).view(np.uint32))
+    g2 = nv.quantize_2d(x.cuda())
+    o2 = oracle.quantize(x, oracle.TWO_D, with_codes_t=True)
+    got = nv.dequantize(g2.t()).cpu().numpy()
+    assert np.array_equal(got.view(np.uint32), oracle.dequantize(o2.transposed()).view(np.uint32))
+
+
+# ----------------------------------------------------------------------- GEMM
+GEMM_SHAPES = [(16, 16, 16), (48, 80, 48), (64, 32, 80), (256, 512, 512), (272, 528, 144),
+               (300 // 16 * 16, 400, 1040)]
+
+
+@pytest.mark.parametrize("decode", ["hw", "perm"])
+@pytest.mark.parametrize("mnk", GEMM_SHAPES)
+def test_gemm_fprop(mnk, decode, monkeypatch):
+    monkeypatch.setenv("NVFP4_GEMM_DECODE", decode)
+    M, N, K = mnk
+    g = torch.Generator().manual_seed(M + N + K)
+    x = inputs.normal(g, M, K, 1.0, 0.001, 50.0)
+    w = inputs.normal(g, N, K, 0.02)
+    say("gemm fprop", mnk, decode)
+    qx, qw = nv.quantize_1d(x.cuda()), nv.quantize_2d(w.cuda())
+    y = nv.gemm(qx, qw)
+    torch.cuda.synchronize()
+    ox, ow = oracle.quantize(x, oracle.ROWWISE), oracle.quantize(w, oracle.TWO_D, with_codes_t=True)
+    c, t = oracle.gemm(ox, ow)
+    assert_gemm_close(y.cpu().numpy(), c, t, f"fprop {mnk} {decode}")
+
+
+@pytest.mark.parametrize("mnk", [(48, 80, 64), (256, 512, 512), (272, 144, 528)])
+def test_gemm_dgrad_uses_transposed_weight(mnk):
+    M, N, K = mnk          # dX [M][N] = dY [M][K] . W [K][N]
+    g = torch.Generator().manual_seed(7)
+    dy = inputs.normal(g, M, K, 1e-3)
+    w = inputs.normal(g, K, N, 0.02)
+    say("gemm dgrad", mnk)
+    qdy = nv.quantize_1d(dy.cuda(), sr_seed=1)
+    qw = nv.quantize_2d(w.cuda())
+    dx = nv.gemm(qdy, qw.t())
+    torch.cuda.synchronize()
+    ody = oracle.quantize(dy, oracle.ROWWISE, sr_seed=1)
+    ow = oracle.quantize(w, oracle.TWO_D, with_codes_t=True)
+    c, t = oracle.gemm(ody, ow.transposed())
+    assert_gemm_close(dx.cpu().numpy(), c, t, f"dgrad {mnk}")
+
+
+@pytest.mark.parametrize("tmn", [(64, 48, 80), (4096, 1024, 1024)])
+def test_gemm_wgrad_rht_sr(tmn):
+    T, F, H = tmn          # dW [F][H] = dY^T [F][T] . X [T][H]
+    g = torch.Generator().manual_seed(8)
+    dy = inputs.student_t3(g, T, F, 1e-3)
+    x = inputs.normal(g, T, H)
+    say("gemm wgrad", tmn)
+    qdy = nv.rht_quantize(dy.cuda(), 1, sr_seed=1, stream_id=0)
+    qx = nv.rht_quantize(x.cuda(), 1, sr_seed=1, stream_id=1)
+    dw = nv.gemm(qdy, qx)
+    torch.cuda.synchronize()
+    ody = oracle.quantize(dy, oracle.COLWISE, rht_seed=1, sr_seed=1, stream_id=0)
+    ox = oracle.quantize(x, oracle.COLWISE, rht_seed=1, sr_seed=1, stream_id=1)
+    assert_operand_equal(qdy, ody, "wgrad dY")
+    assert_operand_equal(qx, ox, "wgrad X")
+    c, t = oracle.gemm(ody, ox)
+    assert_gemm_close(dw.cpu().numpy(), c, t, f"wgrad {tmn}")
+
+
+def test_gemm_ldc_and_zero_operand():
+    g = torch.Generator().manual_seed(9)
+    x = inputs.normal(g, 48, 64)
+    w = torch.zeros(32, 64, dtype=torch.bfloat16)
+    say("gemm ldc/zeros")
+    qx, qw = nv.quantize_1d(x.cuda()), nv.quantize_2d(w.cuda())
+    out = torch.full((48, 40), 7.0, device="cuda")
+    nv.nvfp4_gemm(qx, qw, out, 40)
+    torch.cuda.synchronize()
+    o = out.cpu()
+    assert torch.all(o[:, :32] == 0) and torch.all(o[:, 32:] == 7.0)
+
+
+def test_single_fprop_config():
+    """The 256x512x512 single-Fprop workload, seed 0, end to end."""
+    wl = inputs.single_fprop(0)
+    x, w = wl.tensors["X"], wl.tensors["W"]
+    say("single fprop workload")
+    qx, qw = nv.quantize_1d(x.cuda()), nv.quantize_2d(w.cuda())
+    y = nv.gemm(qx, qw)
+    torch.cuda.synchronize()
+    ox, ow = oracle.quantize(x, oracle.ROWWISE), oracle.quantize(w, oracle.TWO_D, with_codes_t=True)
+    assert_operand_equal(qx, ox, "X")
+    assert_operand_equal(qw, ow, "W")
+    c, t = oracle.gemm(ox, ow)
+    assert_gemm_close(y.cpu().numpy(), c, t, "single fprop")
