@@ -231,6 +231,9 @@ def main():
     ap.add_argument("--no-cpu-baseline", action="store_true")
     ap.add_argument("--no-sweep", action="store_true")
     ap.add_argument("--seed", type=int, default=0)
+    ap.add_argument("--copy-calibration", action="store_true",
+                    help="first run a plain 1 GiB device copy (3 launches), the reference "
+                         "for scaling HBM byte counters")
     args = ap.parse_args()
     if args.gpus != 1 or int(os.environ.get("WORLD_SIZE", "1")) != 1:
         print("bench.py measures one GPU: this build has no multi-GPU path "
@@ -240,6 +243,15 @@ def main():
         print("bench.py needs a GPU", file=sys.stderr)
         sys.exit(2)
     nv.load_library()
+
+    if args.copy_calibration:
+        src = torch.empty(1 << 29, dtype=torch.bfloat16, device="cuda").fill_(1.0)
+        dst = torch.empty_like(src)
+        for _ in range(3):
+            dst.copy_(src)
+        torch.cuda.synchronize()
+        log("copy calibration: 3 x copy of 1 GiB (read 1 GiB + write 1 GiB each)")
+        del src, dst
 
     log("generating inputs (host, seeded)")
     wl = inputs.ffn_down(args.seed, TOKENS, HIDDEN, FFN)

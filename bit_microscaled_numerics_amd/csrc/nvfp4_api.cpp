@@ -56,13 +56,6 @@ int launched(hipError_t e) {
 
 hipStream_t as_stream(void* s) { return reinterpret_cast<hipStream_t>(s); }
 
-// GEMM operand decode: the hardware FP4 convert (exponent) + FP16 mantissa
-// multiply by default; NVFP4_GEMM_DECODE=perm selects the byte-permute decode.
-int gemm_decode_mode() {
-  const char* e = std::getenv("NVFP4_GEMM_DECODE");
-  return (e != nullptr && std::strcmp(e, "perm") == 0) ? 1 : 0;
-}
-
 int check_operand(const nvfp4_operand* q, const char* name) {
   if (q == nullptr) return fail(NVFP4_ERR_NULL, "%s is NULL", name);
   if (q->codes == nullptr || q->scales == nullptr || q->tensor_scale == nullptr)
@@ -83,8 +76,19 @@ int check_operand(const nvfp4_operand* q, const char* name) {
 }
 
 nvfp4::GemmOperand to_kernel(const nvfp4_operand* q) {
+  const int64_t last = ((q->rows - 1) / q->blk_rows) * q->ss_row + ((q->k - 1) / 16) * q->ss_k;
   return nvfp4::GemmOperand{q->codes, q->ld_codes, q->scales, q->ss_row, q->ss_k,
-                            q->blk_rows, q->tensor_scale, q->rows};
+                            q->blk_rows, q->tensor_scale, q->rows, last + 1};
+}
+
+// The GEMM addresses a 256-row slab of codes and the scale array with 32-bit
+// buffer offsets.
+int check_gemm_extent(const nvfp4_operand* q, const char* name) {
+  const int64_t last = ((q->rows - 1) / q->blk_rows) * q->ss_row + ((q->k - 1) / 16) * q->ss_k;
+  if (q->ld_codes > (int64_t(1) << 22) || last >= (int64_t(1) << 31))
+    return fail(NVFP4_ERR_SHAPE, "%s: codes row pitch or scale array beyond the 32-bit offset range",
+                name);
+  return NVFP4_OK;
 }
 
 }  // namespace
@@ -240,6 +244,8 @@ int nvfp4_gemm(const nvfp4_operand* a, const nvfp4_operand* b, float* c, int64_t
   int st = check_operand(a, "a");
   if (st) return st;
   if ((st = check_operand(b, "b"))) return st;
+  if ((st = check_gemm_extent(a, "a"))) return st;
+  if ((st = check_gemm_extent(b, "b"))) return st;
   if (a->k != b->k)
     return fail(NVFP4_ERR_SHAPE, "a.k=%lld != b.k=%lld", (long long)a->k, (long long)b->k);
   if (c == nullptr) return fail(NVFP4_ERR_NULL, "c is NULL");
@@ -247,7 +253,7 @@ int nvfp4_gemm(const nvfp4_operand* a, const nvfp4_operand* b, float* c, int64_t
   if (ldc < b->rows) return fail(NVFP4_ERR_SHAPE, "ldc=%lld < N=%lld", (long long)ldc,
                                  (long long)b->rows);
   return launched(nvfp4::launch_gemm(to_kernel(a), to_kernel(b), a->k, c, ldc,
-                                     gemm_decode_mode(), as_stream(stream)));
+                                     as_stream(stream)));
 }
 
 }  // extern "C"

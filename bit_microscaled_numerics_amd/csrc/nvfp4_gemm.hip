@@ -36,58 +36,31 @@ struct GemmArgs {
   int64_t ldc;
 };
 
-// Eight codes (one 32-bit word, element e in nibble e) times a block scale
-// -> eight FP16 values, element e in lane-vector slot e.
-//
-// DECODE 0: the gfx950 FP4 -> FP16 convert multiplies by 2^floor(log2(scale))
-// only (an E8M0-style scale; low nibble first), which is exact for q * 2^e.
-// One packed FP16 multiply by the scale's mantissa (1 + m/8) completes
-// q * E exactly: 2 + 4 significant bits.
-// DECODE 1: a byte-permute decode (reference variant): FP16 of an E2M1
-// magnitude has a zero low byte; its high byte comes from an 8-entry byte
-// table via v_perm, the sign from bit 3 of the code; then one FP16 multiply
-// by the whole E4M3 value.
+// Decoding.  The gfx950 FP4 -> FP16 convert multiplies by 2^floor(log2 s)
+// of its FP32 scale argument only (an E8M0-style scale; low nibble first),
+// which gives q * 2^e exactly.  One packed FP16 multiply by the E4M3
+// mantissa (1 + m/8) completes q * E exactly: 2 + 4 significant bits.
 struct BlockDec {
   float e;       // E4M3 value as FP32 (the convert takes its exponent)
-  half2v mant;   // {mantissa, mantissa} in FP16 for DECODE 0, {E, E} for DECODE 1
+  half2v mant;   // {mantissa, mantissa} in FP16
 };
 
-template <int DECODE>
 __device__ __forceinline__ BlockDec block_dec(uint32_t code) {
   BlockDec d;
   d.e = e4m3_to_float(code);
-  if constexpr (DECODE == 0) {
-    const uint32_t mb = (__float_as_uint(d.e) >> 20) & 7u;
-    const uint32_t h = 0x3C00u | (mb << 7);
-    d.mant = __builtin_bit_cast(half2v, h | (h << 16));
-  } else {
-    const _Float16 hs = (_Float16)d.e;  // E4M3 values are exact in FP16
-    d.mant = half2v{hs, hs};
-  }
+  const uint32_t mb = (__float_as_uint(d.e) >> 20) & 7u;
+  const uint32_t h = 0x3C00u | (mb << 7);
+  d.mant = __builtin_bit_cast(half2v, h | (h << 16));
   return d;
 }
 
-template <int DECODE>
+// Eight codes (one 32-bit word, element e in nibble e) -> eight FP16 values
+// q * E, element e in lane-vector slot e.
 __device__ __forceinline__ half8 decode8(uint32_t w, const BlockDec& d) {
-  half2v p0, p1, p2, p3;
-  if constexpr (DECODE == 0) {
-    p0 = __builtin_amdgcn_cvt_scalef32_pk_f16_fp4(w, d.e, 0);
-    p1 = __builtin_amdgcn_cvt_scalef32_pk_f16_fp4(w, d.e, 1);
-    p2 = __builtin_amdgcn_cvt_scalef32_pk_f16_fp4(w, d.e, 2);
-    p3 = __builtin_amdgcn_cvt_scalef32_pk_f16_fp4(w, d.e, 3);
-  } else {
-    const uint32_t tab_lo = 0x3E3C3800u;  // 0, 0.5, 1, 1.5
-    const uint32_t tab_hi = 0x46444240u;  // 2, 3, 4, 6
-    const uint32_t sel_e = w & 0x07070707u;          // magnitudes of nibbles 0, 2, 4, 6
-    const uint32_t sel_o = (w >> 4) & 0x07070707u;   // nibbles 1, 3, 5, 7
-    const uint32_t hb_e = __builtin_amdgcn_perm(tab_hi, tab_lo, sel_e) | ((w << 4) & 0x80808080u);
-    const uint32_t hb_o = __builtin_amdgcn_perm(tab_hi, tab_lo, sel_o) | (w & 0x80808080u);
-    // pair j: bytes {0, hb_e[j], 0, hb_o[j]} (selector 0x0C yields a zero byte)
-    p0 = __builtin_bit_cast(half2v, __builtin_amdgcn_perm(hb_o, hb_e, 0x040C000Cu));
-    p1 = __builtin_bit_cast(half2v, __builtin_amdgcn_perm(hb_o, hb_e, 0x050C010Cu));
-    p2 = __builtin_bit_cast(half2v, __builtin_amdgcn_perm(hb_o, hb_e, 0x060C020Cu));
-    p3 = __builtin_bit_cast(half2v, __builtin_amdgcn_perm(hb_o, hb_e, 0x070C030Cu));
-  }
+  half2v p0 = __builtin_amdgcn_cvt_scalef32_pk_f16_fp4(w, d.e, 0);
+  half2v p1 = __builtin_amdgcn_cvt_scalef32_pk_f16_fp4(w, d.e, 1);
+  half2v p2 = __builtin_amdgcn_cvt_scalef32_pk_f16_fp4(w, d.e, 2);
+  half2v p3 = __builtin_amdgcn_cvt_scalef32_pk_f16_fp4(w, d.e, 3);
   p0 *= d.mant;
   p1 *= d.mant;
   p2 *= d.mant;
@@ -96,75 +69,6 @@ __device__ __forceinline__ half8 decode8(uint32_t w, const BlockDec& d) {
   r[0] = p0[0]; r[1] = p0[1]; r[2] = p1[0]; r[3] = p1[1];
   r[4] = p2[0]; r[5] = p2[1]; r[6] = p3[0]; r[7] = p3[1];
   return r;
-}
-
-// Per-lane raw data of one 32-row slab for one 64-wide K step: 32 codes
-// (k = k0 + 32*half .. +31) and the two block-scale bytes, kept raw until the
-// step that consumes them so the load latency hides behind the current step.
-struct Slab {
-  v4u codes;
-  uint32_t s0, s1;
-};
-
-// Row indices past the operand are clamped to its last row: those lanes feed
-// only accumulator rows/columns that are never stored.  Full steps need no
-// K checks; the tail step (K % 64 != 0) zero-fills past K.
-template <bool TAIL, bool LD16>
-__device__ __forceinline__ Slab load_slab(const GemmOperand& op, int64_t row, int64_t kk,
-                                          int64_t K) {
-  Slab s;
-  const int64_t r = row < op.rows ? row : op.rows - 1;
-  const uint8_t* p = op.codes + r * op.ld + kk / 2;
-  const uint8_t* sp = op.scales + (r / op.blk_rows) * op.ss_row + (kk / 16) * op.ss_k;
-  if (!TAIL || kk + 32 <= K) {
-    if (LD16) {
-      s.codes = *reinterpret_cast<const v4u*>(p);
-    } else {  // K % 32 == 16: rows are 8-byte aligned
-      const v2u lo = *reinterpret_cast<const v2u*>(p);
-      const v2u hi = *reinterpret_cast<const v2u*>(p + 8);
-      s.codes = v4u{lo.x, lo.y, hi.x, hi.y};
-    }
-    s.s0 = sp[0];
-    s.s1 = sp[op.ss_k];
-  } else if (kk + 16 <= K) {
-    const v2u h = *reinterpret_cast<const v2u*>(p);
-    s.codes = v4u{h.x, h.y, 0u, 0u};
-    s.s0 = sp[0];
-    s.s1 = 0u;
-  } else {
-    s.codes = v4u{0u, 0u, 0u, 0u};
-    s.s0 = 0u;
-    s.s1 = 0u;
-  }
-  return s;
-}
-
-template <int WM, int WN, int DECODE>
-__device__ __forceinline__ void mma_step(float16v (&acc)[WM][WN], const Slab (&a)[WM],
-                                         const Slab (&b)[WN]) {
-#pragma unroll
-  for (int half = 0; half < 2; ++half) {
-    BlockDec da[WM], db[WN];
-#pragma unroll
-    for (int i = 0; i < WM; ++i) da[i] = block_dec<DECODE>(half ? a[i].s1 : a[i].s0);
-#pragma unroll
-    for (int j = 0; j < WN; ++j) db[j] = block_dec<DECODE>(half ? b[j].s1 : b[j].s0);
-#pragma unroll
-    for (int s = 2 * half; s < 2 * half + 2; ++s) {
-      half8 av[WM], bv[WN];
-#pragma unroll
-      for (int i = 0; i < WM; ++i) av[i] = decode8<DECODE>(a[i].codes[s], da[i]);
-#pragma unroll
-      for (int j = 0; j < WN; ++j) bv[j] = decode8<DECODE>(b[j].codes[s], db[j]);
-#pragma unroll
-      for (int i = 0; i < WM; ++i)
-#pragma unroll
-        for (int j = 0; j < WN; ++j)
-          acc[i][j] = __builtin_amdgcn_mfma_f32_32x32x16_f16(av[i], bv[j], acc[i][j], 0, 0, 0);
-      // keep each step's decode next to its MFMAs (bounds live FP16 operands)
-      __builtin_amdgcn_sched_barrier(0);
-    }
-  }
 }
 
 // Tile order: the grid is 1-D.  Workgroups are dealt round-robin to the 8
@@ -187,90 +91,301 @@ __device__ __forceinline__ void tile_coords(int64_t tiles_m, int64_t tiles_n, in
   tn = in / gm;
 }
 
-// CHECKED: K % 64 != 0; every load checks its K range and zero-fills past K.
-template <int WM, int WN, int DECODE, bool LD16, bool CHECKED>
-__global__ __launch_bounds__(256, 1) void k_gemm(GemmArgs g) {
+constexpr int kTile = 256;  // workgroup tile (rows of A and of B)
+constexpr int kWaveTile = 4; // 32x32 blocks per wave along each dimension
+constexpr uint32_t kBufFlags = 0x00020000u;  // raw 32-bit buffer descriptor word 3
+
+// Buffer view of one operand for one workgroup: codes and scales of the
+// 256-row slab starting at row0.  Loads take the row part of the offset in
+// a VGPR (fixed for the whole K loop) and the K part in an SGPR, so rows past
+// the operand lie beyond num_records whatever the bounds rule includes, and
+// read as zero; no row clamping or per-iteration address arithmetic.
+struct OpView {
+  __amdgpu_buffer_rsrc_t codes, scales;
+  uint32_t voff_codes[kWaveTile];   // per 32-row slab: row * ld + 16 * khalf
+  uint32_t voff_scales[kWaveTile];  // (row / blk) * ss_row + 2 * khalf * ss_k
+  uint32_t ss_k;
+};
+
+__device__ __forceinline__ OpView make_view(const GemmOperand& op, int64_t row0, int wrow0,
+                                            int lrow, int khalf) {
+  OpView v;
+  const int64_t rem_rows = op.rows - row0;
+  const int64_t code_bytes = rem_rows * op.ld;
+  const uint8_t* sbase = op.scales + (row0 / op.blk_rows) * op.ss_row;
+  const int64_t scale_bytes = op.scale_bytes - (row0 / op.blk_rows) * op.ss_row;
+  v.codes = __builtin_amdgcn_make_buffer_rsrc(
+      const_cast<uint8_t*>(op.codes + row0 * op.ld), (short)0,
+      (int)(code_bytes < 0x7FFFFFFF ? code_bytes : 0x7FFFFFFF), (int)kBufFlags);
+  v.scales = __builtin_amdgcn_make_buffer_rsrc(
+      const_cast<uint8_t*>(sbase), (short)0,
+      (int)(scale_bytes < 0x7FFFFFFF ? scale_bytes : 0x7FFFFFFF), (int)kBufFlags);
+#pragma unroll
+  for (int i = 0; i < kWaveTile; ++i) {
+    const int r = wrow0 + 32 * i + lrow;   // row within the workgroup slab
+    v.voff_codes[i] = (uint32_t)(r * op.ld + 16 * khalf);
+    v.voff_scales[i] = (uint32_t)((r / op.blk_rows) * op.ss_row + 2 * khalf * op.ss_k);
+  }
+  v.ss_k = (uint32_t)op.ss_k;
+  return v;
+}
+
+// Per-lane raw data of one 32-row slab for one 64-wide K step: 32 codes
+// (k = k0 + 32*khalf .. +31) and the two block-scale bytes, kept raw until
+// the step that consumes them.
+struct Slab {
+  v4u codes;
+  uint32_t s0, s1;
+};
+
+// kbyte = k0 / 2 (uniform); CHECKED zero-fills codes at k >= K.  kill adds
+// 2^31 to the scales' scalar offset, which puts them past num_records: they
+// read as 0, and a zero scale decodes every code to +-0 (a step that must
+// not contribute, at no VALU cost).
+template <bool CHECKED, bool LD16>
+__device__ __forceinline__ Slab load_slab(const OpView& v, int i, uint32_t kbyte, int khalf,
+                                          int64_t K, uint32_t kill = 0u) {
+  Slab s;
+  if (LD16) {
+    s.codes = __builtin_bit_cast(v4u, __builtin_amdgcn_raw_buffer_load_b128(
+                                          v.codes, v.voff_codes[i], kbyte, 0));
+  } else {  // K % 32 == 16: rows are 8-byte aligned
+    const v2u lo = __builtin_bit_cast(v2u, __builtin_amdgcn_raw_buffer_load_b64(
+                                               v.codes, v.voff_codes[i], kbyte, 0));
+    const v2u hi = __builtin_bit_cast(v2u, __builtin_amdgcn_raw_buffer_load_b64(
+                                               v.codes, v.voff_codes[i] + 8, kbyte, 0));
+    s.codes = v4u{lo.x, lo.y, hi.x, hi.y};
+  }
+  const uint32_t sk = (kbyte / 8) * v.ss_k + kill;  // block index (k0 / 16) times its stride
+  s.s0 = __builtin_amdgcn_raw_buffer_load_b8(v.scales, v.voff_scales[i], sk, 0);
+  s.s1 = __builtin_amdgcn_raw_buffer_load_b8(v.scales, v.voff_scales[i] + v.ss_k, sk, 0);
+  if (CHECKED) {
+    const int64_t kk = 2 * (int64_t)kbyte + 32 * khalf;
+    if (kk + 16 > K) { s.codes = v4u{0u, 0u, 0u, 0u}; s.s0 = 0u; s.s1 = 0u; }
+    else if (kk + 32 > K) { s.codes.z = 0u; s.codes.w = 0u; s.s1 = 0u; }
+  }
+  return s;
+}
+
+// Scale table: E4M3 code -> {FP32 value (the convert takes its exponent),
+// FP16 mantissa pair}.  128 entries in LDS, filled once per workgroup.
+__device__ __forceinline__ v2u scale_entry(uint32_t code) {
+  const BlockDec d = block_dec(code);
+  return v2u{__float_as_uint(d.e), __builtin_bit_cast(uint32_t, d.mant)};
+}
+
+__device__ __forceinline__ BlockDec lut_dec(const v2u* lut, uint32_t code) {
+  const v2u e = lut[code & 0x7Fu];
+  // copy the lanes to scalars first: clang's __builtin_bit_cast of an
+  // ext-vector element expression reads element 0
+  const uint32_t ex = e.x, ey = e.y;
+  BlockDec d;
+  d.e = __uint_as_float(ex);
+  d.mant = __builtin_bit_cast(half2v, ey);
+  return d;
+}
+
+// ---------------------------------------------------------------------------
+// Decode-once GEMM
+// ---------------------------------------------------------------------------
+// Workgroup: 512 threads = 8 waves (two per SIMD) on a 256 x 256 tile; wave w
+// computes rows 128*(w/4) .. +127 and columns 64*(w%4) .. +63 as 4 x 2
+// blocks of 32 x 32 (128 accumulator registers, so two waves fit a SIMD and
+// each covers the other's stalls).  Every element of the A and B tiles is
+// decoded exactly once per K step: thread t decodes chunk t of A and chunk t
+// of B (row t/2, codes 32*(t%2) .. +31 of the step) into FP16 in LDS; the
+// waves read their MFMA operands back with ds_read_b128.  The decode of K
+// step it+1 is interleaved with the MFMAs of step it; raw codes are loaded
+// two K steps ahead.
+//
+// LDS: 2 stages x (A, B) x [256 rows][128 B] = 128 KiB.  A row holds 64 FP16
+// values = 8 chunks of 16 B; chunk j of row r sits at position
+// j ^ ((r >> 1) & 7), which makes both the operand reads (16 consecutive
+// rows, one chunk each) and the decode writes (8 rows x 2 halves) touch 16
+// distinct 16-byte bank groups of the 64-bank LDS.
+constexpr int kBK = 64;
+constexpr int kThreads = 512;
+constexpr int kWM = 4, kWN = 2;                    // 32x32 blocks per wave
+constexpr int kRowBytes = kBK * 2;                 // 128
+constexpr int kOpBytes = kTile * kRowBytes;        // 32 KiB per operand and stage
+constexpr int kLdsBytes = 4 * kOpBytes;            // 128 KiB
+
+__device__ __forceinline__ uint32_t lds_off(int row, int chunk) {
+  return (uint32_t)(row * kRowBytes + ((chunk ^ ((row >> 1) & 7)) << 4));
+}
+
+struct StepOps {
+  half8 a[kWM], b[kWN];
+};
+
+__device__ __forceinline__ void mfma8(float16v (&acc)[kWM][kWN], const StepOps& o) {
+#pragma unroll
+  for (int i = 0; i < kWM; ++i)
+#pragma unroll
+    for (int j = 0; j < kWN; ++j)
+      acc[i][j] = __builtin_amdgcn_mfma_f32_32x32x16_f16(o.a[i], o.b[j], acc[i][j], 0, 0, 0);
+}
+
+// A thread's raw share of one K step: one chunk of A and one of B.
+struct Raw {
+  Slab a, b;
+};
+
+template <bool CHECKED, bool LD16>
+__device__ __forceinline__ void load_raw(Raw& r, const OpView& va, const OpView& vb,
+                                         uint32_t kbyte, int64_t K, uint32_t kill) {
+  r.a = load_slab<CHECKED, LD16>(va, 0, kbyte, threadIdx.x & 1, K, kill);
+  r.b = load_slab<CHECKED, LD16>(vb, 0, kbyte, threadIdx.x & 1, K, kill);
+}
+
+// Decode words p0, p0+1 of this thread's chunk of operand `op` (0 = A,
+// 1 = B) into an LDS stage.
+__device__ __forceinline__ void store_half(uint8_t* stage, const Slab& sl, int op, int p0,
+                                           const v2u* lut) {
+  uint8_t* base = stage + op * kOpBytes;
+  const int row = threadIdx.x >> 1, half = threadIdx.x & 1;
+  const BlockDec d = lut_dec(lut, p0 < 2 ? sl.s0 : sl.s1);
+#pragma unroll
+  for (int p = p0; p < p0 + 2; ++p)
+    *reinterpret_cast<half8*>(base + lds_off(row, 4 * half + p)) = decode8(sl.codes[p], d);
+}
+
+__device__ __forceinline__ void read_ops(StepOps& o, const uint8_t* stage, int wm, int wn,
+                                         int lrow, int lk, int s) {
+#pragma unroll
+  for (int i = 0; i < kWM; ++i)
+    o.a[i] = *reinterpret_cast<const half8*>(stage + lds_off(wm * 128 + 32 * i + lrow, 2 * s + lk));
+#pragma unroll
+  for (int j = 0; j < kWN; ++j)
+    o.b[j] = *reinterpret_cast<const half8*>(stage + kOpBytes +
+                                             lds_off(wn * 64 + 32 * j + lrow, 2 * s + lk));
+}
+
+// 8 x {1 MFMA, 2 VALU}, with the LDS traffic spread in between.
+__device__ __forceinline__ void interleave() {
+#pragma unroll
+  for (int m = 0; m < 8; ++m) {
+    __builtin_amdgcn_sched_group_barrier(0x008, 1, 0);   // MFMA
+    __builtin_amdgcn_sched_group_barrier(0x002, 2, 0);   // VALU
+    if (m < 6) __builtin_amdgcn_sched_group_barrier(0x100, 1, 0);  // DS read
+    if (m % 4 == 1) __builtin_amdgcn_sched_group_barrier(0x200, 1, 0);  // DS write
+  }
+}
+
+template <bool CHECKED, bool LD16>
+__global__ __launch_bounds__(kThreads, 1) void k_gemm(GemmArgs g) {
+  extern __shared__ __attribute__((aligned(16))) uint8_t smem[];
+  __shared__ v2u lut[128];
+  if (threadIdx.x < 128) lut[threadIdx.x] = scale_entry(threadIdx.x);
+
   const int lane = threadIdx.x & 63, wave = threadIdx.x >> 6;
-  const int wm = wave >> 1, wn = wave & 1;
-  const int64_t tiles_m = (g.M + 64 * WM - 1) / (64 * WM);
-  const int64_t tiles_n = (g.N + 64 * WN - 1) / (64 * WN);
+  const int wm = wave >> 2, wn = wave & 3;
+  const int lrow = lane & 31, lk = lane >> 5;
+  const int64_t tiles_m = (g.M + kTile - 1) / kTile, tiles_n = (g.N + kTile - 1) / kTile;
   int64_t tm, tn;
   tile_coords(tiles_m, tiles_n, tm, tn);
-  const int64_t m0 = tm * (64 * WM) + wm * (32 * WM);
-  const int64_t n0 = tn * (64 * WN) + wn * (32 * WN);
-  const int lrow = lane & 31, khalf = lane >> 5;
+  // loader views: this thread's chunk is row threadIdx.x/2 of the tile,
+  // K-half threadIdx.x%2 (slot 0 of the view)
+  OpView va = make_view(g.a, tm * kTile, 0, 0, threadIdx.x & 1);
+  OpView vb = make_view(g.b, tn * kTile, 0, 0, threadIdx.x & 1);
+  {
+    const int r = threadIdx.x >> 1, kh = threadIdx.x & 1;
+    va.voff_codes[0] = (uint32_t)(r * g.a.ld + 16 * kh);
+    va.voff_scales[0] = (uint32_t)((r / g.a.blk_rows) * g.a.ss_row + 2 * kh * g.a.ss_k);
+    vb.voff_codes[0] = (uint32_t)(r * g.b.ld + 16 * kh);
+    vb.voff_scales[0] = (uint32_t)((r / g.b.blk_rows) * g.b.ss_row + 2 * kh * g.b.ss_k);
+  }
 
-  float16v acc[WM][WN];
+  float16v acc[kWM][kWN];
 #pragma unroll
-  for (int i = 0; i < WM; ++i)
+  for (int i = 0; i < kWM; ++i)
 #pragma unroll
-    for (int j = 0; j < WN; ++j)
-#pragma unroll
-      for (int v = 0; v < 16; ++v) acc[i][j][v] = 0.0f;
+    for (int j = 0; j < kWN; ++j) acc[i][j] = float16v{};
 
-  const int64_t steps = (g.K + 63) / 64;
-  Slab a_cur[WM], b_cur[WN];
+  const int64_t steps = (g.K + kBK - 1) / kBK;
+  const int64_t last = steps - 1;
+  auto kbyte = [&](int64_t t) { return (uint32_t)((t < last ? t : last) * 32); };
+  auto kill = [&](int64_t t) { return t > last ? 0x80000000u : 0u; };
+
+  Raw r0, r1;
+  load_raw<CHECKED, LD16>(r0, va, vb, kbyte(0), g.K, 0u);
+  load_raw<CHECKED, LD16>(r1, va, vb, kbyte(1), g.K, kill(1));
+  __syncthreads();  // lookup table ready
+  store_half(smem, r0.a, 0, 0, lut);
+  store_half(smem, r0.a, 0, 2, lut);
+  store_half(smem, r0.b, 1, 0, lut);
+  store_half(smem, r0.b, 1, 2, lut);
+  load_raw<CHECKED, LD16>(r0, va, vb, kbyte(2), g.K, kill(2));
+  __syncthreads();
+  StepOps ops, nxt;
+  read_ops(ops, smem, wm, wn, lrow, lk, 0);
+
+  // Step it multiplies stage it&1 while decoding step it+1 (raw set
+  // (it+1)&1) into the other stage; after the barrier that raw set is
+  // refilled with step it+3.  Two K steps per trip keep the raw sets in fixed
+  // registers; the loop body is branch-free (steps past the last are killed
+  // re-reads that decode to zeros).
+  for (int64_t it = 0; it < steps; it += 2) {
 #pragma unroll
-  for (int i = 0; i < WM; ++i)
-    a_cur[i] = load_slab<CHECKED, LD16>(g.a, m0 + 32 * i + lrow, 32 * khalf, g.K);
+    for (int h = 0; h < 2; ++h) {
+      uint8_t* cur = smem + (h ? 2 * kOpBytes : 0);
+      uint8_t* oth = smem + (h ? 0 : 2 * kOpBytes);
+      Raw& rn = h ? r0 : r1;      // raw data of step it+h+1
 #pragma unroll
-  for (int j = 0; j < WN; ++j)
-    b_cur[j] = load_slab<CHECKED, LD16>(g.b, n0 + 32 * j + lrow, 32 * khalf, g.K);
-  // Prefetch step it+1 (the last step re-reads itself, which keeps the loop
-  // free of branches), then decode and multiply step it.
-  const int64_t k_last = (steps - 1) * 64 + 32 * khalf;
-  for (int64_t it = 0; it < steps; ++it) {
-    Slab a_nxt[WM], b_nxt[WN];
-    int64_t kn = (it + 1) * 64 + 32 * khalf;
-    kn = kn < k_last ? kn : k_last;
-#pragma unroll
-    for (int i = 0; i < WM; ++i)
-      a_nxt[i] = load_slab<CHECKED, LD16>(g.a, m0 + 32 * i + lrow, kn, g.K);
-#pragma unroll
-    for (int j = 0; j < WN; ++j)
-      b_nxt[j] = load_slab<CHECKED, LD16>(g.b, n0 + 32 * j + lrow, kn, g.K);
-    mma_step<WM, WN, DECODE>(acc, a_cur, b_cur);
-#pragma unroll
-    for (int i = 0; i < WM; ++i) a_cur[i] = a_nxt[i];
-#pragma unroll
-    for (int j = 0; j < WN; ++j) b_cur[j] = b_nxt[j];
+      for (int s = 0; s < 4; ++s) {
+        if (s < 3) read_ops(nxt, cur, wm, wn, lrow, lk, s + 1);
+        store_half(oth, s < 2 ? rn.a : rn.b, s < 2 ? 0 : 1, (s & 1) * 2, lut);
+        mfma8(acc, ops);
+        interleave();
+        if (s < 3) ops = nxt;
+      }
+      __syncthreads();
+      __builtin_amdgcn_sched_barrier(0);
+      load_raw<CHECKED, LD16>(rn, va, vb, kbyte(it + h + 3), g.K, kill(it + h + 3));
+      read_ops(ops, oth, wm, wn, lrow, lk, 0);
+      __builtin_amdgcn_sched_barrier(0);
+    }
   }
 
   // Epilogue: lane l holds column (l % 32) of each 32x32 block; accumulator
   // slot v is row (v % 4) + 8 * (v / 4) + 4 * (l / 32).
   const float alpha = (*g.a.ts) * (*g.b.ts);
+  const int64_t m0 = tm * kTile + wm * 128, n0 = tn * kTile + wn * 64;
 #pragma unroll
-  for (int i = 0; i < WM; ++i)
+  for (int i = 0; i < kWM; ++i)
 #pragma unroll
-    for (int j = 0; j < WN; ++j) {
+    for (int j = 0; j < kWN; ++j) {
       const int64_t col = n0 + 32 * j + lrow;
       if (col >= g.N) continue;
 #pragma unroll
       for (int v = 0; v < 16; ++v) {
-        const int64_t row = m0 + 32 * i + (v & 3) + 8 * (v >> 2) + 4 * khalf;
+        const int64_t row = m0 + 32 * i + (v & 3) + 8 * (v >> 2) + 4 * lk;
         if (row < g.M) g.c[row * g.ldc + col] = acc[i][j][v] * alpha;
       }
     }
 }
 
 hipError_t launch_gemm(const GemmOperand& a, const GemmOperand& b, int64_t K, float* c,
-                       int64_t ldc, int decode, hipStream_t s) {
+                       int64_t ldc, hipStream_t s) {
   GemmArgs g{a, b, a.rows, b.rows, K, c, ldc};
-  constexpr int WM = 4, WN = 4;
-  const int64_t tiles = ((g.M + 64 * WM - 1) / (64 * WM)) * ((g.N + 64 * WN - 1) / (64 * WN));
+  const int64_t tiles = ((g.M + kTile - 1) / kTile) * ((g.N + kTile - 1) / kTile);
   const dim3 grid((unsigned)tiles);
   const bool ld16 = (a.ld % 16 == 0) && (b.ld % 16 == 0);
   const bool checked = (K % 64) != 0;
-#define NVFP4_GEMM_LAUNCH(D, L, C) \
-  hipLaunchKernelGGL((k_gemm<WM, WN, D, L, C>), grid, dim3(256), 0, s, g)
-  if (decode == 0) {
-    if (checked) { if (ld16) NVFP4_GEMM_LAUNCH(0, true, true); else NVFP4_GEMM_LAUNCH(0, false, true); }
-    else if (ld16) NVFP4_GEMM_LAUNCH(0, true, false);
-    else NVFP4_GEMM_LAUNCH(0, false, false);
+#define NVFP4_GEMM_LAUNCH(C, L)                                                          \
+  do {                                                                                    \
+    hipError_t e = hipFuncSetAttribute(reinterpret_cast<const void*>(&k_gemm<C, L>),      \
+                                       hipFuncAttributeMaxDynamicSharedMemorySize,       \
+                                       kLdsBytes);                                       \
+    if (e != hipSuccess) return e;                                                        \
+    hipLaunchKernelGGL((k_gemm<C, L>), grid, dim3(kThreads), kLdsBytes, s, g);            \
+  } while (0)
+  if (checked) {
+    if (ld16) NVFP4_GEMM_LAUNCH(true, true);
+    else NVFP4_GEMM_LAUNCH(true, false);
   } else {
-    if (checked) { if (ld16) NVFP4_GEMM_LAUNCH(1, true, true); else NVFP4_GEMM_LAUNCH(1, false, true); }
-    else if (ld16) NVFP4_GEMM_LAUNCH(1, true, false);
-    else NVFP4_GEMM_LAUNCH(1, false, false);
+    if (ld16) NVFP4_GEMM_LAUNCH(false, true);
+    else NVFP4_GEMM_LAUNCH(false, false);
   }
 #undef NVFP4_GEMM_LAUNCH
   return hipGetLastError();

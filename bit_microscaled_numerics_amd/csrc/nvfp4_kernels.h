@@ -35,10 +35,10 @@ struct GemmOperand {
   int32_t blk_rows;
   const float* ts;
   int64_t rows;
+  int64_t scale_bytes;  // size of the scale array (last index + 1)
 };
 
-// decode: 0 = hardware FP4 convert with FP32 scale, 1 = byte-permute decode
 hipError_t launch_gemm(const GemmOperand& a, const GemmOperand& b, int64_t K, float* c,
-                       int64_t ldc, int decode, hipStream_t s);
+                       int64_t ldc, hipStream_t s);
 
 }  // namespace nvfp4

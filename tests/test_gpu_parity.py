@@ -153,21 +153,19 @@ GEMM_SHAPES = [(16, 16, 16), (48, 80, 48), (64, 32, 80), (256, 512, 512), (272, 
                (300 // 16 * 16, 400, 1040)]
 
 
-@pytest.mark.parametrize("decode", ["hw", "perm"])
 @pytest.mark.parametrize("mnk", GEMM_SHAPES)
-def test_gemm_fprop(mnk, decode, monkeypatch):
-    monkeypatch.setenv("NVFP4_GEMM_DECODE", decode)
+def test_gemm_fprop(mnk):
     M, N, K = mnk
     g = torch.Generator().manual_seed(M + N + K)
     x = inputs.normal(g, M, K, 1.0, 0.001, 50.0)
     w = inputs.normal(g, N, K, 0.02)
-    say("gemm fprop", mnk, decode)
+    say("gemm fprop", mnk)
     qx, qw = nv.quantize_1d(x.cuda()), nv.quantize_2d(w.cuda())
     y = nv.gemm(qx, qw)
     torch.cuda.synchronize()
     ox, ow = oracle.quantize(x, oracle.ROWWISE), oracle.quantize(w, oracle.TWO_D, with_codes_t=True)
     c, t = oracle.gemm(ox, ow)
-    assert_gemm_close(y.cpu().numpy(), c, t, f"fprop {mnk} {decode}")
+    assert_gemm_close(y.cpu().numpy(), c, t, f"fprop {mnk}")
 
 
 @pytest.mark.parametrize("mnk", [(48, 80, 64), (256, 512, 512), (272, 144, 528)])
