@@ -49,6 +49,21 @@ def log(*a):
     print("[bench]", *a, file=sys.stderr, flush=True)
 
 
+def gemm_traffic():
+    """HBM bytes per GEMM launch from the committed rocprofv3 FETCH_SIZE /
+    WRITE_SIZE record, or None when the GEMM source changed since."""
+    import hashlib
+    path = os.path.join(ROOT, "profiles", "gemm_traffic.json")
+    if not os.path.exists(path):
+        return None
+    rec = json.load(open(path))
+    m = hashlib.sha256()
+    for f in ("nvfp4_gemm.hip", "nvfp4_device.h"):
+        with open(os.path.join(ROOT, "bit_microscaled_numerics_amd", "csrc", f), "rb") as fh:
+            m.update(fh.read())
+    return rec["traffic_bytes_per_launch"] if m.hexdigest() == rec["source_sha256"] else None
+
+
 class Step:
     """Preallocated buffers and the ordered list of launches of one step."""
 
@@ -300,7 +315,7 @@ def main():
     roofline = {"bound": "mfma", "kernel": "k_gemm (Fprop, Dgrad, Wgrad launches)",
                 "achieved": round(achieved, 1), "peak": MFMA_F16_PEAK_TFLOPS,
                 "unit": "TFLOP/s", "frac": round(achieved / MFMA_F16_PEAK_TFLOPS, 4),
-                "traffic": None}
+                "traffic": gemm_traffic()}
     quant_ms = float(per_op[:, [i for i in range(nops) if i not in gemm_idx]].sum(axis=1).mean())
     quant_bytes = sum(a for (_, kind, a, _) in step.ops if kind == "hbm")
 
