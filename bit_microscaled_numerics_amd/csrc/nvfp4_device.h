@@ -23,12 +23,12 @@ typedef uint32_t v4u __attribute__((ext_vector_type(4)));
 typedef uint32_t v2u __attribute__((ext_vector_type(2)));
 typedef float v4f __attribute__((ext_vector_type(4)));
 
-// Global memory access points of the streaming kernels (one place to change
-// cache policy).
+// Global memory access points of the streaming kernels: non-temporal (each
+// byte is touched once per pass, so it should not displace cached data).
 template <class T>
-__device__ __forceinline__ T ld_(const T* p) { return *p; }
+__device__ __forceinline__ T ld_(const T* p) { return __builtin_nontemporal_load(p); }
 template <class T>
-__device__ __forceinline__ void st_(T v, T* p) { *p = v; }
+__device__ __forceinline__ void st_(T v, T* p) { __builtin_nontemporal_store(v, p); }
 
 // Tensor scale maps the tensor amax onto the largest block scale:
 // 6 (largest E2M1 magnitude) * 448 (largest E4M3 value).
@@ -85,25 +85,31 @@ __device__ __forceinline__ uint32_t e2m1_rtn_index(float a) {
   return i;
 }
 
-// Stochastic rounding of a >= 0 with 16 random bits u.  With lo <= a < hi the
+// Stochastic rounding of a >= 0 with 16 random bits u: with lo <= a < hi the
 // neighbouring grid values and p = (a - lo)/(hi - lo), round up iff
-// u < p * 65536.  lo - a is exact (Sterbenz) and the gaps are powers of two,
-// so p and p * 65536 are exact.  a >= 6 gives index 7.
+// u < p * 65536; a >= 6 gives index 7.  p * 65536 is exact, and the decision
+// is taken on integers from the binary32 fields of a:
+//   a < 0.5            : lo = 0,   gap 0.5 -> p*65536 = a * 2^17 (exact float)
+//   0.5 <= a < 1       : lo = 0.5, gap 0.5 -> p = mantissa / 2^23
+//   1 <= a < 6 (binade [2^e, 2^(e+1)), e = 0..2): the grid points are 2^e and
+//     1.5 * 2^e, so mantissa bit 22 picks the half-binade (the lower grid
+//     point) and p = (mantissa & (2^22 - 1)) / 2^22.
+// Round up iff u * 2^(23-16) < mantissa (first case: u < a * 2^17), resp.
+// u * 2^(22-16) < low 22 mantissa bits.
 __device__ __forceinline__ uint32_t e2m1_sr_index(float a, uint32_t u) {
   a = a < 6.0f ? a : 6.0f;
-  uint32_t i = 0;
-  i += (a >= 0.5f);
-  i += (a >= 1.0f);
-  i += (a >= 1.5f);
-  i += (a >= 2.0f);
-  i += (a >= 3.0f);
-  i += (a >= 4.0f);
-  i += (a >= 6.0f);
-  // grid value of index i and the reciprocal of the gap above it
-  float lo = i < 4u ? 0.5f * (float)i : (i < 7u ? (float)i - 2.0f : 6.0f);
-  float inv_gap = i < 4u ? 2.0f : (i < 6u ? 1.0f : 0.5f);
-  float p65536 = (a - lo) * inv_gap * 65536.0f;
-  return i + (((float)u < p65536) ? 1u : 0u);
+  const uint32_t bits = __float_as_uint(a);
+  const uint32_t e = bits >> 23;          // biased exponent (a >= 0)
+  const uint32_t mant = bits & 0x7FFFFFu;
+  // all three cases are evaluated and selected (no divergent branches)
+  const bool big = e >= 127u, mid = e == 126u;
+  const uint32_t lo_big = 2u * (e - 126u) + (mant >> 22);  // 1 -> 2/3, 2 -> 4/5, 4 -> 6/7
+  const bool up_big = (u << 6) < (mant & 0x3FFFFFu);
+  const bool up_mid = (u << 7) < mant;
+  const bool up_small = (float)u < a * 131072.0f;
+  const uint32_t lo = big ? lo_big : (mid ? 1u : 0u);
+  const bool up = big ? up_big : (mid ? up_mid : up_small);
+  return lo + (up ? 1u : 0u);
 }
 
 // ---------------------------------------------------------------------------
@@ -166,15 +172,18 @@ __device__ __forceinline__ void rht16(float (&v)[16], uint32_t signs) {
 // ---------------------------------------------------------------------------
 // Encoding one group of 8 elements given the block's reciprocal scale
 // ---------------------------------------------------------------------------
-// Codes of z[0..7] (element j in nibble j), round-to-nearest-even.
+// Codes of z[0..7] (element j in nibble j), round-to-nearest-even.  The
+// gfx950 FP4 encode (scale 1.0: no scaling) rounds a binary32 to the nearest
+// E2M1 value with ties to the even code, saturates beyond 6 and keeps the
+// sign of zero -- the same decision as e2m1_rtn_index, taken on the same
+// binary32 v = z * r (checked over millions of inputs around every decision
+// point); it packs two codes per byte, first operand in the low nibble.
 __device__ __forceinline__ uint32_t encode8_rtn(const float* z, float r) {
   uint32_t out = 0;
-#pragma unroll
-  for (int j = 0; j < 8; ++j) {
-    float v = z[j] * r;
-    uint32_t s = (__float_as_uint(v) >> 31) << 3;
-    out |= (s | e2m1_rtn_index(__builtin_fabsf(v))) << (4 * j);
-  }
+  out = __builtin_amdgcn_cvt_scalef32_pk_fp4_f32(out, z[0] * r, z[1] * r, 1.0f, 0);
+  out = __builtin_amdgcn_cvt_scalef32_pk_fp4_f32(out, z[2] * r, z[3] * r, 1.0f, 1);
+  out = __builtin_amdgcn_cvt_scalef32_pk_fp4_f32(out, z[4] * r, z[5] * r, 1.0f, 2);
+  out = __builtin_amdgcn_cvt_scalef32_pk_fp4_f32(out, z[6] * r, z[7] * r, 1.0f, 3);
   return out;
 }
 
@@ -199,6 +208,11 @@ __device__ __forceinline__ uint32_t encode8_zero(const float* z) {
 #pragma unroll
   for (int j = 0; j < 8; ++j) out |= ((__float_as_uint(z[j]) >> 31) << 3) << (4 * j);
   return out;
+}
+
+// A block whose scale is zero encodes as signed zeros (sign-only codes).
+__device__ __forceinline__ uint32_t select_zero_block(uint32_t code, uint32_t q, const float* z) {
+  return code == 0u ? encode8_zero(z) : q;
 }
 
 // Block scale code and reciprocal element scale from a block amax.

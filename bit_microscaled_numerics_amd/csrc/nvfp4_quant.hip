@@ -56,15 +56,16 @@ __device__ __forceinline__ uint32_t pk_max_u16(uint32_t a, uint32_t b) {
 
 __global__ __launch_bounds__(kThreads) void k_amax(const v4u* __restrict__ x, int64_t nvec,
                                                      uint32_t* __restrict__ out) {
+  constexpr int U = 8;  // 16-byte loads in flight per thread
   uint32_t m = 0;
   const int64_t stride = (int64_t)gridDim.x * kThreads;
   int64_t i = (int64_t)blockIdx.x * kThreads + threadIdx.x;
-  for (; i + 3 * stride < nvec; i += 4 * stride) {
-    v4u v[4];
+  for (; i + (U - 1) * stride < nvec; i += U * stride) {
+    v4u v[U];
 #pragma unroll
-    for (int u = 0; u < 4; ++u) v[u] = ld_(&x[i + u * stride]);
+    for (int u = 0; u < U; ++u) v[u] = ld_(&x[i + u * stride]);
 #pragma unroll
-    for (int u = 0; u < 4; ++u) {
+    for (int u = 0; u < U; ++u) {
       m = pk_max_u16(m, v[u].x & 0x7FFF7FFFu);
       m = pk_max_u16(m, v[u].y & 0x7FFF7FFFu);
       m = pk_max_u16(m, v[u].z & 0x7FFF7FFFu);
@@ -72,7 +73,7 @@ __global__ __launch_bounds__(kThreads) void k_amax(const v4u* __restrict__ x, in
     }
   }
   for (; i < nvec; i += stride) {
-    v4u v = ld_(&x[i]);
+    const v4u v = ld_(&x[i]);
     m = pk_max_u16(m, v.x & 0x7FFF7FFFu);
     m = pk_max_u16(m, v.y & 0x7FFF7FFFu);
     m = pk_max_u16(m, v.z & 0x7FFF7FFFu);
@@ -150,10 +151,11 @@ __global__ __launch_bounds__(kThreads) void k_quant_row(
     for (int j = 0; j < 8; ++j) m = fmaxf(m, __builtin_fabsf(z[j]));
     m = fmaxf(m, __shfl_xor(m, 1, 64));
     const BlockScale b = block_scale(m, s_t, t6);
-    uint32_t q;
-    if (b.code == 0u) q = encode8_zero(z);
-    else if (SR) q = encode8_sr(z, b.r, sr_words(seed, stream_id, (uint64_t)i * 8u));
-    else q = encode8_rtn(z, b.r);
+    // computed for every block (a zero scale gives inf/NaN here, discarded by
+    // the select), which keeps the lanes of a wave on one path
+    uint32_t q = SR ? encode8_sr(z, b.r, sr_words(seed, stream_id, (uint64_t)i * 8u))
+                    : encode8_rtn(z, b.r);
+    q = select_zero_block(b.code, q, z);
     st_(q, &codes[i]);
     if ((i & 1) == 0) scales[i >> 1] = (uint8_t)b.code;
   }
@@ -195,10 +197,7 @@ __global__ __launch_bounds__(kThreads) void k_quant_col(
       for (int j = 0; j < 16; ++j) m = fmaxf(m, __builtin_fabsf(v[j]));
       const BlockScale b = block_scale(m, s_t, t6);
       uint32_t q0, q1;
-      if (b.code == 0u) {
-        q0 = encode8_zero(v);
-        q1 = encode8_zero(v + 8);
-      } else if (SR) {
+      if (SR) {
         const uint64_t n0 = (uint64_t)(cc + c) * (uint64_t)rows + (uint64_t)rr;
         q0 = encode8_sr(v, b.r, sr_words(seed, stream_id, n0));
         q1 = encode8_sr(v + 8, b.r, sr_words(seed, stream_id, n0 + 8));
@@ -206,6 +205,8 @@ __global__ __launch_bounds__(kThreads) void k_quant_col(
         q0 = encode8_rtn(v, b.r);
         q1 = encode8_rtn(v + 8, b.r);
       }
+      q0 = select_zero_block(b.code, q0, v);
+      q1 = select_zero_block(b.code, q1, v + 8);
       lds_codes[8 * cg + c][rg] = v2u{q0, q1};
       lds_scales[8 * cg + c][rg] = (uint8_t)b.code;
     }
@@ -267,10 +268,7 @@ __global__ __launch_bounds__(kThreads) void k_quant_2d(
   for (int off = 1; off < 16; off <<= 1) m = fmaxf(m, __shfl_xor(m, off, 64));
   const BlockScale bs = block_scale(m, s_t, t6);
   uint32_t q0, q1;
-  if (bs.code == 0u) {
-    q0 = encode8_zero(z);
-    q1 = encode8_zero(z + 8);
-  } else if (SR) {
+  if (SR) {
     const uint64_t n0 = (uint64_t)row * (uint64_t)cols + (uint64_t)col0;
     q0 = encode8_sr(z, bs.r, sr_words(seed, stream_id, n0));
     q1 = encode8_sr(z + 8, bs.r, sr_words(seed, stream_id, n0 + 8));
@@ -278,9 +276,11 @@ __global__ __launch_bounds__(kThreads) void k_quant_2d(
     q0 = encode8_rtn(z, bs.r);
     q1 = encode8_rtn(z + 8, bs.r);
   }
+  q0 = select_zero_block(bs.code, q0, z);
+  q1 = select_zero_block(bs.code, q1, z + 8);
   if (valid) {
-    st_(v2u{q0, q1},
-                                reinterpret_cast<v2u*>(codes + row * (cols / 2) + col0 / 2));
+    // 8-byte pieces: plain (write-back) stores so L2 merges them into lines
+    *reinterpret_cast<v2u*>(codes + row * (cols / 2) + col0 / 2) = v2u{q0, q1};
     if (r == 0) scales[(row / 16) * (cols / 16) + col0 / 16] = (uint8_t)bs.code;
   }
   if (codes_t == nullptr) return;  // uniform across the grid
@@ -301,8 +301,7 @@ __global__ __launch_bounds__(kThreads) void k_quant_2d(
       lo |= (uint32_t)lds_t[c][16 * qd + j] << (4 * j);
       hi |= (uint32_t)lds_t[c][16 * qd + 8 + j] << (4 * j);
     }
-    st_(v2u{lo, hi},
-                                reinterpret_cast<v2u*>(codes_t + oc * (rows / 2) + orow / 2));
+    *reinterpret_cast<v2u*>(codes_t + oc * (rows / 2) + orow / 2) = v2u{lo, hi};
   }
 }
 
@@ -349,7 +348,7 @@ hipError_t launch_amax(const void* x, int64_t n_elems, float* out, hipStream_t s
   uint32_t* o = reinterpret_cast<uint32_t*>(out);
   hipLaunchKernelGGL(k_zero_u32, dim3(1), dim3(1), 0, s, o);
   const int64_t nvec = n_elems / 8;
-  hipLaunchKernelGGL(k_amax, dim3(grid_for(nvec / 4, 8)), dim3(kThreads), 0, s,
+  hipLaunchKernelGGL(k_amax, dim3(grid_for(nvec / 8, 4)), dim3(kThreads), 0, s,
                      reinterpret_cast<const v4u*>(x), nvec, o);
   return hipGetLastError();
 }

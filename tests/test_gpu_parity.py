@@ -121,6 +121,27 @@ def test_amax_given_skips_the_scan():
                                              amax_given=float(a.cpu()[0]) * 4))
 
 
+@pytest.mark.parametrize("factor", [1e-3, 1e-30])
+def test_given_amax_below_the_data_saturates(factor):
+    """A given amax far below the data: block scales saturate at 448 and
+    |v| is huge, so every code saturates at +-6 (RTN and SR, 1D and 2D)."""
+    x = _tensor("outliers", 272, 144)
+    xd = x.cuda()
+    a = oracle.amax(x) * factor
+    say("amax_given saturation", factor)
+    for gq, oq in [
+        (nv.quantize_1d(xd, amax=a), oracle.quantize(x, oracle.ROWWISE, amax_given=a)),
+        (nv.quantize_1d(xd, sr_seed=3, amax=a),
+         oracle.quantize(x, oracle.ROWWISE, sr_seed=3, amax_given=a)),
+        (nv.quantize_2d(xd, amax=a),
+         oracle.quantize(x, oracle.TWO_D, amax_given=a, with_codes_t=True)),
+        (nv.rht_quantize(xd, 2, amax=a),
+         oracle.quantize(x, oracle.COLWISE, rht_seed=2, amax_given=a)),
+    ]:
+        torch.cuda.synchronize()
+        assert_operand_equal(gq, oq, f"saturation {factor}")
+
+
 def test_sr_is_deterministic_and_seeded():
     x = _tensor("normal", 256, 512)
     xd = x.cuda()
