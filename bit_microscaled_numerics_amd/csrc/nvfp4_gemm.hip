@@ -34,6 +34,7 @@ struct GemmArgs {
   int64_t M, N, K;
   float* c;
   int64_t ldc;
+  int64_t full_tiles;  // tiles computed whole; tiles past them are split in two K halves
 };
 
 // Decoding.  The gfx950 FP4 -> FP16 convert multiplies by 2^floor(log2 s)
@@ -78,17 +79,35 @@ __device__ __forceinline__ half8 decode8(uint32_t w, const BlockDec& d) {
 // XCD at a time share both A rows and B columns in its L2.
 constexpr int kXcds = 8, kGroupM = 8;
 
-__device__ __forceinline__ void tile_coords(int64_t tiles_m, int64_t tiles_n, int64_t& tm,
-                                            int64_t& tn) {
-  const int64_t total = tiles_m * tiles_n, per = total / kXcds;
-  const int64_t b = blockIdx.x;
-  const int64_t t = b < per * kXcds ? (b % kXcds) * per + b / kXcds : b;
+// Linear tile index -> (tile row, tile column): groups of kGroupM tile-rows,
+// M fastest inside a group.
+__device__ __forceinline__ void grouped(int64_t t, int64_t tiles_m, int64_t tiles_n, int64_t& tm,
+                                        int64_t& tn) {
   const int64_t group = t / (kGroupM * tiles_n);
   const int64_t first_m = group * kGroupM;
   const int64_t gm = (tiles_m - first_m) < kGroupM ? (tiles_m - first_m) : kGroupM;
   const int64_t in = t - group * kGroupM * tiles_n;
   tm = first_m + in % gm;
   tn = in / gm;
+}
+
+// Block -> tile and K part.  Blocks below full_tiles take whole tiles
+// (renumbered so each XCD owns a contiguous range); the blocks after them
+// take the remaining tiles two per tile, part 0 / 1 = first / second K half
+// (the last partial round of tiles finishes in half the time).
+__device__ __forceinline__ void block_tile(int64_t full, int64_t tiles_m, int64_t tiles_n,
+                                           int64_t& tm, int64_t& tn, int& part) {
+  const int64_t b = blockIdx.x;
+  int64_t t;
+  if (b < full) {
+    const int64_t per = full / kXcds;
+    t = b < per * kXcds ? (b % kXcds) * per + b / kXcds : b;
+    part = -1;
+  } else {
+    t = full + (b - full) / 2;
+    part = (int)((b - full) & 1);
+  }
+  grouped(t, tiles_m, tiles_n, tm, tn);
 }
 
 constexpr int kTile = 256;  // workgroup tile (rows of A and of B)
@@ -283,7 +302,8 @@ __global__ __launch_bounds__(kThreads, 1) void k_gemm(GemmArgs g) {
   const int lrow = lane & 31, lk = lane >> 5;
   const int64_t tiles_m = (g.M + kTile - 1) / kTile, tiles_n = (g.N + kTile - 1) / kTile;
   int64_t tm, tn;
-  tile_coords(tiles_m, tiles_n, tm, tn);
+  int part;
+  block_tile(g.full_tiles, tiles_m, tiles_n, tm, tn, part);
   // loader views: this thread's chunk is row threadIdx.x/2 of the tile,
   // K-half threadIdx.x%2 (slot 0 of the view)
   OpView va = make_view(g.a, tm * kTile, 0, 0, threadIdx.x & 1);
@@ -302,20 +322,23 @@ __global__ __launch_bounds__(kThreads, 1) void k_gemm(GemmArgs g) {
 #pragma unroll
     for (int j = 0; j < kWN; ++j) acc[i][j] = float16v{};
 
-  const int64_t steps = (g.K + kBK - 1) / kBK;
-  const int64_t last = steps - 1;
+  // K steps [s0, s1): all of them, or one half for a split tile
+  const int64_t steps = (g.K + kBK - 1) / kBK, half_steps = (steps + 1) / 2;
+  const int64_t s0 = part == 1 ? half_steps : 0;
+  const int64_t s1 = part == 0 ? half_steps : steps;
+  const int64_t last = s1 - 1;
   auto kbyte = [&](int64_t t) { return (uint32_t)((t < last ? t : last) * 32); };
   auto kill = [&](int64_t t) { return t > last ? 0x80000000u : 0u; };
 
   Raw r0, r1;
-  load_raw<CHECKED, LD16>(r0, va, vb, kbyte(0), g.K, 0u);
-  load_raw<CHECKED, LD16>(r1, va, vb, kbyte(1), g.K, kill(1));
+  load_raw<CHECKED, LD16>(r0, va, vb, kbyte(s0), g.K, 0u);
+  load_raw<CHECKED, LD16>(r1, va, vb, kbyte(s0 + 1), g.K, kill(s0 + 1));
   __syncthreads();  // lookup table ready
   store_half(smem, r0.a, 0, 0, lut);
   store_half(smem, r0.a, 0, 2, lut);
   store_half(smem, r0.b, 1, 0, lut);
   store_half(smem, r0.b, 1, 2, lut);
-  load_raw<CHECKED, LD16>(r0, va, vb, kbyte(2), g.K, kill(2));
+  load_raw<CHECKED, LD16>(r0, va, vb, kbyte(s0 + 2), g.K, kill(s0 + 2));
   __syncthreads();
   StepOps ops, nxt;
   read_ops(ops, smem, wm, wn, lrow, lk, 0);
@@ -325,7 +348,7 @@ __global__ __launch_bounds__(kThreads, 1) void k_gemm(GemmArgs g) {
   // refilled with step it+3.  Two K steps per trip keep the raw sets in fixed
   // registers; the loop body is branch-free (steps past the last are killed
   // re-reads that decode to zeros).
-  for (int64_t it = 0; it < steps; it += 2) {
+  for (int64_t it = s0; it < s1; it += 2) {
 #pragma unroll
     for (int h = 0; h < 2; ++h) {
       uint8_t* cur = smem + (h ? 2 * kOpBytes : 0);
@@ -348,7 +371,10 @@ __global__ __launch_bounds__(kThreads, 1) void k_gemm(GemmArgs g) {
   }
 
   // Epilogue: lane l holds column (l % 32) of each 32x32 block; accumulator
-  // slot v is row (v % 4) + 8 * (v / 4) + 4 * (l / 32).
+  // slot v is row (v % 4) + 8 * (v / 4) + 4 * (l / 32).  A split tile adds
+  // its half into the zeroed output: with exactly two addends onto zero the
+  // sum does not depend on their order (fp32 addition commutes), so the
+  // result stays deterministic.
   const float alpha = (*g.a.ts) * (*g.b.ts);
   const int64_t m0 = tm * kTile + wm * 128, n0 = tn * kTile + wn * 64;
 #pragma unroll
@@ -360,16 +386,48 @@ __global__ __launch_bounds__(kThreads, 1) void k_gemm(GemmArgs g) {
 #pragma unroll
       for (int v = 0; v < 16; ++v) {
         const int64_t row = m0 + 32 * i + (v & 3) + 8 * (v >> 2) + 4 * lk;
-        if (row < g.M) g.c[row * g.ldc + col] = acc[i][j][v] * alpha;
+        if (row >= g.M) continue;
+        float* dst = &g.c[row * g.ldc + col];
+        if (part < 0) *dst = acc[i][j][v] * alpha;
+        else atomicAdd(dst, acc[i][j][v] * alpha);
       }
     }
 }
 
+// Zero the output tiles that split workgroups add into: one workgroup per
+// tile, same tile order as the GEMM.
+__global__ __launch_bounds__(256) void k_zero_tiles(float* __restrict__ c, int64_t ldc,
+                                                    int64_t M, int64_t N, int64_t tiles_m,
+                                                    int64_t tiles_n, int64_t first) {
+  int64_t tm, tn;
+  grouped(first + blockIdx.x, tiles_m, tiles_n, tm, tn);
+  const int64_t col = tn * kTile + threadIdx.x;
+  if (col >= N) return;
+  for (int64_t r = 0; r < kTile; ++r) {
+    const int64_t row = tm * kTile + r;
+    if (row >= M) break;
+    c[row * ldc + col] = 0.0f;
+  }
+}
+
 hipError_t launch_gemm(const GemmOperand& a, const GemmOperand& b, int64_t K, float* c,
                        int64_t ldc, hipStream_t s) {
-  GemmArgs g{a, b, a.rows, b.rows, K, c, ldc};
-  const int64_t tiles = ((g.M + kTile - 1) / kTile) * ((g.N + kTile - 1) / kTile);
-  const dim3 grid((unsigned)tiles);
+  GemmArgs g{a, b, a.rows, b.rows, K, c, ldc, 0};
+  const int64_t tiles_m = (g.M + kTile - 1) / kTile, tiles_n = (g.N + kTile - 1) / kTile;
+  const int64_t tiles = tiles_m * tiles_n;
+  // One workgroup per CU is resident (LDS).  When the last round is at most
+  // half full, its tiles are split in two K halves so it takes half a round.
+  const int64_t slots = num_cus();
+  const int64_t rem = tiles % slots, steps = (K + kBK - 1) / kBK;
+  const bool split = rem > 0 && 2 * rem <= slots && tiles > slots && steps >= 4;
+  g.full_tiles = split ? tiles - rem : tiles;
+  const dim3 grid((unsigned)(split ? tiles + rem : tiles));
+  if (split) {
+    hipLaunchKernelGGL(k_zero_tiles, dim3((unsigned)rem), dim3(256), 0, s, c, ldc, g.M, g.N,
+                       tiles_m, tiles_n, g.full_tiles);
+    const hipError_t e = hipGetLastError();
+    if (e != hipSuccess) return e;
+  }
   const bool ld16 = (a.ld % 16 == 0) && (b.ld % 16 == 0);
   const bool checked = (K % 64) != 0;
 #define NVFP4_GEMM_LAUNCH(C, L)                                                          \

@@ -251,3 +251,28 @@ def test_single_fprop_config():
     assert_operand_equal(qw, ow, "W")
     c, t = oracle.gemm(ox, ow)
     assert_gemm_close(y.cpu().numpy(), c, t, "single fprop")
+
+
+def test_gemm_split_last_round_is_exact_and_deterministic():
+    """M = 17*256, N = 16*256: 272 tiles on a 256-CU device leave a last
+    round of 16 tiles (the last tile-row), which the GEMM splits into two K
+    halves added into a zeroed output.  Check those tiles densely against the
+    exact oracle, the rest on samples, and two runs bit for bit."""
+    M, N, K = 17 * 256, 16 * 256, 1024
+    g = torch.Generator().manual_seed(40)
+    x = inputs.normal(g, M, K, 1.0, 0.001, 50.0)
+    w = inputs.normal(g, N, K, 0.02)
+    say("gemm split tail", (M, N, K))
+    qx, qw = nv.quantize_1d(x.cuda()), nv.quantize_2d(w.cuda())
+    y1 = nv.gemm(qx, qw)
+    y2 = nv.gemm(qx, qw)
+    torch.cuda.synchronize()
+    c1, c2 = y1.cpu().numpy(), y2.cpu().numpy()
+    assert np.array_equal(c1.view(np.uint32), c2.view(np.uint32))
+    ox, ow = oracle.quantize(x, oracle.ROWWISE), oracle.quantize(w, oracle.TWO_D)
+    rng = np.random.default_rng(1)
+    rows = np.concatenate([np.arange(16 * 256, M), rng.integers(0, 16 * 256, 64)])
+    cols = np.concatenate([np.arange(0, N, 61), [N - 1]])
+    ms, ns = np.meshgrid(rows, cols, indexing="ij")
+    ref, t = oracle.gemm_entries(ox, ow, ms.ravel(), ns.ravel())
+    assert_gemm_close(c1[ms.ravel(), ns.ravel()], ref, t, "split tail")
