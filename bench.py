@@ -6,7 +6,7 @@ all their quantizations) at the 12B hybrid's FFN down-projection shape,
 A step is the whole hot path over one batch of seeded synthetic inputs that
 are resident in HBM before timing starts:
   Q(X)   rowwise 1D RTN          (amax + encode)
-  Q(W)   2D 16x16 RTN + codes_t  (amax + encode)
+  Q(W)   2D 16x16 RTN + transposed codes and scales (amax + encode)
   Fprop  Y  = Q(X) Q(W)^T        M=8192  N=5120  K=20480
   Q(dY)  rowwise 1D SR           (amax + encode)
   Dgrad  dX = Q(dY) Q(W)         M=8192  N=20480 K=5120
@@ -94,9 +94,9 @@ class Step:
              lambda: nv.nvfp4_quantize1d_rtn(x, 0, q.qx.amax, G, q.qx.codes, q.qx.scales,
                                              q.qx.tensor_scale)),
             ("amax W", "hbm", 2 * n_w, lambda: nv.nvfp4_amax(w, q.qw.amax)),
-            ("quant W 2D RTN +codes_t", "hbm", 3.00390625 * n_w,
+            ("quant W 2D RTN +transposed", "hbm", 3.0078125 * n_w,
              lambda: nv.nvfp4_quantize2d_rtn(w, q.qw.amax, G, q.qw.codes, q.qw.codes_t,
-                                             q.qw.scales, q.qw.tensor_scale)),
+                                             q.qw.scales, q.qw.scales_t, q.qw.tensor_scale)),
             ("gemm Fprop", "mfma", 2.0 * T * H * F, lambda: nv.gemm(q.qx, q.qw, q.y)),
             ("amax dY", "hbm", 2 * n_dy, lambda: nv.nvfp4_amax(dy, q.qdy.amax)),
             ("quant dY rowwise SR", "hbm", 2.5625 * n_dy,
@@ -205,9 +205,9 @@ def quant_sweep(steps: int = 10):
             ("1d SR encode", 2.5625 * n, lambda: nv.nvfp4_quantize1d_sr(
                 x, 0, q1.amax, G, 7, 0, q1.codes, q1.scales, q1.tensor_scale)),
             ("2d RTN encode", 2.50390625 * n, lambda: nv.nvfp4_quantize2d_rtn(
-                x, q2.amax, G, q2.codes, None, q2.scales, q2.tensor_scale)),
-            ("2d RTN encode +codes_t", 3.00390625 * n, lambda: nv.nvfp4_quantize2d_rtn(
-                x, q2.amax, G, q2.codes, q2.codes_t, q2.scales, q2.tensor_scale)),
+                x, q2.amax, G, q2.codes, None, q2.scales, None, q2.tensor_scale)),
+            ("2d RTN encode +transposed", 3.0078125 * n, lambda: nv.nvfp4_quantize2d_rtn(
+                x, q2.amax, G, q2.codes, q2.codes_t, q2.scales, q2.scales_t, q2.tensor_scale)),
             ("col RTN encode", 2.5625 * n, lambda: nv.nvfp4_quantize1d_rtn(
                 x, 1, qc.amax, G, qc.codes, qc.scales, qc.tensor_scale)),
             ("amax RHT", 2 * n, lambda: nv.nvfp4_amax_rht(x, 1, qc.amax)),

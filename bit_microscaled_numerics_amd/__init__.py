@@ -68,8 +68,8 @@ def load_library(path: str = LIB_PATH) -> ctypes.CDLL:
         "nvfp4_amax_rht": [vp, i64, i64, u64, vp, vp],
         "nvfp4_quantize1d_rtn": [vp, i64, i64, i32, vp, i32, vp, vp, vp, vp],
         "nvfp4_quantize1d_sr": [vp, i64, i64, i32, vp, i32, u64, u32, vp, vp, vp, vp],
-        "nvfp4_quantize2d_rtn": [vp, i64, i64, vp, i32, vp, vp, vp, vp, vp],
-        "nvfp4_quantize2d_sr": [vp, i64, i64, vp, i32, u64, u32, vp, vp, vp, vp, vp],
+        "nvfp4_quantize2d_rtn": [vp, i64, i64, vp, i32, vp, vp, vp, vp, vp, vp],
+        "nvfp4_quantize2d_sr": [vp, i64, i64, vp, i32, u64, u32, vp, vp, vp, vp, vp, vp],
         "nvfp4_rht_quantize": [vp, i64, i64, u64, i32, u64, u32, vp, i32, vp, vp, vp, vp],
         "nvfp4_dequantize": [ctypes.POINTER(c_operand), vp, vp],
         "nvfp4_gemm": [ctypes.POINTER(c_operand), ctypes.POINTER(c_operand), vp, i64, vp],
@@ -134,19 +134,21 @@ def nvfp4_quantize1d_sr(x, axis, amax_io, amax_mode, seed, stream_id, codes, sca
                                               _p(ts_out), _stream(stream)))
 
 
-def nvfp4_quantize2d_rtn(w, amax_io, amax_mode, codes, codes_t, scales, ts_out, stream=None):
+def nvfp4_quantize2d_rtn(w, amax_io, amax_mode, codes, codes_t, scales, scales_t, ts_out,
+                         stream=None):
     _dev_bf16(w, "w")
     _check(load_library().nvfp4_quantize2d_rtn(_p(w), w.shape[0], w.shape[1], _p(amax_io),
                                                amax_mode, _p(codes), _p(codes_t), _p(scales),
-                                               _p(ts_out), _stream(stream)))
+                                               _p(scales_t), _p(ts_out), _stream(stream)))
 
 
-def nvfp4_quantize2d_sr(w, amax_io, amax_mode, seed, stream_id, codes, codes_t, scales, ts_out,
-                        stream=None):
+def nvfp4_quantize2d_sr(w, amax_io, amax_mode, seed, stream_id, codes, codes_t, scales, scales_t,
+                        ts_out, stream=None):
     _dev_bf16(w, "w")
     _check(load_library().nvfp4_quantize2d_sr(_p(w), w.shape[0], w.shape[1], _p(amax_io),
                                               amax_mode, seed, stream_id, _p(codes), _p(codes_t),
-                                              _p(scales), _p(ts_out), _stream(stream)))
+                                              _p(scales), _p(scales_t), _p(ts_out),
+                                              _stream(stream)))
 
 
 def nvfp4_rht_quantize(x, rht_seed, use_sr, sr_seed, stream_id, amax_io, amax_mode, codes,
@@ -183,6 +185,7 @@ class NVFP4Tensor:
     ss_row: int = 0
     ss_k: int = 1
     codes_t: Optional[torch.Tensor] = None   # 2D weights: the same codes transposed
+    scales_t: Optional[torch.Tensor] = None  # 2D weights: the scale matrix transposed
 
     def c_struct(self) -> c_operand:
         return c_operand(self.codes.data_ptr(), self.codes.shape[1], self.scales.data_ptr(),
@@ -193,6 +196,9 @@ class NVFP4Tensor:
         """A 2D-quantized weight read as its transpose (the Dgrad operand)."""
         if self.blk_rows != 16 or self.codes_t is None:
             raise ValueError("only 2D operands quantized with codes_t can be transposed")
+        if self.scales_t is not None:  # K-contiguous scales (the GEMM's fast path)
+            return NVFP4Tensor(self.codes_t, self.scales_t, self.tensor_scale, self.amax, self.k,
+                               self.rows, 16, self.rows // 16, 1, self.codes, self.scales)
         return NVFP4Tensor(self.codes_t, self.scales, self.tensor_scale, self.amax, self.k,
                            self.rows, 16, self.ss_k, self.ss_row, self.codes)
 
@@ -248,13 +254,16 @@ def quantize_2d(w: torch.Tensor, sr_seed: Optional[int] = None, stream_id: int =
     _dev_bf16(w, "w")
     R, C = w.shape
     codes, scales, ts = _outputs(R, C, w.device, (R // 16, C // 16))
-    codes_t = torch.empty(C, R // 2, dtype=torch.uint8, device=w.device) if with_codes_t else None
+    codes_t = scales_t = None
+    if with_codes_t:
+        codes_t = torch.empty(C, R // 2, dtype=torch.uint8, device=w.device)
+        scales_t = torch.empty(C // 16, R // 16, dtype=torch.uint8, device=w.device)
     am, mode = _amax_arg(w, amax)
     if sr_seed is None:
-        nvfp4_quantize2d_rtn(w, am, mode, codes, codes_t, scales, ts)
+        nvfp4_quantize2d_rtn(w, am, mode, codes, codes_t, scales, scales_t, ts)
     else:
-        nvfp4_quantize2d_sr(w, am, mode, sr_seed, stream_id, codes, codes_t, scales, ts)
-    return NVFP4Tensor(codes, scales, ts, am, R, C, 16, C // 16, 1, codes_t)
+        nvfp4_quantize2d_sr(w, am, mode, sr_seed, stream_id, codes, codes_t, scales, scales_t, ts)
+    return NVFP4Tensor(codes, scales, ts, am, R, C, 16, C // 16, 1, codes_t, scales_t)
 
 
 def rht_quantize(x: torch.Tensor, rht_seed: int, sr_seed: Optional[int] = None,

@@ -180,7 +180,8 @@ int nvfp4_quantize1d_sr(const void* x, int64_t rows, int64_t cols, int axis, flo
 
 static int quantize2d(const void* w, int64_t rows, int64_t cols, float* amax_io, int amax_mode,
                       bool sr, uint64_t seed, uint32_t stream_id, uint8_t* codes,
-                      uint8_t* codes_t, uint8_t* scales, float* ts_out, void* stream) {
+                      uint8_t* codes_t, uint8_t* scales, uint8_t* scales_t, float* ts_out,
+                      void* stream) {
   int st = check_tensor(w, rows, cols, "w");
   if (st) return st;
   if ((st = check_outputs(codes, scales, amax_io, ts_out))) return st;
@@ -194,21 +195,21 @@ static int quantize2d(const void* w, int64_t rows, int64_t cols, float* amax_io,
     if (e != hipSuccess) return launched(e);
   }
   return launched(nvfp4::launch_quant_2d(w, rows, cols, amax_io, sr, seed, stream_id, codes,
-                                         codes_t, scales, ts_out, s));
+                                         codes_t, scales, scales_t, ts_out, s));
 }
 
 int nvfp4_quantize2d_rtn(const void* w, int64_t rows, int64_t cols, float* amax_io, int amax_mode,
-                         uint8_t* codes, uint8_t* codes_t, uint8_t* scales, float* ts_out,
-                         void* stream) {
+                         uint8_t* codes, uint8_t* codes_t, uint8_t* scales, uint8_t* scales_t,
+                         float* ts_out, void* stream) {
   return quantize2d(w, rows, cols, amax_io, amax_mode, false, 0, 0, codes, codes_t, scales,
-                    ts_out, stream);
+                    scales_t, ts_out, stream);
 }
 
 int nvfp4_quantize2d_sr(const void* w, int64_t rows, int64_t cols, float* amax_io, int amax_mode,
                         uint64_t seed, uint32_t stream_id, uint8_t* codes, uint8_t* codes_t,
-                        uint8_t* scales, float* ts_out, void* stream) {
+                        uint8_t* scales, uint8_t* scales_t, float* ts_out, void* stream) {
   return quantize2d(w, rows, cols, amax_io, amax_mode, true, seed, stream_id, codes, codes_t,
-                    scales, ts_out, stream);
+                    scales, scales_t, ts_out, stream);
 }
 
 int nvfp4_rht_quantize(const void* x, int64_t rows, int64_t cols, uint64_t rht_seed, int use_sr,

@@ -10,16 +10,11 @@
 //
 // Exactness: an E2M1 value times an E4M3 scale has at most 6 significant bits
 // and lies in [2^-10, 2688], so it is exact in FP16; FP16 x FP16 products are
-// exact in FP32.  Each element is decoded once, in registers, straight into
-// the v_mfma_f32_32x32x16_f16 operand layout; the only rounding is the FP32
-// accumulation, and the tensor scales are applied once in the epilogue.
-//
-// Layout: a workgroup of 4 waves (2 x 2) computes a (64*WM) x (64*WN) tile;
-// each wave a (32*WM) x (32*WN) sub-tile as WM x WN blocks of 32x32.  Lane l
-// of a wave serves row (l % 32) of a 32-row slab and K-half (l / 32): per
-// 64-wide K step it loads 16 bytes of codes (two 16-element blocks) and the
-// two block scales, and feeds four MFMAs (8 codes each).  A and B use the
-// same lane-to-k assignment, so every k is paired with itself.
+// exact in FP32.  Every element is decoded once per workgroup into FP16 in
+// LDS and fed to v_mfma_f32_32x32x16_f16; the only rounding is the FP32
+// accumulation, and the tensor scales are applied once in the epilogue.  (The
+// gfx950 scaled FP4 MFMA takes power-of-two E8M0 scales per 32 elements, so
+// it cannot apply an E4M3 scale per 16 exactly.)
 #include "nvfp4_device.h"
 #include "nvfp4_kernels.h"
 
@@ -45,15 +40,6 @@ struct BlockDec {
   float e;       // E4M3 value as FP32 (the convert takes its exponent)
   half2v mant;   // {mantissa, mantissa} in FP16
 };
-
-__device__ __forceinline__ BlockDec block_dec(uint32_t code) {
-  BlockDec d;
-  d.e = e4m3_to_float(code);
-  const uint32_t mb = (__float_as_uint(d.e) >> 20) & 7u;
-  const uint32_t h = 0x3C00u | (mb << 7);
-  d.mant = __builtin_bit_cast(half2v, h | (h << 16));
-  return d;
-}
 
 // Eight codes (one 32-bit word, element e in nibble e) -> eight FP16 values
 // q * E, element e in lane-vector slot e.
@@ -111,23 +97,23 @@ __device__ __forceinline__ void block_tile(int64_t full, int64_t tiles_m, int64_
 }
 
 constexpr int kTile = 256;  // workgroup tile (rows of A and of B)
-constexpr int kWaveTile = 4; // 32x32 blocks per wave along each dimension
 constexpr uint32_t kBufFlags = 0x00020000u;  // raw 32-bit buffer descriptor word 3
 
 // Buffer view of one operand for one workgroup: codes and scales of the
-// 256-row slab starting at row0.  Loads take the row part of the offset in
-// a VGPR (fixed for the whole K loop) and the K part in an SGPR, so rows past
-// the operand lie beyond num_records whatever the bounds rule includes, and
-// read as zero; no row clamping or per-iteration address arithmetic.
+// 256-row slab starting at row0.  Loads take this thread's row part of the
+// offset in a VGPR (fixed for the whole K loop) and the K part in an SGPR,
+// so rows past the operand lie beyond num_records and read as zero; no row
+// clamping or per-iteration address arithmetic.
 struct OpView {
   __amdgpu_buffer_rsrc_t codes, scales;
-  uint32_t voff_codes[kWaveTile];   // per 32-row slab: row * ld + 16 * khalf
-  uint32_t voff_scales[kWaveTile];  // (row / blk) * ss_row + 2 * khalf * ss_k
+  uint32_t voff_codes;   // row * ld + 16 * khalf
+  uint32_t voff_scales;  // (row / blk) * ss_row + 2 * khalf * ss_k
+  uint32_t voff_srow;     // (row / blk) * ss_row
   uint32_t ss_k;
 };
 
-__device__ __forceinline__ OpView make_view(const GemmOperand& op, int64_t row0, int wrow0,
-                                            int lrow, int khalf) {
+// Thread t of the workgroup loads row t / 2 of the slab, K-half t % 2.
+__device__ __forceinline__ OpView make_view(const GemmOperand& op, int64_t row0) {
   OpView v;
   const int64_t rem_rows = op.rows - row0;
   const int64_t code_bytes = rem_rows * op.ld;
@@ -139,62 +125,71 @@ __device__ __forceinline__ OpView make_view(const GemmOperand& op, int64_t row0,
   v.scales = __builtin_amdgcn_make_buffer_rsrc(
       const_cast<uint8_t*>(sbase), (short)0,
       (int)(scale_bytes < 0x7FFFFFFF ? scale_bytes : 0x7FFFFFFF), (int)kBufFlags);
-#pragma unroll
-  for (int i = 0; i < kWaveTile; ++i) {
-    const int r = wrow0 + 32 * i + lrow;   // row within the workgroup slab
-    v.voff_codes[i] = (uint32_t)(r * op.ld + 16 * khalf);
-    v.voff_scales[i] = (uint32_t)((r / op.blk_rows) * op.ss_row + 2 * khalf * op.ss_k);
-  }
+  const int r = threadIdx.x >> 1, kh = threadIdx.x & 1;
+  v.voff_codes = (uint32_t)(r * op.ld + 16 * kh);
+  v.voff_srow = (uint32_t)((r / op.blk_rows) * op.ss_row);
+  v.voff_scales = v.voff_srow + (uint32_t)(2 * kh * op.ss_k);
   v.ss_k = (uint32_t)op.ss_k;
   return v;
 }
 
-// Per-lane raw data of one 32-row slab for one 64-wide K step: 32 codes
-// (k = k0 + 32*khalf .. +31) and the two block-scale bytes, kept raw until
-// the step that consumes them.
+// Per-thread raw data of one 64-wide K step of one operand: 32 codes
+// (k = k0 + 32*khalf .. +31) and the scale codes of their two 16-element
+// blocks: byte 0 of s0 and of s1, or (dword scales) bytes 2*khalf and
+// 2*khalf + 1 of s0 == s1.
 struct Slab {
   v4u codes;
   uint32_t s0, s1;
 };
 
-// kbyte = k0 / 2 (uniform); CHECKED zero-fills codes at k >= K.  kill adds
-// 2^31 to the scales' scalar offset, which puts them past num_records: they
-// read as 0, and a zero scale decodes every code to +-0 (a step that must
-// not contribute, at no VALU cost).
-template <bool CHECKED, bool LD16>
-__device__ __forceinline__ Slab load_slab(const OpView& v, int i, uint32_t kbyte, int khalf,
-                                          int64_t K, uint32_t kill = 0u) {
+// Scale addressing, two forms:
+//  - bytes (any layout): two byte loads per step.
+//  - dword (scales contiguous along K, rows 4-byte aligned): one 4-byte load
+//    brings the step's four block scales of the row, both K-halves.
+// kill adds 2^31 to the scales' scalar offset, past num_records: they read
+// 0, and a zero scale decodes every code to +-0, so a step past the last one
+// adds nothing.  kbyte = k0 / 2 (uniform).  Blocks at k >= K are zeroed at
+// decode time through their scale (zero_tail), not here: a select on a
+// loaded value would stall on the load right after issuing it.
+template <bool LD16, bool SDW>
+__device__ __forceinline__ Slab load_slab(const OpView& v, uint32_t kbyte, uint32_t kill) {
   Slab s;
   if (LD16) {
     s.codes = __builtin_bit_cast(v4u, __builtin_amdgcn_raw_buffer_load_b128(
-                                          v.codes, v.voff_codes[i], kbyte, 0));
+                                          v.codes, v.voff_codes, kbyte, 0));
   } else {  // K % 32 == 16: rows are 8-byte aligned
     const v2u lo = __builtin_bit_cast(v2u, __builtin_amdgcn_raw_buffer_load_b64(
-                                               v.codes, v.voff_codes[i], kbyte, 0));
+                                               v.codes, v.voff_codes, kbyte, 0));
     const v2u hi = __builtin_bit_cast(v2u, __builtin_amdgcn_raw_buffer_load_b64(
-                                               v.codes, v.voff_codes[i] + 8, kbyte, 0));
+                                               v.codes, v.voff_codes + 8, kbyte, 0));
     s.codes = v4u{lo.x, lo.y, hi.x, hi.y};
   }
-  const uint32_t sk = (kbyte / 8) * v.ss_k + kill;  // block index (k0 / 16) times its stride
-  s.s0 = __builtin_amdgcn_raw_buffer_load_b8(v.scales, v.voff_scales[i], sk, 0);
-  s.s1 = __builtin_amdgcn_raw_buffer_load_b8(v.scales, v.voff_scales[i] + v.ss_k, sk, 0);
-  if (CHECKED) {
-    const int64_t kk = 2 * (int64_t)kbyte + 32 * khalf;
-    if (kk + 16 > K) { s.codes = v4u{0u, 0u, 0u, 0u}; s.s0 = 0u; s.s1 = 0u; }
-    else if (kk + 32 > K) { s.codes.z = 0u; s.codes.w = 0u; s.s1 = 0u; }
+  if (SDW) {
+    s.s0 = s.s1 = __builtin_amdgcn_raw_buffer_load_b32(v.scales, v.voff_srow, kbyte / 8 + kill, 0);
+  } else {
+    const uint32_t sk = (kbyte / 8) * v.ss_k + kill;  // block index (k0 / 16) times its stride
+    s.s0 = __builtin_amdgcn_raw_buffer_load_b8(v.scales, v.voff_scales, sk, 0);
+    s.s1 = __builtin_amdgcn_raw_buffer_load_b8(v.scales, v.voff_scales + v.ss_k, sk, 0);
   }
   return s;
 }
 
-// Scale table: E4M3 code -> {FP32 value (the convert takes its exponent),
-// FP16 mantissa pair}.  128 entries in LDS, filled once per workgroup.
+// Scale table: E4M3 code (0..127) -> {E as FP32, FP16 mantissa pair}, 1 KiB
+// of LDS filled once per workgroup (one 8-byte LDS read per block scale
+// costs less VALU than decoding the code).  The gfx950 FP8 -> FP32 convert
+// (OCP E4M3FN, subnormals included) gives E exactly; its FP32 mantissa bits
+// give the factor (1 + m/8).
 __device__ __forceinline__ v2u scale_entry(uint32_t code) {
-  const BlockDec d = block_dec(code);
-  return v2u{__float_as_uint(d.e), __builtin_bit_cast(uint32_t, d.mant)};
+  const float e = __builtin_amdgcn_cvt_f32_fp8((int)code, 0);
+  const uint32_t mb = (__float_as_uint(e) >> 20) & 7u;
+  const uint32_t h = 0x3C00u | (mb << 7);
+  return v2u{__float_as_uint(e), h | (h << 16)};
 }
 
-__device__ __forceinline__ BlockDec lut_dec(const v2u* lut, uint32_t code) {
-  const v2u e = lut[code & 0x7Fu];
+// Decode the scale code in bits [pos, pos + 7) of w (the sign bit of an
+// E4M3 code is dropped: block scales are non-negative).
+__device__ __forceinline__ BlockDec scale_dec(const v2u* lut, uint32_t w, uint32_t pos) {
+  const v2u e = lut[__builtin_amdgcn_ubfe(w, pos, 7)];
   // copy the lanes to scalars first: clang's __builtin_bit_cast of an
   // ext-vector element expression reads element 0
   const uint32_t ex = e.x, ey = e.y;
@@ -217,11 +212,17 @@ __device__ __forceinline__ BlockDec lut_dec(const v2u* lut, uint32_t code) {
 // step it+1 is interleaved with the MFMAs of step it; raw codes are loaded
 // two K steps ahead.
 //
-// LDS: 2 stages x (A, B) x [256 rows][128 B] = 128 KiB.  A row holds 64 FP16
-// values = 8 chunks of 16 B; chunk j of row r sits at position
-// j ^ ((r >> 1) & 7), which makes both the operand reads (16 consecutive
-// rows, one chunk each) and the decode writes (8 rows x 2 halves) touch 16
-// distinct 16-byte bank groups of the 64-bank LDS.
+// LDS: (A, B) x 2 stages x [256 rows][128 B] = 128 KiB, ordered A0 A1 B0 B1
+// so an operand's two stages lie within reach of the 16-bit LDS immediate
+// offset from one address register.  A row holds 64 FP16
+// values = 8 chunks of 16 B; chunk j of row r sits at position j ^ f(r),
+// f(r) = ((r >> 1) ^ ((r & 1) << 1)) & 7.  On gfx950 a 16-byte LDS read
+// serves 16 consecutive lanes per cycle over 256 B of banks, a 16-byte write
+// only 8 lanes over 128 B (measured with SQ_LDS_BANK_CONFLICT).  The operand
+// reads (16 consecutive rows, one chunk) then touch 16 distinct 16-byte bank
+// groups since f is a bijection on the even rows and on the odd rows of any
+// 16; the decode writes (4 rows x chunks {p, p + 4} per 8 lanes) touch 8,
+// since f(r) & 3 differs across every aligned group of 4 rows.
 constexpr int kBK = 64;
 constexpr int kThreads = 512;
 constexpr int kWM = 4, kWN = 2;                    // 32x32 blocks per wave
@@ -230,7 +231,8 @@ constexpr int kOpBytes = kTile * kRowBytes;        // 32 KiB per operand and sta
 constexpr int kLdsBytes = 4 * kOpBytes;            // 128 KiB
 
 __device__ __forceinline__ uint32_t lds_off(int row, int chunk) {
-  return (uint32_t)(row * kRowBytes + ((chunk ^ ((row >> 1) & 7)) << 4));
+  const int f = ((row >> 1) ^ ((row & 1) << 1)) & 7;
+  return (uint32_t)(row * kRowBytes + ((chunk ^ f) << 4));
 }
 
 struct StepOps {
@@ -250,25 +252,39 @@ struct Raw {
   Slab a, b;
 };
 
-template <bool CHECKED, bool LD16>
+template <bool LD16, bool SDW>
 __device__ __forceinline__ void load_raw(Raw& r, const OpView& va, const OpView& vb,
-                                         uint32_t kbyte, int64_t K, uint32_t kill) {
-  r.a = load_slab<CHECKED, LD16>(va, 0, kbyte, threadIdx.x & 1, K, kill);
-  r.b = load_slab<CHECKED, LD16>(vb, 0, kbyte, threadIdx.x & 1, K, kill);
+                                         uint32_t kbyte, uint32_t kill) {
+  r.a = load_slab<LD16, SDW>(va, kbyte, kill);
+  r.b = load_slab<LD16, SDW>(vb, kbyte, kill);
+}
+
+// K % 64 != 0: in step t, this thread's blocks start at k = 64 t + 32 khalf
+// and + 16; a block at or past K gets scale code 0, so its codes (whatever
+// bytes the row holds there) decode to +-0.  Byte-loaded scales only.
+template <bool CHECKED>
+__device__ __forceinline__ void zero_tail(Raw& r, int t, int64_t K) {
+  if (!CHECKED) return;
+  const int64_t kk = 64 * (int64_t)t + 32 * (threadIdx.x & 1);
+  if (kk >= K) { r.a.s0 = 0u; r.b.s0 = 0u; }
+  if (kk + 16 >= K) { r.a.s1 = 0u; r.b.s1 = 0u; }
 }
 
 // Decode words p0, p0+1 of this thread's chunk of operand `op` (0 = A,
-// 1 = B) into an LDS stage.
-__device__ __forceinline__ void store_half(uint8_t* stage, const Slab& sl, int op, int p0,
-                                           const v2u* lut) {
-  uint8_t* base = stage + op * kOpBytes;
+// 1 = B) into an LDS stage.  The first block's scale code sits at bit pos0
+// of s0, the second's at bit pos1 of s1.
+__device__ __forceinline__ void store_half(uint8_t* stage, const v2u* lut, const v4u& codes,
+                                           uint32_t s0, uint32_t pos0, uint32_t s1,
+                                           uint32_t pos1, int op, int p0) {
+  uint8_t* base = stage + op * 2 * kOpBytes;
   const int row = threadIdx.x >> 1, half = threadIdx.x & 1;
-  const BlockDec d = lut_dec(lut, p0 < 2 ? sl.s0 : sl.s1);
+  const BlockDec d = p0 < 2 ? scale_dec(lut, s0, pos0) : scale_dec(lut, s1, pos1);
 #pragma unroll
   for (int p = p0; p < p0 + 2; ++p)
-    *reinterpret_cast<half8*>(base + lds_off(row, 4 * half + p)) = decode8(sl.codes[p], d);
+    *reinterpret_cast<half8*>(base + lds_off(row, 4 * half + p)) = decode8(codes[p], d);
 }
 
+// MFMA operands of K sub-step s (16 wide) of this wave's rows and columns.
 __device__ __forceinline__ void read_ops(StepOps& o, const uint8_t* stage, int wm, int wn,
                                          int lrow, int lk, int s) {
 #pragma unroll
@@ -276,7 +292,7 @@ __device__ __forceinline__ void read_ops(StepOps& o, const uint8_t* stage, int w
     o.a[i] = *reinterpret_cast<const half8*>(stage + lds_off(wm * 128 + 32 * i + lrow, 2 * s + lk));
 #pragma unroll
   for (int j = 0; j < kWN; ++j)
-    o.b[j] = *reinterpret_cast<const half8*>(stage + kOpBytes +
+    o.b[j] = *reinterpret_cast<const half8*>(stage + 2 * kOpBytes +
                                              lds_off(wn * 64 + 32 * j + lrow, 2 * s + lk));
 }
 
@@ -291,7 +307,7 @@ __device__ __forceinline__ void interleave() {
   }
 }
 
-template <bool CHECKED, bool LD16>
+template <bool CHECKED, bool LD16, bool SDW>
 __global__ __launch_bounds__(kThreads, 1) void k_gemm(GemmArgs g) {
   extern __shared__ __attribute__((aligned(16))) uint8_t smem[];
   __shared__ v2u lut[128];
@@ -304,17 +320,11 @@ __global__ __launch_bounds__(kThreads, 1) void k_gemm(GemmArgs g) {
   int64_t tm, tn;
   int part;
   block_tile(g.full_tiles, tiles_m, tiles_n, tm, tn, part);
-  // loader views: this thread's chunk is row threadIdx.x/2 of the tile,
-  // K-half threadIdx.x%2 (slot 0 of the view)
-  OpView va = make_view(g.a, tm * kTile, 0, 0, threadIdx.x & 1);
-  OpView vb = make_view(g.b, tn * kTile, 0, 0, threadIdx.x & 1);
-  {
-    const int r = threadIdx.x >> 1, kh = threadIdx.x & 1;
-    va.voff_codes[0] = (uint32_t)(r * g.a.ld + 16 * kh);
-    va.voff_scales[0] = (uint32_t)((r / g.a.blk_rows) * g.a.ss_row + 2 * kh * g.a.ss_k);
-    vb.voff_codes[0] = (uint32_t)(r * g.b.ld + 16 * kh);
-    vb.voff_scales[0] = (uint32_t)((r / g.b.blk_rows) * g.b.ss_row + 2 * kh * g.b.ss_k);
-  }
+  const OpView va = make_view(g.a, tm * kTile);
+  const OpView vb = make_view(g.b, tn * kTile);
+  // Bit positions of this thread's two scale codes: byte 0 of s0 / s1 for
+  // byte loads; in a scale dword, this K-half's pair sits 2 bytes further in.
+  const uint32_t pos0 = SDW ? 16u * (threadIdx.x & 1) : 0u, pos1 = SDW ? pos0 + 8u : 0u;
 
   float16v acc[kWM][kWN];
 #pragma unroll
@@ -322,23 +332,25 @@ __global__ __launch_bounds__(kThreads, 1) void k_gemm(GemmArgs g) {
 #pragma unroll
     for (int j = 0; j < kWN; ++j) acc[i][j] = float16v{};
 
-  // K steps [s0, s1): all of them, or one half for a split tile
-  const int64_t steps = (g.K + kBK - 1) / kBK, half_steps = (steps + 1) / 2;
-  const int64_t s0 = part == 1 ? half_steps : 0;
-  const int64_t s1 = part == 0 ? half_steps : steps;
-  const int64_t last = s1 - 1;
-  auto kbyte = [&](int64_t t) { return (uint32_t)((t < last ? t : last) * 32); };
-  auto kill = [&](int64_t t) { return t > last ? 0x80000000u : 0u; };
+  // K steps [s0, s1): all of them, or one half for a split tile.  32-bit
+  // step arithmetic (K <= 2^23, checked on the host) stays on the scalar unit.
+  const int steps = (int)((g.K + kBK - 1) / kBK), half_steps = (steps + 1) / 2;
+  const int s0 = part == 1 ? half_steps : 0;
+  const int s1 = part == 0 ? half_steps : steps;
+  const int last = s1 - 1;
+  auto kbyte = [&](int t) { return (uint32_t)((t < last ? t : last) * 32); };
+  auto kill = [&](int t) { return t > last ? 0x80000000u : 0u; };
 
   Raw r0, r1;
-  load_raw<CHECKED, LD16>(r0, va, vb, kbyte(s0), g.K, 0u);
-  load_raw<CHECKED, LD16>(r1, va, vb, kbyte(s0 + 1), g.K, kill(s0 + 1));
-  __syncthreads();  // lookup table ready
-  store_half(smem, r0.a, 0, 0, lut);
-  store_half(smem, r0.a, 0, 2, lut);
-  store_half(smem, r0.b, 1, 0, lut);
-  store_half(smem, r0.b, 1, 2, lut);
-  load_raw<CHECKED, LD16>(r0, va, vb, kbyte(s0 + 2), g.K, kill(s0 + 2));
+  load_raw<LD16, SDW>(r0, va, vb, kbyte(s0), 0u);
+  load_raw<LD16, SDW>(r1, va, vb, kbyte(s0 + 1), kill(s0 + 1));
+  __syncthreads();  // scale table ready
+  zero_tail<CHECKED>(r0, s0, g.K);
+  store_half(smem, lut, r0.a.codes, r0.a.s0, pos0, r0.a.s1, pos1, 0, 0);
+  store_half(smem, lut, r0.a.codes, r0.a.s0, pos0, r0.a.s1, pos1, 0, 2);
+  store_half(smem, lut, r0.b.codes, r0.b.s0, pos0, r0.b.s1, pos1, 1, 0);
+  store_half(smem, lut, r0.b.codes, r0.b.s0, pos0, r0.b.s1, pos1, 1, 2);
+  load_raw<LD16, SDW>(r0, va, vb, kbyte(s0 + 2), kill(s0 + 2));
   __syncthreads();
   StepOps ops, nxt;
   read_ops(ops, smem, wm, wn, lrow, lk, 0);
@@ -348,23 +360,25 @@ __global__ __launch_bounds__(kThreads, 1) void k_gemm(GemmArgs g) {
   // refilled with step it+3.  Two K steps per trip keep the raw sets in fixed
   // registers; the loop body is branch-free (steps past the last are killed
   // re-reads that decode to zeros).
-  for (int64_t it = s0; it < s1; it += 2) {
+  for (int it = s0; it < s1; it += 2) {
 #pragma unroll
     for (int h = 0; h < 2; ++h) {
-      uint8_t* cur = smem + (h ? 2 * kOpBytes : 0);
-      uint8_t* oth = smem + (h ? 0 : 2 * kOpBytes);
+      uint8_t* cur = smem + (h ? kOpBytes : 0);
+      uint8_t* oth = smem + (h ? 0 : kOpBytes);
       Raw& rn = h ? r0 : r1;      // raw data of step it+h+1
+      zero_tail<CHECKED>(rn, it + h + 1, g.K);
 #pragma unroll
       for (int s = 0; s < 4; ++s) {
         if (s < 3) read_ops(nxt, cur, wm, wn, lrow, lk, s + 1);
-        store_half(oth, s < 2 ? rn.a : rn.b, s < 2 ? 0 : 1, (s & 1) * 2, lut);
+        if (s < 2) store_half(oth, lut, rn.a.codes, rn.a.s0, pos0, rn.a.s1, pos1, 0, (s & 1) * 2);
+        else store_half(oth, lut, rn.b.codes, rn.b.s0, pos0, rn.b.s1, pos1, 1, (s & 1) * 2);
         mfma8(acc, ops);
         interleave();
         if (s < 3) ops = nxt;
       }
       __syncthreads();
       __builtin_amdgcn_sched_barrier(0);
-      load_raw<CHECKED, LD16>(rn, va, vb, kbyte(it + h + 3), g.K, kill(it + h + 3));
+      load_raw<LD16, SDW>(rn, va, vb, kbyte(it + h + 3), kill(it + h + 3));
       read_ops(ops, oth, wm, wn, lrow, lk, 0);
       __builtin_amdgcn_sched_barrier(0);
     }
@@ -430,20 +444,27 @@ hipError_t launch_gemm(const GemmOperand& a, const GemmOperand& b, int64_t K, fl
   }
   const bool ld16 = (a.ld % 16 == 0) && (b.ld % 16 == 0);
   const bool checked = (K % 64) != 0;
-#define NVFP4_GEMM_LAUNCH(C, L)                                                          \
+  // dword scales: scales contiguous along K, every row's scales 4-byte
+  // aligned (K % 64 == 0 makes each row's K/16 bytes a multiple of 4)
+  auto sdw_ok = [](const GemmOperand& o) {
+    return o.ss_k == 1 && o.ss_row % 4 == 0 && (reinterpret_cast<uintptr_t>(o.scales) & 3) == 0;
+  };
+  const bool sdw = !checked && ld16 && sdw_ok(a) && sdw_ok(b);
+#define NVFP4_GEMM_LAUNCH(C, L, W)                                                       \
   do {                                                                                    \
-    hipError_t e = hipFuncSetAttribute(reinterpret_cast<const void*>(&k_gemm<C, L>),      \
+    hipError_t e = hipFuncSetAttribute(reinterpret_cast<const void*>(&k_gemm<C, L, W>),   \
                                        hipFuncAttributeMaxDynamicSharedMemorySize,       \
                                        kLdsBytes);                                       \
     if (e != hipSuccess) return e;                                                        \
-    hipLaunchKernelGGL((k_gemm<C, L>), grid, dim3(kThreads), kLdsBytes, s, g);            \
+    hipLaunchKernelGGL((k_gemm<C, L, W>), grid, dim3(kThreads), kLdsBytes, s, g);         \
   } while (0)
-  if (checked) {
-    if (ld16) NVFP4_GEMM_LAUNCH(true, true);
-    else NVFP4_GEMM_LAUNCH(true, false);
+  if (sdw) NVFP4_GEMM_LAUNCH(false, true, true);
+  else if (checked) {
+    if (ld16) NVFP4_GEMM_LAUNCH(true, true, false);
+    else NVFP4_GEMM_LAUNCH(true, false, false);
   } else {
-    if (ld16) NVFP4_GEMM_LAUNCH(false, true);
-    else NVFP4_GEMM_LAUNCH(false, false);
+    if (ld16) NVFP4_GEMM_LAUNCH(false, true, false);
+    else NVFP4_GEMM_LAUNCH(false, false, false);
   }
 #undef NVFP4_GEMM_LAUNCH
   return hipGetLastError();

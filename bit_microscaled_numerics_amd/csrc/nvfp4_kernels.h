@@ -21,7 +21,7 @@ hipError_t launch_quant_col(const void* x, int64_t rows, int64_t cols, const flo
                             hipStream_t s);
 hipError_t launch_quant_2d(const void* x, int64_t rows, int64_t cols, const float* amax, bool sr,
                            uint64_t seed, uint32_t stream_id, uint8_t* codes, uint8_t* codes_t,
-                           uint8_t* scales, float* ts_out, hipStream_t s);
+                           uint8_t* scales, uint8_t* scales_t, float* ts_out, hipStream_t s);
 hipError_t launch_dequant(const uint8_t* codes, int64_t ld_codes, const uint8_t* scales,
                           int64_t ss_row, int64_t ss_k, int32_t blk_rows, const float* ts,
                           int64_t rows, int64_t k, float* out, hipStream_t s);

@@ -240,7 +240,7 @@ __global__ __launch_bounds__(kThreads) void k_quant_2d(
     const uint16_t* __restrict__ x, int64_t rows, int64_t cols,
     const float* __restrict__ amax, uint64_t seed, uint32_t stream_id,
     uint8_t* __restrict__ codes, uint8_t* __restrict__ codes_t, uint8_t* __restrict__ scales,
-    float* __restrict__ ts_out) {
+    uint8_t* __restrict__ scales_t, float* __restrict__ ts_out) {
   __shared__ uint8_t lds_t[64][64 + 16];  // [column][row]; padded rows
   const float s_t = tensor_scale_from_amax(*amax);
   const float t6 = 6.0f * s_t;
@@ -281,7 +281,10 @@ __global__ __launch_bounds__(kThreads) void k_quant_2d(
   if (valid) {
     // 8-byte pieces: plain (write-back) stores so L2 merges them into lines
     *reinterpret_cast<v2u*>(codes + row * (cols / 2) + col0 / 2) = v2u{q0, q1};
-    if (r == 0) scales[(row / 16) * (cols / 16) + col0 / 16] = (uint8_t)bs.code;
+    if (r == 0) {
+      scales[(row / 16) * (cols / 16) + col0 / 16] = (uint8_t)bs.code;
+      if (scales_t != nullptr) scales_t[(col0 / 16) * (rows / 16) + row / 16] = (uint8_t)bs.code;
+    }
   }
   if (codes_t == nullptr) return;  // uniform across the grid
 #pragma unroll
@@ -399,15 +402,15 @@ hipError_t launch_quant_col(const void* x, int64_t rows, int64_t cols, const flo
 
 hipError_t launch_quant_2d(const void* x, int64_t rows, int64_t cols, const float* amax, bool sr,
                            uint64_t seed, uint32_t stream_id, uint8_t* codes, uint8_t* codes_t,
-                           uint8_t* scales, float* ts_out, hipStream_t s) {
+                           uint8_t* scales, uint8_t* scales_t, float* ts_out, hipStream_t s) {
   const dim3 g((unsigned)((cols + 63) / 64), (unsigned)((rows + 63) / 64)), b(kThreads);
   const uint16_t* xp = reinterpret_cast<const uint16_t*>(x);
   if (sr)
     hipLaunchKernelGGL(k_quant_2d<true>, g, b, 0, s, xp, rows, cols, amax, seed, stream_id,
-                       codes, codes_t, scales, ts_out);
+                       codes, codes_t, scales, scales_t, ts_out);
   else
     hipLaunchKernelGGL(k_quant_2d<false>, g, b, 0, s, xp, rows, cols, amax, seed, stream_id,
-                       codes, codes_t, scales, ts_out);
+                       codes, codes_t, scales, scales_t, ts_out);
   return hipGetLastError();
 }
 

@@ -104,17 +104,19 @@ int nvfp4_quantize1d_sr(const void* x_bf16, int64_t rows, int64_t cols, int axis
 /* 2D quantization (weights): one E4M3 scale per 16x16 tile (NVIDIA blog, 2D
  * block quantization: the forward and backward passes see the same
  * quantized weight).  Operand = w, I = rows, K = cols.
- * Outputs: codes [rows][cols/2]; codes_t [cols][rows/2] (nullable: the same
- * codes transposed, the Dgrad operand); scales_e4m3 [rows/16][cols/16]. */
+ * Outputs: codes [rows][cols/2]; scales_e4m3 [rows/16][cols/16];
+ * codes_t [cols][rows/2] and scales_t_e4m3 [cols/16][rows/16] (each
+ * nullable): the same codes and scales transposed, which make the Dgrad
+ * operand (w read as [cols][rows]) K-contiguous in both. */
 int nvfp4_quantize2d_rtn(const void* w_bf16, int64_t rows, int64_t cols,
                          float* amax_io, int amax_mode,
                          uint8_t* codes, uint8_t* codes_t, uint8_t* scales_e4m3,
-                         float* tensor_scale_out, void* stream);
+                         uint8_t* scales_t_e4m3, float* tensor_scale_out, void* stream);
 
 int nvfp4_quantize2d_sr(const void* w_bf16, int64_t rows, int64_t cols,
                         float* amax_io, int amax_mode, uint64_t seed, uint32_t stream_id,
                         uint8_t* codes, uint8_t* codes_t, uint8_t* scales_e4m3,
-                        float* tensor_scale_out, void* stream);
+                        uint8_t* scales_t_e4m3, float* tensor_scale_out, void* stream);
 
 /* Weight-gradient operand: the quantized transpose of RHT-transformed x
  * (news item, section 三: RHT on the weight-gradient GEMM inputs; summary
@@ -135,7 +137,12 @@ int nvfp4_rht_quantize(const void* x_bf16, int64_t rows, int64_t cols, uint64_t 
  *  1D rowwise operand: blk_rows 1,  ss_row = k/16, ss_k = 1.
  *  2D operand:         blk_rows 16, ss_row = k/16, ss_k = 1.
  *  2D transposed (codes_t of a [R][C] weight, read as [C][R]):
- *                      blk_rows 16, ss_row = 1,    ss_k = C/16. */
+ *                      scales_t with blk_rows 16, ss_row = R/16, ss_k = 1,
+ *                      or the untransposed scales with ss_row = 1, ss_k = C/16.
+ * Scale codes are finite non-negative E4M3 (0x00..0x7E), as the quantizers
+ * write them; other bytes give unspecified (never out-of-bounds) results.
+ * The GEMM is fastest when ss_k == 1, ss_row is a multiple of 4, the scales
+ * are 4-byte aligned, k is a multiple of 64 and ld_codes of 16. */
 typedef struct {
   const uint8_t* codes;      /* [rows][ld_codes] bytes, 16-byte aligned base; ld_codes >= k/2,
                                 a multiple of 8 (a multiple of 16 takes the faster path) */

@@ -43,6 +43,8 @@ def assert_operand_equal(g: nv.NVFP4Tensor, o: oracle.Operand, name: str = ""):
     if o.codes_t is not None:
         assert g.codes_t is not None
         assert np.array_equal(g.codes_t.cpu().numpy(), o.codes_t), f"{name}: codes_t"
+    if g.scales_t is not None:  # 2D operand: the scale matrix transposed
+        assert np.array_equal(g.scales_t.cpu().numpy(), o.scales.T), f"{name}: scales_t"
 
 
 def assert_gemm_close(c_gpu: np.ndarray, c_ref: np.ndarray, t_ref: np.ndarray, name: str = ""):

@@ -68,11 +68,11 @@ def test_quantize_validation(lib):
     qs = lib.nvfp4_quantize1d_sr
     assert qs(FAKE, 16, 16, 5, FAKE, 0, 1, 0, FAKE, FAKE, FAKE, None) == nv.NVFP4_ERR_ARG
     q2 = lib.nvfp4_quantize2d_rtn
-    assert q2(FAKE, 16, 8, FAKE, 0, FAKE, None, FAKE, FAKE, None) == nv.NVFP4_ERR_SHAPE
-    assert q2(FAKE, 16, 16, FAKE, 0, FAKE, MIS, FAKE, FAKE, None) == nv.NVFP4_ERR_ALIGN
-    assert q2(FAKE, 16, 16, FAKE, 3, FAKE, None, FAKE, FAKE, None) == nv.NVFP4_ERR_ARG
+    assert q2(FAKE, 16, 8, FAKE, 0, FAKE, None, FAKE, None, FAKE, None) == nv.NVFP4_ERR_SHAPE
+    assert q2(FAKE, 16, 16, FAKE, 0, FAKE, MIS, FAKE, None, FAKE, None) == nv.NVFP4_ERR_ALIGN
+    assert q2(FAKE, 16, 16, FAKE, 3, FAKE, None, FAKE, FAKE, FAKE, None) == nv.NVFP4_ERR_ARG
     q2s = lib.nvfp4_quantize2d_sr
-    assert q2s(None, 16, 16, FAKE, 0, 1, 0, FAKE, None, FAKE, FAKE, None) == nv.NVFP4_ERR_NULL
+    assert q2s(None, 16, 16, FAKE, 0, 1, 0, FAKE, None, FAKE, None, FAKE, None) == nv.NVFP4_ERR_NULL
     r = lib.nvfp4_rht_quantize
     assert r(FAKE, 16, 16, 1, 2, 1, 0, FAKE, 0, FAKE, FAKE, FAKE, None) == nv.NVFP4_ERR_ARG
     assert r(FAKE, 8, 16, 1, 0, 1, 0, FAKE, 0, FAKE, FAKE, FAKE, None) == nv.NVFP4_ERR_SHAPE

@@ -5,6 +5,8 @@ be bit-exact; the GEMM must be within 1e-5 * sum_k |a_dec * b_dec| of the
 exact product for every entry.  Sizes span several workgroup tiles with
 ragged tails; the degenerate cases (all-zero tensors, negative zeros, blocks
 whose scale underflows, saturating blocks, K = 16) are included."""
+import dataclasses
+
 import numpy as np
 import pytest
 import torch
@@ -198,12 +200,16 @@ def test_gemm_dgrad_uses_transposed_weight(mnk):
     say("gemm dgrad", mnk)
     qdy = nv.quantize_1d(dy.cuda(), sr_seed=1)
     qw = nv.quantize_2d(w.cuda())
-    dx = nv.gemm(qdy, qw.t())
+    dx = nv.gemm(qdy, qw.t())          # codes_t with the transposed scales
+    strided = dataclasses.replace(qw, scales_t=None).t()   # codes_t, scales read strided
+    assert strided.ss_k != 1
+    dx2 = nv.gemm(qdy, strided)
     torch.cuda.synchronize()
     ody = oracle.quantize(dy, oracle.ROWWISE, sr_seed=1)
     ow = oracle.quantize(w, oracle.TWO_D, with_codes_t=True)
     c, t = oracle.gemm(ody, ow.transposed())
     assert_gemm_close(dx.cpu().numpy(), c, t, f"dgrad {mnk}")
+    assert_gemm_close(dx2.cpu().numpy(), c, t, f"dgrad strided scales {mnk}")
 
 
 @pytest.mark.parametrize("tmn", [(64, 48, 80), (4096, 1024, 1024)])
