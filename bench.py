@@ -76,7 +76,7 @@ class Step:
         f1 = lambda: torch.empty(1, dtype=torch.float32, device=dev)  # noqa: E731
         self.qx = nv.NVFP4Tensor(e(T, F // 2), e(T, F // 16), f1(), f1(), T, F, 1, F // 16, 1)
         self.qw = nv.NVFP4Tensor(e(H, F // 2), e(H // 16, F // 16), f1(), f1(), H, F, 16,
-                                 F // 16, 1, e(F, H // 2))
+                                 F // 16, 1, e(F, H // 2), e(F // 16, H // 16))
         self.qdy = nv.NVFP4Tensor(e(T, H // 2), e(T, H // 16), f1(), f1(), T, H, 1, H // 16, 1)
         self.qdy_t = nv.NVFP4Tensor(e(H, T // 2), e(H, T // 16), f1(), f1(), H, T, 1, T // 16, 1)
         self.qx_t = nv.NVFP4Tensor(e(F, T // 2), e(F, T // 16), f1(), f1(), F, T, 1, T // 16, 1)
