@@ -4,8 +4,9 @@ TEST INFRASTRUCTURE ONLY: the plain, slow reference the GPU library is checked
 against.  Only the tests, the smoke check and the benchmark's CPU-baseline leg
 may import it.  It shares no code with the HIP library and imports nothing
 from it.  The arithmetic lives in ``nvfp4_oracle.c`` (binary32, no FMA
-contraction, exact int64 GEMM); this module is ctypes marshalling over numpy
-arrays.  ``oracle.model`` is a second, pure-numpy model for tiny inputs.
+contraction, exact int64 GEMM) and, for the MXFP4 comparison format,
+``mxfp4_oracle.c``; this module is ctypes marshalling over numpy arrays.
+``oracle.model`` is a second, pure-numpy model for tiny inputs.
 """
 from __future__ import annotations
 
@@ -56,6 +57,14 @@ def _load():
         "orc_e2m1_sr": (ctypes.c_uint8, [ctypes.c_float, ctypes.c_uint16]),
         "orc_e2m1_sr_array": (None, [_f32p, _u16p, _i64, _u8p]),
         "orc_rht16": (None, [_f32p, ctypes.c_uint16, _f32p]),
+        "orc_e8m0_encode": (ctypes.c_uint8, [ctypes.c_float]),
+        "orc_e8m0_encode_array": (None, [_f32p, _i64, _u8p]),
+        "orc_e8m0_decode": (ctypes.c_float, [ctypes.c_uint8]),
+        "orc_mx_quantize": (ctypes.c_int, [_u16p, _i64, _i64, ctypes.c_int, _u64, _u32, _u8p, _u8p]),
+        "orc_mx_dequantize": (None, [_u8p, _u8p, _i64, _i64, _f32p]),
+        "orc_mx_gemm": (ctypes.c_int, [_u8p, _u8p, _i64, _u8p, _u8p, _i64, _i64, _f64p, _f64p]),
+        "orc_mx_gemm_entries": (ctypes.c_int, [_u8p, _u8p, _u8p, _u8p, _i64, _i64p, _i64p, _i64,
+                                               _f64p, _f64p]),
         "orc_amax": (ctypes.c_float, [_u16p, _i64, _i64]),
         "orc_amax_rht": (ctypes.c_float, [_u16p, _i64, _i64, _u64]),
         "orc_tensor_scale": (ctypes.c_float, [ctypes.c_float]),
@@ -267,4 +276,82 @@ def gemm_entries(a: Operand, b: Operand, ms: np.ndarray, ns: np.ndarray):
                                   _ptr(c, _f64p), _ptr(t, _f64p))
     if rc != 0:
         raise ValueError(f"oracle gemm rejected the arguments (status {rc})")
+    return c, t
+
+
+# ---------------------------------------------------------------------------
+# MXFP4 (the comparison format): 32-element blocks along K, power-of-two E8M0
+# block scale, no tensor scale ("Pretraining Large Language Models with
+# NVFP4", summary page, format paragraph).  Arithmetic in mxfp4_oracle.c.
+# ---------------------------------------------------------------------------
+def e8m0_encode(amax: np.ndarray) -> np.ndarray:
+    """E8M0 byte e + 127, e the smallest integer with amax <= 6 * 2^e (clamped)."""
+    a = np.ascontiguousarray(np.asarray(amax, np.float32).ravel())
+    out = np.empty(a.size, np.uint8)
+    _load().orc_e8m0_encode_array(_ptr(a, _f32p), a.size, _ptr(out, _u8p))
+    return out.reshape(np.shape(amax))
+
+
+def e8m0_decode(code: int) -> float:
+    return float(_load().orc_e8m0_decode(code))
+
+
+@dataclass
+class MXOperand:
+    """An MXFP4 GEMM operand, logically [rows][k], K-contiguous."""
+    codes: np.ndarray    # uint8 [rows][k/2], low nibble = even k
+    scales: np.ndarray   # uint8 E8M0 [rows][k/32]
+    rows: int
+    k: int
+
+
+def mx_quantize(x, *, sr_seed: int | None = None, stream_id: int = 0) -> MXOperand:
+    """Rowwise MXFP4 quantization of bf16 x [rows][cols] (cols % 32 == 0)."""
+    x = _as_bf16_bits(x)
+    rows, cols = x.shape
+    codes = np.zeros((rows, cols // 2), np.uint8)
+    scales = np.zeros((rows, cols // 32), np.uint8)
+    rc = _load().orc_mx_quantize(_ptr(x, _u16p), rows, cols, int(sr_seed is not None),
+                                 0 if sr_seed is None else sr_seed, stream_id,
+                                 _ptr(codes, _u8p), _ptr(scales, _u8p))
+    if rc != 0:
+        raise ValueError(f"oracle mx_quantize rejected the arguments (status {rc})")
+    return MXOperand(codes, scales, rows, cols)
+
+
+def mx_dequantize(q: MXOperand) -> np.ndarray:
+    out = np.empty((q.rows, q.k), np.float32)
+    codes, scales = np.ascontiguousarray(q.codes), np.ascontiguousarray(q.scales)
+    _load().orc_mx_dequantize(_ptr(codes, _u8p), _ptr(scales, _u8p), q.rows, q.k, _ptr(out, _f32p))
+    return out
+
+
+def mx_gemm(a: MXOperand, b: MXOperand):
+    """C[m][n] = sum_k A[m,k]*B[n,k] in float64 (exact products), and
+    T = sum_k |A*B|."""
+    assert a.k == b.k
+    c = np.empty((a.rows, b.rows), np.float64)
+    t = np.empty((a.rows, b.rows), np.float64)
+    ac, as_ = np.ascontiguousarray(a.codes), np.ascontiguousarray(a.scales)
+    bc, bs = np.ascontiguousarray(b.codes), np.ascontiguousarray(b.scales)
+    rc = _load().orc_mx_gemm(_ptr(ac, _u8p), _ptr(as_, _u8p), a.rows, _ptr(bc, _u8p),
+                             _ptr(bs, _u8p), b.rows, a.k, _ptr(c, _f64p), _ptr(t, _f64p))
+    if rc != 0:
+        raise ValueError(f"oracle mx_gemm rejected the arguments (status {rc})")
+    return c, t
+
+
+def mx_gemm_entries(a: MXOperand, b: MXOperand, ms: np.ndarray, ns: np.ndarray):
+    assert a.k == b.k
+    ms = np.ascontiguousarray(ms, np.int64)
+    ns = np.ascontiguousarray(ns, np.int64)
+    c = np.empty(ms.size, np.float64)
+    t = np.empty(ms.size, np.float64)
+    ac, as_ = np.ascontiguousarray(a.codes), np.ascontiguousarray(a.scales)
+    bc, bs = np.ascontiguousarray(b.codes), np.ascontiguousarray(b.scales)
+    rc = _load().orc_mx_gemm_entries(_ptr(ac, _u8p), _ptr(as_, _u8p), _ptr(bc, _u8p),
+                                     _ptr(bs, _u8p), a.k, _ptr(ms, _i64p), _ptr(ns, _i64p),
+                                     ms.size, _ptr(c, _f64p), _ptr(t, _f64p))
+    if rc != 0:
+        raise ValueError(f"oracle mx_gemm rejected the arguments (status {rc})")
     return c, t

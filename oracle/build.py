@@ -8,13 +8,13 @@ import subprocess
 import sys
 
 HERE = os.path.dirname(os.path.abspath(__file__))
-SRC = os.path.join(HERE, "nvfp4_oracle.c")
+SRCS = [os.path.join(HERE, f) for f in ("nvfp4_oracle.c", "mxfp4_oracle.c")]
 LIB = os.path.join(HERE, "liboracle.so")
 
 
 def build(verbose: bool = False) -> str:
     cmd = ["gcc", "-O2", "-fopenmp", "-ffp-contract=off", "-fno-fast-math", "-fPIC",
-           "-shared", "-Wall", "-o", LIB + ".tmp", SRC, "-lm"]
+           "-shared", "-Wall", "-o", LIB + ".tmp", *SRCS, "-lm"]
     if verbose:
         print(" ".join(cmd), flush=True)
     subprocess.run(cmd, check=True)

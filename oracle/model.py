@@ -169,3 +169,34 @@ def unpack(packed: np.ndarray) -> np.ndarray:
     out[:, 0::2] = p & 0xF
     out[:, 1::2] = p >> 4
     return out
+
+
+# ---------------------------------------------------------------- MXFP4
+def e8m0_encode(amax: np.ndarray) -> np.ndarray:
+    """E8M0 byte e + 127 with e = ceil(log2(amax / 6)), clamped to [-127, 127];
+    amax == 0 -> 0.  amax / 6 is formed in float64, where it is exact enough
+    for the ceiling (a float32 amax has 24 significant bits); frexp gives
+    amax / 6 = f * 2^x with f in [0.5, 1), so ceil(log2) is x - 1 when f is
+    exactly 0.5 and x otherwise."""
+    a = np.asarray(amax, np.float64)
+    f, x = np.frexp(np.where(a > 0, a / 6.0, 1.0))
+    e = np.where(f == 0.5, x - 1, x)
+    e = np.clip(e, -127, 127)
+    return np.where(a > 0, e + 127, 0).astype(np.uint8)
+
+
+def mx_quantize(x_bits: np.ndarray, sr_seed=None, stream_id=0):
+    """Rowwise MXFP4 of bf16 bits [rows][cols] -> (codes uint8 [rows][cols]
+    unpacked, scales uint8 [rows][cols/32])."""
+    z = (x_bits.astype(np.uint32) << 16).view(F32)
+    R, K = z.shape
+    amax_b = np.abs(z).reshape(R, K // 32, 32).max(axis=2)
+    sc = e8m0_encode(amax_b)
+    inv = np.ldexp(F32(1.0), 127 - sc.astype(np.int32)).astype(F32)   # 2^-e
+    v = (z * np.repeat(inv, 32, axis=1)).astype(F32)
+    if sr_seed is not None:
+        n = np.arange(R * K, dtype=np.uint64)
+        codes = e2m1_sr(v, sr_bits(sr_seed, stream_id, n).reshape(R, K))
+    else:
+        codes = e2m1_rtn(v)
+    return codes, sc
