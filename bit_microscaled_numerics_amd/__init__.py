@@ -31,7 +31,8 @@ NVFP4_ROWWISE, NVFP4_COLWISE = 0, 1
 
 EXPORTED = ("nvfp4_amax", "nvfp4_amax_rht", "nvfp4_quantize1d_rtn", "nvfp4_quantize1d_sr",
             "nvfp4_quantize2d_rtn", "nvfp4_quantize2d_sr", "nvfp4_rht_quantize",
-            "nvfp4_dequantize", "nvfp4_gemm", "nvfp4_status_string", "nvfp4_last_error")
+            "nvfp4_dequantize", "nvfp4_gemm", "nvfp4_status_string", "nvfp4_last_error",
+            "mxfp4_quantize", "mxfp4_dequantize", "mxfp4_gemm")
 
 
 class NVFP4Error(RuntimeError):
@@ -47,6 +48,13 @@ class c_operand(ctypes.Structure):
                 ("ss_k", ctypes.c_int64), ("blk_rows", ctypes.c_int32),
                 ("tensor_scale", ctypes.c_void_p), ("rows", ctypes.c_int64),
                 ("k", ctypes.c_int64)]
+
+
+class c_mx_operand(ctypes.Structure):
+    """Mirror of ``mxfp4_operand``."""
+    _fields_ = [("codes", ctypes.c_void_p), ("ld_codes", ctypes.c_int64),
+                ("scales", ctypes.c_void_p), ("ld_scales", ctypes.c_int64),
+                ("rows", ctypes.c_int64), ("k", ctypes.c_int64)]
 
 
 _lib = None
@@ -73,6 +81,9 @@ def load_library(path: str = LIB_PATH) -> ctypes.CDLL:
         "nvfp4_rht_quantize": [vp, i64, i64, u64, i32, u64, u32, vp, i32, vp, vp, vp, vp],
         "nvfp4_dequantize": [ctypes.POINTER(c_operand), vp, vp],
         "nvfp4_gemm": [ctypes.POINTER(c_operand), ctypes.POINTER(c_operand), vp, i64, vp],
+        "mxfp4_quantize": [vp, i64, i64, i32, u64, u32, vp, vp, vp],
+        "mxfp4_dequantize": [ctypes.POINTER(c_mx_operand), vp, vp],
+        "mxfp4_gemm": [ctypes.POINTER(c_mx_operand), ctypes.POINTER(c_mx_operand), vp, i64, vp],
     }
     for name, args in sigs.items():
         fn = getattr(lib, name)
@@ -289,4 +300,60 @@ def gemm(a: NVFP4Tensor, b: NVFP4Tensor, out: Optional[torch.Tensor] = None) -> 
     if out is None:
         out = torch.empty(a.rows, b.rows, dtype=torch.float32, device=a.codes.device)
     nvfp4_gemm(a, b, out, out.stride(0))
+    return out
+
+
+# ---------------------------------------------------------------- MXFP4
+@dataclass
+class MXFP4Tensor:
+    """An MXFP4 operand, logically [rows][k], K-contiguous (device tensors)."""
+    codes: torch.Tensor    # uint8 [rows][ld_codes]
+    scales: torch.Tensor   # uint8 E8M0 [rows][ld_scales]
+    rows: int
+    k: int
+
+    def c_struct(self) -> c_mx_operand:
+        return c_mx_operand(self.codes.data_ptr(), self.codes.shape[1], self.scales.data_ptr(),
+                            self.scales.shape[1], self.rows, self.k)
+
+
+def mxfp4_quantize(x, use_sr, seed, stream_id, codes, scales, stream=None):
+    _dev_bf16(x, "x")
+    _check(load_library().mxfp4_quantize(_p(x), x.shape[0], x.shape[1], int(use_sr), seed,
+                                         stream_id, _p(codes), _p(scales), _stream(stream)))
+
+
+def mxfp4_dequantize(q: MXFP4Tensor, out, stream=None):
+    op = q.c_struct()
+    _check(load_library().mxfp4_dequantize(ctypes.byref(op), _p(out), _stream(stream)))
+
+
+def mxfp4_gemm(a: MXFP4Tensor, b: MXFP4Tensor, c, ldc: int, stream=None):
+    oa, ob = a.c_struct(), b.c_struct()
+    _check(load_library().mxfp4_gemm(ctypes.byref(oa), ctypes.byref(ob), _p(c), ldc,
+                                      _stream(stream)))
+
+
+def mx_quantize(x: torch.Tensor, sr_seed: Optional[int] = None, stream_id: int = 0) -> MXFP4Tensor:
+    """Rowwise MXFP4 quantization of bf16 x [rows][cols] (cols % 32 == 0)."""
+    _dev_bf16(x, "x")
+    R, C = x.shape
+    codes = torch.empty(R, C // 2, dtype=torch.uint8, device=x.device)
+    scales = torch.empty(R, C // 32, dtype=torch.uint8, device=x.device)
+    mxfp4_quantize(x, sr_seed is not None, 0 if sr_seed is None else sr_seed, stream_id, codes,
+                   scales)
+    return MXFP4Tensor(codes, scales, R, C)
+
+
+def mx_dequantize(q: MXFP4Tensor) -> torch.Tensor:
+    out = torch.empty(q.rows, q.k, dtype=torch.float32, device=q.codes.device)
+    mxfp4_dequantize(q, out)
+    return out
+
+
+def mx_gemm(a: MXFP4Tensor, b: MXFP4Tensor, out: Optional[torch.Tensor] = None) -> torch.Tensor:
+    """C = A B^T in FP32, A [M][K], B [N][K] MXFP4."""
+    if out is None:
+        out = torch.empty(a.rows, b.rows, dtype=torch.float32, device=a.codes.device)
+    mxfp4_gemm(a, b, out, out.stride(0))
     return out

@@ -1,0 +1,65 @@
+// gemm_tiles.h -- workgroup-tile order shared by the NVFP4 and MXFP4 GEMMs
+// (internal to libnvfp4.so): 256 x 256 output tiles, one workgroup per CU,
+// XCD-aware renumbering, and the split of a half-empty last round of tiles
+// into two K halves.
+#pragma once
+
+#include <hip/hip_runtime.h>
+#include <stdint.h>
+
+namespace nvfp4 {
+
+constexpr int kTile = 256;  // workgroup tile (rows of A and of B)
+
+// Tile order: the grid is 1-D.  Workgroups are dealt round-robin to the 8
+// XCDs (each with its own L2), so block b is first renumbered so that every
+// XCD owns a contiguous range of tiles; inside that range tiles run in
+// groups of kGroupM tile-rows, M fastest, so the workgroups resident on one
+// XCD at a time share both A rows and B columns in its L2.
+constexpr int kXcds = 8, kGroupM = 8;
+
+// Linear tile index -> (tile row, tile column): groups of kGroupM tile-rows,
+// M fastest inside a group.
+__device__ __forceinline__ void grouped(int64_t t, int64_t tiles_m, int64_t tiles_n, int64_t& tm,
+                                        int64_t& tn) {
+  const int64_t group = t / (kGroupM * tiles_n);
+  const int64_t first_m = group * kGroupM;
+  const int64_t gm = (tiles_m - first_m) < kGroupM ? (tiles_m - first_m) : kGroupM;
+  const int64_t in = t - group * kGroupM * tiles_n;
+  tm = first_m + in % gm;
+  tn = in / gm;
+}
+
+// Block -> tile and K part.  Blocks below full_tiles take whole tiles
+// (renumbered so each XCD owns a contiguous range); the blocks after them
+// take the remaining tiles two per tile, part 0 / 1 = first / second K half
+// (the last partial round of tiles finishes in half the time).
+__device__ __forceinline__ void block_tile(int64_t full, int64_t tiles_m, int64_t tiles_n,
+                                           int64_t& tm, int64_t& tn, int& part) {
+  const int64_t b = blockIdx.x;
+  int64_t t;
+  if (b < full) {
+    const int64_t per = full / kXcds;
+    t = b < per * kXcds ? (b % kXcds) * per + b / kXcds : b;
+    part = -1;
+  } else {
+    t = full + (b - full) / 2;
+    part = (int)((b - full) & 1);
+  }
+  grouped(t, tiles_m, tiles_n, tm, tn);
+}
+
+// Host-side plan of one launch: tiles_m x tiles_n tiles; grid = full_tiles
+// whole tiles plus 2 workgroups per split tile (when split).
+struct TilePlan {
+  int64_t tiles_m, tiles_n, full_tiles, grid, rem;
+  bool split;
+};
+
+TilePlan plan_tiles(int64_t M, int64_t N, int64_t steps);
+
+// Zero the output tiles the split workgroups add into (no-op without split).
+hipError_t zero_split_tiles(const TilePlan& p, float* c, int64_t ldc, int64_t M, int64_t N,
+                            hipStream_t s);
+
+}  // namespace nvfp4

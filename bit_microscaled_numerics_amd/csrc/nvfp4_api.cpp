@@ -257,4 +257,65 @@ int nvfp4_gemm(const nvfp4_operand* a, const nvfp4_operand* b, float* c, int64_t
                                      as_stream(stream)));
 }
 
+// ---------------------------------------------------------------- MXFP4
+
+int mxfp4_quantize(const void* x, int64_t rows, int64_t cols, int use_sr, uint64_t seed,
+                   uint32_t stream_id, uint8_t* codes, uint8_t* scales, void* stream) {
+  if (x == nullptr || codes == nullptr || scales == nullptr)
+    return fail(NVFP4_ERR_NULL, "x, codes and scales_e8m0 are required");
+  if (rows <= 0 || cols <= 0 || cols % 32)
+    return fail(NVFP4_ERR_SHAPE, "rows=%lld cols=%lld: rows > 0, cols a positive multiple of 32",
+                (long long)rows, (long long)cols);
+  if (!aligned(x, 16)) return fail(NVFP4_ERR_ALIGN, "x must be 16-byte aligned");
+  if (!aligned(codes, 4)) return fail(NVFP4_ERR_ALIGN, "codes must be 4-byte aligned");
+  if (use_sr != 0 && use_sr != 1) return fail(NVFP4_ERR_ARG, "use_sr=%d must be 0 or 1", use_sr);
+  return launched(nvfp4::launch_mx_quant_row(x, rows, cols, use_sr == 1, seed, stream_id, codes,
+                                             scales, as_stream(stream)));
+}
+
+static int check_mx_operand(const mxfp4_operand* q, const char* name, int64_t code_align) {
+  if (q == nullptr) return fail(NVFP4_ERR_NULL, "%s is NULL", name);
+  if (q->codes == nullptr || q->scales == nullptr)
+    return fail(NVFP4_ERR_NULL, "%s: codes and scales are required", name);
+  if (q->rows <= 0 || q->k <= 0 || q->k % 32)
+    return fail(NVFP4_ERR_SHAPE, "%s: rows=%lld k=%lld: rows > 0, k a positive multiple of 32",
+                name, (long long)q->rows, (long long)q->k);
+  if (q->ld_codes < q->k / 2 || q->ld_scales < q->k / 32)
+    return fail(NVFP4_ERR_SHAPE, "%s: ld_codes >= k/2 and ld_scales >= k/32 required", name);
+  if (q->ld_codes % code_align || !aligned(q->codes, (uintptr_t)code_align))
+    return fail(NVFP4_ERR_ALIGN, "%s: codes and ld_codes must be %lld-byte aligned", name,
+                (long long)code_align);
+  if (q->ld_codes > (int64_t(1) << 22) || q->rows * q->ld_scales >= (int64_t(1) << 31))
+    return fail(NVFP4_ERR_SHAPE, "%s: codes row pitch or scale array beyond the 32-bit offset range",
+                name);
+  return NVFP4_OK;
+}
+
+static nvfp4::MxOperand mx_kernel(const mxfp4_operand* q) {
+  return nvfp4::MxOperand{q->codes, q->ld_codes, q->scales, q->ld_scales, q->rows, q->k};
+}
+
+int mxfp4_dequantize(const mxfp4_operand* q, float* out, void* stream) {
+  int st = check_mx_operand(q, "q", 4);
+  if (st) return st;
+  if (out == nullptr) return fail(NVFP4_ERR_NULL, "out is NULL");
+  if (!aligned(out, 16)) return fail(NVFP4_ERR_ALIGN, "out must be 16-byte aligned");
+  return launched(nvfp4::launch_mx_dequant(mx_kernel(q), out, as_stream(stream)));
+}
+
+int mxfp4_gemm(const mxfp4_operand* a, const mxfp4_operand* b, float* c, int64_t ldc,
+               void* stream) {
+  int st = check_mx_operand(a, "a", 16);
+  if (st) return st;
+  if ((st = check_mx_operand(b, "b", 16))) return st;
+  if (a->k != b->k)
+    return fail(NVFP4_ERR_SHAPE, "a.k=%lld != b.k=%lld", (long long)a->k, (long long)b->k);
+  if (c == nullptr) return fail(NVFP4_ERR_NULL, "c is NULL");
+  if (!aligned(c, 4)) return fail(NVFP4_ERR_ALIGN, "c must be 4-byte aligned");
+  if (ldc < b->rows) return fail(NVFP4_ERR_SHAPE, "ldc=%lld < N=%lld", (long long)ldc,
+                                 (long long)b->rows);
+  return launched(nvfp4::launch_mx_gemm(mx_kernel(a), mx_kernel(b), a->k, c, ldc,
+                                        as_stream(stream)));
+}
+
 }  // extern "C"

@@ -17,6 +17,7 @@
 // it cannot apply an E4M3 scale per 16 exactly.)
 #include "nvfp4_device.h"
 #include "nvfp4_kernels.h"
+#include "gemm_tiles.h"
 
 namespace nvfp4 {
 
@@ -58,45 +59,6 @@ __device__ __forceinline__ half8 decode8(uint32_t w, const BlockDec& d) {
   return r;
 }
 
-// Tile order: the grid is 1-D.  Workgroups are dealt round-robin to the 8
-// XCDs (each with its own L2), so block b is first renumbered so that every
-// XCD owns a contiguous range of tiles; inside that range tiles run in
-// groups of kGroupM tile-rows, M fastest, so the workgroups resident on one
-// XCD at a time share both A rows and B columns in its L2.
-constexpr int kXcds = 8, kGroupM = 8;
-
-// Linear tile index -> (tile row, tile column): groups of kGroupM tile-rows,
-// M fastest inside a group.
-__device__ __forceinline__ void grouped(int64_t t, int64_t tiles_m, int64_t tiles_n, int64_t& tm,
-                                        int64_t& tn) {
-  const int64_t group = t / (kGroupM * tiles_n);
-  const int64_t first_m = group * kGroupM;
-  const int64_t gm = (tiles_m - first_m) < kGroupM ? (tiles_m - first_m) : kGroupM;
-  const int64_t in = t - group * kGroupM * tiles_n;
-  tm = first_m + in % gm;
-  tn = in / gm;
-}
-
-// Block -> tile and K part.  Blocks below full_tiles take whole tiles
-// (renumbered so each XCD owns a contiguous range); the blocks after them
-// take the remaining tiles two per tile, part 0 / 1 = first / second K half
-// (the last partial round of tiles finishes in half the time).
-__device__ __forceinline__ void block_tile(int64_t full, int64_t tiles_m, int64_t tiles_n,
-                                           int64_t& tm, int64_t& tn, int& part) {
-  const int64_t b = blockIdx.x;
-  int64_t t;
-  if (b < full) {
-    const int64_t per = full / kXcds;
-    t = b < per * kXcds ? (b % kXcds) * per + b / kXcds : b;
-    part = -1;
-  } else {
-    t = full + (b - full) / 2;
-    part = (int)((b - full) & 1);
-  }
-  grouped(t, tiles_m, tiles_n, tm, tn);
-}
-
-constexpr int kTile = 256;  // workgroup tile (rows of A and of B)
 constexpr uint32_t kBufFlags = 0x00020000u;  // raw 32-bit buffer descriptor word 3
 
 // Buffer view of one operand for one workgroup: codes and scales of the
@@ -424,22 +386,37 @@ __global__ __launch_bounds__(256) void k_zero_tiles(float* __restrict__ c, int64
   }
 }
 
-hipError_t launch_gemm(const GemmOperand& a, const GemmOperand& b, int64_t K, float* c,
-                       int64_t ldc, hipStream_t s) {
-  GemmArgs g{a, b, a.rows, b.rows, K, c, ldc, 0};
-  const int64_t tiles_m = (g.M + kTile - 1) / kTile, tiles_n = (g.N + kTile - 1) / kTile;
-  const int64_t tiles = tiles_m * tiles_n;
+TilePlan plan_tiles(int64_t M, int64_t N, int64_t steps) {
+  TilePlan p;
+  p.tiles_m = (M + kTile - 1) / kTile;
+  p.tiles_n = (N + kTile - 1) / kTile;
+  const int64_t tiles = p.tiles_m * p.tiles_n;
   // One workgroup per CU is resident (LDS).  When the last round is at most
   // half full, its tiles are split in two K halves so it takes half a round.
   const int64_t slots = num_cus();
-  const int64_t rem = tiles % slots, steps = (K + kBK - 1) / kBK;
-  const bool split = rem > 0 && 2 * rem <= slots && tiles > slots && steps >= 4;
-  g.full_tiles = split ? tiles - rem : tiles;
-  const dim3 grid((unsigned)(split ? tiles + rem : tiles));
-  if (split) {
-    hipLaunchKernelGGL(k_zero_tiles, dim3((unsigned)rem), dim3(256), 0, s, c, ldc, g.M, g.N,
-                       tiles_m, tiles_n, g.full_tiles);
-    const hipError_t e = hipGetLastError();
+  p.rem = tiles % slots;
+  p.split = p.rem > 0 && 2 * p.rem <= slots && tiles > slots && steps >= 4;
+  p.full_tiles = p.split ? tiles - p.rem : tiles;
+  p.grid = p.split ? tiles + p.rem : tiles;
+  return p;
+}
+
+hipError_t zero_split_tiles(const TilePlan& p, float* c, int64_t ldc, int64_t M, int64_t N,
+                            hipStream_t s) {
+  if (!p.split) return hipSuccess;
+  hipLaunchKernelGGL(k_zero_tiles, dim3((unsigned)p.rem), dim3(256), 0, s, c, ldc, M, N,
+                     p.tiles_m, p.tiles_n, p.full_tiles);
+  return hipGetLastError();
+}
+
+hipError_t launch_gemm(const GemmOperand& a, const GemmOperand& b, int64_t K, float* c,
+                       int64_t ldc, hipStream_t s) {
+  GemmArgs g{a, b, a.rows, b.rows, K, c, ldc, 0};
+  const TilePlan plan = plan_tiles(g.M, g.N, (K + kBK - 1) / kBK);
+  g.full_tiles = plan.full_tiles;
+  const dim3 grid((unsigned)plan.grid);
+  {
+    const hipError_t e = zero_split_tiles(plan, c, ldc, g.M, g.N, s);
     if (e != hipSuccess) return e;
   }
   const bool ld16 = (a.ld % 16 == 0) && (b.ld % 16 == 0);

@@ -41,4 +41,20 @@ struct GemmOperand {
 hipError_t launch_gemm(const GemmOperand& a, const GemmOperand& b, int64_t K, float* c,
                        int64_t ldc, hipStream_t s);
 
+// MXFP4 (comparison format): rowwise, 32-element blocks, E8M0 scales.
+struct MxOperand {
+  const uint8_t* codes;
+  int64_t ld;          // bytes per row of codes
+  const uint8_t* scales;
+  int64_t ld_scales;   // bytes per row of scales
+  int64_t rows, k;
+};
+
+hipError_t launch_mx_quant_row(const void* x, int64_t rows, int64_t cols, bool sr, uint64_t seed,
+                               uint32_t stream_id, uint8_t* codes, uint8_t* scales,
+                               hipStream_t s);
+hipError_t launch_mx_dequant(const MxOperand& q, float* out, hipStream_t s);
+hipError_t launch_mx_gemm(const MxOperand& a, const MxOperand& b, int64_t K, float* c,
+                          int64_t ldc, hipStream_t s);
+
 }  // namespace nvfp4

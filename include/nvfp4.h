@@ -170,6 +170,50 @@ int nvfp4_dequantize(const nvfp4_operand* q, float* out, void* stream);
 int nvfp4_gemm(const nvfp4_operand* a, const nvfp4_operand* b, float* c, int64_t ldc,
                void* stream);
 
+/* ------------------------------------------------------------------------
+ * MXFP4, the format NVFP4 is measured against: 32-element blocks along K, a
+ * power-of-two (UE8M0) block scale, no tensor scale ("Pretraining Large
+ * Language Models with NVFP4", summary page, format paragraph).  Its scales
+ * are what gfx950's scaled FP4 matrix instructions consume, so its GEMM runs
+ * on them directly.
+ *
+ * Scale of a block with largest magnitude amax_b: E = 2^e, e the smallest
+ * integer with amax_b <= 6 * 2^e (every block's largest |v| then lies in
+ * (3, 6] -- the rounding whose worst case leaves +-4 and +-6 unused, same
+ * paragraph), clamped to [-127, 127], stored as the byte e + 127 (an all-zero
+ * block gets byte 0).  Element code = E2M1(z * 2^-e), RTN or SR exactly as
+ * for NVFP4.  Output bit-identical to the CPU reference for finite inputs.
+ * ------------------------------------------------------------------------ */
+
+/* Rowwise MXFP4 quantization of bf16 x [rows][cols] (16-byte aligned; cols a
+ * positive multiple of 32).  codes [rows][cols/2] (4-byte aligned),
+ * scales_e8m0 [rows][cols/32].  use_sr: 0 = RTN, 1 = SR with
+ * Philox4x32-10(key = seed, counter = (n/8, stream_id, 0)), n = r*cols + k. */
+int mxfp4_quantize(const void* x_bf16, int64_t rows, int64_t cols, int use_sr, uint64_t seed,
+                   uint32_t stream_id, uint8_t* codes, uint8_t* scales_e8m0, void* stream);
+
+/* An MXFP4 operand, logically [rows][k], K-contiguous: code of (r, k) in
+ * codes[r * ld_codes + k/2] (low nibble = even k), its scale in
+ * scales[r * ld_scales + k/32].  The scale array spans rows * ld_scales
+ * bytes; scale bytes are 0x00..0xFE as the quantizer writes them. */
+typedef struct {
+  const uint8_t* codes;
+  int64_t ld_codes;    /* >= k/2; GEMM: multiple of 16 and 16-byte aligned codes */
+  const uint8_t* scales;
+  int64_t ld_scales;   /* >= k/32; the GEMM is fastest with a multiple of 4 */
+  int64_t rows, k;     /* rows > 0, k a positive multiple of 32 */
+} mxfp4_operand;
+
+/* out[r][k] = E2M1(code) * 2^(scale - 127) as FP32 [rows][k] (exact). */
+int mxfp4_dequantize(const mxfp4_operand* q, float* out, void* stream);
+
+/* C[m][n] = sum_k A[m,k] * B[n,k] in FP32 on the scaled FP4 matrix cores
+ * (v_mfma_scale_f32_32x32x64_f8f6f4, E2M1 x E2M1, E8M0 scales per 32),
+ * A = [M][K], B = [N][K], C row-major with ldc >= N.  Products are exact; the
+ * only rounding is the FP32 accumulation. */
+int mxfp4_gemm(const mxfp4_operand* a, const mxfp4_operand* b, float* c, int64_t ldc,
+               void* stream);
+
 /* Human-readable name of a status code (static storage). */
 const char* nvfp4_status_string(int status);
 

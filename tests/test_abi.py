@@ -23,7 +23,8 @@ def lib():
 
 def declared():
     text = open(HEADER).read()
-    return sorted(set(re.findall(r"^\s*(?:int|const char\*)\s+(nvfp4_\w+)\s*\(", text, re.M)))
+    return sorted(set(re.findall(r"^\s*(?:int|const char\*)\s+((?:nvfp4|mxfp4)_\w+)\s*\(", text,
+                                 re.M)))
 
 
 def test_header_and_binding_agree():
@@ -110,3 +111,31 @@ def test_python_layer_refuses_cpu_tensors():
     x = torch.zeros(16, 16, dtype=torch.bfloat16)
     with pytest.raises(ValueError):
         nv.quantize_1d(x)
+
+
+def _mx(**kw):
+    base = dict(codes=FAKE, ld_codes=32, scales=FAKE, ld_scales=2, rows=16, k=64)
+    base.update(kw)
+    return nv.c_mx_operand(**base)
+
+
+def test_mxfp4_validation(lib):
+    q = lib.mxfp4_quantize
+    assert q(None, 16, 64, 0, 1, 0, FAKE, FAKE, None) == nv.NVFP4_ERR_NULL
+    assert q(FAKE, 16, 48, 0, 1, 0, FAKE, FAKE, None) == nv.NVFP4_ERR_SHAPE
+    assert q(FAKE, 0, 64, 0, 1, 0, FAKE, FAKE, None) == nv.NVFP4_ERR_SHAPE
+    assert q(MIS, 16, 64, 0, 1, 0, FAKE, FAKE, None) == nv.NVFP4_ERR_ALIGN
+    assert q(FAKE, 16, 64, 2, 1, 0, FAKE, FAKE, None) == nv.NVFP4_ERR_ARG
+    g, d = lib.mxfp4_gemm, lib.mxfp4_dequantize
+    ok = _mx()
+    assert g(None, ctypes.byref(ok), FAKE, 16, None) == nv.NVFP4_ERR_NULL
+    assert g(ctypes.byref(ok), ctypes.byref(_mx(k=96, ld_codes=48, ld_scales=3)), FAKE, 16,
+             None) == nv.NVFP4_ERR_SHAPE                                   # a.k != b.k
+    assert g(ctypes.byref(ok), ctypes.byref(_mx(k=48)), FAKE, 16, None) == nv.NVFP4_ERR_SHAPE
+    assert g(ctypes.byref(ok), ctypes.byref(_mx(ld_codes=24)), FAKE, 16, None) == nv.NVFP4_ERR_SHAPE
+    assert g(ctypes.byref(ok), ctypes.byref(_mx(ld_codes=40)), FAKE, 16, None) == nv.NVFP4_ERR_ALIGN
+    assert g(ctypes.byref(ok), ctypes.byref(_mx(ld_scales=1)), FAKE, 16, None) == nv.NVFP4_ERR_SHAPE
+    assert g(ctypes.byref(ok), ctypes.byref(ok), FAKE, 8, None) == nv.NVFP4_ERR_SHAPE   # ldc < N
+    assert g(ctypes.byref(ok), ctypes.byref(ok), None, 16, None) == nv.NVFP4_ERR_NULL
+    assert d(ctypes.byref(ok), MIS, None) == nv.NVFP4_ERR_ALIGN
+    assert d(ctypes.byref(_mx(codes=None)), FAKE, None) == nv.NVFP4_ERR_NULL
