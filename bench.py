@@ -40,6 +40,7 @@ from bit_microscaled_numerics_amd import inputs  # noqa: E402
 METRIC = "NVFP4 quantize GB/s + NVFP4-linear GEMM TFLOP/s at 8192×5120×20480"
 HBM_PEAK_GBS = 8000.0          # MI355X HBM3E
 MFMA_F16_PEAK_TFLOPS = 2500.0  # MI355X dense FP16/BF16 matrix peak
+MFMA_FP4_PEAK_TFLOPS = 10100.0  # MI355X dense FP4 (scaled MX) matrix peak
 
 TOKENS, HIDDEN, FFN = 8192, 5120, 20480
 RHT_SEED, SR_SEED = 1, 1
@@ -47,6 +48,9 @@ RHT_SEED, SR_SEED = 1, 1
 
 def log(*a):
     print("[bench]", *a, file=sys.stderr, flush=True)
+
+
+GEMM_SOURCES = ("nvfp4_gemm.hip", "gemm_tiles.h", "nvfp4_device.h")
 
 
 def gemm_traffic():
@@ -58,7 +62,7 @@ def gemm_traffic():
         return None
     rec = json.load(open(path))
     m = hashlib.sha256()
-    for f in ("nvfp4_gemm.hip", "nvfp4_device.h"):
+    for f in GEMM_SOURCES:
         with open(os.path.join(ROOT, "bit_microscaled_numerics_amd", "csrc", f), "rb") as fh:
             m.update(fh.read())
     return rec["traffic_bytes_per_launch"] if m.hexdigest() == rec["source_sha256"] else None
@@ -197,6 +201,7 @@ def quant_sweep(steps: int = 10):
         q1 = nv.quantize_1d(x)
         q2 = nv.quantize_2d(x)
         qc = nv.quantize_1d(x, nv.NVFP4_COLWISE)
+        qm = nv.mx_quantize(x)
         G = nv.NVFP4_AMAX_GIVEN
         variants = [
             ("amax", 2 * n, lambda: nv.nvfp4_amax(x, q1.amax)),
@@ -218,6 +223,10 @@ def quant_sweep(steps: int = 10):
             ("RHT SR incl. amax", 4.5625 * n, lambda: nv.nvfp4_rht_quantize(
                 x, 1, 1, 7, 0, qc.amax, nv.NVFP4_AMAX_COMPUTE, qc.codes, qc.scales,
                 qc.tensor_scale)),
+            ("MXFP4 RTN (single pass)", 2.53125 * n, lambda: nv.mxfp4_quantize(
+                x, 0, 0, 0, qm.codes, qm.scales)),
+            ("MXFP4 SR (single pass)", 2.53125 * n, lambda: nv.mxfp4_quantize(
+                x, 1, 7, 0, qm.codes, qm.scales)),
         ]
         s = torch.cuda.current_stream()
         for name, nbytes, fn in variants:
@@ -233,8 +242,62 @@ def quant_sweep(steps: int = 10):
             out[f"{dist} {name}"] = {"us": round(ms * 1e3, 1),
                                      "GB/s": round(nbytes / (ms * 1e-3) / 1e9, 1),
                                      "frac": round(nbytes / (ms * 1e-3) / 1e9 / HBM_PEAK_GBS, 3)}
-        del x, q1, q2, qc
+        del x, q1, q2, qc, qm
         torch.cuda.empty_cache()
+    return out
+
+
+def _median_ms(fn, reps: int) -> float:
+    s = torch.cuda.current_stream()
+    fn()
+    ev = [torch.cuda.Event(enable_timing=True) for _ in range(reps + 1)]
+    s.synchronize()
+    for i in range(reps):
+        ev[i].record(s)
+        fn()
+    ev[reps].record(s)
+    s.synchronize()
+    return float(np.median([ev[i].elapsed_time(ev[i + 1]) for i in range(reps)]))
+
+
+def mx_comparison(step: "Step", reps: int):
+    """The same three GEMMs with MXFP4 operands on the scaled FP4 matrix cores
+    (the format the NVFP4 pages compare against), and the relative
+    quantization error of both formats on the step's tensors."""
+    x, w, dy = step.x, step.w, step.dy
+    T, F = x.shape
+    H = w.shape[0]
+    qx, qw, qdy = nv.mx_quantize(x), nv.mx_quantize(w), nv.mx_quantize(dy)
+    wt, dyt, xt = w.t().contiguous(), dy.t().contiguous(), x.t().contiguous()
+    qwt, qdyt, qxt = nv.mx_quantize(wt), nv.mx_quantize(dyt, sr_seed=SR_SEED), nv.mx_quantize(xt)
+    out = {}
+    for name, a, b, c in [("Fprop", qx, qw, step.y), ("Dgrad", qdy, qwt, step.dx),
+                          ("Wgrad", qdyt, qxt, step.dw)]:
+        ms = _median_ms(lambda: nv.mx_gemm(a, b, c), reps)
+        tf = 2.0 * a.rows * b.rows * a.k / (ms * 1e-3) / 1e12
+        out[f"gemm {name} {a.rows}x{b.rows}x{a.k}"] = {
+            "us": round(ms * 1e3, 1), "TFLOP/s": round(tf, 1),
+            "frac_fp4_peak": round(tf / MFMA_FP4_PEAK_TFLOPS, 3)}
+    n = x.numel()
+    ms = _median_ms(lambda: nv.mxfp4_quantize(x, 0, 0, 0, qx.codes, qx.scales), reps)
+    out["quantize X RTN (single pass)"] = {"us": round(ms * 1e3, 1),
+                                           "GB/s": round(2.53125 * n / (ms * 1e-3) / 1e9, 1)}
+
+    def rel_err(deq, ref):
+        r = ref.float()
+        return round(float(torch.linalg.vector_norm(deq - r) / torch.linalg.vector_norm(r)), 5)
+    out["relative quantization error"] = {
+        "X (NVFP4 1D RTN | MXFP4 RTN)": [rel_err(nv.dequantize(step.qx), x),
+                                         rel_err(nv.mx_dequantize(qx), x)],
+        "W (NVFP4 2D RTN | MXFP4 RTN)": [rel_err(nv.dequantize(step.qw), w),
+                                         rel_err(nv.mx_dequantize(qw), w)],
+        "dY (NVFP4 1D RTN | MXFP4 RTN)": [rel_err(nv.dequantize(nv.quantize_1d(dy)), dy),
+                                          rel_err(nv.mx_dequantize(qdy), dy)],
+        "dY (NVFP4 1D SR | MXFP4 SR)": [rel_err(nv.dequantize(step.qdy), dy),
+                                        rel_err(nv.mx_dequantize(nv.mx_quantize(dy, SR_SEED)), dy)],
+    }
+    del qx, qw, qdy, qwt, qdyt, qxt, wt, dyt, xt
+    torch.cuda.empty_cache()
     return out
 
 
@@ -245,6 +308,7 @@ def main():
     ap.add_argument("--warmup", type=int, default=3)
     ap.add_argument("--no-cpu-baseline", action="store_true")
     ap.add_argument("--no-sweep", action="store_true")
+    ap.add_argument("--no-mx", action="store_true", help="skip the MXFP4 comparison")
     ap.add_argument("--seed", type=int, default=0)
     ap.add_argument("--copy-calibration", action="store_true",
                     help="first run a plain 1 GiB device copy (3 launches), the reference "
@@ -338,6 +402,9 @@ def main():
         "roofline": roofline,
         "wall_s_timed": round(wall, 4),
     }
+    if not args.no_mx:
+        log("MXFP4 comparison")
+        result["mxfp4_comparison"] = mx_comparison(step, max(args.steps, 5))
     if not args.no_sweep:
         log("quantize sweep 32768x8192")
         result["quantize_sweep_32768x8192"] = quant_sweep()
