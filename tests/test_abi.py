@@ -139,3 +139,13 @@ def test_mxfp4_validation(lib):
     assert g(ctypes.byref(ok), ctypes.byref(ok), None, 16, None) == nv.NVFP4_ERR_NULL
     assert d(ctypes.byref(ok), MIS, None) == nv.NVFP4_ERR_ALIGN
     assert d(ctypes.byref(_mx(codes=None)), FAKE, None) == nv.NVFP4_ERR_NULL
+
+
+def test_linear_rejects_cpu_tensors():
+    """The training layer has no CPU path: CPU tensors are refused before any
+    library call."""
+    from bit_microscaled_numerics_amd import linear as L
+    import torch
+    x = torch.zeros(16, 32, dtype=torch.bfloat16)
+    with pytest.raises(RuntimeError, match="no CPU fallback"):
+        L.linear_fwd_bwd(x, torch.zeros(16, 32, dtype=torch.bfloat16), x[:, :16].contiguous(), 1, 1)
