@@ -260,6 +260,63 @@ def _median_ms(fn, reps: int) -> float:
     return float(np.median([ev[i].elapsed_time(ev[i + 1]) for i in range(reps)]))
 
 
+def quality(step: "Step"):
+    """How closely each quantized GEMM tracks the unquantized FP32 product at
+    the step's shapes: cosine similarity and relative Frobenius error
+    ("NVFP4：让大模型从零预训练跑在4位浮点上", section 4.2's cosine measure), for
+    the recipe, the recipe without the Wgrad RHT, RHT also on Fprop and Dgrad
+    (an ablation the pages leave unvalidated: "Pretraining Large Language
+    Models with NVFP4", limitations paragraph), and MXFP4; on the step's
+    gradient and on a Student-t (3 dof) gradient of the same scale."""
+    x, w, dy = step.x, step.w, step.dy
+    xt, wt = x.t().contiguous(), w.t().contiguous()
+
+    def cmp(got, ref):
+        g, r = got.flatten().float(), ref.flatten()
+        cos = torch.nn.functional.cosine_similarity(g, r, dim=0)
+        rel = torch.linalg.vector_norm(g - r) / torch.linalg.vector_norm(r)
+        return {"cos": round(float(cos), 5), "rel_err": round(float(rel), 5)}
+
+    xf, wf = x.float(), w.float()
+    out = {}
+    yref = xf @ wt.float()
+    out["Fprop recipe (X 1D, W 2D)"] = cmp(nv.gemm(nv.quantize_1d(x), nv.quantize_2d(w)), yref)
+    out["Fprop RHT along K (X, W 1D)"] = cmp(
+        nv.gemm(nv.rht_quantize(xt, RHT_SEED), nv.rht_quantize(wt, RHT_SEED)), yref)
+    out["Fprop MXFP4"] = cmp(nv.mx_gemm(nv.mx_quantize(x), nv.mx_quantize(w)), yref)
+    del yref
+    g = torch.Generator(device=dy.device).manual_seed(7)
+    z = torch.randn(4, *dy.shape, generator=g, device=dy.device)
+    t3 = (z[0] / torch.sqrt((z[1] ** 2 + z[2] ** 2 + z[3] ** 2) / 3)).mul_(float(dy.float().std()))
+    del z
+    for tag, d in [("", dy), (" t3", t3.to(torch.bfloat16))]:
+        dt = d.t().contiguous()
+        df = d.float()
+        dxref = df @ wf
+        qw = nv.quantize_2d(w)
+        out[f"Dgrad recipe (dY 1D SR){tag}"] = cmp(
+            nv.gemm(nv.quantize_1d(d, sr_seed=SR_SEED), qw.t()), dxref)
+        out[f"Dgrad RHT along K (dY SR, W 1D){tag}"] = cmp(
+            nv.gemm(nv.rht_quantize(dt, RHT_SEED, sr_seed=SR_SEED), nv.rht_quantize(w, RHT_SEED)),
+            dxref)
+        out[f"Dgrad MXFP4 SR{tag}"] = cmp(
+            nv.mx_gemm(nv.mx_quantize(d, SR_SEED), nv.mx_quantize(wt)), dxref)
+        del dxref, qw
+        dwref = dt.float() @ xf
+        out[f"Wgrad recipe (RHT, dY SR){tag}"] = cmp(
+            nv.gemm(nv.rht_quantize(d, RHT_SEED, sr_seed=SR_SEED, stream_id=1),
+                    nv.rht_quantize(x, RHT_SEED)), dwref)
+        out[f"Wgrad no RHT (dY SR){tag}"] = cmp(
+            nv.gemm(nv.quantize_1d(d, nv.NVFP4_COLWISE, sr_seed=SR_SEED, stream_id=1),
+                    nv.quantize_1d(x, nv.NVFP4_COLWISE)), dwref)
+        out[f"Wgrad MXFP4 SR{tag}"] = cmp(
+            nv.mx_gemm(nv.mx_quantize(dt, SR_SEED), nv.mx_quantize(xt)), dwref)
+        del dwref, dt, df
+    del t3, xt, wt, xf, wf
+    torch.cuda.empty_cache()
+    return out
+
+
 def mx_comparison(step: "Step", reps: int):
     """The same three GEMMs with MXFP4 operands on the scaled FP4 matrix cores
     (the format the NVFP4 pages compare against), and the relative
@@ -309,6 +366,8 @@ def main():
     ap.add_argument("--no-cpu-baseline", action="store_true")
     ap.add_argument("--no-sweep", action="store_true")
     ap.add_argument("--no-mx", action="store_true", help="skip the MXFP4 comparison")
+    ap.add_argument("--no-quality", action="store_true",
+                    help="skip the cosine / error comparison with FP32 products")
     ap.add_argument("--seed", type=int, default=0)
     ap.add_argument("--copy-calibration", action="store_true",
                     help="first run a plain 1 GiB device copy (3 launches), the reference "
@@ -405,6 +464,9 @@ def main():
     if not args.no_mx:
         log("MXFP4 comparison")
         result["mxfp4_comparison"] = mx_comparison(step, max(args.steps, 5))
+    if not args.no_quality:
+        log("quality (cosine vs FP32 products)")
+        result["quality"] = quality(step)
     if not args.no_sweep:
         log("quantize sweep 32768x8192")
         result["quantize_sweep_32768x8192"] = quant_sweep()
