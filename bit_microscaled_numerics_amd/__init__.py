@@ -32,7 +32,7 @@ NVFP4_ROWWISE, NVFP4_COLWISE = 0, 1
 EXPORTED = ("nvfp4_amax", "nvfp4_amax_rht", "nvfp4_quantize1d_rtn", "nvfp4_quantize1d_sr",
             "nvfp4_quantize2d_rtn", "nvfp4_quantize2d_sr", "nvfp4_rht_quantize",
             "nvfp4_dequantize", "nvfp4_gemm", "nvfp4_status_string", "nvfp4_last_error",
-            "mxfp4_quantize", "mxfp4_dequantize", "mxfp4_gemm")
+            "nvfp4_gemm_bf16", "mxfp4_quantize", "mxfp4_dequantize", "mxfp4_gemm")
 
 
 class NVFP4Error(RuntimeError):
@@ -81,6 +81,7 @@ def load_library(path: str = LIB_PATH) -> ctypes.CDLL:
         "nvfp4_rht_quantize": [vp, i64, i64, u64, i32, u64, u32, vp, i32, vp, vp, vp, vp],
         "nvfp4_dequantize": [ctypes.POINTER(c_operand), vp, vp],
         "nvfp4_gemm": [ctypes.POINTER(c_operand), ctypes.POINTER(c_operand), vp, i64, vp],
+        "nvfp4_gemm_bf16": [ctypes.POINTER(c_operand), ctypes.POINTER(c_operand), vp, i64, vp, vp],
         "mxfp4_quantize": [vp, i64, i64, i32, u64, u32, vp, vp, vp],
         "mxfp4_dequantize": [ctypes.POINTER(c_mx_operand), vp, vp],
         "mxfp4_gemm": [ctypes.POINTER(c_mx_operand), ctypes.POINTER(c_mx_operand), vp, i64, vp],
@@ -293,6 +294,23 @@ def dequantize(q: NVFP4Tensor) -> torch.Tensor:
     out = torch.empty(q.rows, q.k, dtype=torch.float32, device=q.codes.device)
     nvfp4_dequantize(q, out)
     return out
+
+
+def nvfp4_gemm_bf16(a: "NVFP4Tensor", b: "NVFP4Tensor", c, ldc: int, amax_out=None, stream=None):
+    oa, ob = a.c_struct(), b.c_struct()
+    _check(load_library().nvfp4_gemm_bf16(ctypes.byref(oa), ctypes.byref(ob), _p(c), ldc,
+                                          _p(amax_out), _stream(stream)))
+
+
+def gemm_bf16(a: NVFP4Tensor, b: NVFP4Tensor, out: Optional[torch.Tensor] = None,
+              with_amax: bool = True):
+    """C = s_a s_b A B^T rounded to BF16, and (with_amax) max |C| as a device
+    float, ready to pass as the given amax of C's quantization."""
+    if out is None:
+        out = torch.empty(a.rows, b.rows, dtype=torch.bfloat16, device=a.codes.device)
+    amax = torch.empty(1, dtype=torch.float32, device=a.codes.device) if with_amax else None
+    nvfp4_gemm_bf16(a, b, out, out.stride(0), amax)
+    return out, amax
 
 
 def gemm(a: NVFP4Tensor, b: NVFP4Tensor, out: Optional[torch.Tensor] = None) -> torch.Tensor:

@@ -56,7 +56,8 @@ struct TilePlan {
   bool split;
 };
 
-TilePlan plan_tiles(int64_t M, int64_t N, int64_t steps);
+// allow_split: the output can take two FP32 addends per element.
+TilePlan plan_tiles(int64_t M, int64_t N, int64_t steps, bool allow_split = true);
 
 // Zero the output tiles the split workgroups add into (no-op without split).
 hipError_t zero_split_tiles(const TilePlan& p, float* c, int64_t ldc, int64_t M, int64_t N,

@@ -257,6 +257,25 @@ int nvfp4_gemm(const nvfp4_operand* a, const nvfp4_operand* b, float* c, int64_t
                                      as_stream(stream)));
 }
 
+int nvfp4_gemm_bf16(const nvfp4_operand* a, const nvfp4_operand* b, uint16_t* c, int64_t ldc,
+                    float* amax_out, void* stream) {
+  int st = check_operand(a, "a");
+  if (st) return st;
+  if ((st = check_operand(b, "b"))) return st;
+  if ((st = check_gemm_extent(a, "a"))) return st;
+  if ((st = check_gemm_extent(b, "b"))) return st;
+  if (a->k != b->k)
+    return fail(NVFP4_ERR_SHAPE, "a.k=%lld != b.k=%lld", (long long)a->k, (long long)b->k);
+  if (c == nullptr) return fail(NVFP4_ERR_NULL, "c is NULL");
+  if (!aligned(c, 2)) return fail(NVFP4_ERR_ALIGN, "c must be 2-byte aligned");
+  if (amax_out != nullptr && !aligned(amax_out, 4))
+    return fail(NVFP4_ERR_ALIGN, "amax_out must be 4-byte aligned");
+  if (ldc < b->rows) return fail(NVFP4_ERR_SHAPE, "ldc=%lld < N=%lld", (long long)ldc,
+                                 (long long)b->rows);
+  return launched(nvfp4::launch_gemm_bf16(to_kernel(a), to_kernel(b), a->k, c, ldc, amax_out,
+                                          as_stream(stream)));
+}
+
 // ---------------------------------------------------------------- MXFP4
 
 int mxfp4_quantize(const void* x, int64_t rows, int64_t cols, int use_sr, uint64_t seed,

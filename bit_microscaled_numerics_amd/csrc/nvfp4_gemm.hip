@@ -28,7 +28,9 @@ typedef float float16v __attribute__((ext_vector_type(16)));
 struct GemmArgs {
   GemmOperand a, b;
   int64_t M, N, K;
-  float* c;
+  float* c;             // FP32 output, or
+  uint16_t* cb;         // BF16 output (with the BF16 epilogue)
+  uint32_t* amax;       // BF16 epilogue: binary32 bits of max |C| (nullable)
   int64_t ldc;
   int64_t full_tiles;  // tiles computed whole; tiles past them are split in two K halves
 };
@@ -269,7 +271,7 @@ __device__ __forceinline__ void interleave() {
   }
 }
 
-template <bool CHECKED, bool LD16, bool SDW>
+template <bool CHECKED, bool LD16, bool SDW, bool BF16>
 __global__ __launch_bounds__(kThreads, 1) void k_gemm(GemmArgs g) {
   extern __shared__ __attribute__((aligned(16))) uint8_t smem[];
   __shared__ v2u lut[128];
@@ -351,8 +353,14 @@ __global__ __launch_bounds__(kThreads, 1) void k_gemm(GemmArgs g) {
   // its half into the zeroed output: with exactly two addends onto zero the
   // sum does not depend on their order (fp32 addition commutes), so the
   // result stays deterministic.
+  //
+  // BF16 epilogue (no split tiles): C rounds to BF16 (nearest, ties to even)
+  // and the largest |BF16 value| of the tile goes into *g.amax by one
+  // atomic max per wave on its binary32 bits (monotone for non-negative
+  // values), so the next quantization of C can take its amax as given.
   const float alpha = (*g.a.ts) * (*g.b.ts);
   const int64_t m0 = tm * kTile + wm * 128, n0 = tn * kTile + wn * 64;
+  uint32_t mag = 0u;   // largest |bf16| bits seen by this lane
 #pragma unroll
   for (int i = 0; i < kWM; ++i)
 #pragma unroll
@@ -363,12 +371,27 @@ __global__ __launch_bounds__(kThreads, 1) void k_gemm(GemmArgs g) {
       for (int v = 0; v < 16; ++v) {
         const int64_t row = m0 + 32 * i + (v & 3) + 8 * (v >> 2) + 4 * lk;
         if (row >= g.M) continue;
-        float* dst = &g.c[row * g.ldc + col];
-        if (part < 0) *dst = acc[i][j][v] * alpha;
-        else atomicAdd(dst, acc[i][j][v] * alpha);
+        const float val = acc[i][j][v] * alpha;
+        if (BF16) {
+          const uint32_t u = __float_as_uint(val);
+          const uint32_t h = (u + 0x7FFFu + ((u >> 16) & 1u)) >> 16;
+          g.cb[row * g.ldc + col] = (uint16_t)h;
+          mag = max(mag, h & 0x7FFFu);
+        } else {
+          float* dst = &g.c[row * g.ldc + col];
+          if (part < 0) *dst = val;
+          else atomicAdd(dst, val);
+        }
       }
     }
+  if (BF16 && g.amax != nullptr) {
+#pragma unroll
+    for (int off = 32; off > 0; off >>= 1) mag = max(mag, (uint32_t)__shfl_xor((int)mag, off, 64));
+    if (lane == 0) atomicMax(g.amax, mag << 16);
+  }
 }
+
+__global__ void k_zero_word(uint32_t* p) { *p = 0u; }
 
 // Zero the output tiles that split workgroups add into: one workgroup per
 // tile, same tile order as the GEMM.
@@ -386,7 +409,7 @@ __global__ __launch_bounds__(256) void k_zero_tiles(float* __restrict__ c, int64
   }
 }
 
-TilePlan plan_tiles(int64_t M, int64_t N, int64_t steps) {
+TilePlan plan_tiles(int64_t M, int64_t N, int64_t steps, bool allow_split) {
   TilePlan p;
   p.tiles_m = (M + kTile - 1) / kTile;
   p.tiles_n = (N + kTile - 1) / kTile;
@@ -395,7 +418,7 @@ TilePlan plan_tiles(int64_t M, int64_t N, int64_t steps) {
   // half full, its tiles are split in two K halves so it takes half a round.
   const int64_t slots = num_cus();
   p.rem = tiles % slots;
-  p.split = p.rem > 0 && 2 * p.rem <= slots && tiles > slots && steps >= 4;
+  p.split = allow_split && p.rem > 0 && 2 * p.rem <= slots && tiles > slots && steps >= 4;
   p.full_tiles = p.split ? tiles - p.rem : tiles;
   p.grid = p.split ? tiles + p.rem : tiles;
   return p;
@@ -409,10 +432,17 @@ hipError_t zero_split_tiles(const TilePlan& p, float* c, int64_t ldc, int64_t M,
   return hipGetLastError();
 }
 
-hipError_t launch_gemm(const GemmOperand& a, const GemmOperand& b, int64_t K, float* c,
-                       int64_t ldc, hipStream_t s) {
-  GemmArgs g{a, b, a.rows, b.rows, K, c, ldc, 0};
-  const TilePlan plan = plan_tiles(g.M, g.N, (K + kBK - 1) / kBK);
+static hipError_t launch_gemm_any(const GemmOperand& a, const GemmOperand& b, int64_t K,
+                                  float* c, uint16_t* cb, uint32_t* amax, int64_t ldc,
+                                  hipStream_t s) {
+  const bool bf16 = cb != nullptr;
+  GemmArgs g{a, b, a.rows, b.rows, K, c, cb, amax, ldc, 0};
+  if (bf16 && amax != nullptr) {
+    hipLaunchKernelGGL(k_zero_word, dim3(1), dim3(1), 0, s, amax);
+    const hipError_t e = hipGetLastError();
+    if (e != hipSuccess) return e;
+  }
+  const TilePlan plan = plan_tiles(g.M, g.N, (K + kBK - 1) / kBK, !bf16);
   g.full_tiles = plan.full_tiles;
   const dim3 grid((unsigned)plan.grid);
   {
@@ -427,13 +457,18 @@ hipError_t launch_gemm(const GemmOperand& a, const GemmOperand& b, int64_t K, fl
     return o.ss_k == 1 && o.ss_row % 4 == 0 && (reinterpret_cast<uintptr_t>(o.scales) & 3) == 0;
   };
   const bool sdw = !checked && ld16 && sdw_ok(a) && sdw_ok(b);
-#define NVFP4_GEMM_LAUNCH(C, L, W)                                                       \
+#define NVFP4_GEMM_LAUNCH_B(C, L, W, B)                                                  \
   do {                                                                                    \
-    hipError_t e = hipFuncSetAttribute(reinterpret_cast<const void*>(&k_gemm<C, L, W>),   \
+    hipError_t e = hipFuncSetAttribute(reinterpret_cast<const void*>(&k_gemm<C, L, W, B>), \
                                        hipFuncAttributeMaxDynamicSharedMemorySize,       \
                                        kLdsBytes);                                       \
     if (e != hipSuccess) return e;                                                        \
-    hipLaunchKernelGGL((k_gemm<C, L, W>), grid, dim3(kThreads), kLdsBytes, s, g);         \
+    hipLaunchKernelGGL((k_gemm<C, L, W, B>), grid, dim3(kThreads), kLdsBytes, s, g);      \
+  } while (0)
+#define NVFP4_GEMM_LAUNCH(C, L, W)          \
+  do {                                     \
+    if (bf16) NVFP4_GEMM_LAUNCH_B(C, L, W, true);  \
+    else NVFP4_GEMM_LAUNCH_B(C, L, W, false);      \
   } while (0)
   if (sdw) NVFP4_GEMM_LAUNCH(false, true, true);
   else if (checked) {
@@ -444,7 +479,18 @@ hipError_t launch_gemm(const GemmOperand& a, const GemmOperand& b, int64_t K, fl
     else NVFP4_GEMM_LAUNCH(false, false, false);
   }
 #undef NVFP4_GEMM_LAUNCH
+#undef NVFP4_GEMM_LAUNCH_B
   return hipGetLastError();
+}
+
+hipError_t launch_gemm(const GemmOperand& a, const GemmOperand& b, int64_t K, float* c,
+                       int64_t ldc, hipStream_t s) {
+  return launch_gemm_any(a, b, K, c, nullptr, nullptr, ldc, s);
+}
+
+hipError_t launch_gemm_bf16(const GemmOperand& a, const GemmOperand& b, int64_t K, uint16_t* c,
+                            int64_t ldc, float* amax, hipStream_t s) {
+  return launch_gemm_any(a, b, K, nullptr, c, reinterpret_cast<uint32_t*>(amax), ldc, s);
 }
 
 }  // namespace nvfp4

@@ -40,6 +40,8 @@ struct GemmOperand {
 
 hipError_t launch_gemm(const GemmOperand& a, const GemmOperand& b, int64_t K, float* c,
                        int64_t ldc, hipStream_t s);
+hipError_t launch_gemm_bf16(const GemmOperand& a, const GemmOperand& b, int64_t K, uint16_t* c,
+                            int64_t ldc, float* amax, hipStream_t s);
 
 // MXFP4 (comparison format): rowwise, 32-element blocks, E8M0 scales.
 struct MxOperand {

@@ -170,6 +170,16 @@ int nvfp4_dequantize(const nvfp4_operand* q, float* out, void* stream);
 int nvfp4_gemm(const nvfp4_operand* a, const nvfp4_operand* b, float* c, int64_t ldc,
                void* stream);
 
+/* As nvfp4_gemm with a fused epilogue: C is written as BF16 [M][N] (ldc >= N
+ * elements, 2-byte aligned; each entry the FP32 result rounded to nearest,
+ * ties to even) and, when amax_out is not NULL, *amax_out receives max |C|
+ * over the BF16 values -- the tensor amax the next layer's quantization of C
+ * needs, without its separate full read of C (the cost named in "Pretraining
+ * Large Language Models with NVFP4", summary page, limitations paragraph).
+ * Pass it with NVFP4_AMAX_GIVEN.  Same operands and validation as nvfp4_gemm. */
+int nvfp4_gemm_bf16(const nvfp4_operand* a, const nvfp4_operand* b, uint16_t* c_bf16, int64_t ldc,
+                    float* amax_out, void* stream);
+
 /* ------------------------------------------------------------------------
  * MXFP4, the format NVFP4 is measured against: 32-element blocks along K, a
  * power-of-two (UE8M0) block scale, no tensor scale ("Pretraining Large

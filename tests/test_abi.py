@@ -149,3 +149,13 @@ def test_linear_rejects_cpu_tensors():
     x = torch.zeros(16, 32, dtype=torch.bfloat16)
     with pytest.raises(RuntimeError, match="no CPU fallback"):
         L.linear_fwd_bwd(x, torch.zeros(16, 32, dtype=torch.bfloat16), x[:, :16].contiguous(), 1, 1)
+
+
+def test_gemm_bf16_validation(lib):
+    g = lib.nvfp4_gemm_bf16
+    ok = _op()
+    assert g(ctypes.byref(ok), ctypes.byref(ok), None, 16, None, None) == nv.NVFP4_ERR_NULL
+    assert g(ctypes.byref(ok), ctypes.byref(ok), MIS, 16, None, None) == nv.NVFP4_ERR_ALIGN
+    assert g(ctypes.byref(ok), ctypes.byref(ok), FAKE, 16, MIS, None) == nv.NVFP4_ERR_ALIGN
+    assert g(ctypes.byref(ok), ctypes.byref(ok), FAKE, 8, None, None) == nv.NVFP4_ERR_SHAPE
+    assert g(ctypes.byref(ok), ctypes.byref(_op(k=48)), FAKE, 16, None, None) == nv.NVFP4_ERR_SHAPE

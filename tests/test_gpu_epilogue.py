@@ -1,0 +1,74 @@
+"""The fused GEMM epilogue (BF16 output + max |C|): on shapes where the FP32
+path computes every tile whole, the BF16 output is exactly the FP32 output
+rounded to nearest-even; the amax is exactly max |C| over the written BF16
+values; quantizing C with that amax given equals quantizing it with a computed
+amax byte for byte; at the benchmark's Fprop shape the BF16 output matches the
+oracle's exact product within the GEMM tolerance plus BF16 rounding."""
+import numpy as np
+import pytest
+import torch
+
+import oracle
+import bit_microscaled_numerics_amd as nv
+from bit_microscaled_numerics_amd import inputs
+from parity import GEMM_TOL, say
+
+pytestmark = pytest.mark.gpu
+
+
+def rne_bf16_bits(f32: np.ndarray) -> np.ndarray:
+    u = f32.astype(np.float32).view(np.uint32).astype(np.uint64)
+    return ((u + 0x7FFF + ((u >> 16) & 1)) >> 16).astype(np.uint16)
+
+
+def _ops(M, N, K, seed):
+    g = torch.Generator().manual_seed(seed)
+    x = inputs.normal(g, M, K, 1.0, 0.001, 50.0)
+    w = inputs.normal(g, N, K, 0.02)
+    return nv.quantize_1d(x.cuda()), nv.quantize_2d(w.cuda()), x, w
+
+
+@pytest.mark.parametrize("mnk", [(48, 80, 64), (272, 144, 528), (512, 768, 1024), (16, 16, 16)])
+def test_bf16_is_rounded_fp32_and_amax_exact(mnk):
+    M, N, K = mnk
+    qa, qb, _, _ = _ops(M, N, K, M + N + K)
+    say("gemm bf16", mnk)
+    c32 = nv.gemm(qa, qb)
+    cb, amax = nv.gemm_bf16(qa, qb)
+    torch.cuda.synchronize()
+    got = cb.cpu().view(torch.int16).numpy().view(np.uint16)
+    assert np.array_equal(got, rne_bf16_bits(c32.cpu().numpy()))
+    mag = (got & 0x7FFF).astype(np.uint32) << 16
+    assert float(amax.cpu()[0]) == float(mag.max().view(np.float32))
+
+
+def test_given_amax_feeds_the_next_quantization():
+    qa, qb, _, _ = _ops(256, 512, 256, 3)
+    cb, amax = nv.gemm_bf16(qa, qb)
+    q_given = nv.quantize_1d(cb, amax=amax)
+    q_comp = nv.quantize_1d(cb)
+    torch.cuda.synchronize()
+    assert torch.equal(q_given.amax, q_comp.amax)
+    assert torch.equal(q_given.codes, q_comp.codes)
+    assert torch.equal(q_given.scales, q_comp.scales)
+
+
+def test_fprop_shape_against_oracle():
+    wl = inputs.ffn_down(0)
+    X, W = wl.tensors["X"], wl.tensors["W"]
+    say("gemm bf16 fprop 8192x5120x20480")
+    qx, qw = nv.quantize_1d(X.cuda()), nv.quantize_2d(W.cuda())
+    cb, amax = nv.gemm_bf16(qx, qw)
+    torch.cuda.synchronize()
+    y = cb.float().cpu().numpy().astype(np.float64)
+    assert np.all(np.isfinite(y))
+    assert float(amax.cpu()[0]) == float(np.abs(y).max())
+    ox = oracle.quantize(X, oracle.ROWWISE)
+    ow = oracle.quantize(W, oracle.TWO_D, with_codes_t=True)
+    rng = np.random.default_rng(2)
+    ms = np.concatenate([[0, 8191, 255, 256], rng.integers(0, 8192, 1500)])
+    ns = np.concatenate([[0, 5119, 256, 255], rng.integers(0, 5120, 1500)])
+    ref, t = oracle.gemm_entries(ox, ow, ms, ns)
+    err = np.abs(y[ms, ns] - ref)
+    lim = GEMM_TOL * t + 2.0 ** -8 * np.abs(ref)
+    assert np.all(err <= lim), float(np.max(err / np.maximum(lim, 1e-300)))
