@@ -393,11 +393,17 @@ def main():
     ap.add_argument("--no-mx", action="store_true", help="skip the MXFP4 comparison")
     ap.add_argument("--no-quality", action="store_true",
                     help="skip the cosine / error comparison with FP32 products")
+    ap.add_argument("--step-only", action="store_true",
+                    help="time the step and stop: no MXFP4, epilogue, quality, sweep or CPU "
+                         "sections (for profiler runs, whose per-kernel averages then cover "
+                         "the step's launches alone)")
     ap.add_argument("--seed", type=int, default=0)
     ap.add_argument("--copy-calibration", action="store_true",
                     help="first run a plain 1 GiB device copy (3 launches), the reference "
                          "for scaling HBM byte counters")
     args = ap.parse_args()
+    if args.step_only:
+        args.no_mx = args.no_quality = args.no_sweep = args.no_cpu_baseline = True
     if args.gpus != 1 or int(os.environ.get("WORLD_SIZE", "1")) != 1:
         print("bench.py measures one GPU: this build has no multi-GPU path "
               "(rerun with --gpus 1)", file=sys.stderr)
@@ -489,8 +495,9 @@ def main():
     if not args.no_mx:
         log("MXFP4 comparison")
         result["mxfp4_comparison"] = mx_comparison(step, max(args.steps, 5))
-    log("fused epilogue")
-    result["fused_epilogue"] = fused_epilogue(step, max(args.steps, 5))
+    if not args.step_only:
+        log("fused epilogue")
+        result["fused_epilogue"] = fused_epilogue(step, max(args.steps, 5))
     if not args.no_quality:
         log("quality (cosine vs FP32 products)")
         result["quality"] = quality(step)
