@@ -271,6 +271,53 @@ __device__ __forceinline__ void interleave() {
   }
 }
 
+// Shared epilogue of both kernels: this lane's accumulators of WM x WN
+// blocks starting at (m0, n0).  Lane l holds column (l % 32) of each 32x32
+// block; accumulator slot v is row (v % 4) + 8 (v / 4) + 4 (l / 32).  A split
+// tile adds its half into the zeroed output: with exactly two addends onto
+// zero the sum does not depend on their order (fp32 addition commutes), so
+// the result stays deterministic.
+//
+// BF16 epilogue (no split tiles): C rounds to BF16 (nearest, ties to even)
+// and the largest |BF16 value| of the tile goes into *g.amax by one atomic
+// max per wave on its binary32 bits (monotone for non-negative values), so
+// the next quantization of C can take its amax as given.
+template <bool BF16, int WM, int WN>
+__device__ __forceinline__ void store_c(const GemmArgs& g, float16v (&acc)[WM][WN], int64_t m0,
+                                        int64_t n0, int part) {
+  const int lane = threadIdx.x & 63, lrow = lane & 31, lk = lane >> 5;
+  const float alpha = (*g.a.ts) * (*g.b.ts);
+  uint32_t mag = 0u;   // largest |bf16| bits seen by this lane
+#pragma unroll
+  for (int i = 0; i < WM; ++i)
+#pragma unroll
+    for (int j = 0; j < WN; ++j) {
+      const int64_t col = n0 + 32 * j + lrow;
+      if (col >= g.N) continue;
+#pragma unroll
+      for (int v = 0; v < 16; ++v) {
+        const int64_t row = m0 + 32 * i + (v & 3) + 8 * (v >> 2) + 4 * lk;
+        if (row >= g.M) continue;
+        const float val = acc[i][j][v] * alpha;
+        if (BF16) {
+          const uint32_t u = __float_as_uint(val);
+          const uint32_t h = (u + 0x7FFFu + ((u >> 16) & 1u)) >> 16;
+          g.cb[row * g.ldc + col] = (uint16_t)h;
+          mag = max(mag, h & 0x7FFFu);
+        } else {
+          float* dst = &g.c[row * g.ldc + col];
+          if (part < 0) *dst = val;
+          else atomicAdd(dst, val);
+        }
+      }
+    }
+  if (BF16 && g.amax != nullptr) {
+#pragma unroll
+    for (int off = 32; off > 0; off >>= 1) mag = max(mag, (uint32_t)__shfl_xor((int)mag, off, 64));
+    if (lane == 0) atomicMax(g.amax, mag << 16);
+  }
+}
+
 template <bool CHECKED, bool LD16, bool SDW, bool BF16>
 __global__ __launch_bounds__(kThreads, 1) void k_gemm(GemmArgs g) {
   extern __shared__ __attribute__((aligned(16))) uint8_t smem[];
@@ -348,47 +395,316 @@ __global__ __launch_bounds__(kThreads, 1) void k_gemm(GemmArgs g) {
     }
   }
 
-  // Epilogue: lane l holds column (l % 32) of each 32x32 block; accumulator
-  // slot v is row (v % 4) + 8 * (v / 4) + 4 * (l / 32).  A split tile adds
-  // its half into the zeroed output: with exactly two addends onto zero the
-  // sum does not depend on their order (fp32 addition commutes), so the
-  // result stays deterministic.
-  //
-  // BF16 epilogue (no split tiles): C rounds to BF16 (nearest, ties to even)
-  // and the largest |BF16 value| of the tile goes into *g.amax by one
-  // atomic max per wave on its binary32 bits (monotone for non-negative
-  // values), so the next quantization of C can take its amax as given.
-  const float alpha = (*g.a.ts) * (*g.b.ts);
-  const int64_t m0 = tm * kTile + wm * 128, n0 = tn * kTile + wn * 64;
-  uint32_t mag = 0u;   // largest |bf16| bits seen by this lane
+  store_c<BF16, kWM, kWN>(g, acc, tm * kTile + wm * 128, tn * kTile + wn * 64, part);
+}
+
+// ---------------------------------------------------------------------------
+// Fast path: raw operands moved global -> LDS by the load unit
+// ---------------------------------------------------------------------------
+// Used when both operands have K-contiguous, 4-byte aligned scale rows
+// (dword scales), rows a multiple of 16 bytes and K / 64 steps a multiple of
+// 4 (of 8 when the last round of tiles is split).  Same tile (256 x 256) and
+// decode as above, different division of work:
+//  - 4 waves, one per SIMD.  Wave w owns B rows 64w .. +63 of the tile and
+//    all 256 A rows: 8 x 2 blocks of 32 x 32, 256 FP32 accumulators per lane
+//    (they live in the accumulation registers).  A is decoded once per
+//    workgroup into FP16 in LDS as above; B is private to its wave, so each
+//    lane decodes its own B fragments straight into MFMA operand registers.
+//    LDS traffic per step: 32 KiB of decoded A written, 128 KiB read (the
+//    8-wave kernel: 64 KiB and 192 KiB).
+//  - Inside a 64-wide K step, lane half lk takes K 32 lk .. +31, 8 per
+//    16-wide sub-step.  The same permutation on A and B leaves the sum
+//    unchanged, and a lane's B operand for a step is one 16-byte chunk of
+//    codes and one scale dword.
+//  - Raw codes and scales reach LDS through buffer loads that write LDS
+//    directly, two K steps (64 bytes of a row) at a time, so one load
+//    instruction covers 16 rows x 64 B instead of 32 rows x 32 B: half the
+//    cache lines per byte.  Each wave loads exactly the A rows it decodes and
+//    the B rows it multiplies, so the raw data is wave-private: no barrier,
+//    only the wave's own load counter.  Two slots per operand; a slot is
+//    refilled two steps before it is read, with no register cost.
+constexpr int kThreads4 = 256;
+constexpr int kMB = 8, kNB = 2;              // 32 x 32 blocks per wave
+constexpr int kStage4 = kTile * kRowBytes;   // 32 KiB of decoded A per stage
+constexpr int kRawRow = 64;                  // bytes of a row per 2-step group
+constexpr int kRawBytes = kTile * kRawRow;   // 16 KiB per operand and slot
+constexpr int kScRow = 8;                    // scale bytes of a row per group
+constexpr int kScBytes = kTile * kScRow;     // 2 KiB
+// s_waitcnt immediate: vmcnt <= 12, expcnt and lgkmcnt not waited on
+constexpr int kVmcnt12 = 12 | (7 << 4) | (15 << 8);
+
+typedef __attribute__((address_space(3))) void* lds_ptr_t;
+
+// E4M3 scale code in bits [pos, pos + 7) of w -> {E, mantissa pair} in ALU
+// (the table read of scale_dec would add an LDS wait next to the operand
+// reads).
+__device__ __forceinline__ BlockDec scale_alu(uint32_t w, uint32_t pos) {
+  const uint32_t code = __builtin_amdgcn_ubfe(w, pos, 7);
+  const float e = __builtin_amdgcn_cvt_f32_fp8((int)code, 0);
+  const uint32_t h = 0x3C00u | (__builtin_amdgcn_ubfe(__float_as_uint(e), 20, 3) << 7);
+  BlockDec d;
+  d.e = e;
+  d.mant = __builtin_bit_cast(half2v, h | (h << 16));
+  return d;
+}
+
+// Raw layout [row][4 chunks of 16 B], chunk c of row r at position
+// c ^ rg(r): the 16-byte reads of the A decode (8 rows x 2 chunks per 16
+// lanes) and of the B fragments (16 rows x 1 chunk) then hit distinct banks.
+__device__ __forceinline__ int raw_g(int r) { return ((r >> 1) & 2) | ((r >> 3) & 1); }
+__device__ __forceinline__ uint32_t raw_off(int r, int c) {
+  return (uint32_t)(r * kRawRow + ((c ^ raw_g(r)) << 4));
+}
+
+struct DmaOp {
+  __amdgpu_buffer_rsrc_t codes, scales;
+  uint32_t voff_c[4];   // this wave's 16-row code loads
+  uint32_t voff_s[2];   // this wave's 32-row scale loads
+};
+
+// Code load q covers rows crow[q] .. +15 (lane l: row + l / 4, position
+// l % 4); scale load q covers rows srow[q] .. +31 (lane l: row + l / 2, the
+// dword of group step l % 2).
+__device__ __forceinline__ DmaOp make_dma(const GemmOperand& op, int64_t row0, const int (&crow)[4],
+                                          const int (&srow)[2]) {
+  DmaOp v;
+  const int64_t rem_rows = op.rows - row0;
+  const int64_t code_bytes = rem_rows * op.ld;
+  const uint8_t* sbase = op.scales + (row0 / op.blk_rows) * op.ss_row;
+  const int64_t scale_bytes = op.scale_bytes - (row0 / op.blk_rows) * op.ss_row;
+  v.codes = __builtin_amdgcn_make_buffer_rsrc(
+      const_cast<uint8_t*>(op.codes + row0 * op.ld), (short)0,
+      (int)(code_bytes < 0x7FFFFFFF ? code_bytes : 0x7FFFFFFF), (int)kBufFlags);
+  v.scales = __builtin_amdgcn_make_buffer_rsrc(
+      const_cast<uint8_t*>(sbase), (short)0,
+      (int)(scale_bytes < 0x7FFFFFFF ? scale_bytes : 0x7FFFFFFF), (int)kBufFlags);
+  const int lane = threadIdx.x & 63;
 #pragma unroll
-  for (int i = 0; i < kWM; ++i)
+  for (int q = 0; q < 4; ++q) {
+    const int r = crow[q] + (lane >> 2);
+    v.voff_c[q] = (uint32_t)(r * op.ld + 16 * ((lane & 3) ^ raw_g(r)));
+  }
 #pragma unroll
-    for (int j = 0; j < kWN; ++j) {
-      const int64_t col = n0 + 32 * j + lrow;
-      if (col >= g.N) continue;
+  for (int q = 0; q < 2; ++q) {
+    const int r = srow[q] + (lane >> 1);
+    v.voff_s[q] = (uint32_t)((r / op.blk_rows) * op.ss_row + 4 * (lane & 1));
+  }
+  return v;
+}
+
+// Steps x0, x0 + 1 of this wave's rows into a slot (6 load instructions).
+// Scale dwords of steps past the last read 0 (offset 2^31, past
+// num_records), so their blocks decode to zero whatever the codes; the code
+// offset is clamped to the last step.
+__device__ __forceinline__ void dma_group(const DmaOp& v, uint8_t* raw, uint8_t* sc,
+                                          const int (&crow)[4], const int (&srow)[2], int x0,
+                                          int last) {
+  const int lane = threadIdx.x & 63;
+  const uint32_t kb = (uint32_t)((x0 < last ? x0 : last) * 32);
 #pragma unroll
-      for (int v = 0; v < 16; ++v) {
-        const int64_t row = m0 + 32 * i + (v & 3) + 8 * (v >> 2) + 4 * lk;
-        if (row >= g.M) continue;
-        const float val = acc[i][j][v] * alpha;
-        if (BF16) {
-          const uint32_t u = __float_as_uint(val);
-          const uint32_t h = (u + 0x7FFFu + ((u >> 16) & 1u)) >> 16;
-          g.cb[row * g.ldc + col] = (uint16_t)h;
-          mag = max(mag, h & 0x7FFFu);
+  for (int q = 0; q < 4; ++q)
+    __builtin_amdgcn_raw_ptr_buffer_load_lds(v.codes, (lds_ptr_t)(raw + crow[q] * kRawRow), 16,
+                                             v.voff_c[q], kb, 0, 0);
+  const uint32_t dead = (x0 + (lane & 1) > last) ? 0x80000000u : 0u;
+#pragma unroll
+  for (int q = 0; q < 2; ++q)
+    __builtin_amdgcn_raw_ptr_buffer_load_lds(v.scales, (lds_ptr_t)(sc + srow[q] * kScRow), 4,
+                                             v.voff_s[q] + dead, (uint32_t)(4 * x0), 0, 0);
+}
+
+// A thread's raw share of one step, read back from a slot: two rows' 16-byte
+// chunks (K-half kh of group step u) and their scale dwords.
+struct RawRegs {
+  v4u codes[2];
+  uint32_t sc[2];
+};
+
+__device__ __forceinline__ void read_raw(RawRegs& r, const uint8_t* raw, const uint8_t* sc,
+                                         int row0, int row1, int kh, int u) {
+  r.codes[0] = *reinterpret_cast<const v4u*>(raw + raw_off(row0, 2 * u + kh));
+  r.codes[1] = *reinterpret_cast<const v4u*>(raw + raw_off(row1, 2 * u + kh));
+  r.sc[0] = *reinterpret_cast<const uint32_t*>(sc + row0 * kScRow + 4 * u);
+  r.sc[1] = *reinterpret_cast<const uint32_t*>(sc + row1 * kScRow + 4 * u);
+}
+
+// Decode word p of A row (t / 2) + 128 q into a stage (chunk 4 (t % 2) + p).
+__device__ __forceinline__ void store_a(uint8_t* stage, const RawRegs& r, int q, int p,
+                                        uint32_t pos0, uint32_t pos1) {
+  const int row = (threadIdx.x >> 1) + 128 * q, h = threadIdx.x & 1;
+  const BlockDec d = scale_alu(r.sc[q], p < 2 ? pos0 : pos1);
+  *reinterpret_cast<half8*>(stage + lds_off(row, 4 * h + p)) = decode8(r.codes[q][p], d);
+}
+
+struct OpsA { half8 a[kMB]; };
+struct OpsB { half8 b[kNB]; };
+
+// B fragments of sub-step s: word s of each block's chunk.
+__device__ __forceinline__ void dec_b(OpsB& o, const RawRegs& r, int s, uint32_t pos0,
+                                      uint32_t pos1) {
+#pragma unroll
+  for (int j = 0; j < kNB; ++j)
+    o.b[j] = decode8(r.codes[j][s], scale_alu(r.sc[j], s < 2 ? pos0 : pos1));
+}
+
+// A fragments of sub-step s (chunk 4 lk + s of rows 32 i + lane % 32).
+__device__ __forceinline__ void read_a(OpsA& o, const uint8_t* stage, int lrow, int lk, int s) {
+#pragma unroll
+  for (int i = 0; i < kMB; ++i)
+    o.a[i] = *reinterpret_cast<const half8*>(stage + lds_off(32 * i + lrow, 4 * lk + s));
+}
+
+__device__ __forceinline__ void mfma16(float16v (&acc)[kMB][kNB], const OpsA& a, const OpsB& b) {
+#pragma unroll
+  for (int i = 0; i < kMB; ++i)
+#pragma unroll
+    for (int j = 0; j < kNB; ++j)
+      acc[i][j] = __builtin_amdgcn_mfma_f32_32x32x16_f16(a.a[i], b.b[j], acc[i][j], 0, 0, 0);
+}
+
+// 16 x {1 MFMA, 3 VALU}, with the LDS reads and writes spread in between.
+__device__ __forceinline__ void interleave16() {
+#pragma unroll
+  for (int m = 0; m < 16; ++m) {
+    __builtin_amdgcn_sched_group_barrier(0x008, 1, 0);   // MFMA
+    __builtin_amdgcn_sched_group_barrier(0x002, 3, 0);   // VALU
+    if (m < 9) __builtin_amdgcn_sched_group_barrier(0x100, 1, 0);   // DS read
+    if (m % 5 == 1) __builtin_amdgcn_sched_group_barrier(0x200, 1, 0);  // DS write
+  }
+}
+
+template <bool BF16>
+__global__ __launch_bounds__(kThreads4, 1) void k_gemm_dma(GemmArgs g) {
+  extern __shared__ __attribute__((aligned(16))) uint8_t smem[];   // decoded A, 2 stages
+  // raw slots as separate arrays (one LDS object per slot)
+  __shared__ __attribute__((aligned(16))) uint8_t rawA0[kRawBytes], rawA1[kRawBytes];
+  __shared__ __attribute__((aligned(16))) uint8_t rawB0[kRawBytes], rawB1[kRawBytes];
+  __shared__ __attribute__((aligned(16))) uint8_t scA0[kScBytes], scA1[kScBytes];
+  __shared__ __attribute__((aligned(16))) uint8_t scB0[kScBytes], scB1[kScBytes];
+
+  const int t = threadIdx.x, lane = t & 63;
+  // wave and tile indices in scalar registers: the buffer descriptors and LDS
+  // load bases built from them must be uniform
+  const int wave = __builtin_amdgcn_readfirstlane(t >> 6);
+  const int lrow = lane & 31, lk = lane >> 5;
+  const int64_t tiles_m = (g.M + kTile - 1) / kTile, tiles_n = (g.N + kTile - 1) / kTile;
+  int64_t tm, tn;
+  int part;
+  block_tile(g.full_tiles, tiles_m, tiles_n, tm, tn, part);
+  tm = __builtin_amdgcn_readfirstlane((int)tm);
+  tn = __builtin_amdgcn_readfirstlane((int)tn);
+  part = __builtin_amdgcn_readfirstlane(part);
+
+  const int a_crow[4] = {32 * wave, 32 * wave + 16, 128 + 32 * wave, 128 + 32 * wave + 16};
+  const int a_srow[2] = {32 * wave, 128 + 32 * wave};
+  const int b_crow[4] = {64 * wave, 64 * wave + 16, 64 * wave + 32, 64 * wave + 48};
+  const int b_srow[2] = {64 * wave, 64 * wave + 32};
+  const DmaOp va = make_dma(g.a, tm * kTile, a_crow, a_srow);
+  const DmaOp vb = make_dma(g.b, tn * kTile, b_crow, b_srow);
+  // A rows this thread decodes; B rows whose fragments this lane holds
+  const int ar0 = t >> 1, ar1 = 128 + (t >> 1), ah = t & 1;
+  const int br0 = 64 * wave + lrow, br1 = br0 + 32;
+  // bit positions of the step's two block scales in a scale dword
+  const uint32_t apos0 = 16u * ah, apos1 = apos0 + 8u;
+  const uint32_t bpos0 = 16u * lk, bpos1 = bpos0 + 8u;
+
+  float16v acc[kMB][kNB];
+#pragma unroll
+  for (int i = 0; i < kMB; ++i)
+#pragma unroll
+    for (int j = 0; j < kNB; ++j) acc[i][j] = float16v{};
+
+  const int steps = (int)(g.K / kBK), half_steps = (steps + 1) / 2;
+  const int s0 = part == 1 ? half_steps : 0;
+  const int s1 = part == 0 ? half_steps : steps;
+  const int last = s1 - 1;
+
+  // groups 0 and 1 (steps s0 .. s0 + 3) of A and B
+  dma_group(va, rawA0, scA0, a_crow, a_srow, s0, last);
+  dma_group(vb, rawB0, scB0, b_crow, b_srow, s0, last);
+  dma_group(va, rawA1, scA1, a_crow, a_srow, s0 + 2, last);
+  dma_group(vb, rawB1, scB1, b_crow, b_srow, s0 + 2, last);
+  __builtin_amdgcn_s_waitcnt(kVmcnt12);   // group 0 of A and B has landed
+  __builtin_amdgcn_sched_barrier(0);
+  RawRegs ra, rb;
+  read_raw(ra, rawA0, scA0, ar0, ar1, ah, 0);
+#pragma unroll
+  for (int q = 0; q < 2; ++q)
+#pragma unroll
+    for (int p = 0; p < 4; ++p) store_a(smem, ra, q, p, apos0, apos1);
+  read_raw(ra, rawA0, scA0, ar0, ar1, ah, 1);
+  read_raw(rb, rawB0, scB0, br0, br1, lk, 0);
+  OpsB bcur, bnxt;
+  dec_b(bcur, rb, 0, bpos0, bpos1);
+  __syncthreads();
+  OpsA acur, anxt;
+  read_a(acur, smem, lrow, lk, 0);
+
+  // Step x (h = (x - s0) % 4) multiplies decoded A stage h % 2 with B(x)
+  // (decoded one sub-step ahead from rb) while decoding A(x+1) (ra) into
+  // the other stage.  Raw group slot of steps x, x+1 (x even): h / 2.  At
+  // the last sub-step: barrier (A(x+1) is complete), then an even step
+  // refills its A slot with the group of steps x+4, x+5 and an odd step its B
+  // slot with steps x+3, x+4 -- both slots were last read a step earlier;
+  // then ra / rb are reloaded with A(x+2) / B(x+1), whose group was loaded
+  // two steps ago.  The loads of the two groups issued since (12
+  // instructions) may still be in flight.
+  for (int it = s0; it < s1; it += 4) {
+#pragma unroll
+    for (int h = 0; h < 4; ++h) {
+      const int x = it + h;
+      uint8_t* cur = smem + ((h & 1) ? kStage4 : 0);
+      uint8_t* oth = smem + ((h & 1) ? 0 : kStage4);
+      const int a2 = ((h + 2) >> 1) & 1, b1 = ((h + 1) >> 1) & 1;   // slots of A(x+2), B(x+1)
+#pragma unroll
+      for (int s = 0; s < 4; ++s) {
+        if (s < 3) {
+          read_a(anxt, cur, lrow, lk, s + 1);
+          dec_b(bnxt, rb, s + 1, bpos0, bpos1);
+          if (s == 0) {
+            store_a(oth, ra, 0, 0, apos0, apos1);
+            store_a(oth, ra, 0, 1, apos0, apos1);
+            store_a(oth, ra, 0, 2, apos0, apos1);
+          } else if (s == 1) {
+            store_a(oth, ra, 0, 3, apos0, apos1);
+            store_a(oth, ra, 1, 0, apos0, apos1);
+            store_a(oth, ra, 1, 1, apos0, apos1);
+          } else {
+            store_a(oth, ra, 1, 2, apos0, apos1);
+            store_a(oth, ra, 1, 3, apos0, apos1);
+          }
+          mfma16(acc, acur, bcur);
+          interleave16();
+          acur = anxt;
+          bcur = bnxt;
         } else {
-          float* dst = &g.c[row * g.ldc + col];
-          if (part < 0) *dst = val;
-          else atomicAdd(dst, val);
+          // this wave's decode writes done, then the workgroup barrier; no
+          // memory fence, which would also wait for the raw loads in flight
+          asm volatile("s_waitcnt lgkmcnt(0)\n\ts_barrier" ::: "memory");
+          __builtin_amdgcn_sched_barrier(0);
+          if ((h & 1) == 0)
+            dma_group(va, (h >> 1) ? rawA1 : rawA0, (h >> 1) ? scA1 : scA0, a_crow, a_srow,
+                      x + 4, last);
+          else
+            dma_group(vb, (h >> 1) ? rawB1 : rawB0, (h >> 1) ? scB1 : scB0, b_crow, b_srow,
+                      x + 3, last);
+          __builtin_amdgcn_s_waitcnt(kVmcnt12);
+          __builtin_amdgcn_sched_barrier(0);
+          read_a(anxt, oth, lrow, lk, 0);
+          read_raw(ra, a2 ? rawA1 : rawA0, a2 ? scA1 : scA0, ar0, ar1, ah, h & 1);
+          read_raw(rb, b1 ? rawB1 : rawB0, b1 ? scB1 : scB0, br0, br1, lk, (h + 1) & 1);
+          dec_b(bnxt, rb, 0, bpos0, bpos1);
+          mfma16(acc, acur, bcur);
+          interleave16();
+          acur = anxt;
+          bcur = bnxt;
+          __builtin_amdgcn_sched_barrier(0);
         }
       }
     }
-  if (BF16 && g.amax != nullptr) {
-#pragma unroll
-    for (int off = 32; off > 0; off >>= 1) mag = max(mag, (uint32_t)__shfl_xor((int)mag, off, 64));
-    if (lane == 0) atomicMax(g.amax, mag << 16);
   }
+  __builtin_amdgcn_s_waitcnt(0);   // loads of the groups past the end
+
+  store_c<BF16, kMB, kNB>(g, acc, tm * kTile, tn * kTile + wave * 64, part);
 }
 
 __global__ void k_zero_word(uint32_t* p) { *p = 0u; }
@@ -457,6 +773,10 @@ static hipError_t launch_gemm_any(const GemmOperand& a, const GemmOperand& b, in
     return o.ss_k == 1 && o.ss_row % 4 == 0 && (reinterpret_cast<uintptr_t>(o.scales) & 3) == 0;
   };
   const bool sdw = !checked && ld16 && sdw_ok(a) && sdw_ok(b);
+  // fast path: whole 4-step trips in every K range a workgroup takes (codes
+  // are 16-byte aligned, checked by the API)
+  const int64_t steps = K / kBK;
+  const bool dma = sdw && steps % 4 == 0 && (!plan.split || steps % 8 == 0);
 #define NVFP4_GEMM_LAUNCH_B(C, L, W, B)                                                  \
   do {                                                                                    \
     hipError_t e = hipFuncSetAttribute(reinterpret_cast<const void*>(&k_gemm<C, L, W, B>), \
@@ -470,7 +790,16 @@ static hipError_t launch_gemm_any(const GemmOperand& a, const GemmOperand& b, in
     if (bf16) NVFP4_GEMM_LAUNCH_B(C, L, W, true);  \
     else NVFP4_GEMM_LAUNCH_B(C, L, W, false);      \
   } while (0)
-  if (sdw) NVFP4_GEMM_LAUNCH(false, true, true);
+  if (dma) {
+    // 64 KiB of dynamic LDS (decoded A) on top of the 72 KiB of raw slots
+    const void* fn = bf16 ? reinterpret_cast<const void*>(&k_gemm_dma<true>)
+                          : reinterpret_cast<const void*>(&k_gemm_dma<false>);
+    const hipError_t e =
+        hipFuncSetAttribute(fn, hipFuncAttributeMaxDynamicSharedMemorySize, 2 * kStage4);
+    if (e != hipSuccess) return e;
+    if (bf16) hipLaunchKernelGGL((k_gemm_dma<true>), grid, dim3(kThreads4), 2 * kStage4, s, g);
+    else hipLaunchKernelGGL((k_gemm_dma<false>), grid, dim3(kThreads4), 2 * kStage4, s, g);
+  } else if (sdw) NVFP4_GEMM_LAUNCH(false, true, true);
   else if (checked) {
     if (ld16) NVFP4_GEMM_LAUNCH(true, true, false);
     else NVFP4_GEMM_LAUNCH(true, false, false);

@@ -231,6 +231,25 @@ def test_gemm_wgrad_rht_sr(tmn):
     assert_gemm_close(dw.cpu().numpy(), c, t, f"wgrad {tmn}")
 
 
+# Which kernel runs: with dword scales (K-contiguous, K % 64 == 0) a K that
+# is a multiple of 256 takes the fast path (raw operands loaded straight to
+# LDS, whole 4-step trips); other multiples of 64 take the general kernel.
+@pytest.mark.parametrize("mnk", [(272, 400, 512), (48, 80, 256), (64, 96, 1280),   # fast path
+                                 (272, 528, 320), (256, 256, 192), (64, 48, 704)])  # general
+def test_gemm_fast_path_and_fallback(mnk):
+    M, N, K = mnk
+    g = torch.Generator().manual_seed(M + N + K)
+    x = inputs.normal(g, M, K, 1.0, 0.001, 50.0)
+    w = inputs.normal(g, N, K, 0.02)
+    say("gemm fast/general", mnk)
+    qx, qw = nv.quantize_1d(x.cuda()), nv.quantize_2d(w.cuda())
+    y = nv.gemm(qx, qw)
+    torch.cuda.synchronize()
+    ox, ow = oracle.quantize(x, oracle.ROWWISE), oracle.quantize(w, oracle.TWO_D)
+    c, t = oracle.gemm(ox, ow)
+    assert_gemm_close(y.cpu().numpy(), c, t, f"fast/general {mnk}")
+
+
 def test_gemm_ldc_and_zero_operand():
     g = torch.Generator().manual_seed(9)
     x = inputs.normal(g, 48, 64)
@@ -259,12 +278,15 @@ def test_single_fprop_config():
     assert_gemm_close(y.cpu().numpy(), c, t, "single fprop")
 
 
-def test_gemm_split_last_round_is_exact_and_deterministic():
+@pytest.mark.parametrize("K", [1024, 768])
+def test_gemm_split_last_round_is_exact_and_deterministic(K):
     """M = 17*256, N = 16*256: 272 tiles on a 256-CU device leave a last
     round of 16 tiles (the last tile-row), which the GEMM splits into two K
     halves added into a zeroed output.  Check those tiles densely against the
-    exact oracle, the rest on samples, and two runs bit for bit."""
-    M, N, K = 17 * 256, 16 * 256, 1024
+    exact oracle, the rest on samples, and two runs bit for bit.  K = 1024
+    (16 steps, 8 per half) runs on the fast path, K = 768 (6 per half) on the
+    general kernel."""
+    M, N = 17 * 256, 16 * 256
     g = torch.Generator().manual_seed(40)
     x = inputs.normal(g, M, K, 1.0, 0.001, 50.0)
     w = inputs.normal(g, N, K, 0.02)
