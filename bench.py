@@ -466,7 +466,7 @@ def main():
     gemm_ms = float(per_op[:, gemm_idx].mean())
     gemm_flops_launch = gemm_flops / len(gemm_idx)
     achieved = gemm_flops_launch / (gemm_ms * 1e-3) / 1e12
-    roofline = {"bound": "mfma", "kernel": "k_gemm (Fprop, Dgrad, Wgrad launches)",
+    roofline = {"bound": "mfma", "kernel": "k_gemm_dma (Fprop, Dgrad, Wgrad launches)",
                 "achieved": round(achieved, 1), "peak": MFMA_F16_PEAK_TFLOPS,
                 "unit": "TFLOP/s", "frac": round(achieved / MFMA_F16_PEAK_TFLOPS, 4),
                 "traffic": gemm_traffic()}
