@@ -498,6 +498,15 @@ def main():
     if not args.step_only:
         log("fused epilogue")
         result["fused_epilogue"] = fused_epilogue(step, max(args.steps, 5))
+    if not args.step_only:
+        log("matrix-core ceiling (probe)")
+        ceil = {}
+        for mode, name in ((nv.PROBE_ZEROS, "zeros"), (nv.PROBE_NVFP4_LIKE, "nvfp4-like"),
+                           (nv.PROBE_UNIFORM, "uniform fp16")):
+            tf, ghz = nv.probe_mfma(mode, 200000)   # ~50 ms: the sustained clock
+            ceil[name] = {"TFLOP/s": round(tf, 1), "clock_GHz": round(ghz, 3)}
+        ceil["gemm_frac_of_nvfp4_like"] = round(achieved / ceil["nvfp4-like"]["TFLOP/s"], 4)
+        result["mfma_ceiling"] = ceil
     if not args.no_quality:
         log("quality (cosine vs FP32 products)")
         result["quality"] = quality(step)

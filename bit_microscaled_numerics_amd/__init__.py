@@ -32,7 +32,8 @@ NVFP4_ROWWISE, NVFP4_COLWISE = 0, 1
 EXPORTED = ("nvfp4_amax", "nvfp4_amax_rht", "nvfp4_quantize1d_rtn", "nvfp4_quantize1d_sr",
             "nvfp4_quantize2d_rtn", "nvfp4_quantize2d_sr", "nvfp4_rht_quantize",
             "nvfp4_dequantize", "nvfp4_gemm", "nvfp4_status_string", "nvfp4_last_error",
-            "nvfp4_gemm_bf16", "mxfp4_quantize", "mxfp4_dequantize", "mxfp4_gemm")
+            "nvfp4_gemm_bf16", "mxfp4_quantize", "mxfp4_dequantize", "mxfp4_gemm",
+            "nvfp4_probe_mfma")
 
 
 class NVFP4Error(RuntimeError):
@@ -85,6 +86,7 @@ def load_library(path: str = LIB_PATH) -> ctypes.CDLL:
         "mxfp4_quantize": [vp, i64, i64, i32, u64, u32, vp, vp, vp],
         "mxfp4_dequantize": [ctypes.POINTER(c_mx_operand), vp, vp],
         "mxfp4_gemm": [ctypes.POINTER(c_mx_operand), ctypes.POINTER(c_mx_operand), vp, i64, vp],
+        "nvfp4_probe_mfma": [i32, i32, ctypes.POINTER(ctypes.c_float), ctypes.POINTER(ctypes.c_float)],
     }
     for name, args in sigs.items():
         fn = getattr(lib, name)
@@ -375,3 +377,15 @@ def mx_gemm(a: MXFP4Tensor, b: MXFP4Tensor, out: Optional[torch.Tensor] = None) 
         out = torch.empty(a.rows, b.rows, dtype=torch.float32, device=a.codes.device)
     mxfp4_gemm(a, b, out, out.stride(0))
     return out
+
+
+PROBE_ZEROS, PROBE_NVFP4_LIKE, PROBE_UNIFORM = 0, 1, 2
+
+
+def probe_mfma(mode: int, iters: int = 8000):
+    """(TFLOP/s, clock GHz) of the FP16 matrix cores running the GEMM's MFMA
+    pattern from registers on operand data of kind ``mode`` (measurement
+    support: the ceiling the GEMM's roofline fraction is read against)."""
+    tf, ghz = ctypes.c_float(), ctypes.c_float()
+    _check(load_library().nvfp4_probe_mfma(mode, iters, ctypes.byref(tf), ctypes.byref(ghz)))
+    return tf.value, ghz.value

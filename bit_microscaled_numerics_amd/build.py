@@ -15,7 +15,7 @@ CSRC = os.path.join(HERE, "csrc")
 ROOT = os.path.dirname(HERE)
 BUILD = os.path.join(ROOT, "_build", "nvfp4")
 LIB = os.path.join(HERE, "libnvfp4.so")
-SOURCES = ["nvfp4_api.cpp", "nvfp4_quant.hip", "nvfp4_gemm.hip", "mxfp4.hip"]
+SOURCES = ["nvfp4_api.cpp", "nvfp4_quant.hip", "nvfp4_gemm.hip", "mxfp4.hip", "mfma_probe.hip"]
 ARCH = os.environ.get("NVFP4_OFFLOAD_ARCH", "gfx950")
 
 CFLAGS = ["-O3", "-std=c++17", "-fPIC", "-ffp-contract=off", f"--offload-arch={ARCH}",

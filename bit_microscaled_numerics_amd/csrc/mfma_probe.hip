@@ -1,0 +1,134 @@
+// mfma_probe.hip -- measurement support, not part of the quantize/GEMM path:
+// the sustained throughput and shader clock of the FP16 matrix cores on
+// operand data of a chosen kind, the context for reading the GEMM's roofline
+// fraction.  The MI355X holds its clock only while power allows, and the
+// power drawn by v_mfma_f32_32x32x16_f16 depends on the operand bits: zeros
+// run near the top clock, decoded NVFP4 values (what the GEMM multiplies)
+// and uniform FP16 well below it.
+//
+// Layout of the probe: 256 workgroups x 4 waves (one wave per SIMD on 256
+// CUs), each wave 8 x 2 independent 32 x 32 accumulators fed from registers
+// -- the GEMM fast path's MFMA pattern with no loads, decode or LDS.  Wave 0
+// of every workgroup reads the shader-clock counter (s_memtime) and the
+// 100 MHz real-time counter (s_memrealtime) around the loop.
+#include "nvfp4_kernels.h"
+
+namespace nvfp4 {
+namespace {
+
+typedef _Float16 half8 __attribute__((ext_vector_type(8)));
+typedef float float16v __attribute__((ext_vector_type(16)));
+
+constexpr int kProbeWgs = 256, kProbeThreads = 256, kProbeVecs = 10;   // half8 per thread
+
+__device__ __forceinline__ uint32_t mix32(uint32_t x) {   // integer hash (xorshift-multiply)
+  x ^= x >> 16; x *= 0x7feb352du; x ^= x >> 15; x *= 0x846ca68bu; x ^= x >> 16;
+  return x;
+}
+
+// mode 0: zeros; 1: E2M1 x E4M3-mantissa values / 16 with random signs (the
+// decoded operands of the NVFP4 GEMM); 2: uniform in [-1, 1).
+__global__ void k_probe_fill(_Float16* v, int64_t n, int mode) {
+  const int64_t i = (int64_t)blockIdx.x * blockDim.x + threadIdx.x;
+  if (i >= n) return;
+  const uint32_t h = mix32((uint32_t)i * 2654435761u + 12345u);
+  float x = 0.f;
+  if (mode == 1) {
+    const float q[8] = {0.f, .5f, 1.f, 1.5f, 2.f, 3.f, 4.f, 6.f};
+    x = q[h & 7] * (1.f + (float)((h >> 3) & 7) / 8.f) * ((h >> 6) & 1 ? -1.f : 1.f) / 16.f;
+  } else if (mode == 2) {
+    x = (float)(h >> 8) / 8388608.f - 1.f;
+  }
+  v[i] = (_Float16)x;
+}
+
+__global__ __launch_bounds__(kProbeThreads, 1) void k_probe_mfma(const half8* src, float* sink,
+                                                                 unsigned long long* clk, int iters) {
+  const int gt = blockIdx.x * kProbeThreads + threadIdx.x;
+  half8 a[8], b[2];
+#pragma unroll
+  for (int i = 0; i < 8; ++i) a[i] = src[gt * kProbeVecs + i];
+#pragma unroll
+  for (int j = 0; j < 2; ++j) b[j] = src[gt * kProbeVecs + 8 + j];
+  float16v acc[8][2];
+#pragma unroll
+  for (int i = 0; i < 8; ++i)
+#pragma unroll
+    for (int j = 0; j < 2; ++j) acc[i][j] = float16v{};
+  const unsigned long long t0 = __builtin_amdgcn_s_memtime();
+  const unsigned long long r0 = __builtin_amdgcn_s_memrealtime();
+  for (int it = 0; it < iters; ++it) {
+#pragma unroll
+    for (int i = 0; i < 8; ++i)
+#pragma unroll
+      for (int j = 0; j < 2; ++j)
+        acc[i][j] = __builtin_amdgcn_mfma_f32_32x32x16_f16(a[i], b[j], acc[i][j], 0, 0, 0);
+  }
+  const unsigned long long t1 = __builtin_amdgcn_s_memtime();
+  const unsigned long long r1 = __builtin_amdgcn_s_memrealtime();
+  float s = 0.f;
+#pragma unroll
+  for (int i = 0; i < 8; ++i)
+#pragma unroll
+    for (int j = 0; j < 2; ++j)
+#pragma unroll
+      for (int v = 0; v < 16; ++v) s += acc[i][j][v];
+  sink[gt] = s;   // keeps the MFMAs live
+  if (threadIdx.x == 0) {
+    clk[4 * blockIdx.x + 0] = t0;
+    clk[4 * blockIdx.x + 1] = t1;
+    clk[4 * blockIdx.x + 2] = r0;
+    clk[4 * blockIdx.x + 3] = r1;
+  }
+}
+
+}  // namespace
+
+hipError_t probe_mfma(int mode, int iters, float* tflops, float* ghz) {
+  const int64_t n = (int64_t)kProbeWgs * kProbeThreads * kProbeVecs * 8;   // halves
+  _Float16* src = nullptr;
+  float* sink = nullptr;
+  unsigned long long* clk = nullptr;
+  hipEvent_t e0 = nullptr, e1 = nullptr;
+  hipError_t e = hipMalloc(&src, n * sizeof(_Float16));
+  if (e == hipSuccess) e = hipMalloc(&sink, (size_t)kProbeWgs * kProbeThreads * sizeof(float));
+  if (e == hipSuccess) e = hipMalloc(&clk, (size_t)kProbeWgs * 4 * sizeof(unsigned long long));
+  if (e == hipSuccess) e = hipEventCreate(&e0);
+  if (e == hipSuccess) e = hipEventCreate(&e1);
+  if (e == hipSuccess) {
+    hipLaunchKernelGGL(k_probe_fill, dim3((unsigned)((n + 255) / 256)), dim3(256), 0, nullptr, src, n,
+                       mode);
+    const half8* s8 = reinterpret_cast<const half8*>(src);
+    // warm-up launch, then the timed one
+    hipLaunchKernelGGL(k_probe_mfma, dim3(kProbeWgs), dim3(kProbeThreads), 0, nullptr, s8, sink, clk,
+                       iters / 8 + 1);
+    e = hipEventRecord(e0, nullptr);
+    hipLaunchKernelGGL(k_probe_mfma, dim3(kProbeWgs), dim3(kProbeThreads), 0, nullptr, s8, sink, clk,
+                       iters);
+    if (e == hipSuccess) e = hipGetLastError();
+    if (e == hipSuccess) e = hipEventRecord(e1, nullptr);
+    if (e == hipSuccess) e = hipEventSynchronize(e1);
+  }
+  if (e == hipSuccess) {
+    float ms = 0.f;
+    e = hipEventElapsedTime(&ms, e0, e1);
+    unsigned long long c[kProbeWgs * 4];
+    if (e == hipSuccess) e = hipMemcpy(c, clk, sizeof(c), hipMemcpyDeviceToHost);
+    if (e == hipSuccess) {
+      double f = 0.0;
+      for (int b = 0; b < kProbeWgs; ++b)
+        f += (double)(c[4 * b + 1] - c[4 * b]) / (double)(c[4 * b + 3] - c[4 * b + 2]) * 0.1;
+      *ghz = (float)(f / kProbeWgs);
+      const double flops = 2.0 * 32 * 32 * 16 * 16 * (double)iters * 4 * kProbeWgs;
+      *tflops = (float)(flops / (ms * 1e-3) / 1e12);
+    }
+  }
+  if (e0) (void)hipEventDestroy(e0);
+  if (e1) (void)hipEventDestroy(e1);
+  if (src) (void)hipFree(src);
+  if (sink) (void)hipFree(sink);
+  if (clk) (void)hipFree(clk);
+  return e;
+}
+
+}  // namespace nvfp4

@@ -159,3 +159,14 @@ def test_gemm_bf16_validation(lib):
     assert g(ctypes.byref(ok), ctypes.byref(ok), FAKE, 16, MIS, None) == nv.NVFP4_ERR_ALIGN
     assert g(ctypes.byref(ok), ctypes.byref(ok), FAKE, 8, None, None) == nv.NVFP4_ERR_SHAPE
     assert g(ctypes.byref(ok), ctypes.byref(_op(k=48)), FAKE, 16, None, None) == nv.NVFP4_ERR_SHAPE
+
+
+def test_probe_mfma_validation(lib):
+    """The measurement probe refuses bad arguments before touching the device."""
+    f = ctypes.c_float()
+    p = lib.nvfp4_probe_mfma
+    assert p(1, 100, None, ctypes.byref(f)) == nv.NVFP4_ERR_NULL
+    assert p(1, 100, ctypes.byref(f), None) == nv.NVFP4_ERR_NULL
+    assert p(3, 100, ctypes.byref(f), ctypes.byref(f)) == nv.NVFP4_ERR_ARG
+    assert p(-1, 100, ctypes.byref(f), ctypes.byref(f)) == nv.NVFP4_ERR_ARG
+    assert p(1, 0, ctypes.byref(f), ctypes.byref(f)) == nv.NVFP4_ERR_ARG
