@@ -5,12 +5,12 @@ all their quantizations) at the 12B hybrid's FFN down-projection shape,
 
 A step is the whole hot path over one batch of seeded synthetic inputs that
 are resident in HBM before timing starts:
-  Q(X)   rowwise 1D RTN          (amax + encode)
+  Q(X)   rowwise 1D RTN          (amax and RHT amax of X in one read + encode)
   Q(W)   2D 16x16 RTN + transposed codes and scales (amax + encode)
   Fprop  Y  = Q(X) Q(W)^T        M=8192  N=5120  K=20480
-  Q(dY)  rowwise 1D SR           (amax + encode)
+  Q(dY)  rowwise 1D SR           (amax and RHT amax of dY in one read + encode)
   Dgrad  dX = Q(dY) Q(W)         M=8192  N=20480 K=5120
-  Q(RHT(dY)^T) SR, Q(RHT(X)^T) RTN (RHT amax + transpose-encode each)
+  Q(RHT(dY)^T) SR, Q(RHT(X)^T) RTN (transpose-encode each)
   Wgrad  dW = dY^T X             M=5120  N=20480 K=8192
 Outputs are preallocated; nothing is allocated inside the timed region.
 
@@ -90,10 +90,12 @@ class Step:
         C, G = nv.NVFP4_AMAX_COMPUTE, nv.NVFP4_AMAX_GIVEN
         q = self
         n_x, n_w, n_dy = x.numel(), w.numel(), dy.numel()
-        # (name, kind, algorithmic bytes or flops, callable); amax passes are
-        # separate launches so each kernel is timed on its own.
+        # (name, kind, algorithmic bytes or flops, callable); each launch is
+        # timed on its own.  X and dY are quantized both plainly and under the
+        # RHT, so one read gives both of their amaxes.
         self.ops = [
-            ("amax X", "hbm", 2 * n_x, lambda: nv.nvfp4_amax(x, q.qx.amax)),
+            ("amax X + RHT X", "hbm", 2 * n_x,
+             lambda: nv.nvfp4_amax_both(x, RHT_SEED, q.qx.amax, q.qx_t.amax)),
             ("quant X rowwise RTN", "hbm", 2.5625 * n_x,
              lambda: nv.nvfp4_quantize1d_rtn(x, 0, q.qx.amax, G, q.qx.codes, q.qx.scales,
                                              q.qx.tensor_scale)),
@@ -102,16 +104,15 @@ class Step:
              lambda: nv.nvfp4_quantize2d_rtn(w, q.qw.amax, G, q.qw.codes, q.qw.codes_t,
                                              q.qw.scales, q.qw.scales_t, q.qw.tensor_scale)),
             ("gemm Fprop", "mfma", 2.0 * T * H * F, lambda: nv.gemm(q.qx, q.qw, q.y)),
-            ("amax dY", "hbm", 2 * n_dy, lambda: nv.nvfp4_amax(dy, q.qdy.amax)),
+            ("amax dY + RHT dY", "hbm", 2 * n_dy,
+             lambda: nv.nvfp4_amax_both(dy, RHT_SEED, q.qdy.amax, q.qdy_t.amax)),
             ("quant dY rowwise SR", "hbm", 2.5625 * n_dy,
              lambda: nv.nvfp4_quantize1d_sr(dy, 0, q.qdy.amax, G, SR_SEED, 0, q.qdy.codes,
                                             q.qdy.scales, q.qdy.tensor_scale)),
             ("gemm Dgrad", "mfma", 2.0 * T * F * H, lambda: nv.gemm(q.qdy, q.qw.t(), q.dx)),
-            ("amax RHT dY", "hbm", 2 * n_dy, lambda: nv.nvfp4_amax_rht(dy, RHT_SEED, q.qdy_t.amax)),
             ("quant dY^T RHT SR", "hbm", 2.5625 * n_dy,
              lambda: nv.nvfp4_rht_quantize(dy, RHT_SEED, 1, SR_SEED, 1, q.qdy_t.amax, G,
                                            q.qdy_t.codes, q.qdy_t.scales, q.qdy_t.tensor_scale)),
-            ("amax RHT X", "hbm", 2 * n_x, lambda: nv.nvfp4_amax_rht(x, RHT_SEED, q.qx_t.amax)),
             ("quant X^T RHT RTN", "hbm", 2.5625 * n_x,
              lambda: nv.nvfp4_rht_quantize(x, RHT_SEED, 0, 0, 0, q.qx_t.amax, G, q.qx_t.codes,
                                            q.qx_t.scales, q.qx_t.tensor_scale)),

@@ -33,7 +33,7 @@ EXPORTED = ("nvfp4_amax", "nvfp4_amax_rht", "nvfp4_quantize1d_rtn", "nvfp4_quant
             "nvfp4_quantize2d_rtn", "nvfp4_quantize2d_sr", "nvfp4_rht_quantize",
             "nvfp4_dequantize", "nvfp4_gemm", "nvfp4_status_string", "nvfp4_last_error",
             "nvfp4_gemm_bf16", "mxfp4_quantize", "mxfp4_dequantize", "mxfp4_gemm",
-            "nvfp4_probe_mfma")
+            "nvfp4_probe_mfma", "nvfp4_amax_both")
 
 
 class NVFP4Error(RuntimeError):
@@ -75,6 +75,7 @@ def load_library(path: str = LIB_PATH) -> ctypes.CDLL:
     sigs = {
         "nvfp4_amax": [vp, i64, i64, vp, vp],
         "nvfp4_amax_rht": [vp, i64, i64, u64, vp, vp],
+        "nvfp4_amax_both": [vp, i64, i64, u64, vp, vp, vp],
         "nvfp4_quantize1d_rtn": [vp, i64, i64, i32, vp, i32, vp, vp, vp, vp],
         "nvfp4_quantize1d_sr": [vp, i64, i64, i32, vp, i32, u64, u32, vp, vp, vp, vp],
         "nvfp4_quantize2d_rtn": [vp, i64, i64, vp, i32, vp, vp, vp, vp, vp, vp],
@@ -125,6 +126,12 @@ def _dev_bf16(x: torch.Tensor, name: str):
 def nvfp4_amax(x, amax_out, stream=None):
     _dev_bf16(x, "x")
     _check(load_library().nvfp4_amax(_p(x), x.shape[0], x.shape[1], _p(amax_out), _stream(stream)))
+
+
+def nvfp4_amax_both(x, rht_seed, amax_out, amax_rht_out, stream=None):
+    _dev_bf16(x, "x")
+    _check(load_library().nvfp4_amax_both(_p(x), x.shape[0], x.shape[1], rht_seed, _p(amax_out),
+                                          _p(amax_rht_out), _stream(stream)))
 
 
 def nvfp4_amax_rht(x, rht_seed, amax_out, stream=None):
@@ -245,6 +252,13 @@ def amax_rht(x: torch.Tensor, rht_seed: int) -> torch.Tensor:
     out = torch.empty(1, dtype=torch.float32, device=x.device)
     nvfp4_amax_rht(x, rht_seed, out)
     return out
+
+
+def amax_both(x: torch.Tensor, rht_seed: int):
+    """(max |x|, max |RHT(x^T)|) from one read of x, as two 1-element tensors."""
+    out = torch.empty(2, dtype=torch.float32, device=x.device)
+    nvfp4_amax_both(x, rht_seed, out[0:1], out[1:2])
+    return out[0:1], out[1:2]
 
 
 def quantize_1d(x: torch.Tensor, axis: int = NVFP4_ROWWISE, sr_seed: Optional[int] = None,

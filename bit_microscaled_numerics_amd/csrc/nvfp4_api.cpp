@@ -142,6 +142,19 @@ int nvfp4_amax_rht(const void* x, int64_t rows, int64_t cols, uint64_t rht_seed,
   return launched(nvfp4::launch_amax_rht(x, rows, cols, rht_seed, amax_out, as_stream(stream)));
 }
 
+int nvfp4_amax_both(const void* x, int64_t rows, int64_t cols, uint64_t rht_seed, float* amax_out,
+                    float* amax_rht_out, void* stream) {
+  int st = check_tensor(x, rows, cols, "x");
+  if (st) return st;
+  if (amax_out == nullptr || amax_rht_out == nullptr)
+    return fail(NVFP4_ERR_NULL, "amax_out / amax_rht_out is NULL");
+  if (!aligned(amax_out, 4) || !aligned(amax_rht_out, 4))
+    return fail(NVFP4_ERR_ALIGN, "amax_out / amax_rht_out must be 4-byte aligned");
+  if (amax_out == amax_rht_out) return fail(NVFP4_ERR_ARG, "amax_out and amax_rht_out alias");
+  return launched(nvfp4::launch_amax_rht(x, rows, cols, rht_seed, amax_rht_out, as_stream(stream),
+                                         amax_out));
+}
+
 static int quantize1d(const void* x, int64_t rows, int64_t cols, int axis, float* amax_io,
                       int amax_mode, bool sr, uint64_t seed, uint32_t stream_id, uint8_t* codes,
                       uint8_t* scales, float* ts_out, void* stream) {

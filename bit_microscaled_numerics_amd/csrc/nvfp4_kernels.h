@@ -10,8 +10,9 @@ namespace nvfp4 {
 int num_cus();  // compute units of the current device (cached per device)
 
 hipError_t launch_amax(const void* x, int64_t n_elems, float* out, hipStream_t s);
+// out_plain (nullable): also max |x| from the same read
 hipError_t launch_amax_rht(const void* x, int64_t rows, int64_t cols, uint64_t rht_seed,
-                           float* out, hipStream_t s);
+                           float* out, hipStream_t s, float* out_plain = nullptr);
 hipError_t launch_quant_row(const void* x, int64_t rows, int64_t cols, const float* amax,
                             bool sr, uint64_t seed, uint32_t stream_id, uint8_t* codes,
                             uint8_t* scales, float* ts_out, hipStream_t s);

@@ -106,13 +106,17 @@ __device__ __forceinline__ void tile_column(const Tile16x8& t, int c, float (&v)
 }
 
 // amax of RHT(x^T): each work item is 16 consecutive rows x 8 columns.
+// PLAIN: also max |x| over the same elements (before the transform) into
+// *out_plain, so one read of the tensor gives both statistics.
+template <bool PLAIN>
 __global__ __launch_bounds__(kThreads) void k_amax_rht(const uint16_t* __restrict__ x,
                                                          int64_t rows, int64_t cols,
                                                          uint64_t rht_seed,
-                                                         uint32_t* __restrict__ out) {
+                                                         uint32_t* __restrict__ out,
+                                                         uint32_t* __restrict__ out_plain) {
   const uint32_t signs = rht_sign_bits(rht_seed);
   const int64_t cg_n = cols / 8, items = (rows / 16) * cg_n;
-  float m = 0.0f;
+  float m = 0.0f, p = 0.0f;
   for (int64_t it = (int64_t)blockIdx.x * kThreads + threadIdx.x; it < items;
        it += (int64_t)gridDim.x * kThreads) {
     const int64_t rg = it / cg_n, cg = it - rg * cg_n;
@@ -122,12 +126,20 @@ __global__ __launch_bounds__(kThreads) void k_amax_rht(const uint16_t* __restric
     for (int c = 0; c < 8; ++c) {
       float v[16];
       tile_column(t, c, v);
+      if (PLAIN) {
+#pragma unroll
+        for (int j = 0; j < 16; ++j) p = fmaxf(p, __builtin_fabsf(v[j]));
+      }
       rht16(v, signs);
 #pragma unroll
       for (int j = 0; j < 16; ++j) m = fmaxf(m, __builtin_fabsf(v[j]));
     }
   }
   block_max_atomic(__float_as_uint(m), out);
+  if (PLAIN) {
+    __syncthreads();   // the reduction slots are reused
+    block_max_atomic(__float_as_uint(p), out_plain);
+  }
 }
 
 // ---------------------------------------------------------------------------
@@ -357,12 +369,19 @@ hipError_t launch_amax(const void* x, int64_t n_elems, float* out, hipStream_t s
 }
 
 hipError_t launch_amax_rht(const void* x, int64_t rows, int64_t cols, uint64_t rht_seed,
-                           float* out, hipStream_t s) {
+                           float* out, hipStream_t s, float* out_plain) {
   uint32_t* o = reinterpret_cast<uint32_t*>(out);
+  uint32_t* op = reinterpret_cast<uint32_t*>(out_plain);
   hipLaunchKernelGGL(k_zero_u32, dim3(1), dim3(1), 0, s, o);
+  if (op != nullptr) hipLaunchKernelGGL(k_zero_u32, dim3(1), dim3(1), 0, s, op);
   const int64_t items = (rows / 16) * (cols / 8);
-  hipLaunchKernelGGL(k_amax_rht, dim3(grid_for(items, 8)), dim3(kThreads), 0, s,
-                     reinterpret_cast<const uint16_t*>(x), rows, cols, rht_seed, o);
+  const uint16_t* xh = reinterpret_cast<const uint16_t*>(x);
+  if (op != nullptr)
+    hipLaunchKernelGGL(k_amax_rht<true>, dim3(grid_for(items, 8)), dim3(kThreads), 0, s, xh, rows,
+                       cols, rht_seed, o, op);
+  else
+    hipLaunchKernelGGL(k_amax_rht<false>, dim3(grid_for(items, 8)), dim3(kThreads), 0, s, xh, rows,
+                       cols, rht_seed, o, nullptr);
   return hipGetLastError();
 }
 

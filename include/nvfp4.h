@@ -83,6 +83,17 @@ int nvfp4_amax(const void* x_bf16, int64_t rows, int64_t cols, float* amax_out, 
 int nvfp4_amax_rht(const void* x_bf16, int64_t rows, int64_t cols, uint64_t rht_seed,
                    float* amax_out, void* stream);
 
+/* Both statistics of one tensor from a single read: *amax_out = max |x| (as
+ * nvfp4_amax) and *amax_rht_out = max |RHT(x^T)| (as nvfp4_amax_rht, same
+ * seed).  A tensor quantized both plainly and under the transform -- X and dY
+ * in the linear-layer recipe, where Fprop / Dgrad take them rowwise and Wgrad
+ * takes their RHT transposes ("Pretraining Large Language Models with
+ * NVFP4", summary page, recipe paragraph) -- needs both, and each is a full
+ * scan of the tensor.  Same shape rules as nvfp4_amax_rht; the two outputs
+ * must not alias. */
+int nvfp4_amax_both(const void* x_bf16, int64_t rows, int64_t cols, uint64_t rht_seed,
+                    float* amax_out, float* amax_rht_out, void* stream);
+
 /* 1D quantization (activations, gradients), round-to-nearest-even.
  * axis NVFP4_ROWWISE: operand = x,   I = rows, K = cols.
  * axis NVFP4_COLWISE: operand = x^T, I = cols, K = rows (Wgrad layout).

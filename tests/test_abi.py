@@ -170,3 +170,11 @@ def test_probe_mfma_validation(lib):
     assert p(3, 100, ctypes.byref(f), ctypes.byref(f)) == nv.NVFP4_ERR_ARG
     assert p(-1, 100, ctypes.byref(f), ctypes.byref(f)) == nv.NVFP4_ERR_ARG
     assert p(1, 0, ctypes.byref(f), ctypes.byref(f)) == nv.NVFP4_ERR_ARG
+
+
+def test_amax_both_validation(lib):
+    f = lib.nvfp4_amax_both
+    assert f(FAKE, 32, 16, 1, None, FAKE, None) == nv.NVFP4_ERR_NULL
+    assert f(FAKE, 32, 16, 1, FAKE, None, None) == nv.NVFP4_ERR_NULL
+    assert f(FAKE, 32, 16, 1, FAKE, FAKE, None) == nv.NVFP4_ERR_ARG
+    assert f(FAKE, 32, 16, 1, MIS, FAKE + 16, None) == nv.NVFP4_ERR_ALIGN

@@ -62,6 +62,11 @@ def test_amax(shape, kind):
     got = nv.amax_rht(x.cuda(), 1234)
     torch.cuda.synchronize()
     assert float(got.cpu()[0]) == oracle.amax_rht(x, 1234)
+    say("amax_both", shape, kind)
+    plain, rht = nv.amax_both(x.cuda(), 1234)
+    torch.cuda.synchronize()
+    assert float(plain.cpu()[0]) == oracle.amax(x)
+    assert float(rht.cpu()[0]) == oracle.amax_rht(x, 1234)
 
 
 @pytest.mark.parametrize("shape", SHAPES)
