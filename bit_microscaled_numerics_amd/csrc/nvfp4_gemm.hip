@@ -401,7 +401,7 @@ __global__ __launch_bounds__(kThreads, 1) void k_gemm(GemmArgs g) {
 // ---------------------------------------------------------------------------
 // Fast path: raw operands moved global -> LDS by the load unit
 // ---------------------------------------------------------------------------
-// Used when both operands have K-contiguous, 4-byte aligned scale rows
+// Used when both operands have K-contiguous, 16-byte aligned scale rows
 // (dword scales), rows a multiple of 16 bytes and K / 64 steps a multiple of
 // 4 (of 8 when the last round of tiles is split).  Same tile (256 x 256) and
 // decode as above, different division of work:
@@ -416,22 +416,25 @@ __global__ __launch_bounds__(kThreads, 1) void k_gemm(GemmArgs g) {
 //    16-wide sub-step.  The same permutation on A and B leaves the sum
 //    unchanged, and a lane's B operand for a step is one 16-byte chunk of
 //    codes and one scale dword.
-//  - Raw codes and scales reach LDS through buffer loads that write LDS
-//    directly, two K steps (64 bytes of a row) at a time, so one load
-//    instruction covers 16 rows x 64 B instead of 32 rows x 32 B: half the
-//    cache lines per byte.  Each wave loads exactly the A rows it decodes and
-//    the B rows it multiplies, so the raw data is wave-private: no barrier,
-//    only the wave's own load counter.  Two slots per operand; a slot is
-//    refilled two steps before it is read, with no register cost.
+//  - Raw codes reach LDS through buffer loads that write LDS directly, two K
+//    steps (64 bytes of a row) at a time, so one load instruction covers 16
+//    rows x 64 B instead of 32 rows x 32 B: half the cache lines per byte.
+//    Scales come four steps (16 bytes of a row) per load, one row per lane,
+//    and each thread keeps its rows' 4-step group in registers.  Each wave
+//    loads exactly the A rows it decodes and the B rows it multiplies, so the
+//    raw data is wave-private: no barrier, only the wave's own load counter.
+//    Two code slots per operand, refilled two steps before they are read;
+//    one scale slot per operand, refilled right after the wave has read it
+//    into registers, four steps before it is needed.
 constexpr int kThreads4 = 256;
 constexpr int kMB = 8, kNB = 2;              // 32 x 32 blocks per wave
 constexpr int kStage4 = kTile * kRowBytes;   // 32 KiB of decoded A per stage
 constexpr int kRawRow = 64;                  // bytes of a row per 2-step group
 constexpr int kRawBytes = kTile * kRawRow;   // 16 KiB per operand and slot
-constexpr int kScRow = 8;                    // scale bytes of a row per group
-constexpr int kScBytes = kTile * kScRow;     // 2 KiB
-// s_waitcnt immediate: vmcnt <= 12, expcnt and lgkmcnt not waited on
-constexpr int kVmcnt12 = 12 | (7 << 4) | (15 << 8);
+constexpr int kScRow = 16;                   // scale bytes of a row per 4-step group
+constexpr int kScBytes = kTile * kScRow;     // 4 KiB
+// s_waitcnt immediate: vmcnt <= n, expcnt and lgkmcnt not waited on
+constexpr int vmcnt_imm(int n) { return (n & 15) | ((n >> 4) << 14) | (7 << 4) | (15 << 8); }
 
 typedef __attribute__((address_space(3))) void* lds_ptr_t;
 
@@ -459,14 +462,14 @@ __device__ __forceinline__ uint32_t raw_off(int r, int c) {
 struct DmaOp {
   __amdgpu_buffer_rsrc_t codes, scales;
   uint32_t voff_c[4];   // this wave's 16-row code loads
-  uint32_t voff_s[2];   // this wave's 32-row scale loads
+  uint32_t voff_s;      // this wave's 64-row scale load
 };
 
 // Code load q covers rows crow[q] .. +15 (lane l: row + l / 4, position
-// l % 4); scale load q covers rows srow[q] .. +31 (lane l: row + l / 2, the
-// dword of group step l % 2).
+// l % 4); the scale load covers 64 rows, lane l row srow(l) (16 bytes: the
+// scale dwords of 4 steps), written to scale slot row 64 w + l.
 __device__ __forceinline__ DmaOp make_dma(const GemmOperand& op, int64_t row0, const int (&crow)[4],
-                                          const int (&srow)[2]) {
+                                          int srow_l) {
   DmaOp v;
   const int64_t rem_rows = op.rows - row0;
   const int64_t code_bytes = rem_rows * op.ld;
@@ -484,32 +487,28 @@ __device__ __forceinline__ DmaOp make_dma(const GemmOperand& op, int64_t row0, c
     const int r = crow[q] + (lane >> 2);
     v.voff_c[q] = (uint32_t)(r * op.ld + 16 * ((lane & 3) ^ raw_g(r)));
   }
-#pragma unroll
-  for (int q = 0; q < 2; ++q) {
-    const int r = srow[q] + (lane >> 1);
-    v.voff_s[q] = (uint32_t)((r / op.blk_rows) * op.ss_row + 4 * (lane & 1));
-  }
+  v.voff_s = (uint32_t)((srow_l / op.blk_rows) * op.ss_row);
   return v;
 }
 
-// Steps x0, x0 + 1 of this wave's rows into a slot (6 load instructions).
-// Scale dwords of steps past the last read 0 (offset 2^31, past
-// num_records), so their blocks decode to zero whatever the codes; the code
-// offset is clamped to the last step.
-__device__ __forceinline__ void dma_group(const DmaOp& v, uint8_t* raw, uint8_t* sc,
-                                          const int (&crow)[4], const int (&srow)[2], int x0,
+// Steps x0, x0 + 1 of this wave's rows' codes into a slot (4 load
+// instructions); the code offset is clamped to the last step.
+__device__ __forceinline__ void dma_codes(const DmaOp& v, uint8_t* raw, const int (&crow)[4], int x0,
                                           int last) {
-  const int lane = threadIdx.x & 63;
   const uint32_t kb = (uint32_t)((x0 < last ? x0 : last) * 32);
 #pragma unroll
   for (int q = 0; q < 4; ++q)
     __builtin_amdgcn_raw_ptr_buffer_load_lds(v.codes, (lds_ptr_t)(raw + crow[q] * kRawRow), 16,
                                              v.voff_c[q], kb, 0, 0);
-  const uint32_t dead = (x0 + (lane & 1) > last) ? 0x80000000u : 0u;
-#pragma unroll
-  for (int q = 0; q < 2; ++q)
-    __builtin_amdgcn_raw_ptr_buffer_load_lds(v.scales, (lds_ptr_t)(sc + srow[q] * kScRow), 4,
-                                             v.voff_s[q] + dead, (uint32_t)(4 * x0), 0, 0);
+}
+
+// Scale dwords of steps x0 .. x0 + 3 of this wave's 64 rows into the scale
+// slot (one 16-byte load per lane).  Groups past the last step read 0
+// (offset 2^31, past num_records): their blocks decode to zero.
+__device__ __forceinline__ void dma_scales(const DmaOp& v, uint8_t* sc, int wave, int x0, int last) {
+  const uint32_t dead = x0 > last ? 0x80000000u : 0u;
+  __builtin_amdgcn_raw_ptr_buffer_load_lds(v.scales, (lds_ptr_t)(sc + 64 * wave * kScRow), 16,
+                                           v.voff_s + dead, (uint32_t)(4 * x0), 0, 0);
 }
 
 // A thread's raw share of one step, read back from a slot: two rows' 16-byte
@@ -519,12 +518,20 @@ struct RawRegs {
   uint32_t sc[2];
 };
 
-__device__ __forceinline__ void read_raw(RawRegs& r, const uint8_t* raw, const uint8_t* sc,
-                                         int row0, int row1, int kh, int u) {
+// codes of group step u; scale dwords of 4-step group step u4 from the
+// registers that hold the group (read from the scale slot once per group)
+__device__ __forceinline__ void read_raw(RawRegs& r, const uint8_t* raw, const v4u (&sg)[2],
+                                         int row0, int row1, int kh, int u, int u4) {
   r.codes[0] = *reinterpret_cast<const v4u*>(raw + raw_off(row0, 2 * u + kh));
   r.codes[1] = *reinterpret_cast<const v4u*>(raw + raw_off(row1, 2 * u + kh));
-  r.sc[0] = *reinterpret_cast<const uint32_t*>(sc + row0 * kScRow + 4 * u);
-  r.sc[1] = *reinterpret_cast<const uint32_t*>(sc + row1 * kScRow + 4 * u);
+  r.sc[0] = sg[0][u4];
+  r.sc[1] = sg[1][u4];
+}
+
+// The 4-step scale group of two slot rows into registers.
+__device__ __forceinline__ void read_sg(v4u (&sg)[2], const uint8_t* sc, int idx0) {
+  sg[0] = *reinterpret_cast<const v4u*>(sc + idx0 * kScRow);
+  sg[1] = *reinterpret_cast<const v4u*>(sc + (idx0 + 32) * kScRow);
 }
 
 // Decode word p of A row (t / 2) + 128 q into a stage (chunk 4 (t % 2) + p).
@@ -575,11 +582,10 @@ __device__ __forceinline__ void interleave16() {
 template <bool BF16>
 __global__ __launch_bounds__(kThreads4, 1) void k_gemm_dma(GemmArgs g) {
   extern __shared__ __attribute__((aligned(16))) uint8_t smem[];   // decoded A, 2 stages
-  // raw slots as separate arrays (one LDS object per slot)
+  // raw code slots and scale slots as separate arrays (one LDS object each)
   __shared__ __attribute__((aligned(16))) uint8_t rawA0[kRawBytes], rawA1[kRawBytes];
   __shared__ __attribute__((aligned(16))) uint8_t rawB0[kRawBytes], rawB1[kRawBytes];
-  __shared__ __attribute__((aligned(16))) uint8_t scA0[kScBytes], scA1[kScBytes];
-  __shared__ __attribute__((aligned(16))) uint8_t scB0[kScBytes], scB1[kScBytes];
+  __shared__ __attribute__((aligned(16))) uint8_t scA[kScBytes], scB[kScBytes];
 
   const int t = threadIdx.x, lane = t & 63;
   // wave and tile indices in scalar registers: the buffer descriptors and LDS
@@ -595,14 +601,17 @@ __global__ __launch_bounds__(kThreads4, 1) void k_gemm_dma(GemmArgs g) {
   part = __builtin_amdgcn_readfirstlane(part);
 
   const int a_crow[4] = {32 * wave, 32 * wave + 16, 128 + 32 * wave, 128 + 32 * wave + 16};
-  const int a_srow[2] = {32 * wave, 128 + 32 * wave};
   const int b_crow[4] = {64 * wave, 64 * wave + 16, 64 * wave + 32, 64 * wave + 48};
-  const int b_srow[2] = {64 * wave, 64 * wave + 32};
+  // scale slot row 64 w + l holds A row 32 w + l (l < 32) or 128 + 32 w + l - 32,
+  // and B row 64 w + l
+  const int a_srow = lane < 32 ? 32 * wave + lane : 128 + 32 * wave + lane - 32;
   const DmaOp va = make_dma(g.a, tm * kTile, a_crow, a_srow);
-  const DmaOp vb = make_dma(g.b, tn * kTile, b_crow, b_srow);
-  // A rows this thread decodes; B rows whose fragments this lane holds
+  const DmaOp vb = make_dma(g.b, tn * kTile, b_crow, 64 * wave + lane);
+  // A rows this thread decodes; B rows whose fragments this lane holds; and
+  // their scale slot rows (the second row's is 32 further)
   const int ar0 = t >> 1, ar1 = 128 + (t >> 1), ah = t & 1;
   const int br0 = 64 * wave + lrow, br1 = br0 + 32;
+  const int a_sidx = 64 * wave + (lane >> 1), b_sidx = br0;
   // bit positions of the step's two block scales in a scale dword
   const uint32_t apos0 = 16u * ah, apos1 = apos0 + 8u;
   const uint32_t bpos0 = 16u * lk, bpos1 = bpos0 + 8u;
@@ -618,21 +627,30 @@ __global__ __launch_bounds__(kThreads4, 1) void k_gemm_dma(GemmArgs g) {
   const int s1 = part == 0 ? half_steps : steps;
   const int last = s1 - 1;
 
-  // groups 0 and 1 (steps s0 .. s0 + 3) of A and B
-  dma_group(va, rawA0, scA0, a_crow, a_srow, s0, last);
-  dma_group(vb, rawB0, scB0, b_crow, b_srow, s0, last);
-  dma_group(va, rawA1, scA1, a_crow, a_srow, s0 + 2, last);
-  dma_group(vb, rawB1, scB1, b_crow, b_srow, s0 + 2, last);
-  __builtin_amdgcn_s_waitcnt(kVmcnt12);   // group 0 of A and B has landed
+  // scale group 0 (steps s0 .. s0 + 3), code groups 0 and 1 (steps s0 .. s0 + 3)
+  dma_scales(va, scA, wave, s0, last);
+  dma_scales(vb, scB, wave, s0, last);
+  dma_codes(va, rawA0, a_crow, s0, last);
+  dma_codes(vb, rawB0, b_crow, s0, last);
+  dma_codes(va, rawA1, a_crow, s0 + 2, last);
+  dma_codes(vb, rawB1, b_crow, s0 + 2, last);
+  __builtin_amdgcn_s_waitcnt(vmcnt_imm(8));   // scale group 0 and code group 0 landed
   __builtin_amdgcn_sched_barrier(0);
+  v4u sa[2], sb[2];   // scale dwords of the current 4-step groups
+  read_sg(sa, scA, a_sidx);
+  read_sg(sb, scB, b_sidx);
+  __builtin_amdgcn_s_waitcnt(0xC07F);   // lgkmcnt(0): the slots are read before reloading them
+  __builtin_amdgcn_sched_barrier(0);
+  dma_scales(va, scA, wave, s0 + 4, last);
+  dma_scales(vb, scB, wave, s0 + 4, last);
   RawRegs ra, rb;
-  read_raw(ra, rawA0, scA0, ar0, ar1, ah, 0);
+  read_raw(ra, rawA0, sa, ar0, ar1, ah, 0, 0);
 #pragma unroll
   for (int q = 0; q < 2; ++q)
 #pragma unroll
     for (int p = 0; p < 4; ++p) store_a(smem, ra, q, p, apos0, apos1);
-  read_raw(ra, rawA0, scA0, ar0, ar1, ah, 1);
-  read_raw(rb, rawB0, scB0, br0, br1, lk, 0);
+  read_raw(ra, rawA0, sa, ar0, ar1, ah, 1, 1);
+  read_raw(rb, rawB0, sb, br0, br1, lk, 0, 0);
   OpsB bcur, bnxt;
   dec_b(bcur, rb, 0, bpos0, bpos1);
   __syncthreads();
@@ -641,20 +659,23 @@ __global__ __launch_bounds__(kThreads4, 1) void k_gemm_dma(GemmArgs g) {
 
   // Step x (h = (x - s0) % 4) multiplies decoded A stage h % 2 with B(x)
   // (decoded one sub-step ahead from rb) while decoding A(x+1) (ra) into
-  // the other stage.  Raw group slot of steps x, x+1 (x even): h / 2.  At
-  // the last sub-step: barrier (A(x+1) is complete), then an even step
-  // refills its A slot with the group of steps x+4, x+5 and an odd step its B
-  // slot with steps x+3, x+4 -- both slots were last read a step earlier;
-  // then ra / rb are reloaded with A(x+2) / B(x+1), whose group was loaded
-  // two steps ago.  The loads of the two groups issued since (12
-  // instructions) may still be in flight.
+  // the other stage.  Raw code slot of steps x, x+1 (x even): h / 2.  At the
+  // last sub-step: barrier (A(x+1) is complete), then an even step refills
+  // its A code slot with steps x+4, x+5 and an odd step its B slot with steps
+  // x+3, x+4 (both last read a step earlier), and ra / rb are reloaded with
+  // A(x+2) / B(x+1), whose codes were loaded two steps ago.  Scales: the
+  // registers sa / sb hold a 4-step group; at h = 2 (A) and h = 3 (B) they
+  // move on to the next group and its slot is refilled with the group after.
+  // Load order per trip: A codes, B codes, A codes + A scales, B codes + B
+  // scales; the counts below leave exactly the loads issued since the ones
+  // needed in flight.
   for (int it = s0; it < s1; it += 4) {
 #pragma unroll
     for (int h = 0; h < 4; ++h) {
       const int x = it + h;
       uint8_t* cur = smem + ((h & 1) ? kStage4 : 0);
       uint8_t* oth = smem + ((h & 1) ? 0 : kStage4);
-      const int a2 = ((h + 2) >> 1) & 1, b1 = ((h + 1) >> 1) & 1;   // slots of A(x+2), B(x+1)
+      const int a2 = ((h + 2) >> 1) & 1, b1 = ((h + 1) >> 1) & 1;   // code slots of A(x+2), B(x+1)
 #pragma unroll
       for (int s = 0; s < 4; ++s) {
         if (s < 3) {
@@ -681,18 +702,24 @@ __global__ __launch_bounds__(kThreads4, 1) void k_gemm_dma(GemmArgs g) {
           // memory fence, which would also wait for the raw loads in flight
           asm volatile("s_waitcnt lgkmcnt(0)\n\ts_barrier" ::: "memory");
           __builtin_amdgcn_sched_barrier(0);
-          if ((h & 1) == 0)
-            dma_group(va, (h >> 1) ? rawA1 : rawA0, (h >> 1) ? scA1 : scA0, a_crow, a_srow,
-                      x + 4, last);
-          else
-            dma_group(vb, (h >> 1) ? rawB1 : rawB0, (h >> 1) ? scB1 : scB0, b_crow, b_srow,
-                      x + 3, last);
-          __builtin_amdgcn_s_waitcnt(kVmcnt12);
+          if ((h & 1) == 0) dma_codes(va, (h >> 1) ? rawA1 : rawA0, a_crow, x + 4, last);
+          else dma_codes(vb, (h >> 1) ? rawB1 : rawB0, b_crow, x + 3, last);
+          if (h == 0) __builtin_amdgcn_s_waitcnt(vmcnt_imm(10));
+          else if (h == 2) __builtin_amdgcn_s_waitcnt(vmcnt_imm(8));
+          else __builtin_amdgcn_s_waitcnt(vmcnt_imm(9));
           __builtin_amdgcn_sched_barrier(0);
           read_a(anxt, oth, lrow, lk, 0);
-          read_raw(ra, a2 ? rawA1 : rawA0, a2 ? scA1 : scA0, ar0, ar1, ah, h & 1);
-          read_raw(rb, b1 ? rawB1 : rawB0, b1 ? scB1 : scB0, br0, br1, lk, (h + 1) & 1);
+          if (h == 2) read_sg(sa, scA, a_sidx);
+          if (h == 3) read_sg(sb, scB, b_sidx);
+          read_raw(ra, a2 ? rawA1 : rawA0, sa, ar0, ar1, ah, h & 1, (h + 2) & 3);
+          read_raw(rb, b1 ? rawB1 : rawB0, sb, br0, br1, lk, (h + 1) & 1, (h + 1) & 3);
           dec_b(bnxt, rb, 0, bpos0, bpos1);
+          if (h >= 2) {
+            __builtin_amdgcn_s_waitcnt(0xC07F);   // lgkmcnt(0): slot read before its reload
+            __builtin_amdgcn_sched_barrier(0);
+            if (h == 2) dma_scales(va, scA, wave, it + 8, last);
+            else dma_scales(vb, scB, wave, it + 8, last);
+          }
           mfma16(acc, acur, bcur);
           interleave16();
           acur = anxt;
@@ -773,10 +800,13 @@ static hipError_t launch_gemm_any(const GemmOperand& a, const GemmOperand& b, in
     return o.ss_k == 1 && o.ss_row % 4 == 0 && (reinterpret_cast<uintptr_t>(o.scales) & 3) == 0;
   };
   const bool sdw = !checked && ld16 && sdw_ok(a) && sdw_ok(b);
-  // fast path: whole 4-step trips in every K range a workgroup takes (codes
-  // are 16-byte aligned, checked by the API)
+  // fast path: whole 4-step trips in every K range a workgroup takes, scale
+  // rows 16-byte aligned (codes are 16-byte aligned, checked by the API)
   const int64_t steps = K / kBK;
-  const bool dma = sdw && steps % 4 == 0 && (!plan.split || steps % 8 == 0);
+  auto sc16 = [](const GemmOperand& o) {   // 4-step scale groups as 16-byte loads
+    return o.ss_row % 16 == 0 && (reinterpret_cast<uintptr_t>(o.scales) & 15) == 0;
+  };
+  const bool dma = sdw && steps % 4 == 0 && (!plan.split || steps % 8 == 0) && sc16(a) && sc16(b);
 #define NVFP4_GEMM_LAUNCH_B(C, L, W, B)                                                  \
   do {                                                                                    \
     hipError_t e = hipFuncSetAttribute(reinterpret_cast<const void*>(&k_gemm<C, L, W, B>), \

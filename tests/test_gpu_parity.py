@@ -255,6 +255,31 @@ def test_gemm_fast_path_and_fallback(mnk):
     assert_gemm_close(y.cpu().numpy(), c, t, f"fast/general {mnk}")
 
 
+def test_gemm_padded_scale_rows():
+    """Scale rows padded to a pitch that is a multiple of 4 but not of 16
+    bytes: the fast path needs 16-byte scale rows, so this K = 512 GEMM takes
+    the general kernel; both operands padded alike, result as the oracle's."""
+    import dataclasses
+    M, N, K = 272, 144, 512
+    g = torch.Generator().manual_seed(77)
+    x = inputs.normal(g, M, K, 1.0, 0.001, 50.0)
+    w = inputs.normal(g, N, K, 0.02)
+    say("gemm padded scale rows", (M, N, K))
+    qx, qw = nv.quantize_1d(x.cuda()), nv.quantize_2d(w.cuda())
+
+    def pad(q):
+        rows = q.scales.numel() // (K // 16)
+        p = torch.zeros(rows, K // 16 + 4, dtype=torch.uint8, device="cuda")
+        p[:, :K // 16] = q.scales.view(rows, K // 16)
+        return dataclasses.replace(q, scales=p, ss_row=K // 16 + 4, scales_t=None)
+
+    y = nv.gemm(pad(qx), pad(qw))
+    torch.cuda.synchronize()
+    ox, ow = oracle.quantize(x, oracle.ROWWISE), oracle.quantize(w, oracle.TWO_D)
+    c, t = oracle.gemm(ox, ow)
+    assert_gemm_close(y.cpu().numpy(), c, t, "padded scale rows")
+
+
 def test_gemm_ldc_and_zero_operand():
     g = torch.Generator().manual_seed(9)
     x = inputs.normal(g, 48, 64)
