@@ -33,7 +33,7 @@ EXPORTED = ("nvfp4_amax", "nvfp4_amax_rht", "nvfp4_quantize1d_rtn", "nvfp4_quant
             "nvfp4_quantize2d_rtn", "nvfp4_quantize2d_sr", "nvfp4_rht_quantize",
             "nvfp4_dequantize", "nvfp4_gemm", "nvfp4_status_string", "nvfp4_last_error",
             "nvfp4_gemm_bf16", "mxfp4_quantize", "mxfp4_dequantize", "mxfp4_gemm",
-            "nvfp4_probe_mfma", "nvfp4_amax_both")
+            "nvfp4_probe_mfma", "nvfp4_probe_scratch_bytes", "nvfp4_amax_both")
 
 
 class NVFP4Error(RuntimeError):
@@ -87,7 +87,7 @@ def load_library(path: str = LIB_PATH) -> ctypes.CDLL:
         "mxfp4_quantize": [vp, i64, i64, i32, u64, u32, vp, vp, vp],
         "mxfp4_dequantize": [ctypes.POINTER(c_mx_operand), vp, vp],
         "mxfp4_gemm": [ctypes.POINTER(c_mx_operand), ctypes.POINTER(c_mx_operand), vp, i64, vp],
-        "nvfp4_probe_mfma": [i32, i32, ctypes.POINTER(ctypes.c_float), ctypes.POINTER(ctypes.c_float)],
+        "nvfp4_probe_mfma": [i32, i32, vp, i64, vp],
     }
     for name, args in sigs.items():
         fn = getattr(lib, name)
@@ -97,6 +97,8 @@ def load_library(path: str = LIB_PATH) -> ctypes.CDLL:
     lib.nvfp4_status_string.restype = ctypes.c_char_p
     lib.nvfp4_last_error.argtypes = []
     lib.nvfp4_last_error.restype = ctypes.c_char_p
+    lib.nvfp4_probe_scratch_bytes.argtypes = []
+    lib.nvfp4_probe_scratch_bytes.restype = ctypes.c_int64
     _lib = lib
     return lib
 
@@ -399,7 +401,16 @@ PROBE_ZEROS, PROBE_NVFP4_LIKE, PROBE_UNIFORM = 0, 1, 2
 def probe_mfma(mode: int, iters: int = 8000):
     """(TFLOP/s, clock GHz) of the FP16 matrix cores running the GEMM's MFMA
     pattern from registers on operand data of kind ``mode`` (measurement
-    support: the ceiling the GEMM's roofline fraction is read against)."""
-    tf, ghz = ctypes.c_float(), ctypes.c_float()
-    _check(load_library().nvfp4_probe_mfma(mode, iters, ctypes.byref(tf), ctypes.byref(ghz)))
-    return tf.value, ghz.value
+    support: the ceiling the GEMM's roofline fraction is read against).
+    Synchronizes the device; the library call itself only enqueues."""
+    lib = load_library()
+    nbytes = int(lib.nvfp4_probe_scratch_bytes())
+    scratch = torch.empty(nbytes, dtype=torch.uint8, device="cuda")
+    _check(lib.nvfp4_probe_mfma(mode, iters, _p(scratch), nbytes, _stream(None)))
+    torch.cuda.synchronize()
+    wgs = 256
+    st = scratch[nbytes - wgs * 32:].view(torch.int64).cpu().view(wgs, 4).tolist()
+    ghz = sum((t1 - t0) / (r1 - r0) * 0.1 for t0, t1, r0, r1 in st) / wgs
+    secs = (max(r[3] for r in st) - min(r[2] for r in st)) * 1e-8
+    flops = 2.0 * 32 * 32 * 16 * 16 * iters * 4 * wgs
+    return flops / secs / 1e12, ghz

@@ -84,51 +84,26 @@ __global__ __launch_bounds__(kProbeThreads, 1) void k_probe_mfma(const half8* sr
 
 }  // namespace
 
-hipError_t probe_mfma(int mode, int iters, float* tflops, float* ghz) {
+// Scratch layout: operands (kProbeWgs * 256 threads * 10 half8), the sink
+// (one float per thread), then the stamps (4 x uint64 per workgroup).
+int64_t probe_scratch_bytes() {
+  return (int64_t)kProbeWgs * kProbeThreads * (kProbeVecs * 16 + 4) + (int64_t)kProbeWgs * 32;
+}
+
+hipError_t probe_mfma(int mode, int iters, void* scratch, hipStream_t s) {
+  uint8_t* base = static_cast<uint8_t*>(scratch);
   const int64_t n = (int64_t)kProbeWgs * kProbeThreads * kProbeVecs * 8;   // halves
-  _Float16* src = nullptr;
-  float* sink = nullptr;
-  unsigned long long* clk = nullptr;
-  hipEvent_t e0 = nullptr, e1 = nullptr;
-  hipError_t e = hipMalloc(&src, n * sizeof(_Float16));
-  if (e == hipSuccess) e = hipMalloc(&sink, (size_t)kProbeWgs * kProbeThreads * sizeof(float));
-  if (e == hipSuccess) e = hipMalloc(&clk, (size_t)kProbeWgs * 4 * sizeof(unsigned long long));
-  if (e == hipSuccess) e = hipEventCreate(&e0);
-  if (e == hipSuccess) e = hipEventCreate(&e1);
-  if (e == hipSuccess) {
-    hipLaunchKernelGGL(k_probe_fill, dim3((unsigned)((n + 255) / 256)), dim3(256), 0, nullptr, src, n,
-                       mode);
-    const half8* s8 = reinterpret_cast<const half8*>(src);
-    // warm-up launch, then the timed one
-    hipLaunchKernelGGL(k_probe_mfma, dim3(kProbeWgs), dim3(kProbeThreads), 0, nullptr, s8, sink, clk,
-                       iters / 8 + 1);
-    e = hipEventRecord(e0, nullptr);
-    hipLaunchKernelGGL(k_probe_mfma, dim3(kProbeWgs), dim3(kProbeThreads), 0, nullptr, s8, sink, clk,
-                       iters);
-    if (e == hipSuccess) e = hipGetLastError();
-    if (e == hipSuccess) e = hipEventRecord(e1, nullptr);
-    if (e == hipSuccess) e = hipEventSynchronize(e1);
-  }
-  if (e == hipSuccess) {
-    float ms = 0.f;
-    e = hipEventElapsedTime(&ms, e0, e1);
-    unsigned long long c[kProbeWgs * 4];
-    if (e == hipSuccess) e = hipMemcpy(c, clk, sizeof(c), hipMemcpyDeviceToHost);
-    if (e == hipSuccess) {
-      double f = 0.0;
-      for (int b = 0; b < kProbeWgs; ++b)
-        f += (double)(c[4 * b + 1] - c[4 * b]) / (double)(c[4 * b + 3] - c[4 * b + 2]) * 0.1;
-      *ghz = (float)(f / kProbeWgs);
-      const double flops = 2.0 * 32 * 32 * 16 * 16 * (double)iters * 4 * kProbeWgs;
-      *tflops = (float)(flops / (ms * 1e-3) / 1e12);
-    }
-  }
-  if (e0) (void)hipEventDestroy(e0);
-  if (e1) (void)hipEventDestroy(e1);
-  if (src) (void)hipFree(src);
-  if (sink) (void)hipFree(sink);
-  if (clk) (void)hipFree(clk);
-  return e;
+  _Float16* src = reinterpret_cast<_Float16*>(base);
+  float* sink = reinterpret_cast<float*>(base + n * 2);
+  unsigned long long* clk =
+      reinterpret_cast<unsigned long long*>(base + n * 2 + (int64_t)kProbeWgs * kProbeThreads * 4);
+  hipLaunchKernelGGL(k_probe_fill, dim3((unsigned)((n + 255) / 256)), dim3(256), 0, s, src, n, mode);
+  const half8* s8 = reinterpret_cast<const half8*>(src);
+  // a short warm-up, then the run whose stamps stay in the scratch
+  hipLaunchKernelGGL(k_probe_mfma, dim3(kProbeWgs), dim3(kProbeThreads), 0, s, s8, sink, clk,
+                     iters / 8 + 1);
+  hipLaunchKernelGGL(k_probe_mfma, dim3(kProbeWgs), dim3(kProbeThreads), 0, s, s8, sink, clk, iters);
+  return hipGetLastError();
 }
 
 }  // namespace nvfp4

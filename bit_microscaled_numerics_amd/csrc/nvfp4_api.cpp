@@ -350,12 +350,17 @@ int mxfp4_gemm(const mxfp4_operand* a, const mxfp4_operand* b, float* c, int64_t
                                         as_stream(stream)));
 }
 
-int nvfp4_probe_mfma(int mode, int iters, float* tflops_out, float* clock_ghz_out) {
-  if (tflops_out == nullptr || clock_ghz_out == nullptr)
-    return fail(NVFP4_ERR_NULL, "tflops_out / clock_ghz_out is NULL");
+int64_t nvfp4_probe_scratch_bytes(void) { return nvfp4::probe_scratch_bytes(); }
+
+int nvfp4_probe_mfma(int mode, int iters, void* scratch, int64_t scratch_bytes, void* stream) {
+  if (scratch == nullptr) return fail(NVFP4_ERR_NULL, "scratch is NULL");
+  if (!aligned(scratch, 256)) return fail(NVFP4_ERR_ALIGN, "scratch must be 256-byte aligned");
+  if (scratch_bytes < nvfp4::probe_scratch_bytes())
+    return fail(NVFP4_ERR_SHAPE, "scratch_bytes=%lld < %lld", (long long)scratch_bytes,
+                (long long)nvfp4::probe_scratch_bytes());
   if (mode < 0 || mode > 2) return fail(NVFP4_ERR_ARG, "mode=%d (0, 1 or 2)", mode);
   if (iters < 1 || iters > 1000000) return fail(NVFP4_ERR_ARG, "iters=%d (1 .. 1000000)", iters);
-  return launched(nvfp4::probe_mfma(mode, iters, tflops_out, clock_ghz_out));
+  return launched(nvfp4::probe_mfma(mode, iters, scratch, as_stream(stream)));
 }
 
 }  // extern "C"

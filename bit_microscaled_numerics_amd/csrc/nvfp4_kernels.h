@@ -60,8 +60,9 @@ hipError_t launch_mx_dequant(const MxOperand& q, float* out, hipStream_t s);
 hipError_t launch_mx_gemm(const MxOperand& a, const MxOperand& b, int64_t K, float* c,
                           int64_t ldc, hipStream_t s);
 
-// Measurement support: MFMA-only throughput and shader clock on operand
-// data of kind `mode` (0 zeros, 1 decoded-NVFP4-like, 2 uniform FP16).
-hipError_t probe_mfma(int mode, int iters, float* tflops, float* ghz);
+// Measurement support: MFMA-only run on operand data of kind `mode` (0 zeros,
+// 1 decoded-NVFP4-like, 2 uniform FP16), clock stamps left in the scratch.
+int64_t probe_scratch_bytes();
+hipError_t probe_mfma(int mode, int iters, void* scratch, hipStream_t s);
 
 }  // namespace nvfp4

@@ -237,19 +237,25 @@ int mxfp4_gemm(const mxfp4_operand* a, const mxfp4_operand* b, float* c, int64_t
 
 /* ------------------------------------------------------------------------
  * Measurement support (not part of the quantize / GEMM path): the sustained
- * throughput and shader clock of the FP16 matrix cores on the current device
- * running the GEMM fast path's MFMA pattern (v_mfma_f32_32x32x16_f16, 8 x 2
- * independent accumulators per wave, one wave per SIMD, 256 workgroups) from
- * registers, with no loads, decode or LDS -- the ceiling the GEMM's roofline
- * fraction should be read against.  The sustained clock depends on the power
- * the operand bits draw, so `mode` picks the operand data: 0 zeros, 1 values
- * like the GEMM's decoded operands (E2M1 x E4M3 mantissa, random signs), 2
- * uniform FP16 in [-1, 1).  iters: 1 .. 1000000 loop trips (16 MFMAs each);
- * about 8000 runs ~2 ms.  Allocates and frees its own device memory, runs on
- * the null stream and synchronizes.  Writes TFLOP/s (2 * 32 * 32 * 16 FLOP
- * per MFMA) and the mean clock in GHz (shader-clock counter against the
- * 100 MHz real-time counter, per workgroup). */
-int nvfp4_probe_mfma(int mode, int iters, float* tflops_out, float* clock_ghz_out);
+ * throughput and shader clock of the FP16 matrix cores running the GEMM fast
+ * path's MFMA pattern (v_mfma_f32_32x32x16_f16, 8 x 2 independent
+ * accumulators per wave, one wave per SIMD, 256 workgroups of 256 threads)
+ * from registers, with no loads, decode or LDS -- the ceiling the GEMM's
+ * roofline fraction should be read against.  The sustained clock depends on
+ * the power the operand bits draw, so `mode` picks the operand data: 0 zeros,
+ * 1 values like the GEMM's decoded operands (E2M1 x E4M3 mantissa, random
+ * signs), 2 uniform FP16 in [-1, 1).
+ *
+ * Enqueues on `stream`: fill the operands, a warm-up run, then a run of
+ * `iters` loop trips (1 .. 1000000; 16 MFMAs of 2*32*32*16 FLOP per wave per
+ * trip; ~200000 runs ~50 ms).  `scratch` is caller-owned device memory of at
+ * least nvfp4_probe_scratch_bytes() bytes, 256-byte aligned.  After the
+ * stream completes, the last 256 * 4 uint64 of that size hold, per workgroup
+ * b, {shader-clock counter at start, at end, 100 MHz real-time counter at
+ * start, at end} of the timed run: the clock is d(shader) / d(real-time) *
+ * 100 MHz, and the run's duration is (max end - min start) real-time ticks. */
+int64_t nvfp4_probe_scratch_bytes(void);
+int nvfp4_probe_mfma(int mode, int iters, void* scratch, int64_t scratch_bytes, void* stream);
 
 /* Human-readable name of a status code (static storage). */
 const char* nvfp4_status_string(int status);

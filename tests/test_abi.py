@@ -23,7 +23,7 @@ def lib():
 
 def declared():
     text = open(HEADER).read()
-    return sorted(set(re.findall(r"^\s*(?:int|const char\*)\s+((?:nvfp4|mxfp4)_\w+)\s*\(", text,
+    return sorted(set(re.findall(r"^\s*(?:int|int64_t|const char\*)\s+((?:nvfp4|mxfp4)_\w+)\s*\(", text,
                                  re.M)))
 
 
@@ -163,13 +163,15 @@ def test_gemm_bf16_validation(lib):
 
 def test_probe_mfma_validation(lib):
     """The measurement probe refuses bad arguments before touching the device."""
-    f = ctypes.c_float()
     p = lib.nvfp4_probe_mfma
-    assert p(1, 100, None, ctypes.byref(f)) == nv.NVFP4_ERR_NULL
-    assert p(1, 100, ctypes.byref(f), None) == nv.NVFP4_ERR_NULL
-    assert p(3, 100, ctypes.byref(f), ctypes.byref(f)) == nv.NVFP4_ERR_ARG
-    assert p(-1, 100, ctypes.byref(f), ctypes.byref(f)) == nv.NVFP4_ERR_ARG
-    assert p(1, 0, ctypes.byref(f), ctypes.byref(f)) == nv.NVFP4_ERR_ARG
+    n = lib.nvfp4_probe_scratch_bytes()
+    assert n > 0
+    assert p(1, 100, None, n, None) == nv.NVFP4_ERR_NULL
+    assert p(1, 100, FAKE + 16, n, None) == nv.NVFP4_ERR_ALIGN
+    assert p(1, 100, FAKE, n - 1, None) == nv.NVFP4_ERR_SHAPE
+    assert p(3, 100, FAKE, n, None) == nv.NVFP4_ERR_ARG
+    assert p(-1, 100, FAKE, n, None) == nv.NVFP4_ERR_ARG
+    assert p(1, 0, FAKE, n, None) == nv.NVFP4_ERR_ARG
 
 
 def test_amax_both_validation(lib):
