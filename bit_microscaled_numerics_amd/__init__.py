@@ -33,7 +33,8 @@ EXPORTED = ("nvfp4_amax", "nvfp4_amax_rht", "nvfp4_quantize1d_rtn", "nvfp4_quant
             "nvfp4_quantize2d_rtn", "nvfp4_quantize2d_sr", "nvfp4_rht_quantize",
             "nvfp4_dequantize", "nvfp4_gemm", "nvfp4_status_string", "nvfp4_last_error",
             "nvfp4_gemm_bf16", "mxfp4_quantize", "mxfp4_dequantize", "mxfp4_gemm",
-            "nvfp4_probe_mfma", "nvfp4_probe_scratch_bytes", "nvfp4_amax_both")
+            "nvfp4_probe_mfma", "nvfp4_probe_scratch_bytes", "nvfp4_amax_both",
+            "nvfp4_quantize_row_rht")
 
 
 class NVFP4Error(RuntimeError):
@@ -81,6 +82,8 @@ def load_library(path: str = LIB_PATH) -> ctypes.CDLL:
         "nvfp4_quantize2d_rtn": [vp, i64, i64, vp, i32, vp, vp, vp, vp, vp, vp],
         "nvfp4_quantize2d_sr": [vp, i64, i64, vp, i32, u64, u32, vp, vp, vp, vp, vp, vp],
         "nvfp4_rht_quantize": [vp, i64, i64, u64, i32, u64, u32, vp, i32, vp, vp, vp, vp],
+        "nvfp4_quantize_row_rht": [vp, i64, i64, u64, i32, u64, u32, u32, vp, vp, vp, vp, vp, vp,
+                                   vp, vp, vp],
         "nvfp4_dequantize": [ctypes.POINTER(c_operand), vp, vp],
         "nvfp4_gemm": [ctypes.POINTER(c_operand), ctypes.POINTER(c_operand), vp, i64, vp],
         "nvfp4_gemm_bf16": [ctypes.POINTER(c_operand), ctypes.POINTER(c_operand), vp, i64, vp, vp],
@@ -181,6 +184,16 @@ def nvfp4_rht_quantize(x, rht_seed, use_sr, sr_seed, stream_id, amax_io, amax_mo
                                              int(use_sr), sr_seed, stream_id, _p(amax_io),
                                              amax_mode, _p(codes), _p(scales), _p(ts_out),
                                              _stream(stream)))
+
+
+def nvfp4_quantize_row_rht(x, rht_seed, use_sr, sr_seed, stream_id_row, stream_id_rht, amax_row,
+                           amax_rht, codes_row, scales_row, ts_row, codes_rht, scales_rht, ts_rht,
+                           stream=None):
+    _dev_bf16(x, "x")
+    _check(load_library().nvfp4_quantize_row_rht(
+        _p(x), x.shape[0], x.shape[1], rht_seed, int(use_sr), sr_seed, stream_id_row,
+        stream_id_rht, _p(amax_row), _p(amax_rht), _p(codes_row), _p(scales_row), _p(ts_row),
+        _p(codes_rht), _p(scales_rht), _p(ts_rht), _stream(stream)))
 
 
 def nvfp4_dequantize(q: "NVFP4Tensor", out, stream=None):
@@ -306,6 +319,23 @@ def rht_quantize(x: torch.Tensor, rht_seed: int, sr_seed: Optional[int] = None,
     nvfp4_rht_quantize(x, rht_seed, sr_seed is not None, 0 if sr_seed is None else sr_seed,
                        stream_id, am, mode, codes, scales, ts)
     return NVFP4Tensor(codes, scales, ts, am, C, R, 1, R // 16, 1)
+
+
+def quantize_row_rht(x: torch.Tensor, rht_seed: int, sr_seed: Optional[int] = None,
+                     stream_ids=(0, 1)):
+    """(rowwise 1D operand of x, Wgrad operand RHT(x)^T) from one read of x,
+    byte-identical to quantize_1d(x, ...) and rht_quantize(x, ...) with the
+    same seeds and stream ids; the two amaxes come from one amax_both pass."""
+    _dev_bf16(x, "x")
+    R, C = x.shape
+    am_row, am_rht = amax_both(x, rht_seed)
+    codes_r, scales_r, ts_r = _outputs(R, C, x.device, (R, C // 16))
+    codes_t, scales_t, ts_t = _outputs(C, R, x.device, (C, R // 16))
+    nvfp4_quantize_row_rht(x, rht_seed, sr_seed is not None, 0 if sr_seed is None else sr_seed,
+                           stream_ids[0], stream_ids[1], am_row, am_rht, codes_r, scales_r, ts_r,
+                           codes_t, scales_t, ts_t)
+    return (NVFP4Tensor(codes_r, scales_r, ts_r, am_row, R, C, 1, C // 16, 1),
+            NVFP4Tensor(codes_t, scales_t, ts_t, am_rht, C, R, 1, R // 16, 1))
 
 
 def dequantize(q: NVFP4Tensor) -> torch.Tensor:

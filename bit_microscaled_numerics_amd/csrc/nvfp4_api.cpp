@@ -243,6 +243,23 @@ int nvfp4_rht_quantize(const void* x, int64_t rows, int64_t cols, uint64_t rht_s
                                           sr_seed, stream_id, codes, scales, ts_out, s));
 }
 
+int nvfp4_quantize_row_rht(const void* x, int64_t rows, int64_t cols, uint64_t rht_seed,
+                           int use_sr, uint64_t sr_seed, uint32_t stream_id_row,
+                           uint32_t stream_id_rht, const float* amax_row, const float* amax_rht,
+                           uint8_t* codes_row, uint8_t* scales_row, float* ts_row_out,
+                           uint8_t* codes_rht, uint8_t* scales_rht, float* ts_rht_out,
+                           void* stream) {
+  int st = check_tensor(x, rows, cols, "x");
+  if (st) return st;
+  if ((st = check_outputs(codes_row, scales_row, amax_row, ts_row_out))) return st;
+  if ((st = check_outputs(codes_rht, scales_rht, amax_rht, ts_rht_out))) return st;
+  if (use_sr != 0 && use_sr != 1) return fail(NVFP4_ERR_ARG, "use_sr=%d must be 0 or 1", use_sr);
+  return launched(nvfp4::launch_quant_row_rht(x, rows, cols, rht_seed, use_sr == 1, sr_seed,
+                                              stream_id_row, stream_id_rht, amax_row, amax_rht,
+                                              codes_row, scales_row, ts_row_out, codes_rht,
+                                              scales_rht, ts_rht_out, as_stream(stream)));
+}
+
 int nvfp4_dequantize(const nvfp4_operand* q, float* out, void* stream) {
   int st = check_operand(q, "q");
   if (st) return st;

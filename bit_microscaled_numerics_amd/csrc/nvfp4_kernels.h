@@ -20,6 +20,12 @@ hipError_t launch_quant_col(const void* x, int64_t rows, int64_t cols, const flo
                             bool rht, uint64_t rht_seed, bool sr, uint64_t seed,
                             uint32_t stream_id, uint8_t* codes, uint8_t* scales, float* ts_out,
                             hipStream_t s);
+// rowwise 1D (amax_row given) and RHT transpose (amax_rht given) from one read
+hipError_t launch_quant_row_rht(const void* x, int64_t rows, int64_t cols, uint64_t rht_seed,
+                               bool sr, uint64_t seed, uint32_t stream_row, uint32_t stream_col,
+                               const float* amax_row, const float* amax_rht, uint8_t* codes_row,
+                               uint8_t* scales_row, float* ts_row, uint8_t* codes_col,
+                               uint8_t* scales_col, float* ts_col, hipStream_t s);
 hipError_t launch_quant_2d(const void* x, int64_t rows, int64_t cols, const float* amax, bool sr,
                            uint64_t seed, uint32_t stream_id, uint8_t* codes, uint8_t* codes_t,
                            uint8_t* scales, uint8_t* scales_t, float* ts_out, hipStream_t s);

@@ -182,11 +182,24 @@ __global__ __launch_bounds__(kThreads) void k_quant_row(
 // stores run along the output's contiguous dimension.
 constexpr int kColTileR = 256, kColTileC = 128;
 
-template <bool SR, bool RHT>
+// ROW: the same read also yields the rowwise 1D operand of x (blocks of 16
+// along cols: the two lanes holding a row's adjacent 8-column pieces), with
+// its own given amax and SR stream -- the tensors the recipe quantizes both
+// ways (X, dY) are then read once.
+struct RowOut {
+  const float* amax;
+  uint32_t stream_id;
+  uint8_t* codes;    // [rows][cols/2]
+  uint8_t* scales;   // [rows][cols/16]
+  float* ts_out;
+};
+
+template <bool SR, bool RHT, bool ROW>
 __global__ __launch_bounds__(kThreads) void k_quant_col(
     const uint16_t* __restrict__ x, int64_t rows, int64_t cols,
     const float* __restrict__ amax, uint64_t rht_seed, uint64_t seed, uint32_t stream_id,
-    uint8_t* __restrict__ codes, uint8_t* __restrict__ scales, float* __restrict__ ts_out) {
+    uint8_t* __restrict__ codes, uint8_t* __restrict__ scales, float* __restrict__ ts_out,
+    RowOut ro) {
   __shared__ v2u lds_codes[kColTileC][kColTileR / 16];   // 8 bytes = 16 codes per block
   __shared__ uint8_t lds_scales[kColTileC][kColTileR / 16];
   const float s_t = tensor_scale_from_amax(*amax);
@@ -199,6 +212,32 @@ __global__ __launch_bounds__(kThreads) void k_quant_col(
   if (rr < rows && cc < cols) {
     Tile16x8 t;
     tile_load(t, x, cols, rr, cc);
+    if (ROW) {
+      // rows rr .. rr+15, columns cc .. cc+7: half of a 16-wide block each;
+      // the partner lane (cg ^ 1) holds the other half (cols % 16 == 0, so
+      // both halves are in range together)
+      const float s_r = tensor_scale_from_amax(*ro.amax);
+      const float t6r = 6.0f * s_r;
+      if (blockIdx.x == 0 && blockIdx.y == 0 && threadIdx.x == 0) *ro.ts_out = s_r;
+#pragma unroll
+      for (int i = 0; i < 16; ++i) {
+        const v4u w = t.row[i];
+        float z[8] = {bf16_lo(w.x), bf16_hi(w.x), bf16_lo(w.y), bf16_hi(w.y),
+                      bf16_lo(w.z), bf16_hi(w.z), bf16_lo(w.w), bf16_hi(w.w)};
+        float m = 0.0f;
+#pragma unroll
+        for (int j = 0; j < 8; ++j) m = fmaxf(m, __builtin_fabsf(z[j]));
+        m = fmaxf(m, __shfl_xor(m, 1, 64));
+        const BlockScale b = block_scale(m, s_r, t6r);
+        const int64_t row = rr + i;
+        uint32_t q = SR ? encode8_sr(z, b.r, sr_words(seed, ro.stream_id,
+                                                      (uint64_t)row * (uint64_t)cols + (uint64_t)cc))
+                        : encode8_rtn(z, b.r);
+        q = select_zero_block(b.code, q, z);
+        *reinterpret_cast<uint32_t*>(ro.codes + row * (cols / 2) + cc / 2) = q;
+        if ((cg & 1) == 0) ro.scales[row * (cols / 16) + cc / 16] = (uint8_t)b.code;
+      }
+    }
 #pragma unroll
     for (int c = 0; c < 8; ++c) {
       float v[16];
@@ -409,13 +448,31 @@ hipError_t launch_quant_col(const void* x, int64_t rows, int64_t cols, const flo
                (unsigned)((rows + kColTileR - 1) / kColTileR)), b(kThreads);
   const uint16_t* xp = reinterpret_cast<const uint16_t*>(x);
 #define NVFP4_COL(SRV, RHTV)                                                                  \
-  hipLaunchKernelGGL((k_quant_col<SRV, RHTV>), g, b, 0, s, xp, rows, cols, amax, rht_seed,   \
-                     seed, stream_id, codes, scales, ts_out)
+  hipLaunchKernelGGL((k_quant_col<SRV, RHTV, false>), g, b, 0, s, xp, rows, cols, amax,       \
+                     rht_seed, seed, stream_id, codes, scales, ts_out, RowOut{})
   if (sr && rht) NVFP4_COL(true, true);
   else if (sr) NVFP4_COL(true, false);
   else if (rht) NVFP4_COL(false, true);
   else NVFP4_COL(false, false);
 #undef NVFP4_COL
+  return hipGetLastError();
+}
+
+hipError_t launch_quant_row_rht(const void* x, int64_t rows, int64_t cols, uint64_t rht_seed,
+                               bool sr, uint64_t seed, uint32_t stream_row, uint32_t stream_col,
+                               const float* amax_row, const float* amax_rht, uint8_t* codes_row,
+                               uint8_t* scales_row, float* ts_row, uint8_t* codes_col,
+                               uint8_t* scales_col, float* ts_col, hipStream_t s) {
+  const dim3 g((unsigned)((cols + kColTileC - 1) / kColTileC),
+               (unsigned)((rows + kColTileR - 1) / kColTileR)), b(kThreads);
+  const uint16_t* xp = reinterpret_cast<const uint16_t*>(x);
+  const RowOut ro{amax_row, stream_row, codes_row, scales_row, ts_row};
+  if (sr)
+    hipLaunchKernelGGL((k_quant_col<true, true, true>), g, b, 0, s, xp, rows, cols, amax_rht,
+                       rht_seed, seed, stream_col, codes_col, scales_col, ts_col, ro);
+  else
+    hipLaunchKernelGGL((k_quant_col<false, true, true>), g, b, 0, s, xp, rows, cols, amax_rht,
+                       rht_seed, seed, stream_col, codes_col, scales_col, ts_col, ro);
   return hipGetLastError();
 }
 

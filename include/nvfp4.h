@@ -143,6 +143,22 @@ int nvfp4_rht_quantize(const void* x_bf16, int64_t rows, int64_t cols, uint64_t 
                        uint8_t* codes, uint8_t* scales_e4m3, float* tensor_scale_out,
                        void* stream);
 
+/* The two quantizations of one tensor that the recipe needs both of -- the
+ * rowwise 1D operand (as nvfp4_quantize1d_*, axis NVFP4_ROWWISE) and the RHT
+ * transpose (as nvfp4_rht_quantize) -- from a single read of x.  X (Fprop
+ * rowwise, Wgrad under the RHT) and dY (Dgrad rowwise with SR, Wgrad under
+ * the RHT with SR) are such tensors ("Pretraining Large Language Models with
+ * NVFP4", summary page, recipe paragraph).  Both amaxes are given (e.g. from
+ * nvfp4_amax_both); use_sr applies to both outputs, each with its own SR
+ * stream id.  Outputs and their validation as in the two single calls; the
+ * results are byte-identical to them. */
+int nvfp4_quantize_row_rht(const void* x_bf16, int64_t rows, int64_t cols, uint64_t rht_seed,
+                           int use_sr, uint64_t sr_seed, uint32_t stream_id_row,
+                           uint32_t stream_id_rht, const float* amax_row, const float* amax_rht,
+                           uint8_t* codes_row, uint8_t* scales_row, float* tensor_scale_row_out,
+                           uint8_t* codes_rht, uint8_t* scales_rht, float* tensor_scale_rht_out,
+                           void* stream);
+
 /* A quantized GEMM operand, logically [rows][k], K-contiguous.  The scale of
  * element (r, k) is scales[(r / blk_rows) * ss_row + (k / 16) * ss_k].
  *  1D rowwise operand: blk_rows 1,  ss_row = k/16, ss_k = 1.

@@ -180,3 +180,18 @@ def test_amax_both_validation(lib):
     assert f(FAKE, 32, 16, 1, FAKE, None, None) == nv.NVFP4_ERR_NULL
     assert f(FAKE, 32, 16, 1, FAKE, FAKE, None) == nv.NVFP4_ERR_ARG
     assert f(FAKE, 32, 16, 1, MIS, FAKE + 16, None) == nv.NVFP4_ERR_ALIGN
+
+
+def test_quantize_row_rht_validation(lib):
+    f = lib.nvfp4_quantize_row_rht
+    args = [FAKE, 32, 16, 1, 0, 0, 0, 1, FAKE, FAKE, FAKE, FAKE, FAKE, FAKE, FAKE, FAKE, None]
+    a = list(args); a[10] = None   # codes_row
+    assert f(*a) == nv.NVFP4_ERR_NULL
+    a = list(args); a[13] = None   # codes_rht
+    assert f(*a) == nv.NVFP4_ERR_NULL
+    a = list(args); a[10] = MIS
+    assert f(*a) == nv.NVFP4_ERR_ALIGN
+    a = list(args); a[4] = 2       # use_sr
+    assert f(*a) == nv.NVFP4_ERR_ARG
+    a = list(args); a[1] = 24      # rows not a multiple of 16
+    assert f(*a) == nv.NVFP4_ERR_SHAPE

@@ -99,6 +99,29 @@ def test_rht_quantize(shape, kind, sr):
 @pytest.mark.parametrize("shape", SHAPES)
 @pytest.mark.parametrize("kind", KINDS)
 @pytest.mark.parametrize("sr", [False, True])
+def test_quantize_row_rht_one_read(shape, kind, sr):
+    """Rowwise operand and RHT transpose from one read: each bit-exact with the
+    oracle and byte-identical to the two single calls (same seeds, streams)."""
+    x = _tensor(kind, *shape, seed=5)
+    sr_seed = 31 if sr else None
+    say("quantize_row_rht", shape, kind, sr)
+    gr, gt = nv.quantize_row_rht(x.cuda(), 99, sr_seed=sr_seed, stream_ids=(0, 1))
+    kw0 = {"sr_seed": 31, "stream_id": 0} if sr else {}
+    kw1 = {"sr_seed": 31, "stream_id": 1} if sr else {}
+    sr_ = nv.quantize_1d(x.cuda(), nv.NVFP4_ROWWISE, **kw0)
+    st_ = nv.rht_quantize(x.cuda(), 99, **kw1)
+    torch.cuda.synchronize()
+    assert_operand_equal(gr, oracle.quantize(x, oracle.ROWWISE, **kw0), f"row {shape} {kind} {sr}")
+    assert_operand_equal(gt, oracle.quantize(x, oracle.COLWISE, rht_seed=99, **kw1),
+                         f"rht {shape} {kind} {sr}")
+    for a, b in ((gr, sr_), (gt, st_)):
+        assert torch.equal(a.codes, b.codes) and torch.equal(a.scales, b.scales)
+        assert torch.equal(a.tensor_scale, b.tensor_scale)
+
+
+@pytest.mark.parametrize("shape", SHAPES)
+@pytest.mark.parametrize("kind", KINDS)
+@pytest.mark.parametrize("sr", [False, True])
 def test_quantize_2d(shape, kind, sr):
     x = _tensor(kind, *shape, seed=3)
     kw = {"sr_seed": 5, "stream_id": 2} if sr else {}
