@@ -30,34 +30,56 @@ __device__ __forceinline__ void grouped(int64_t t, int64_t tiles_m, int64_t tile
   tn = in / gm;
 }
 
-// Block -> tile and K part.  Blocks below full_tiles take whole tiles
-// (renumbered so each XCD owns a contiguous range); the blocks after them
-// take the remaining tiles two per tile, part 0 / 1 = first / second K half
-// (the last partial round of tiles finishes in half the time).
-__device__ __forceinline__ void block_tile(int64_t full, int64_t tiles_m, int64_t tiles_n,
-                                           int64_t& tm, int64_t& tn, int& part) {
+// How the tiles of a last, partial round of workgroups are cut (whole tiles
+// before them run as usual): into two K halves that add into a zeroed
+// output, into two half-width (256 x 128) tiles that each write their own
+// columns, or both (four pieces).  The half-width cut needs no FP32 addends,
+// so it also serves outputs that cannot take them (BF16).
+enum TailMode { kTailWhole = 0, kTailK = 1, kTailN = 2, kTailNK = 3 };
+
+// Block -> tile, K part (-1 whole, 0 / 1 halves) and N half (-1 full width,
+// 0 / 1).  Blocks below full take whole tiles, renumbered so each XCD owns a
+// contiguous range; the blocks after them take the remaining tiles, 2 or 4
+// pieces each by the tail mode.
+__device__ __forceinline__ void block_tile(int64_t full, int64_t tiles_m, int64_t tiles_n, int tail,
+                                           int64_t& tm, int64_t& tn, int& part, int& nh) {
   const int64_t b = blockIdx.x;
   int64_t t;
+  part = -1;
+  nh = -1;
   if (b < full) {
     const int64_t per = full / kXcds;
     t = b < per * kXcds ? (b % kXcds) * per + b / kXcds : b;
-    part = -1;
   } else {
-    t = full + (b - full) / 2;
-    part = (int)((b - full) & 1);
+    const int pieces = tail == kTailNK ? 4 : 2;
+    const int64_t q = b - full;
+    t = full + q / pieces;
+    const int sub = (int)(q % pieces);
+    if (tail & kTailK) part = tail == kTailNK ? sub >> 1 : sub;
+    if (tail & kTailN) nh = sub & 1;
   }
   grouped(t, tiles_m, tiles_n, tm, tn);
 }
 
+// The K-split-only form (tail mode kTailK when the grid goes past full).
+__device__ __forceinline__ void block_tile(int64_t full, int64_t tiles_m, int64_t tiles_n,
+                                           int64_t& tm, int64_t& tn, int& part) {
+  int nh;
+  block_tile(full, tiles_m, tiles_n, kTailK, tm, tn, part, nh);
+}
+
 // Host-side plan of one launch: tiles_m x tiles_n tiles; grid = full_tiles
-// whole tiles plus 2 workgroups per split tile (when split).
+// whole tiles plus 2 or 4 workgroups per tail tile.
 struct TilePlan {
   int64_t tiles_m, tiles_n, full_tiles, grid, rem;
-  bool split;
+  int tail;     // TailMode
+  bool split;   // tail tiles are cut along K (the output takes two FP32 addends)
 };
 
-// allow_split: the output can take two FP32 addends per element.
-TilePlan plan_tiles(int64_t M, int64_t N, int64_t steps, bool allow_split = true);
+// allow_split: the output can take two FP32 addends per element;
+// allow_narrow: the kernel can run half-width tail tiles.
+TilePlan plan_tiles(int64_t M, int64_t N, int64_t steps, bool allow_split = true,
+                    bool allow_narrow = false);
 
 // Zero the output tiles the split workgroups add into (no-op without split).
 hipError_t zero_split_tiles(const TilePlan& p, float* c, int64_t ldc, int64_t M, int64_t N,

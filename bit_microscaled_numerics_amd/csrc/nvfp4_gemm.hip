@@ -32,7 +32,8 @@ struct GemmArgs {
   uint16_t* cb;         // BF16 output (with the BF16 epilogue)
   uint32_t* amax;       // BF16 epilogue: binary32 bits of max |C| (nullable)
   int64_t ldc;
-  int64_t full_tiles;  // tiles computed whole; tiles past them are split in two K halves
+  int64_t full_tiles;  // tiles computed whole; tiles past them are cut by `tail`
+  int tail;            // TailMode of the tiles past full_tiles
 };
 
 // Decoding.  The gfx950 FP4 -> FP16 convert multiplies by 2^floor(log2 s)
@@ -493,11 +494,12 @@ __device__ __forceinline__ DmaOp make_dma(const GemmOperand& op, int64_t row0, c
 
 // Steps x0, x0 + 1 of this wave's rows' codes into a slot (4 load
 // instructions); the code offset is clamped to the last step.
+template <int NQ>
 __device__ __forceinline__ void dma_codes(const DmaOp& v, uint8_t* raw, const int (&crow)[4], int x0,
                                           int last) {
   const uint32_t kb = (uint32_t)((x0 < last ? x0 : last) * 32);
 #pragma unroll
-  for (int q = 0; q < 4; ++q)
+  for (int q = 0; q < NQ; ++q)
     __builtin_amdgcn_raw_ptr_buffer_load_lds(v.codes, (lds_ptr_t)(raw + crow[q] * kRawRow), 16,
                                              v.voff_c[q], kb, 0, 0);
 }
@@ -545,11 +547,12 @@ __device__ __forceinline__ void store_a(uint8_t* stage, const RawRegs& r, int q,
 struct OpsA { half8 a[kMB]; };
 struct OpsB { half8 b[kNB]; };
 
-// B fragments of sub-step s: word s of each block's chunk.
+// B fragments of sub-step s: word s of each of the NB blocks' chunks.
+template <int NB>
 __device__ __forceinline__ void dec_b(OpsB& o, const RawRegs& r, int s, uint32_t pos0,
                                       uint32_t pos1) {
 #pragma unroll
-  for (int j = 0; j < kNB; ++j)
+  for (int j = 0; j < NB; ++j)
     o.b[j] = decode8(r.codes[j][s], scale_alu(r.sc[j], s < 2 ? pos0 : pos1));
 }
 
@@ -560,11 +563,12 @@ __device__ __forceinline__ void read_a(OpsA& o, const uint8_t* stage, int lrow, 
     o.a[i] = *reinterpret_cast<const half8*>(stage + lds_off(32 * i + lrow, 4 * lk + s));
 }
 
-__device__ __forceinline__ void mfma16(float16v (&acc)[kMB][kNB], const OpsA& a, const OpsB& b) {
+template <int NB>
+__device__ __forceinline__ void mfma16(float16v (&acc)[kMB][NB], const OpsA& a, const OpsB& b) {
 #pragma unroll
   for (int i = 0; i < kMB; ++i)
 #pragma unroll
-    for (int j = 0; j < kNB; ++j)
+    for (int j = 0; j < NB; ++j)
       acc[i][j] = __builtin_amdgcn_mfma_f32_32x32x16_f16(a.a[i], b.b[j], acc[i][j], 0, 0, 0);
 }
 
@@ -579,48 +583,40 @@ __device__ __forceinline__ void interleave16() {
   }
 }
 
-template <bool BF16>
-__global__ __launch_bounds__(kThreads4, 1) void k_gemm_dma(GemmArgs g) {
-  extern __shared__ __attribute__((aligned(16))) uint8_t smem[];   // decoded A, 2 stages
-  // raw code slots and scale slots as separate arrays (one LDS object each)
-  __shared__ __attribute__((aligned(16))) uint8_t rawA0[kRawBytes], rawA1[kRawBytes];
-  __shared__ __attribute__((aligned(16))) uint8_t rawB0[kRawBytes], rawB1[kRawBytes];
-  __shared__ __attribute__((aligned(16))) uint8_t scA[kScBytes], scB[kScBytes];
-
+// One tile (or half-width tail tile) of the fast path: A rows tm * 256 ..
+// +255, B rows b_row0 .. + 64 NB * 4 - 1 (NB blocks of 32 per wave: 2 for
+// a whole 256-wide tile, 1 for a half-width one), K part `part`.
+template <bool BF16, int NB>
+__device__ __forceinline__ void gemm_dma_tile(const GemmArgs& g, int64_t tm, int64_t b_row0,
+                                              int part, int wave, uint8_t* smem, uint8_t* rawA0,
+                                              uint8_t* rawA1, uint8_t* rawB0, uint8_t* rawB1,
+                                              uint8_t* scA, uint8_t* scB) {
   const int t = threadIdx.x, lane = t & 63;
-  // wave and tile indices in scalar registers: the buffer descriptors and LDS
-  // load bases built from them must be uniform
-  const int wave = __builtin_amdgcn_readfirstlane(t >> 6);
   const int lrow = lane & 31, lk = lane >> 5;
-  const int64_t tiles_m = (g.M + kTile - 1) / kTile, tiles_n = (g.N + kTile - 1) / kTile;
-  int64_t tm, tn;
-  int part;
-  block_tile(g.full_tiles, tiles_m, tiles_n, tm, tn, part);
-  tm = __builtin_amdgcn_readfirstlane((int)tm);
-  tn = __builtin_amdgcn_readfirstlane((int)tn);
-  part = __builtin_amdgcn_readfirstlane(part);
-
   const int a_crow[4] = {32 * wave, 32 * wave + 16, 128 + 32 * wave, 128 + 32 * wave + 16};
-  const int b_crow[4] = {64 * wave, 64 * wave + 16, 64 * wave + 32, 64 * wave + 48};
+  // B rows of this wave: 32 NB from 32 NB w (the code loads of a half-width
+  // tile repeat their two row ranges; only NB * 2 of them are issued)
+  const int bw = 32 * NB * wave;
+  const int b_crow[4] = {bw, bw + 16, bw + 32 * (NB - 1), bw + 32 * (NB - 1) + 16};
   // scale slot row 64 w + l holds A row 32 w + l (l < 32) or 128 + 32 w + l - 32,
-  // and B row 64 w + l
+  // and B row bw + l (whole tile) or bw + l % 32 (half-width, repeated)
   const int a_srow = lane < 32 ? 32 * wave + lane : 128 + 32 * wave + lane - 32;
   const DmaOp va = make_dma(g.a, tm * kTile, a_crow, a_srow);
-  const DmaOp vb = make_dma(g.b, tn * kTile, b_crow, 64 * wave + lane);
+  const DmaOp vb = make_dma(g.b, b_row0, b_crow, NB == 2 ? bw + lane : bw + (lane & 31));
   // A rows this thread decodes; B rows whose fragments this lane holds; and
   // their scale slot rows (the second row's is 32 further)
   const int ar0 = t >> 1, ar1 = 128 + (t >> 1), ah = t & 1;
-  const int br0 = 64 * wave + lrow, br1 = br0 + 32;
-  const int a_sidx = 64 * wave + (lane >> 1), b_sidx = br0;
+  const int br0 = bw + lrow, br1 = NB == 2 ? br0 + 32 : br0;
+  const int a_sidx = 64 * wave + (lane >> 1), b_sidx = 64 * wave + lrow;
   // bit positions of the step's two block scales in a scale dword
   const uint32_t apos0 = 16u * ah, apos1 = apos0 + 8u;
   const uint32_t bpos0 = 16u * lk, bpos1 = bpos0 + 8u;
 
-  float16v acc[kMB][kNB];
+  float16v acc[kMB][NB];
 #pragma unroll
   for (int i = 0; i < kMB; ++i)
 #pragma unroll
-    for (int j = 0; j < kNB; ++j) acc[i][j] = float16v{};
+    for (int j = 0; j < NB; ++j) acc[i][j] = float16v{};
 
   const int steps = (int)(g.K / kBK), half_steps = (steps + 1) / 2;
   const int s0 = part == 1 ? half_steps : 0;
@@ -630,11 +626,12 @@ __global__ __launch_bounds__(kThreads4, 1) void k_gemm_dma(GemmArgs g) {
   // scale group 0 (steps s0 .. s0 + 3), code groups 0 and 1 (steps s0 .. s0 + 3)
   dma_scales(va, scA, wave, s0, last);
   dma_scales(vb, scB, wave, s0, last);
-  dma_codes(va, rawA0, a_crow, s0, last);
-  dma_codes(vb, rawB0, b_crow, s0, last);
-  dma_codes(va, rawA1, a_crow, s0 + 2, last);
-  dma_codes(vb, rawB1, b_crow, s0 + 2, last);
-  __builtin_amdgcn_s_waitcnt(vmcnt_imm(8));   // scale group 0 and code group 0 landed
+  dma_codes<4>(va, rawA0, a_crow, s0, last);
+  dma_codes<2 * NB>(vb, rawB0, b_crow, s0, last);
+  dma_codes<4>(va, rawA1, a_crow, s0 + 2, last);
+  dma_codes<2 * NB>(vb, rawB1, b_crow, s0 + 2, last);
+  // scale group 0 and code group 0 landed (code group 1 may be in flight)
+  __builtin_amdgcn_s_waitcnt(vmcnt_imm(4 + 2 * NB));
   __builtin_amdgcn_sched_barrier(0);
   v4u sa[2], sb[2];   // scale dwords of the current 4-step groups
   read_sg(sa, scA, a_sidx);
@@ -652,7 +649,7 @@ __global__ __launch_bounds__(kThreads4, 1) void k_gemm_dma(GemmArgs g) {
   read_raw(ra, rawA0, sa, ar0, ar1, ah, 1, 1);
   read_raw(rb, rawB0, sb, br0, br1, lk, 0, 0);
   OpsB bcur, bnxt;
-  dec_b(bcur, rb, 0, bpos0, bpos1);
+  dec_b<NB>(bcur, rb, 0, bpos0, bpos1);
   __syncthreads();
   OpsA acur, anxt;
   read_a(acur, smem, lrow, lk, 0);
@@ -680,7 +677,7 @@ __global__ __launch_bounds__(kThreads4, 1) void k_gemm_dma(GemmArgs g) {
       for (int s = 0; s < 4; ++s) {
         if (s < 3) {
           read_a(anxt, cur, lrow, lk, s + 1);
-          dec_b(bnxt, rb, s + 1, bpos0, bpos1);
+          dec_b<NB>(bnxt, rb, s + 1, bpos0, bpos1);
           if (s == 0) {
             store_a(oth, ra, 0, 0, apos0, apos1);
             store_a(oth, ra, 0, 1, apos0, apos1);
@@ -693,7 +690,7 @@ __global__ __launch_bounds__(kThreads4, 1) void k_gemm_dma(GemmArgs g) {
             store_a(oth, ra, 1, 2, apos0, apos1);
             store_a(oth, ra, 1, 3, apos0, apos1);
           }
-          mfma16(acc, acur, bcur);
+          mfma16<NB>(acc, acur, bcur);
           interleave16();
           acur = anxt;
           bcur = bnxt;
@@ -702,25 +699,27 @@ __global__ __launch_bounds__(kThreads4, 1) void k_gemm_dma(GemmArgs g) {
           // memory fence, which would also wait for the raw loads in flight
           asm volatile("s_waitcnt lgkmcnt(0)\n\ts_barrier" ::: "memory");
           __builtin_amdgcn_sched_barrier(0);
-          if ((h & 1) == 0) dma_codes(va, (h >> 1) ? rawA1 : rawA0, a_crow, x + 4, last);
-          else dma_codes(vb, (h >> 1) ? rawB1 : rawB0, b_crow, x + 3, last);
-          if (h == 0) __builtin_amdgcn_s_waitcnt(vmcnt_imm(10));
-          else if (h == 2) __builtin_amdgcn_s_waitcnt(vmcnt_imm(8));
-          else __builtin_amdgcn_s_waitcnt(vmcnt_imm(9));
+          if ((h & 1) == 0) dma_codes<4>(va, (h >> 1) ? rawA1 : rawA0, a_crow, x + 4, last);
+          else dma_codes<2 * NB>(vb, (h >> 1) ? rawB1 : rawB0, b_crow, x + 3, last);
+          // per trip the loads go A codes (4), B codes (2 NB), A codes + A
+          // scales, B codes + B scales (scales after the reads)
+          if (h == 0) __builtin_amdgcn_s_waitcnt(vmcnt_imm(2 * NB + 6));
+          else if (h == 2) __builtin_amdgcn_s_waitcnt(vmcnt_imm(2 * NB + 4));
+          else __builtin_amdgcn_s_waitcnt(vmcnt_imm(2 * NB + 5));
           __builtin_amdgcn_sched_barrier(0);
           read_a(anxt, oth, lrow, lk, 0);
           if (h == 2) read_sg(sa, scA, a_sidx);
           if (h == 3) read_sg(sb, scB, b_sidx);
           read_raw(ra, a2 ? rawA1 : rawA0, sa, ar0, ar1, ah, h & 1, (h + 2) & 3);
           read_raw(rb, b1 ? rawB1 : rawB0, sb, br0, br1, lk, (h + 1) & 1, (h + 1) & 3);
-          dec_b(bnxt, rb, 0, bpos0, bpos1);
+          dec_b<NB>(bnxt, rb, 0, bpos0, bpos1);
           if (h >= 2) {
             __builtin_amdgcn_s_waitcnt(0xC07F);   // lgkmcnt(0): slot read before its reload
             __builtin_amdgcn_sched_barrier(0);
             if (h == 2) dma_scales(va, scA, wave, it + 8, last);
             else dma_scales(vb, scB, wave, it + 8, last);
           }
-          mfma16(acc, acur, bcur);
+          mfma16<NB>(acc, acur, bcur);
           interleave16();
           acur = anxt;
           bcur = bnxt;
@@ -731,7 +730,33 @@ __global__ __launch_bounds__(kThreads4, 1) void k_gemm_dma(GemmArgs g) {
   }
   __builtin_amdgcn_s_waitcnt(0);   // loads of the groups past the end
 
-  store_c<BF16, kMB, kNB>(g, acc, tm * kTile, tn * kTile + wave * 64, part);
+  store_c<BF16, kMB, NB>(g, acc, tm * kTile, b_row0 + bw, part);
+}
+
+template <bool BF16>
+__global__ __launch_bounds__(kThreads4, 1) void k_gemm_dma(GemmArgs g) {
+  extern __shared__ __attribute__((aligned(16))) uint8_t smem[];   // decoded A, 2 stages
+  // raw code slots and scale slots as separate arrays (one LDS object each)
+  __shared__ __attribute__((aligned(16))) uint8_t rawA0[kRawBytes], rawA1[kRawBytes];
+  __shared__ __attribute__((aligned(16))) uint8_t rawB0[kRawBytes], rawB1[kRawBytes];
+  __shared__ __attribute__((aligned(16))) uint8_t scA[kScBytes], scB[kScBytes];
+  // wave and tile indices in scalar registers: the buffer descriptors and LDS
+  // load bases built from them must be uniform
+  const int wave = __builtin_amdgcn_readfirstlane(threadIdx.x >> 6);
+  const int64_t tiles_m = (g.M + kTile - 1) / kTile, tiles_n = (g.N + kTile - 1) / kTile;
+  int64_t tm, tn;
+  int part, nh;
+  block_tile(g.full_tiles, tiles_m, tiles_n, g.tail, tm, tn, part, nh);
+  tm = __builtin_amdgcn_readfirstlane((int)tm);
+  tn = __builtin_amdgcn_readfirstlane((int)tn);
+  part = __builtin_amdgcn_readfirstlane(part);
+  nh = __builtin_amdgcn_readfirstlane(nh);
+  if (nh < 0)
+    gemm_dma_tile<BF16, 2>(g, tm, tn * kTile, part, wave, smem, rawA0, rawA1, rawB0, rawB1, scA,
+                           scB);
+  else
+    gemm_dma_tile<BF16, 1>(g, tm, tn * kTile + 128 * nh, part, wave, smem, rawA0, rawA1, rawB0,
+                           rawB1, scA, scB);
 }
 
 __global__ void k_zero_word(uint32_t* p) { *p = 0u; }
@@ -752,18 +777,27 @@ __global__ __launch_bounds__(256) void k_zero_tiles(float* __restrict__ c, int64
   }
 }
 
-TilePlan plan_tiles(int64_t M, int64_t N, int64_t steps, bool allow_split) {
+TilePlan plan_tiles(int64_t M, int64_t N, int64_t steps, bool allow_split, bool allow_narrow) {
   TilePlan p;
   p.tiles_m = (M + kTile - 1) / kTile;
   p.tiles_n = (N + kTile - 1) / kTile;
   const int64_t tiles = p.tiles_m * p.tiles_n;
-  // One workgroup per CU is resident (LDS).  When the last round is at most
-  // half full, its tiles are split in two K halves so it takes half a round.
+  // One workgroup per CU is resident (LDS).  A last round that would leave
+  // CUs idle is cut into more, shorter pieces: four (half-width x K halves,
+  // about 0.3 of a round) when they still fit one round, else two K halves
+  // (half a round), else two half-width tiles (about 0.6 of a round).
   const int64_t slots = num_cus();
   p.rem = tiles % slots;
-  p.split = allow_split && p.rem > 0 && 2 * p.rem <= slots && tiles > slots && steps >= 4;
-  p.full_tiles = p.split ? tiles - p.rem : tiles;
-  p.grid = p.split ? tiles + p.rem : tiles;
+  p.tail = kTailWhole;
+  if (tiles > slots && p.rem > 0) {
+    if (allow_split && allow_narrow && 4 * p.rem <= slots && steps >= 4) p.tail = kTailNK;
+    else if (allow_split && 2 * p.rem <= slots && steps >= 4) p.tail = kTailK;
+    else if (allow_narrow && 2 * p.rem <= slots) p.tail = kTailN;
+  }
+  p.split = (p.tail & kTailK) != 0;
+  const int64_t pieces = p.tail == kTailNK ? 4 : 2;
+  p.full_tiles = p.tail == kTailWhole ? tiles : tiles - p.rem;
+  p.grid = p.tail == kTailWhole ? tiles : p.full_tiles + pieces * p.rem;
   return p;
 }
 
@@ -779,17 +813,10 @@ static hipError_t launch_gemm_any(const GemmOperand& a, const GemmOperand& b, in
                                   float* c, uint16_t* cb, uint32_t* amax, int64_t ldc,
                                   hipStream_t s) {
   const bool bf16 = cb != nullptr;
-  GemmArgs g{a, b, a.rows, b.rows, K, c, cb, amax, ldc, 0};
+  GemmArgs g{a, b, a.rows, b.rows, K, c, cb, amax, ldc, 0, kTailWhole};
   if (bf16 && amax != nullptr) {
     hipLaunchKernelGGL(k_zero_word, dim3(1), dim3(1), 0, s, amax);
     const hipError_t e = hipGetLastError();
-    if (e != hipSuccess) return e;
-  }
-  const TilePlan plan = plan_tiles(g.M, g.N, (K + kBK - 1) / kBK, !bf16);
-  g.full_tiles = plan.full_tiles;
-  const dim3 grid((unsigned)plan.grid);
-  {
-    const hipError_t e = zero_split_tiles(plan, c, ldc, g.M, g.N, s);
     if (e != hipSuccess) return e;
   }
   const bool ld16 = (a.ld % 16 == 0) && (b.ld % 16 == 0);
@@ -806,7 +833,19 @@ static hipError_t launch_gemm_any(const GemmOperand& a, const GemmOperand& b, in
   auto sc16 = [](const GemmOperand& o) {   // 4-step scale groups as 16-byte loads
     return o.ss_row % 16 == 0 && (reinterpret_cast<uintptr_t>(o.scales) & 15) == 0;
   };
-  const bool dma = sdw && steps % 4 == 0 && (!plan.split || steps % 8 == 0) && sc16(a) && sc16(b);
+  const bool dma = sdw && steps % 4 == 0 && sc16(a) && sc16(b);
+  // The tail plan: K halves need an FP32 output (two addends onto zero) and,
+  // on the fast path, whole 4-step trips per half; half-width tail tiles
+  // exist on the fast path only.
+  const TilePlan plan = plan_tiles(g.M, g.N, (K + kBK - 1) / kBK, !bf16 && (!dma || steps % 8 == 0),
+                                   dma);
+  g.full_tiles = plan.full_tiles;
+  g.tail = plan.tail;
+  const dim3 grid((unsigned)plan.grid);
+  {
+    const hipError_t e = zero_split_tiles(plan, c, ldc, g.M, g.N, s);
+    if (e != hipSuccess) return e;
+  }
 #define NVFP4_GEMM_LAUNCH_B(C, L, W, B)                                                  \
   do {                                                                                    \
     hipError_t e = hipFuncSetAttribute(reinterpret_cast<const void*>(&k_gemm<C, L, W, B>), \

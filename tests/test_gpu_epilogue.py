@@ -72,3 +72,30 @@ def test_fprop_shape_against_oracle():
     err = np.abs(y[ms, ns] - ref)
     lim = GEMM_TOL * t + 2.0 ** -8 * np.abs(ref)
     assert np.all(err <= lim), float(np.max(err / np.maximum(lim, 1e-300)))
+
+
+def test_half_width_tail_tiles_bf16():
+    """17 x 16 tiles leave a last round of 16 tiles; with a BF16 output they
+    run as 32 half-width (256 x 128) workgroups over the whole K.  Those tiles
+    (the last tile-row) are checked densely against the oracle within the GEMM
+    tolerance plus BF16 rounding, the amax against the written values, and two
+    runs bit for bit."""
+    M, N, K = 17 * 256, 16 * 256, 1024
+    qa, qb, x, w = _ops(M, N, K, 41)
+    say("gemm bf16 half-width tail", (M, N, K))
+    cb1, amax = nv.gemm_bf16(qa, qb)
+    cb2, _ = nv.gemm_bf16(qa, qb)
+    torch.cuda.synchronize()
+    assert torch.equal(cb1, cb2)
+    y = cb1.float().cpu().numpy().astype(np.float64)
+    assert float(amax.cpu()[0]) == float(np.abs(y).max())
+    ox, ow = oracle.quantize(x, oracle.ROWWISE), oracle.quantize(w, oracle.TWO_D)
+    rng = np.random.default_rng(3)
+    rows = np.concatenate([np.arange(16 * 256, M, 3), rng.integers(0, 16 * 256, 48)])
+    cols = np.concatenate([np.arange(0, N, 29), [127, 128, N - 1]])
+    ms, ns = np.meshgrid(rows, cols, indexing="ij")
+    ms, ns = ms.ravel(), ns.ravel()
+    ref, t = oracle.gemm_entries(ox, ow, ms, ns)
+    err = np.abs(y[ms, ns] - ref)
+    lim = GEMM_TOL * t + 2.0 ** -8 * np.abs(ref)
+    assert np.all(err <= lim), float(np.max(err / np.maximum(lim, 1e-300)))

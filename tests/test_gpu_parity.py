@@ -331,14 +331,16 @@ def test_single_fprop_config():
     assert_gemm_close(y.cpu().numpy(), c, t, "single fprop")
 
 
-@pytest.mark.parametrize("K", [1024, 768])
+@pytest.mark.parametrize("K", [1024, 768, 1040])
 def test_gemm_split_last_round_is_exact_and_deterministic(K):
     """M = 17*256, N = 16*256: 272 tiles on a 256-CU device leave a last
-    round of 16 tiles (the last tile-row), which the GEMM splits into two K
-    halves added into a zeroed output.  Check those tiles densely against the
-    exact oracle, the rest on samples, and two runs bit for bit.  K = 1024
-    (16 steps, 8 per half) runs on the fast path, K = 768 (6 per half) on the
-    general kernel."""
+    round of 16 tiles (the last tile-row), which the GEMM cuts into shorter
+    pieces.  Check those tiles densely against the exact oracle, the rest on
+    samples, and two runs bit for bit.  K = 1024 (16 steps): fast path, four
+    pieces per tile (half-width x K halves added into a zeroed output);
+    K = 768 (12 steps, halves not whole 4-step trips): fast path, two
+    half-width pieces; K = 1040 (not a multiple of 64): general kernel, two
+    K halves."""
     M, N = 17 * 256, 16 * 256
     g = torch.Generator().manual_seed(40)
     x = inputs.normal(g, M, K, 1.0, 0.001, 50.0)
