@@ -99,17 +99,17 @@ __device__ __forceinline__ uint32_t e2m1_rtn_index(float a) {
 __device__ __forceinline__ uint32_t e2m1_sr_index(float a, uint32_t u) {
   a = a < 6.0f ? a : 6.0f;
   const uint32_t bits = __float_as_uint(a);
-  const uint32_t e = bits >> 23;          // biased exponent (a >= 0)
+  const int d = (int)(bits >> 23) - 126;  // binade of a relative to [0.5, 1)
   const uint32_t mant = bits & 0x7FFFFFu;
-  // all three cases are evaluated and selected (no divergent branches)
-  const bool big = e >= 127u, mid = e == 126u;
-  const uint32_t lo_big = 2u * (e - 126u) + (mant >> 22);  // 1 -> 2/3, 2 -> 4/5, 4 -> 6/7
-  const bool up_big = (u << 6) < (mant & 0x3FFFFFu);
-  const bool up_mid = (u << 7) < mant;
+  // Lower grid index without branches: 2d + bit 22 for d >= 1 (2..7), 1 for
+  // d == 0 and 0 below -- the largest of 2d + bit 22, d + 1 and 0.
+  const int lo = max(max(2 * d + (int)(mant >> 22), d + 1), 0);
+  // From 0.5 up, p * 2^23: all 23 mantissa bits in [0.5, 1), the low 22
+  // doubled above 1, compared with u * 2^7.
+  const uint32_t f23 = d >= 1 ? (mant << 1) & 0x7FFFFFu : mant;
+  const bool up_int = (u << 7) < f23;
   const bool up_small = (float)u < a * 131072.0f;
-  const uint32_t lo = big ? lo_big : (mid ? 1u : 0u);
-  const bool up = big ? up_big : (mid ? up_mid : up_small);
-  return lo + (up ? 1u : 0u);
+  return (uint32_t)lo + ((d >= 0 ? up_int : up_small) ? 1u : 0u);
 }
 
 // ---------------------------------------------------------------------------

@@ -280,82 +280,106 @@ __global__ __launch_bounds__(kThreads) void k_quant_col(
 }
 
 // ---------------------------------------------------------------------------
-// 2D: 16x16 tiles, one lane per tile row (16 lanes per tile)
+// 2D: 16x16 blocks
 // ---------------------------------------------------------------------------
-// Workgroup: 64 rows x 64 columns (4 x 4 tiles); wave w holds tile row w,
-// lane = r + 16 * tc.  The tile amax is a 16-lane xor reduction.  The
-// transposed codes go through LDS as bytes [column][row] and are packed by
-// columns.
+// Workgroup tile 256 rows x 128 columns, the thread layout of the colwise
+// kernel: thread t holds rows 16 (t / 16) .. +15 and columns 8 (t % 16) .. +7,
+// so a 16x16 block is the micro-tiles of two adjacent lanes.  Each element is
+// encoded once, a row of 8 columns to a dword (the rowwise codes, stored
+// directly); the transposed codes are the same nibbles, transposed in
+// registers and staged in LDS so that their stores run along the rows of the
+// transposed output.
+
+// 8 x 8 transpose of 4-bit entries (in[i] nibble j -> out[j] nibble i): swap
+// the off-diagonal 4x4 blocks (16-bit halves), then 2x2 blocks (bytes), then
+// single nibbles.
+__device__ __forceinline__ void nibble_transpose8(const uint32_t* in, uint32_t* out) {
+  uint32_t a[8], b[8];
+#pragma unroll
+  for (int i = 0; i < 4; ++i) {
+    a[i] = (in[i] & 0xFFFFu) | (in[i + 4] << 16);
+    a[i + 4] = (in[i] >> 16) | (in[i + 4] & 0xFFFF0000u);
+  }
+#pragma unroll
+  for (int k = 0; k < 4; ++k) {
+    const int i = (k & 1) + 4 * (k >> 1);   // 0, 1, 4, 5
+    b[i] = (a[i] & 0x00FF00FFu) | ((a[i + 2] & 0x00FF00FFu) << 8);
+    b[i + 2] = ((a[i] >> 8) & 0x00FF00FFu) | (a[i + 2] & 0xFF00FF00u);
+  }
+#pragma unroll
+  for (int i = 0; i < 8; i += 2) {
+    out[i] = (b[i] & 0x0F0F0F0Fu) | ((b[i + 1] & 0x0F0F0F0Fu) << 4);
+    out[i + 1] = ((b[i] >> 4) & 0x0F0F0F0Fu) | (b[i + 1] & 0xF0F0F0F0u);
+  }
+}
+
 template <bool SR>
 __global__ __launch_bounds__(kThreads) void k_quant_2d(
     const uint16_t* __restrict__ x, int64_t rows, int64_t cols,
     const float* __restrict__ amax, uint64_t seed, uint32_t stream_id,
     uint8_t* __restrict__ codes, uint8_t* __restrict__ codes_t, uint8_t* __restrict__ scales,
     uint8_t* __restrict__ scales_t, float* __restrict__ ts_out) {
-  __shared__ uint8_t lds_t[64][64 + 16];  // [column][row]; padded rows
+  __shared__ v2u lds_codes[kColTileC][kColTileR / 16];   // [column][row group]
   const float s_t = tensor_scale_from_amax(*amax);
   const float t6 = 6.0f * s_t;
   if (blockIdx.x == 0 && blockIdx.y == 0 && threadIdx.x == 0) *ts_out = s_t;
-  const int lane = threadIdx.x & 63, w = threadIdx.x >> 6;
-  const int r = lane & 15, tc = lane >> 4;
-  const int64_t row = (int64_t)blockIdx.y * 64 + 16 * w + r;
-  const int64_t col0 = (int64_t)blockIdx.x * 64 + 16 * tc;
-  const bool valid = row < rows && col0 < cols;  // whole tiles are in or out
-  float z[16];
-  if (valid) {
-    const v4u* p = reinterpret_cast<const v4u*>(x + row * cols + col0);
-    const v4u a = ld_(p), b = ld_(p + 1);
-    const uint32_t wds[8] = {a.x, a.y, a.z, a.w, b.x, b.y, b.z, b.w};
+  const int64_t r0 = (int64_t)blockIdx.y * kColTileR, c0 = (int64_t)blockIdx.x * kColTileC;
+  const int cg = threadIdx.x & 15, rg = threadIdx.x >> 4;
+  const int64_t rr = r0 + 16 * rg, cc = c0 + 8 * cg;
+  // rows and cols are multiples of 16: a lane pair is in range together
+  if (rr < rows && cc < cols) {
+    Tile16x8 t;
+    tile_load(t, x, cols, rr, cc);
+    // block amax on the bf16 magnitudes (their bit patterns order like the
+    // values), two per 32-bit lane op, then the partner lane's half
+    uint32_t mp = 0;
 #pragma unroll
-    for (int j = 0; j < 8; ++j) { z[2 * j] = bf16_lo(wds[j]); z[2 * j + 1] = bf16_hi(wds[j]); }
-  } else {
+    for (int i = 0; i < 16; ++i) {
+      mp = pk_max_u16(mp, t.row[i].x & 0x7FFF7FFFu);
+      mp = pk_max_u16(mp, t.row[i].y & 0x7FFF7FFFu);
+      mp = pk_max_u16(mp, t.row[i].z & 0x7FFF7FFFu);
+      mp = pk_max_u16(mp, t.row[i].w & 0x7FFF7FFFu);
+    }
+    float m = fmaxf(bf16_lo(mp), bf16_hi(mp));
+    m = fmaxf(m, __shfl_xor(m, 1, 64));
+    const BlockScale b = block_scale(m, s_t, t6);
+    uint32_t q[16];
 #pragma unroll
-    for (int j = 0; j < 16; ++j) z[j] = 0.0f;
-  }
-  float m = 0.0f;
+    for (int i = 0; i < 16; ++i) {
+      const v4u w = t.row[i];
+      float z[8] = {bf16_lo(w.x), bf16_hi(w.x), bf16_lo(w.y), bf16_hi(w.y),
+                    bf16_lo(w.z), bf16_hi(w.z), bf16_lo(w.w), bf16_hi(w.w)};
+      const int64_t row = rr + i;
+      q[i] = SR ? encode8_sr(z, b.r, sr_words(seed, stream_id,
+                                               (uint64_t)row * (uint64_t)cols + (uint64_t)cc))
+                : encode8_rtn(z, b.r);
+      q[i] = select_zero_block(b.code, q[i], z);
+      *reinterpret_cast<uint32_t*>(codes + row * (cols / 2) + cc / 2) = q[i];
+    }
+    if ((cg & 1) == 0) {
+      scales[(rr / 16) * (cols / 16) + cc / 16] = (uint8_t)b.code;
+      if (scales_t != nullptr) scales_t[(cc / 16) * (rows / 16) + rr / 16] = (uint8_t)b.code;
+    }
+    if (codes_t != nullptr) {
+      uint32_t lo[8], hi[8];
+      nibble_transpose8(q, lo);       // rows rr .. rr+7 of each column
+      nibble_transpose8(q + 8, hi);   // rows rr+8 .. rr+15
 #pragma unroll
-  for (int j = 0; j < 16; ++j) m = fmaxf(m, __builtin_fabsf(z[j]));
-#pragma unroll
-  for (int off = 1; off < 16; off <<= 1) m = fmaxf(m, __shfl_xor(m, off, 64));
-  const BlockScale bs = block_scale(m, s_t, t6);
-  uint32_t q0, q1;
-  if (SR) {
-    const uint64_t n0 = (uint64_t)row * (uint64_t)cols + (uint64_t)col0;
-    q0 = encode8_sr(z, bs.r, sr_words(seed, stream_id, n0));
-    q1 = encode8_sr(z + 8, bs.r, sr_words(seed, stream_id, n0 + 8));
-  } else {
-    q0 = encode8_rtn(z, bs.r);
-    q1 = encode8_rtn(z + 8, bs.r);
-  }
-  q0 = select_zero_block(bs.code, q0, z);
-  q1 = select_zero_block(bs.code, q1, z + 8);
-  if (valid) {
-    // 8-byte pieces: plain (write-back) stores so L2 merges them into lines
-    *reinterpret_cast<v2u*>(codes + row * (cols / 2) + col0 / 2) = v2u{q0, q1};
-    if (r == 0) {
-      scales[(row / 16) * (cols / 16) + col0 / 16] = (uint8_t)bs.code;
-      if (scales_t != nullptr) scales_t[(col0 / 16) * (rows / 16) + row / 16] = (uint8_t)bs.code;
+      for (int c = 0; c < 8; ++c) lds_codes[8 * cg + c][rg] = v2u{lo[c], hi[c]};
     }
   }
   if (codes_t == nullptr) return;  // uniform across the grid
-#pragma unroll
-  for (int j = 0; j < 16; ++j) {
-    const uint32_t q = j < 8 ? q0 : q1;
-    lds_t[16 * tc + j][16 * w + r] = (uint8_t)((q >> (4 * (j & 7))) & 0xFu);
-  }
   __syncthreads();
-  // thread t packs column t/4, rows 16*(t%4) .. +15 -> 8 bytes of codes_t
-  const int c = threadIdx.x >> 2, qd = threadIdx.x & 3;
-  const int64_t oc = (int64_t)blockIdx.x * 64 + c;
-  const int64_t orow = (int64_t)blockIdx.y * 64 + 16 * qd;
-  if (oc < cols && orow < rows) {
-    uint32_t lo = 0, hi = 0;
+  // 2048 (column, row-group) pieces per tile; 16 consecutive threads write one
+  // column's 128 contiguous code bytes
+  const int64_t ld_t = rows / 2;
 #pragma unroll
-    for (int j = 0; j < 8; ++j) {
-      lo |= (uint32_t)lds_t[c][16 * qd + j] << (4 * j);
-      hi |= (uint32_t)lds_t[c][16 * qd + 8 + j] << (4 * j);
-    }
-    *reinterpret_cast<v2u*>(codes_t + oc * (rows / 2) + orow / 2) = v2u{lo, hi};
+  for (int j = 0; j < (kColTileC * kColTileR / 16) / kThreads; ++j) {
+    const int p = threadIdx.x + kThreads * j;
+    const int col = p >> 4, g = p & 15;
+    const int64_t oc = c0 + col, orow = r0 + 16 * g;
+    if (oc < cols && orow < rows)
+      st_(lds_codes[col][g], reinterpret_cast<v2u*>(codes_t + oc * ld_t + orow / 2));
   }
 }
 
@@ -479,7 +503,8 @@ hipError_t launch_quant_row_rht(const void* x, int64_t rows, int64_t cols, uint6
 hipError_t launch_quant_2d(const void* x, int64_t rows, int64_t cols, const float* amax, bool sr,
                            uint64_t seed, uint32_t stream_id, uint8_t* codes, uint8_t* codes_t,
                            uint8_t* scales, uint8_t* scales_t, float* ts_out, hipStream_t s) {
-  const dim3 g((unsigned)((cols + 63) / 64), (unsigned)((rows + 63) / 64)), b(kThreads);
+  const dim3 g((unsigned)((cols + kColTileC - 1) / kColTileC),
+               (unsigned)((rows + kColTileR - 1) / kColTileR)), b(kThreads);
   const uint16_t* xp = reinterpret_cast<const uint16_t*>(x);
   if (sr)
     hipLaunchKernelGGL(k_quant_2d<true>, g, b, 0, s, xp, rows, cols, amax, seed, stream_id,
