@@ -85,33 +85,6 @@ __device__ __forceinline__ uint32_t e2m1_rtn_index(float a) {
   return i;
 }
 
-// Stochastic rounding of a >= 0 with 16 random bits u: with lo <= a < hi the
-// neighbouring grid values and p = (a - lo)/(hi - lo), round up iff
-// u < p * 65536; a >= 6 gives index 7.  p * 65536 is exact, and the decision
-// is taken on integers from the binary32 fields of a:
-//   a < 0.5            : lo = 0,   gap 0.5 -> p*65536 = a * 2^17 (exact float)
-//   0.5 <= a < 1       : lo = 0.5, gap 0.5 -> p = mantissa / 2^23
-//   1 <= a < 6 (binade [2^e, 2^(e+1)), e = 0..2): the grid points are 2^e and
-//     1.5 * 2^e, so mantissa bit 22 picks the half-binade (the lower grid
-//     point) and p = (mantissa & (2^22 - 1)) / 2^22.
-// Round up iff u * 2^(23-16) < mantissa (first case: u < a * 2^17), resp.
-// u * 2^(22-16) < low 22 mantissa bits.
-__device__ __forceinline__ uint32_t e2m1_sr_index(float a, uint32_t u) {
-  a = a < 6.0f ? a : 6.0f;
-  const uint32_t bits = __float_as_uint(a);
-  const int d = (int)(bits >> 23) - 126;  // binade of a relative to [0.5, 1)
-  const uint32_t mant = bits & 0x7FFFFFu;
-  // Lower grid index without branches: 2d + bit 22 for d >= 1 (2..7), 1 for
-  // d == 0 and 0 below -- the largest of 2d + bit 22, d + 1 and 0.
-  const int lo = max(max(2 * d + (int)(mant >> 22), d + 1), 0);
-  // From 0.5 up, p * 2^23: all 23 mantissa bits in [0.5, 1), the low 22
-  // doubled above 1, compared with u * 2^7.
-  const uint32_t f23 = d >= 1 ? (mant << 1) & 0x7FFFFFu : mant;
-  const bool up_int = (u << 7) < f23;
-  const bool up_small = (float)u < a * 131072.0f;
-  return (uint32_t)lo + ((d >= 0 ? up_int : up_small) ? 1u : 0u);
-}
-
 // ---------------------------------------------------------------------------
 // Philox4x32-10 -- [SC11]
 // ---------------------------------------------------------------------------
@@ -123,9 +96,10 @@ __device__ __forceinline__ u32x4 philox4x32_10(u32x4 c, uint32_t k0, uint32_t k1
     uint64_t p0 = (uint64_t)0xD2511F53u * c.x;
     uint64_t p1 = (uint64_t)0xCD9E8D57u * c.z;
     u32x4 n;
-    n.x = (uint32_t)(p1 >> 32) ^ c.y ^ k0;
+    // three-input XOR in one instruction (truth table 0x96)
+    n.x = __builtin_amdgcn_bitop3_b32((uint32_t)(p1 >> 32), c.y, k0, 0x96);
     n.y = (uint32_t)p1;
-    n.z = (uint32_t)(p0 >> 32) ^ c.w ^ k1;
+    n.z = __builtin_amdgcn_bitop3_b32((uint32_t)(p0 >> 32), c.w, k1, 0x96);
     n.w = (uint32_t)p0;
     c = n;
     k0 += 0x9E3779B9u;
@@ -187,18 +161,47 @@ __device__ __forceinline__ uint32_t encode8_rtn(const float* z, float r) {
   return out;
 }
 
+// Stochastic rounding of v onto the E2M1 grid, returned as the grid value
+// itself (sign of v kept), with 16 random bits u: with lo <= |v| < hi the
+// neighbouring grid values and p = (|v| - lo)/(hi - lo), round away from zero
+// iff u < p * 65536; |v| >= 6 gives 6.  Above 0.5 the grid spacing within a
+// binade is a power of two, so the decision is an add-and-truncate on the
+// binary32 bits of a = min(|v|, 6):
+//   1 <= a < 6: the grid keeps 1 mantissa bit (2^e, 1.5 * 2^e).  The low 22
+//     bits f are p * 2^22, and f > u * 2^6  <=>  f + (2^22 - 1 - u * 2^6)
+//     carries into bit 22; clearing the low 22 bits then leaves hi or lo
+//     (the carry may run into the exponent: 1.75.. -> 2, and a < 6 tops out
+//     at 6).
+//   0.5 <= a < 1: no mantissa bit is kept (grid 0.5, 1): the same with 23
+//     bits and u * 2^7.
+//   a < 0.5 (grid 0, 0.5): p * 65536 = a * 2^17, an exact float; compared
+//     with u as a float.
+// The hardware FP4 encode then maps each grid value to its code exactly.
+__device__ __forceinline__ float e2m1_sr_value(float v, uint32_t u) {
+  const float a = fminf(__builtin_fabsf(v), 6.0f);
+  const uint32_t bits = __float_as_uint(a);
+  const bool ge1 = bits >= 0x3F800000u;
+  const uint32_t mask = ge1 ? 0x3FFFFFu : 0x7FFFFFu;
+  const uint32_t u7 = u << 7;
+  const uint32_t us = ge1 ? (u7 >> 1) : u7;
+  const uint32_t rounded = (bits + (mask - us)) & ~mask;
+  const uint32_t small = ((float)u < a * 131072.0f) ? 0x3F000000u : 0u;
+  const uint32_t mag = bits < 0x3F000000u ? small : rounded;
+  return __uint_as_float(mag | (__float_as_uint(v) & 0x80000000u));
+}
+
 // Stochastic rounding with the 8 16-bit halves of w (element j takes word
-// j/2, low half for even j).
+// j/2, low half for even j); codes packed as in encode8_rtn.
 __device__ __forceinline__ uint32_t encode8_sr(const float* z, float r, u32x4 w) {
-  uint32_t words[4] = {w.x, w.y, w.z, w.w};
   uint32_t out = 0;
-#pragma unroll
-  for (int j = 0; j < 8; ++j) {
-    float v = z[j] * r;
-    uint32_t s = (__float_as_uint(v) >> 31) << 3;
-    uint32_t u = (j & 1) ? (words[j >> 1] >> 16) : (words[j >> 1] & 0xFFFFu);
-    out |= (s | e2m1_sr_index(__builtin_fabsf(v), u)) << (4 * j);
-  }
+  out = __builtin_amdgcn_cvt_scalef32_pk_fp4_f32(
+      out, e2m1_sr_value(z[0] * r, w.x & 0xFFFFu), e2m1_sr_value(z[1] * r, w.x >> 16), 1.0f, 0);
+  out = __builtin_amdgcn_cvt_scalef32_pk_fp4_f32(
+      out, e2m1_sr_value(z[2] * r, w.y & 0xFFFFu), e2m1_sr_value(z[3] * r, w.y >> 16), 1.0f, 1);
+  out = __builtin_amdgcn_cvt_scalef32_pk_fp4_f32(
+      out, e2m1_sr_value(z[4] * r, w.z & 0xFFFFu), e2m1_sr_value(z[5] * r, w.z >> 16), 1.0f, 2);
+  out = __builtin_amdgcn_cvt_scalef32_pk_fp4_f32(
+      out, e2m1_sr_value(z[6] * r, w.w & 0xFFFFu), e2m1_sr_value(z[7] * r, w.w >> 16), 1.0f, 3);
   return out;
 }
 

@@ -13,6 +13,7 @@
 // Hadamard transforms, 2D block quantization, stochastic rounding); news item
 // "Soumith Chintala 发布 NVFP4 训练详解文章", section 三 (1D blocks for
 // activations and gradients, 2D for weights, RHT on Wgrad inputs).
+#include "gemm_tiles.h"
 #include "nvfp4_device.h"
 #include "nvfp4_kernels.h"
 
@@ -54,30 +55,34 @@ __device__ __forceinline__ uint32_t pk_max_u16(uint32_t a, uint32_t b) {
   return lo | (hi << 16);
 }
 
+// Each workgroup reads whole 32 KiB chunks (8 loads of 16 bytes per thread,
+// the lanes of a wave on consecutive 16-byte pieces); chunks are dealt to the
+// workgroups in turn.  On MI355X this runs at 0.72 of the HBM peak, against
+// 0.59 for a grid-stride loop whose loads in flight lie a whole grid apart.
+constexpr int kAmaxU = 8;
+constexpr int64_t kAmaxChunk = (int64_t)kAmaxU * kThreads;  // 16-byte vectors
+
+__device__ __forceinline__ uint32_t amax_acc(uint32_t m, const v4u v) {
+  m = pk_max_u16(m, v.x & 0x7FFF7FFFu);
+  m = pk_max_u16(m, v.y & 0x7FFF7FFFu);
+  m = pk_max_u16(m, v.z & 0x7FFF7FFFu);
+  return pk_max_u16(m, v.w & 0x7FFF7FFFu);
+}
+
 __global__ __launch_bounds__(kThreads) void k_amax(const v4u* __restrict__ x, int64_t nvec,
                                                      uint32_t* __restrict__ out) {
-  constexpr int U = 8;  // 16-byte loads in flight per thread
   uint32_t m = 0;
-  const int64_t stride = (int64_t)gridDim.x * kThreads;
-  int64_t i = (int64_t)blockIdx.x * kThreads + threadIdx.x;
-  for (; i + (U - 1) * stride < nvec; i += U * stride) {
-    v4u v[U];
+  for (int64_t c = (int64_t)blockIdx.x * kAmaxChunk; c < nvec;
+       c += (int64_t)gridDim.x * kAmaxChunk) {
+    if (c + kAmaxChunk <= nvec) {
+      v4u v[kAmaxU];
 #pragma unroll
-    for (int u = 0; u < U; ++u) v[u] = ld_(&x[i + u * stride]);
+      for (int u = 0; u < kAmaxU; ++u) v[u] = ld_(&x[c + u * kThreads + threadIdx.x]);
 #pragma unroll
-    for (int u = 0; u < U; ++u) {
-      m = pk_max_u16(m, v[u].x & 0x7FFF7FFFu);
-      m = pk_max_u16(m, v[u].y & 0x7FFF7FFFu);
-      m = pk_max_u16(m, v[u].z & 0x7FFF7FFFu);
-      m = pk_max_u16(m, v[u].w & 0x7FFF7FFFu);
+      for (int u = 0; u < kAmaxU; ++u) m = amax_acc(m, v[u]);
+    } else {
+      for (int64_t i = c + threadIdx.x; i < nvec; i += kThreads) m = amax_acc(m, ld_(&x[i]));
     }
-  }
-  for (; i < nvec; i += stride) {
-    const v4u v = ld_(&x[i]);
-    m = pk_max_u16(m, v.x & 0x7FFF7FFFu);
-    m = pk_max_u16(m, v.y & 0x7FFF7FFFu);
-    m = pk_max_u16(m, v.z & 0x7FFF7FFFu);
-    m = pk_max_u16(m, v.w & 0x7FFF7FFFu);
   }
   uint32_t lo = m & 0xFFFFu, hi = m >> 16;
   uint32_t bf = lo > hi ? lo : hi;
@@ -145,6 +150,14 @@ __global__ __launch_bounds__(kThreads) void k_amax_rht(const uint16_t* __restric
 // ---------------------------------------------------------------------------
 // 1D rowwise: blocks of 16 along cols, two lanes per block
 // ---------------------------------------------------------------------------
+// Each workgroup takes 16 KiB chunks of the input (4 vectors of 8 elements
+// per thread, loaded before any is encoded), dealt to the workgroups in turn.
+// A vector's partner (i ^ 1, the other half of its 16-block) is always in the
+// same wave and in range together with it: chunks start at even vectors and
+// the vector count is even (cols % 16 == 0).
+constexpr int kRowU = 4;
+constexpr int64_t kRowChunk = (int64_t)kRowU * kThreads;
+
 template <bool SR>
 __global__ __launch_bounds__(kThreads) void k_quant_row(
     const v4u* __restrict__ x, int64_t nvec, const float* __restrict__ amax,
@@ -153,23 +166,34 @@ __global__ __launch_bounds__(kThreads) void k_quant_row(
   const float s_t = tensor_scale_from_amax(*amax);
   const float t6 = 6.0f * s_t;
   if (blockIdx.x == 0 && threadIdx.x == 0) *ts_out = s_t;
-  const int64_t stride = (int64_t)gridDim.x * kThreads;  // even: lane pairs stay together
-  for (int64_t i = (int64_t)blockIdx.x * kThreads + threadIdx.x; i < nvec; i += stride) {
-    const v4u v = ld_(&x[i]);
-    float z[8] = {bf16_lo(v.x), bf16_hi(v.x), bf16_lo(v.y), bf16_hi(v.y),
-                  bf16_lo(v.z), bf16_hi(v.z), bf16_lo(v.w), bf16_hi(v.w)};
-    float m = 0.0f;
+  for (int64_t c = (int64_t)blockIdx.x * kRowChunk; c < nvec;
+       c += (int64_t)gridDim.x * kRowChunk) {
+    v4u vs[kRowU];
 #pragma unroll
-    for (int j = 0; j < 8; ++j) m = fmaxf(m, __builtin_fabsf(z[j]));
-    m = fmaxf(m, __shfl_xor(m, 1, 64));
-    const BlockScale b = block_scale(m, s_t, t6);
-    // computed for every block (a zero scale gives inf/NaN here, discarded by
-    // the select), which keeps the lanes of a wave on one path
-    uint32_t q = SR ? encode8_sr(z, b.r, sr_words(seed, stream_id, (uint64_t)i * 8u))
-                    : encode8_rtn(z, b.r);
-    q = select_zero_block(b.code, q, z);
-    st_(q, &codes[i]);
-    if ((i & 1) == 0) scales[i >> 1] = (uint8_t)b.code;
+    for (int u = 0; u < kRowU; ++u) {
+      const int64_t i = c + u * kThreads + threadIdx.x;
+      if (i < nvec) vs[u] = ld_(&x[i]);
+    }
+#pragma unroll
+    for (int u = 0; u < kRowU; ++u) {
+      const int64_t i = c + u * kThreads + threadIdx.x;
+      if (i >= nvec) continue;
+      const v4u v = vs[u];
+      float z[8] = {bf16_lo(v.x), bf16_hi(v.x), bf16_lo(v.y), bf16_hi(v.y),
+                    bf16_lo(v.z), bf16_hi(v.z), bf16_lo(v.w), bf16_hi(v.w)};
+      float m = 0.0f;
+#pragma unroll
+      for (int j = 0; j < 8; ++j) m = fmaxf(m, __builtin_fabsf(z[j]));
+      m = fmaxf(m, __shfl_xor(m, 1, 64));
+      const BlockScale b = block_scale(m, s_t, t6);
+      // computed for every block (a zero scale gives inf/NaN here, discarded
+      // by the select), which keeps the lanes of a wave on one path
+      uint32_t q = SR ? encode8_sr(z, b.r, sr_words(seed, stream_id, (uint64_t)i * 8u))
+                      : encode8_rtn(z, b.r);
+      q = select_zero_block(b.code, q, z);
+      st_(q, &codes[i]);
+      if ((i & 1) == 0) scales[i >> 1] = (uint8_t)b.code;
+    }
   }
 }
 
@@ -181,6 +205,29 @@ __global__ __launch_bounds__(kThreads) void k_quant_row(
 // contiguous bytes each.  Codes are staged in LDS as [column][row/2] so the
 // stores run along the output's contiguous dimension.
 constexpr int kColTileR = 256, kColTileC = 128;
+
+// Tile of the 1-D grid over ceil(rows/256) x ceil(cols/128) workgroup tiles.
+// Workgroups are dealt round-robin to the 8 XCDs, each with its own L2, so
+// block b is renumbered so that every XCD owns a contiguous range of tiles,
+// taken in bands of 8 tile-rows with the rows fastest.  Neighbouring tiles
+// write pieces of the same cache lines (8-byte rowwise scale pieces, 16-byte
+// colwise ones, 64-byte rowwise code pieces); this way the pieces meet in
+// one L2 while both tiles are resident rather than reaching HBM as separate
+// partial-line writes.
+__device__ __forceinline__ void quant_tile(int64_t rows, int64_t cols, int64_t& r0, int64_t& c0) {
+  const int64_t gy = (rows + kColTileR - 1) / kColTileR, gx = (cols + kColTileC - 1) / kColTileC;
+  const int64_t n = gx * gy, b = blockIdx.x, per = n / kXcds;
+  const int64_t t = b < per * kXcds ? (b % kXcds) * per + b / kXcds : b;
+  int64_t ty, tx;
+  grouped(t, gy, gx, ty, tx);
+  r0 = ty * kColTileR;
+  c0 = tx * kColTileC;
+}
+
+static dim3 quant_tile_grid(int64_t rows, int64_t cols) {
+  return dim3((unsigned)(((rows + kColTileR - 1) / kColTileR) *
+                         ((cols + kColTileC - 1) / kColTileC)));
+}
 
 // ROW: the same read also yields the rowwise 1D operand of x (blocks of 16
 // along cols: the two lanes holding a row's adjacent 8-column pieces), with
@@ -204,9 +251,10 @@ __global__ __launch_bounds__(kThreads) void k_quant_col(
   __shared__ uint8_t lds_scales[kColTileC][kColTileR / 16];
   const float s_t = tensor_scale_from_amax(*amax);
   const float t6 = 6.0f * s_t;
-  if (blockIdx.x == 0 && blockIdx.y == 0 && threadIdx.x == 0) *ts_out = s_t;
+  if (blockIdx.x == 0 && threadIdx.x == 0) *ts_out = s_t;
   const uint32_t signs = RHT ? rht_sign_bits(rht_seed) : 0u;
-  const int64_t r0 = (int64_t)blockIdx.y * kColTileR, c0 = (int64_t)blockIdx.x * kColTileC;
+  int64_t r0, c0;
+  quant_tile(rows, cols, r0, c0);
   const int cg = threadIdx.x & 15, rg = threadIdx.x >> 4;
   const int64_t rr = r0 + 16 * rg, cc = c0 + 8 * cg;
   if (rr < rows && cc < cols) {
@@ -218,7 +266,7 @@ __global__ __launch_bounds__(kThreads) void k_quant_col(
       // both halves are in range together)
       const float s_r = tensor_scale_from_amax(*ro.amax);
       const float t6r = 6.0f * s_r;
-      if (blockIdx.x == 0 && blockIdx.y == 0 && threadIdx.x == 0) *ro.ts_out = s_r;
+      if (blockIdx.x == 0 && threadIdx.x == 0) *ro.ts_out = s_r;
 #pragma unroll
       for (int i = 0; i < 16; ++i) {
         const v4u w = t.row[i];
@@ -322,8 +370,9 @@ __global__ __launch_bounds__(kThreads) void k_quant_2d(
   __shared__ v2u lds_codes[kColTileC][kColTileR / 16];   // [column][row group]
   const float s_t = tensor_scale_from_amax(*amax);
   const float t6 = 6.0f * s_t;
-  if (blockIdx.x == 0 && blockIdx.y == 0 && threadIdx.x == 0) *ts_out = s_t;
-  const int64_t r0 = (int64_t)blockIdx.y * kColTileR, c0 = (int64_t)blockIdx.x * kColTileC;
+  if (blockIdx.x == 0 && threadIdx.x == 0) *ts_out = s_t;
+  int64_t r0, c0;
+  quant_tile(rows, cols, r0, c0);
   const int cg = threadIdx.x & 15, rg = threadIdx.x >> 4;
   const int64_t rr = r0 + 16 * rg, cc = c0 + 8 * cg;
   // rows and cols are multiples of 16: a lane pair is in range together
@@ -426,7 +475,8 @@ hipError_t launch_amax(const void* x, int64_t n_elems, float* out, hipStream_t s
   uint32_t* o = reinterpret_cast<uint32_t*>(out);
   hipLaunchKernelGGL(k_zero_u32, dim3(1), dim3(1), 0, s, o);
   const int64_t nvec = n_elems / 8;
-  hipLaunchKernelGGL(k_amax, dim3(grid_for(nvec / 8, 4)), dim3(kThreads), 0, s,
+  const int64_t chunks = (nvec + kAmaxChunk - 1) / kAmaxChunk;
+  hipLaunchKernelGGL(k_amax, dim3(grid_for(chunks * kThreads, 8)), dim3(kThreads), 0, s,
                      reinterpret_cast<const v4u*>(x), nvec, o);
   return hipGetLastError();
 }
@@ -452,7 +502,8 @@ hipError_t launch_quant_row(const void* x, int64_t rows, int64_t cols, const flo
                             bool sr, uint64_t seed, uint32_t stream_id, uint8_t* codes,
                             uint8_t* scales, float* ts_out, hipStream_t s) {
   const int64_t nvec = rows * cols / 8;
-  const dim3 g(grid_for(nvec, 16)), b(kThreads);
+  const int64_t chunks = (nvec + kRowChunk - 1) / kRowChunk;
+  const dim3 g(grid_for(chunks * kThreads, 8)), b(kThreads);
   const v4u* xv = reinterpret_cast<const v4u*>(x);
   uint32_t* cv = reinterpret_cast<uint32_t*>(codes);
   if (sr)
@@ -468,8 +519,7 @@ hipError_t launch_quant_col(const void* x, int64_t rows, int64_t cols, const flo
                             bool rht, uint64_t rht_seed, bool sr, uint64_t seed,
                             uint32_t stream_id, uint8_t* codes, uint8_t* scales, float* ts_out,
                             hipStream_t s) {
-  const dim3 g((unsigned)((cols + kColTileC - 1) / kColTileC),
-               (unsigned)((rows + kColTileR - 1) / kColTileR)), b(kThreads);
+  const dim3 g = quant_tile_grid(rows, cols), b(kThreads);
   const uint16_t* xp = reinterpret_cast<const uint16_t*>(x);
 #define NVFP4_COL(SRV, RHTV)                                                                  \
   hipLaunchKernelGGL((k_quant_col<SRV, RHTV, false>), g, b, 0, s, xp, rows, cols, amax,       \
@@ -487,8 +537,7 @@ hipError_t launch_quant_row_rht(const void* x, int64_t rows, int64_t cols, uint6
                                const float* amax_row, const float* amax_rht, uint8_t* codes_row,
                                uint8_t* scales_row, float* ts_row, uint8_t* codes_col,
                                uint8_t* scales_col, float* ts_col, hipStream_t s) {
-  const dim3 g((unsigned)((cols + kColTileC - 1) / kColTileC),
-               (unsigned)((rows + kColTileR - 1) / kColTileR)), b(kThreads);
+  const dim3 g = quant_tile_grid(rows, cols), b(kThreads);
   const uint16_t* xp = reinterpret_cast<const uint16_t*>(x);
   const RowOut ro{amax_row, stream_row, codes_row, scales_row, ts_row};
   if (sr)
@@ -503,8 +552,7 @@ hipError_t launch_quant_row_rht(const void* x, int64_t rows, int64_t cols, uint6
 hipError_t launch_quant_2d(const void* x, int64_t rows, int64_t cols, const float* amax, bool sr,
                            uint64_t seed, uint32_t stream_id, uint8_t* codes, uint8_t* codes_t,
                            uint8_t* scales, uint8_t* scales_t, float* ts_out, hipStream_t s) {
-  const dim3 g((unsigned)((cols + kColTileC - 1) / kColTileC),
-               (unsigned)((rows + kColTileR - 1) / kColTileR)), b(kThreads);
+  const dim3 g = quant_tile_grid(rows, cols), b(kThreads);
   const uint16_t* xp = reinterpret_cast<const uint16_t*>(x);
   if (sr)
     hipLaunchKernelGGL(k_quant_2d<true>, g, b, 0, s, xp, rows, cols, amax, seed, stream_id,
