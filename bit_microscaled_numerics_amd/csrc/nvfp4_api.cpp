@@ -32,6 +32,8 @@ int check_tensor(const void* x, int64_t rows, int64_t cols, const char* name) {
   if (rows <= 0 || cols <= 0 || rows % 16 || cols % 16)
     return fail(NVFP4_ERR_SHAPE, "%s: rows=%lld cols=%lld must be positive multiples of 16", name,
                 (long long)rows, (long long)cols);
+  if (cols > (int64_t(1) << 28))
+    return fail(NVFP4_ERR_SHAPE, "%s: cols=%lld exceeds 2^28", name, (long long)cols);
   if (!aligned(x, 16)) return fail(NVFP4_ERR_ALIGN, "%s must be 16-byte aligned", name);
   return NVFP4_OK;
 }

@@ -57,6 +57,14 @@ __device__ __forceinline__ uint32_t e4m3_from_float(float x) {
   return c > 0x7Eu ? 0x7Eu : c;
 }
 
+// The same encode by the gfx950 FP8 convert (OCP E4M3, round to nearest
+// even, subnormals kept) after clamping to 448: equal to e4m3_from_float for
+// every binary32 in [0, 448] (all 1.14e9 patterns compared on MI355X), and
+// both give 0x7E above.
+__device__ __forceinline__ uint32_t e4m3_code(float x) {
+  return (uint32_t)__builtin_amdgcn_cvt_pk_fp8_f32(fminf(x, 448.0f), 0.0f, 0, false) & 0xFFu;
+}
+
 // E4M3FN code (0..0x7E) -> binary32 (branch-free: both forms are computed
 // and the exponent field selects; the subnormal form is m * 2^-9, exact).
 __device__ __forceinline__ float e4m3_to_float(uint32_t c) {
@@ -218,19 +226,58 @@ __device__ __forceinline__ uint32_t select_zero_block(uint32_t code, uint32_t q,
   return code == 0u ? encode8_zero(z) : q;
 }
 
+__device__ __forceinline__ float tensor_scale_from_amax(float amax_t) {
+  return amax_t > 0.0f ? amax_t / kScaleDen : 1.0f;
+}
+
 // Block scale code and reciprocal element scale from a block amax.
 struct BlockScale { uint32_t code; float r; };
 
-__device__ __forceinline__ BlockScale block_scale(float amax_b, float s_t, float t6) {
-  BlockScale b;
-  b.code = e4m3_from_float(amax_b / t6);
-  float d = e4m3_to_float(b.code) * s_t;
-  b.r = 1.0f / d;
-  return b;
+// Per-tensor constants of the block-scale step.  rtab (LDS) holds the 127
+// possible reciprocals r = 1 / (float(E) * s_t), E4M3 codes 0 .. 0x7E, each
+// computed exactly as the per-block formula would, so a lookup returns the
+// same binary32 as the division it replaces.
+constexpr int kE4m3Codes = 127;
+
+struct ScaleCtx {
+  float s_t, t6, rt6;  // tensor scale, 6 * s_t, and the rounded 1 / t6
+  const float* rtab;
+};
+
+// Every thread gets the constants; the thread with slot e < 127 fills
+// rtab[e].  The caller synchronises the workgroup before the first lookup.
+__device__ __forceinline__ ScaleCtx scale_ctx(float amax_t, float* rtab, int slot) {
+  ScaleCtx c;
+  c.s_t = tensor_scale_from_amax(amax_t);
+  c.t6 = 6.0f * c.s_t;
+  c.rt6 = 1.0f / c.t6;
+  c.rtab = rtab;
+  if (slot >= 0 && slot < kE4m3Codes) rtab[slot] = 1.0f / (e4m3_to_float((uint32_t)slot) * c.s_t);
+  return c;
 }
 
-__device__ __forceinline__ float tensor_scale_from_amax(float amax_t) {
-  return amax_t > 0.0f ? amax_t / kScaleDen : 1.0f;
+// E4M3 code of the correctly rounded quotient q = amax_b / t6.  q' =
+// amax_b * fl(1/t6) is within 3 ulps of q (two roundings of relative size
+// 2^-24 each, plus q's own half ulp), so the two give the same code unless a
+// point where the code changes lies between them.  Those points are the
+// midpoints between E4M3 values: binary32 patterns whose low 20 bits are
+// 0x80000 above 2^-6 (3 significand bits kept) and 0 below it (the
+// subnormal steps of 2^-9 put the midpoints at odd multiples of 2^-10).  If
+// q' lies within 8 patterns of such a point (about one block in 2^16), the
+// quotient is taken by the correctly rounded division instead.
+__device__ __forceinline__ uint32_t scale_code(float amax_b, const ScaleCtx& c) {
+  float q = amax_b * c.rt6;
+  const uint32_t b = __float_as_uint(q);
+  const uint32_t centre = b < 0x3C800000u ? 0u : 0x80000u;
+  if (((b - centre + 8u) & 0xFFFFFu) < 16u) q = amax_b / c.t6;
+  return e4m3_code(q);
+}
+
+__device__ __forceinline__ BlockScale block_scale(float amax_b, const ScaleCtx& c) {
+  BlockScale b;
+  b.code = scale_code(amax_b, c);
+  b.r = c.rtab[b.code];
+  return b;
 }
 
 // ---------------------------------------------------------------------------

@@ -163,9 +163,10 @@ __global__ __launch_bounds__(kThreads) void k_quant_row(
     const v4u* __restrict__ x, int64_t nvec, const float* __restrict__ amax,
     uint64_t seed, uint32_t stream_id, uint32_t* __restrict__ codes,
     uint8_t* __restrict__ scales, float* __restrict__ ts_out) {
-  const float s_t = tensor_scale_from_amax(*amax);
-  const float t6 = 6.0f * s_t;
-  if (blockIdx.x == 0 && threadIdx.x == 0) *ts_out = s_t;
+  __shared__ float rtab[kE4m3Codes];
+  const ScaleCtx sc = scale_ctx(*amax, rtab, threadIdx.x);
+  if (blockIdx.x == 0 && threadIdx.x == 0) *ts_out = sc.s_t;
+  __syncthreads();
   for (int64_t c = (int64_t)blockIdx.x * kRowChunk; c < nvec;
        c += (int64_t)gridDim.x * kRowChunk) {
     v4u vs[kRowU];
@@ -185,7 +186,7 @@ __global__ __launch_bounds__(kThreads) void k_quant_row(
 #pragma unroll
       for (int j = 0; j < 8; ++j) m = fmaxf(m, __builtin_fabsf(z[j]));
       m = fmaxf(m, __shfl_xor(m, 1, 64));
-      const BlockScale b = block_scale(m, s_t, t6);
+      const BlockScale b = block_scale(m, sc);
       // computed for every block (a zero scale gives inf/NaN here, discarded
       // by the select), which keeps the lanes of a wave on one path
       uint32_t q = SR ? encode8_sr(z, b.r, sr_words(seed, stream_id, (uint64_t)i * 8u))
@@ -249,9 +250,15 @@ __global__ __launch_bounds__(kThreads) void k_quant_col(
     RowOut ro) {
   __shared__ v2u lds_codes[kColTileC][kColTileR / 16];   // 8 bytes = 16 codes per block
   __shared__ uint8_t lds_scales[kColTileC][kColTileR / 16];
-  const float s_t = tensor_scale_from_amax(*amax);
-  const float t6 = 6.0f * s_t;
-  if (blockIdx.x == 0 && threadIdx.x == 0) *ts_out = s_t;
+  __shared__ float rtab[kE4m3Codes], rtab_row[ROW ? kE4m3Codes : 1];
+  const ScaleCtx sc = scale_ctx(*amax, rtab, threadIdx.x);
+  if (blockIdx.x == 0 && threadIdx.x == 0) *ts_out = sc.s_t;
+  ScaleCtx sr_ctx;
+  if (ROW) {
+    sr_ctx = scale_ctx(*ro.amax, rtab_row, (int)threadIdx.x - 128);
+    if (blockIdx.x == 0 && threadIdx.x == 0) *ro.ts_out = sr_ctx.s_t;
+  }
+  __syncthreads();
   const uint32_t signs = RHT ? rht_sign_bits(rht_seed) : 0u;
   int64_t r0, c0;
   quant_tile(rows, cols, r0, c0);
@@ -263,10 +270,12 @@ __global__ __launch_bounds__(kThreads) void k_quant_col(
     if (ROW) {
       // rows rr .. rr+15, columns cc .. cc+7: half of a 16-wide block each;
       // the partner lane (cg ^ 1) holds the other half (cols % 16 == 0, so
-      // both halves are in range together)
-      const float s_r = tensor_scale_from_amax(*ro.amax);
-      const float t6r = 6.0f * s_r;
-      if (blockIdx.x == 0 && threadIdx.x == 0) *ro.ts_out = s_r;
+      // both halves are in range together).  Row i's outputs sit at a
+      // uniform offset i * pitch from row rr's.
+      uint8_t* const rcodes = ro.codes + rr * (cols / 2) + cc / 2;
+      uint8_t* const rscales = ro.scales + rr * (cols / 16) + cc / 16;
+      const uint32_t pc = (uint32_t)(cols / 2), ps = (uint32_t)(cols / 16);  // 16 rows < 2^32
+      const uint64_t n_row0 = (uint64_t)rr * (uint64_t)cols + (uint64_t)cc;
 #pragma unroll
       for (int i = 0; i < 16; ++i) {
         const v4u w = t.row[i];
@@ -276,16 +285,16 @@ __global__ __launch_bounds__(kThreads) void k_quant_col(
 #pragma unroll
         for (int j = 0; j < 8; ++j) m = fmaxf(m, __builtin_fabsf(z[j]));
         m = fmaxf(m, __shfl_xor(m, 1, 64));
-        const BlockScale b = block_scale(m, s_r, t6r);
-        const int64_t row = rr + i;
+        const BlockScale b = block_scale(m, sr_ctx);
         uint32_t q = SR ? encode8_sr(z, b.r, sr_words(seed, ro.stream_id,
-                                                      (uint64_t)row * (uint64_t)cols + (uint64_t)cc))
+                                                      n_row0 + (uint64_t)i * (uint64_t)cols))
                         : encode8_rtn(z, b.r);
         q = select_zero_block(b.code, q, z);
-        *reinterpret_cast<uint32_t*>(ro.codes + row * (cols / 2) + cc / 2) = q;
-        if ((cg & 1) == 0) ro.scales[row * (cols / 16) + cc / 16] = (uint8_t)b.code;
+        *reinterpret_cast<uint32_t*>(rcodes + i * pc) = q;
+        if ((cg & 1) == 0) rscales[i * ps] = (uint8_t)b.code;
       }
     }
+    const uint64_t n_col0 = (uint64_t)cc * (uint64_t)rows + (uint64_t)rr;
 #pragma unroll
     for (int c = 0; c < 8; ++c) {
       float v[16];
@@ -294,10 +303,10 @@ __global__ __launch_bounds__(kThreads) void k_quant_col(
       float m = 0.0f;
 #pragma unroll
       for (int j = 0; j < 16; ++j) m = fmaxf(m, __builtin_fabsf(v[j]));
-      const BlockScale b = block_scale(m, s_t, t6);
+      const BlockScale b = block_scale(m, sc);
       uint32_t q0, q1;
       if (SR) {
-        const uint64_t n0 = (uint64_t)(cc + c) * (uint64_t)rows + (uint64_t)rr;
+        const uint64_t n0 = n_col0 + (uint64_t)c * (uint64_t)rows;
         q0 = encode8_sr(v, b.r, sr_words(seed, stream_id, n0));
         q1 = encode8_sr(v + 8, b.r, sr_words(seed, stream_id, n0 + 8));
       } else {
@@ -368,9 +377,10 @@ __global__ __launch_bounds__(kThreads) void k_quant_2d(
     uint8_t* __restrict__ codes, uint8_t* __restrict__ codes_t, uint8_t* __restrict__ scales,
     uint8_t* __restrict__ scales_t, float* __restrict__ ts_out) {
   __shared__ v2u lds_codes[kColTileC][kColTileR / 16];   // [column][row group]
-  const float s_t = tensor_scale_from_amax(*amax);
-  const float t6 = 6.0f * s_t;
-  if (blockIdx.x == 0 && threadIdx.x == 0) *ts_out = s_t;
+  __shared__ float rtab[kE4m3Codes];
+  const ScaleCtx sc = scale_ctx(*amax, rtab, threadIdx.x);
+  if (blockIdx.x == 0 && threadIdx.x == 0) *ts_out = sc.s_t;
+  __syncthreads();
   int64_t r0, c0;
   quant_tile(rows, cols, r0, c0);
   const int cg = threadIdx.x & 15, rg = threadIdx.x >> 4;
@@ -391,19 +401,22 @@ __global__ __launch_bounds__(kThreads) void k_quant_2d(
     }
     float m = fmaxf(bf16_lo(mp), bf16_hi(mp));
     m = fmaxf(m, __shfl_xor(m, 1, 64));
-    const BlockScale b = block_scale(m, s_t, t6);
+    const BlockScale b = block_scale(m, sc);
     uint32_t q[16];
+    // row i's codes sit at a uniform offset i * pitch from row rr's
+    uint8_t* const rcodes = codes + rr * (cols / 2) + cc / 2;
+    const uint32_t pc = (uint32_t)(cols / 2);  // 16 rows of codes span < 2^32 bytes
+    const uint64_t n_row0 = (uint64_t)rr * (uint64_t)cols + (uint64_t)cc;
 #pragma unroll
     for (int i = 0; i < 16; ++i) {
       const v4u w = t.row[i];
       float z[8] = {bf16_lo(w.x), bf16_hi(w.x), bf16_lo(w.y), bf16_hi(w.y),
                     bf16_lo(w.z), bf16_hi(w.z), bf16_lo(w.w), bf16_hi(w.w)};
-      const int64_t row = rr + i;
       q[i] = SR ? encode8_sr(z, b.r, sr_words(seed, stream_id,
-                                               (uint64_t)row * (uint64_t)cols + (uint64_t)cc))
+                                               n_row0 + (uint64_t)i * (uint64_t)cols))
                 : encode8_rtn(z, b.r);
       q[i] = select_zero_block(b.code, q[i], z);
-      *reinterpret_cast<uint32_t*>(codes + row * (cols / 2) + cc / 2) = q[i];
+      *reinterpret_cast<uint32_t*>(rcodes + i * pc) = q[i];
     }
     if ((cg & 1) == 0) {
       scales[(rr / 16) * (cols / 16) + cc / 16] = (uint8_t)b.code;

@@ -34,7 +34,8 @@
  *    allocates, frees or synchronises.  `stream` is a hipStream_t (NULL = the
  *    default stream); all work is enqueued on it, in order.
  *  - bf16 inputs are row-major [rows][cols] with 16-byte aligned base
- *    pointers; rows and cols are positive multiples of 16.
+ *    pointers; rows and cols are positive multiples of 16, and cols is at
+ *    most 2^28 (16 rows of packed codes then span less than 2^32 bytes).
  *  - Packed codes hold two elements per byte, the even-k element in the low
  *    nibble; code = sign << 3 | magnitude index (0, .5, 1, 1.5, 2, 3, 4, 6).
  *  - Arguments are validated before anything is enqueued; on error nothing
@@ -58,7 +59,7 @@ extern "C" {
 enum {
   NVFP4_OK = 0,
   NVFP4_ERR_NULL = -1,   /* a required pointer is NULL */
-  NVFP4_ERR_SHAPE = -2,  /* a dimension is not a positive multiple of 16, or mismatched */
+  NVFP4_ERR_SHAPE = -2,  /* a dimension is not a positive multiple of 16, too large, or mismatched */
   NVFP4_ERR_ALIGN = -3,  /* a base pointer or leading dimension is misaligned */
   NVFP4_ERR_ARG = -4,    /* an enum argument is out of range */
   NVFP4_ERR_LAUNCH = -5  /* the HIP runtime refused a launch */

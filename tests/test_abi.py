@@ -51,6 +51,7 @@ def test_amax_validation(lib):
     assert lib.nvfp4_amax(FAKE, 16, 24, FAKE, None) == nv.NVFP4_ERR_SHAPE
     assert lib.nvfp4_amax(FAKE, 0, 16, FAKE, None) == nv.NVFP4_ERR_SHAPE
     assert lib.nvfp4_amax(FAKE, -16, 16, FAKE, None) == nv.NVFP4_ERR_SHAPE
+    assert lib.nvfp4_amax(FAKE, 16, (1 << 28) + 16, FAKE, None) == nv.NVFP4_ERR_SHAPE
     assert lib.nvfp4_amax(MIS, 16, 16, FAKE, None) == nv.NVFP4_ERR_ALIGN
     assert lib.nvfp4_amax(FAKE, 16, 16, None, None) == nv.NVFP4_ERR_NULL
     assert "16" in lib.nvfp4_last_error().decode() or lib.nvfp4_last_error()
