@@ -307,7 +307,10 @@ __device__ __forceinline__ void store_c(const GemmArgs& g, float16v (&acc)[WM][W
           mag = max(mag, h & 0x7FFFu);
         } else {
           float* dst = &g.c[row * g.ldc + col];
-          if (part < 0) *dst = val;
+          // whole tiles stream C out past the caches (it is not read again
+          // here, and cached it would displace operand rows that other tiles
+          // still read); a split tile adds its half into the zeroed output
+          if (part < 0) __builtin_nontemporal_store(val, dst);
           else atomicAdd(dst, val);
         }
       }
