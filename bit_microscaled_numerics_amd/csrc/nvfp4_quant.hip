@@ -24,7 +24,11 @@ constexpr int kThreads = 256;
 // ---------------------------------------------------------------------------
 // amax
 // ---------------------------------------------------------------------------
-__global__ void k_zero_u32(uint32_t* p) { *p = 0u; }
+// Zero one or two 32-bit words (the amax accumulators) in one launch.
+__global__ void k_zero_u32(uint32_t* p, uint32_t* q) {
+  *p = 0u;
+  if (q != nullptr) *q = 0u;
+}
 
 // Block-wide max of non-negative float bit patterns, then one atomic per
 // workgroup.  Non-negative binary32 values order like their bit patterns.
@@ -477,6 +481,16 @@ __global__ __launch_bounds__(kThreads) void k_dequant(
 // ---------------------------------------------------------------------------
 // launchers
 // ---------------------------------------------------------------------------
+// Workgroups for `chunks` equal pieces of work, at most per_cu per CU,
+// chosen so that every workgroup takes the same number of pieces (up to one)
+// instead of a last trip that only some of them make.
+static int balanced_grid(int64_t chunks, int per_cu) {
+  const int64_t cap = (int64_t)num_cus() * per_cu;
+  if (chunks <= cap) return (int)(chunks < 1 ? 1 : chunks);
+  const int64_t trips = (chunks + cap - 1) / cap;
+  return (int)((chunks + trips - 1) / trips);
+}
+
 static int grid_for(int64_t items, int per_cu) {
   int64_t g = (items + kThreads - 1) / kThreads;
   int64_t cap = (int64_t)num_cus() * per_cu;
@@ -486,10 +500,10 @@ static int grid_for(int64_t items, int per_cu) {
 
 hipError_t launch_amax(const void* x, int64_t n_elems, float* out, hipStream_t s) {
   uint32_t* o = reinterpret_cast<uint32_t*>(out);
-  hipLaunchKernelGGL(k_zero_u32, dim3(1), dim3(1), 0, s, o);
+  hipLaunchKernelGGL(k_zero_u32, dim3(1), dim3(1), 0, s, o, nullptr);
   const int64_t nvec = n_elems / 8;
   const int64_t chunks = (nvec + kAmaxChunk - 1) / kAmaxChunk;
-  hipLaunchKernelGGL(k_amax, dim3(grid_for(chunks * kThreads, 8)), dim3(kThreads), 0, s,
+  hipLaunchKernelGGL(k_amax, dim3(balanced_grid(chunks, 8)), dim3(kThreads), 0, s,
                      reinterpret_cast<const v4u*>(x), nvec, o);
   return hipGetLastError();
 }
@@ -498,15 +512,14 @@ hipError_t launch_amax_rht(const void* x, int64_t rows, int64_t cols, uint64_t r
                            float* out, hipStream_t s, float* out_plain) {
   uint32_t* o = reinterpret_cast<uint32_t*>(out);
   uint32_t* op = reinterpret_cast<uint32_t*>(out_plain);
-  hipLaunchKernelGGL(k_zero_u32, dim3(1), dim3(1), 0, s, o);
-  if (op != nullptr) hipLaunchKernelGGL(k_zero_u32, dim3(1), dim3(1), 0, s, op);
+  hipLaunchKernelGGL(k_zero_u32, dim3(1), dim3(1), 0, s, o, op);
   const int64_t items = (rows / 16) * (cols / 8);
   const uint16_t* xh = reinterpret_cast<const uint16_t*>(x);
   if (op != nullptr)
-    hipLaunchKernelGGL(k_amax_rht<true>, dim3(grid_for(items, 8)), dim3(kThreads), 0, s, xh, rows,
+    hipLaunchKernelGGL(k_amax_rht<true>, dim3(balanced_grid((items + kThreads - 1) / kThreads, 8)), dim3(kThreads), 0, s, xh, rows,
                        cols, rht_seed, o, op);
   else
-    hipLaunchKernelGGL(k_amax_rht<false>, dim3(grid_for(items, 8)), dim3(kThreads), 0, s, xh, rows,
+    hipLaunchKernelGGL(k_amax_rht<false>, dim3(balanced_grid((items + kThreads - 1) / kThreads, 8)), dim3(kThreads), 0, s, xh, rows,
                        cols, rht_seed, o, nullptr);
   return hipGetLastError();
 }
