@@ -406,7 +406,7 @@ def main():
     if args.step_only:
         args.no_mx = args.no_quality = args.no_sweep = args.no_cpu_baseline = True
     if args.gpus != 1 or int(os.environ.get("WORLD_SIZE", "1")) != 1:
-        print("bench.py measures one GPU: this build has no multi-GPU path "
+        print("bench.py measures one GPU: the library has no multi-GPU path "
               "(rerun with --gpus 1)", file=sys.stderr)
         sys.exit(2)
     if not torch.cuda.is_available():
