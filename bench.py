@@ -398,6 +398,9 @@ def main():
                     help="time the step and stop: no MXFP4, epilogue, quality, sweep or CPU "
                          "sections (for profiler runs, whose per-kernel averages then cover "
                          "the step's launches alone)")
+    ap.add_argument("--sweep-only", action="store_true",
+                    help="run only the 32768x8192 quantize sweep and print its JSON (for "
+                         "profiler runs over the quantizer kernels on large tensors)")
     ap.add_argument("--seed", type=int, default=0)
     ap.add_argument("--copy-calibration", action="store_true",
                     help="first run a plain 1 GiB device copy (3 launches), the reference "
@@ -422,6 +425,11 @@ def main():
         torch.cuda.synchronize()
         log("copy calibration: 3 x copy of 1 GiB (read 1 GiB + write 1 GiB each)")
         del src, dst
+    if args.sweep_only:
+        log("quantize sweep 32768x8192")
+        print(json.dumps({"quantize_sweep_32768x8192": quant_sweep(max(args.steps, 2))}),
+              flush=True)
+        return
 
     log("generating inputs (host, seeded)")
     wl = inputs.ffn_down(args.seed, TOKENS, HIDDEN, FFN)

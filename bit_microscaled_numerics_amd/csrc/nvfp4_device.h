@@ -62,7 +62,8 @@ __device__ __forceinline__ uint32_t e4m3_from_float(float x) {
 // every binary32 in [0, 448] (all 1.14e9 patterns compared on MI355X), and
 // both give 0x7E above.
 __device__ __forceinline__ uint32_t e4m3_code(float x) {
-  return (uint32_t)__builtin_amdgcn_cvt_pk_fp8_f32(fminf(x, 448.0f), 0.0f, 0, false) & 0xFFu;
+  // x >= 0 here; the mask keeps any code a 7-bit table index
+  return (uint32_t)__builtin_amdgcn_cvt_pk_fp8_f32(fminf(x, 448.0f), 0.0f, 0, false) & 0x7Fu;
 }
 
 // E4M3FN code (0..0x7E) -> binary32 (branch-free: both forms are computed
@@ -233,18 +234,19 @@ __device__ __forceinline__ float tensor_scale_from_amax(float amax_t) {
 // Block scale code and reciprocal element scale from a block amax.
 struct BlockScale { uint32_t code; float r; };
 
-// Per-tensor constants of the block-scale step.  rtab (LDS) holds the 127
-// possible reciprocals r = 1 / (float(E) * s_t), E4M3 codes 0 .. 0x7E, each
+// Per-tensor constants of the block-scale step.  rtab (LDS) holds the
+// reciprocals r = 1 / (float(E) * s_t) of the E4M3 codes 0 .. 0x7E (and of
+// 0x7F, which no scale takes: a 7-bit code always indexes the table), each
 // computed exactly as the per-block formula would, so a lookup returns the
 // same binary32 as the division it replaces.
-constexpr int kE4m3Codes = 127;
+constexpr int kE4m3Codes = 128;
 
 struct ScaleCtx {
   float s_t, t6, rt6;  // tensor scale, 6 * s_t, and the rounded 1 / t6
   const float* rtab;
 };
 
-// Every thread gets the constants; the thread with slot e < 127 fills
+// Every thread gets the constants; the thread with slot e < 128 fills
 // rtab[e].  The caller synchronises the workgroup before the first lookup.
 __device__ __forceinline__ ScaleCtx scale_ctx(float amax_t, float* rtab, int slot) {
   ScaleCtx c;
