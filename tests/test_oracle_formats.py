@@ -210,3 +210,36 @@ def test_e2m1_sr_unbiased_over_seeds():
     p = 0.3 / 0.5
     sigma = 0.5 * math.sqrt(p * (1 - p) / seeds.size)
     assert abs(vals.mean() - 0.3) < 4 * sigma + 0.5 * 2 ** -16
+
+
+def test_e2m1_rtn_exhaustive_step_function():
+    """Every binary32 in [0, 8] (1.09e9 values, in chunks): the RTN code is a
+    non-decreasing step function of the value that changes exactly seven
+    times, each time by one, at the midpoints between grid values: the upper
+    code takes the midpoint itself where its index is even (0.75, 1.75, 3.5)
+    and starts one ulp above where it is odd (0.25, 1.25, 2.5, 5).  Codes of
+    values in (6, 8] stay at 7."""
+    end = int(np.float32(8.0).view(np.uint32))
+    step = 1 << 24
+    idx = np.arange(step, dtype=np.uint32)
+    buf = np.empty(step, np.uint32)
+    changes = []
+    prev = None
+    for lo in range(0, end + 1, step):
+        n = min(step, end + 1 - lo)
+        bits = np.add(idx[:n], np.uint32(lo), out=buf[:n])
+        codes = oracle.e2m1_rtn(bits.view(np.float32))
+        if prev is not None:
+            assert codes[0] >= prev
+            if codes[0] != prev:
+                changes.append((lo, int(prev), int(codes[0])))
+        up = codes[1:] != codes[:-1]
+        if up.any():
+            for i in np.nonzero(up)[0]:
+                assert codes[i + 1] == codes[i] + 1
+                changes.append((lo + int(i) + 1, int(codes[i]), int(codes[i + 1])))
+        prev = codes[-1]
+    f = lambda x: int(np.float32(x).view(np.uint32))   # noqa: E731
+    expect = [(f(0.25) + 1, 0, 1), (f(0.75), 1, 2), (f(1.25) + 1, 2, 3), (f(1.75), 3, 4),
+              (f(2.5) + 1, 4, 5), (f(3.5), 5, 6), (f(5.0) + 1, 6, 7)]
+    assert changes == expect
