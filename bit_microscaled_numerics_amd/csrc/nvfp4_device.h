@@ -44,7 +44,8 @@ __device__ __forceinline__ float bf16_hi(uint32_t w) { return __uint_as_float(w 
 // 448 (code 0x7E).  Subnormal range (x < 2^-6): the code is rint(x * 2^9),
 // an exact scaling; 8 there is the smallest normal.  Normal range: round the
 // binary32 mantissa to 3 bits (add half-ulp-minus-one plus the kept lsb) and
-// rebias the exponent from 127 to 7.
+// rebias the exponent from 127 to 7.  This is the bit-level definition; the
+// kernels take the same codes from the hardware encode (e4m3_code below).
 __device__ __forceinline__ uint32_t e4m3_from_float(float x) {
   if (!(x > 0.0f)) return 0u;
   if (x >= 448.0f) return 0x7Eu;
@@ -81,7 +82,9 @@ __device__ __forceinline__ float e4m3_to_float(uint32_t c) {
 // Round-to-nearest-even magnitude index of a >= 0, saturating at 6.  The
 // decision points are the midpoints between grid values; at a midpoint the
 // even index wins, so the comparison is >= where the upper neighbour has an
-// even index and > where it has an odd one.
+// even index and > where it has an odd one.  This is the bit-level
+// definition; the kernels take the same decision from the hardware FP4
+// encode (encode8_rtn below).
 __device__ __forceinline__ uint32_t e2m1_rtn_index(float a) {
   uint32_t i = 0;
   i += (a > 0.25f);
