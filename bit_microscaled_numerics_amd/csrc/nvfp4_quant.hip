@@ -2,8 +2,10 @@
 // and under the 16-point RHT), 1D rowwise, 1D colwise (transpose-quantize,
 // optional RHT), 2D 16x16 tiles (optional transposed codes) and dequantize.
 //
-// All are HBM-bound: 16-byte loads (8 bf16 per lane), lanes of a wave on
+// Built for HBM bandwidth: 16-byte loads (8 bf16 per lane), lanes of a wave on
 // consecutive 16-byte chunks, packed 4-bit stores, no re-reads inside a pass.
+// The amax and RTN kernels are bound by HBM; the stochastic-rounding encodes
+// by their rounding arithmetic (about 20 VALU per element, plus Philox).
 // The tensor scale is re-derived from the device amax by every workgroup, so
 // no host round trip separates the amax pass from the encode pass.
 //
