@@ -170,6 +170,7 @@ __global__ __launch_bounds__(kThreads) void k_quant_row(
     uint64_t seed, uint32_t stream_id, uint32_t* __restrict__ codes,
     uint8_t* __restrict__ scales, float* __restrict__ ts_out) {
   __shared__ float rtab[kE4m3Codes];
+  static_assert(kThreads >= kE4m3Codes, "one thread per table entry");
   const ScaleCtx sc = scale_ctx(*amax, rtab, threadIdx.x);
   if (blockIdx.x == 0 && threadIdx.x == 0) *ts_out = sc.s_t;
   __syncthreads();
@@ -257,6 +258,7 @@ __global__ __launch_bounds__(kThreads) void k_quant_col(
   __shared__ v2u lds_codes[kColTileC][kColTileR / 16];   // 8 bytes = 16 codes per block
   __shared__ uint8_t lds_scales[kColTileC][kColTileR / 16];
   __shared__ float rtab[kE4m3Codes], rtab_row[ROW ? kE4m3Codes : 1];
+  static_assert(kThreads >= 2 * kE4m3Codes, "threads 0..127 fill rtab, 128..255 rtab_row");
   const ScaleCtx sc = scale_ctx(*amax, rtab, threadIdx.x);
   if (blockIdx.x == 0 && threadIdx.x == 0) *ts_out = sc.s_t;
   ScaleCtx sr_ctx;
