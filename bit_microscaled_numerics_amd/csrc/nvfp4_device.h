@@ -34,6 +34,16 @@ __device__ __forceinline__ void st_(T v, T* p) { __builtin_nontemporal_store(v, 
 // 6 (largest E2M1 magnitude) * 448 (largest E4M3 value).
 constexpr float kScaleDen = 2688.0f;
 
+// Bit casts usable on the host as well, so the pure bit-level routines below
+// (the E4M3 and E2M1 definitions, the stochastic-rounding decision) also
+// compile for the CPU, where the tests run them against the CPU reference.
+__host__ __device__ __forceinline__ uint32_t f32_bits(float x) {
+  return __builtin_bit_cast(uint32_t, x);
+}
+__host__ __device__ __forceinline__ float f32_from(uint32_t u) {
+  return __builtin_bit_cast(float, u);
+}
+
 __device__ __forceinline__ float bf16_lo(uint32_t w) { return __uint_as_float(w << 16); }
 __device__ __forceinline__ float bf16_hi(uint32_t w) { return __uint_as_float(w & 0xFFFF0000u); }
 
@@ -46,11 +56,11 @@ __device__ __forceinline__ float bf16_hi(uint32_t w) { return __uint_as_float(w 
 // binary32 mantissa to 3 bits (add half-ulp-minus-one plus the kept lsb) and
 // rebias the exponent from 127 to 7.  This is the bit-level definition; the
 // kernels take the same codes from the hardware encode (e4m3_code below).
-__device__ __forceinline__ uint32_t e4m3_from_float(float x) {
+__host__ __device__ __forceinline__ uint32_t e4m3_from_float(float x) {
   if (!(x > 0.0f)) return 0u;
   if (x >= 448.0f) return 0x7Eu;
   if (x < 0.015625f) return (uint32_t)__builtin_rintf(x * 512.0f);
-  uint32_t u = __float_as_uint(x);
+  uint32_t u = f32_bits(x);
   u += 0x7FFFFu + ((u >> 20) & 1u);
   uint32_t e = (u >> 23) - 120u;  // 127 - 7
   uint32_t m = (u >> 20) & 7u;
@@ -85,7 +95,7 @@ __device__ __forceinline__ float e4m3_to_float(uint32_t c) {
 // even index and > where it has an odd one.  This is the bit-level
 // definition; the kernels take the same decision from the hardware FP4
 // encode (encode8_rtn below).
-__device__ __forceinline__ uint32_t e2m1_rtn_index(float a) {
+__host__ __device__ __forceinline__ uint32_t e2m1_rtn_index(float a) {
   uint32_t i = 0;
   i += (a > 0.25f);
   i += (a >= 0.75f);
@@ -155,6 +165,37 @@ __device__ __forceinline__ void rht16(float (&v)[16], uint32_t signs) {
   for (int j = 0; j < 16; ++j) v[j] *= 0.25f;
 }
 
+// The same transform of a 16-block held by two lanes of a wave, 8 elements
+// each: the lane with hi == false holds elements 0..7, its partner (lane ^ 1)
+// elements 8..15.  Sign flips and the butterflies over index bits 0..2 run
+// inside each lane; the last stage pairs element j with j + 8 across the two
+// lanes (the low lane keeps the sum, the high lane the difference); then the
+// exact * 1/4.  Every output is the same chain of binary32 operations as in
+// rht16.  Both lanes of a pair must execute this together.
+__device__ __forceinline__ void rht16_pair(float (&v)[8], uint32_t signs, bool hi) {
+  const uint32_t s = hi ? signs >> 8 : signs;
+#pragma unroll
+  for (int j = 0; j < 8; ++j)
+    v[j] = __uint_as_float(__float_as_uint(v[j]) ^ (((s >> j) & 1u) << 31));
+#pragma unroll
+  for (int h = 1; h < 8; h <<= 1) {
+#pragma unroll
+    for (int j = 0; j < 8; ++j) {
+      if (j & h) continue;
+      float a = v[j], b = v[j + h];
+      v[j] = a + b;
+      v[j + h] = a - b;
+    }
+  }
+#pragma unroll
+  for (int j = 0; j < 8; ++j) {
+    const float p = __shfl_xor(v[j], 1, 64);
+    v[j] = hi ? p - v[j] : v[j] + p;
+  }
+#pragma unroll
+  for (int j = 0; j < 8; ++j) v[j] *= 0.25f;
+}
+
 // ---------------------------------------------------------------------------
 // Encoding one group of 8 elements given the block's reciprocal scale
 // ---------------------------------------------------------------------------
@@ -189,9 +230,9 @@ __device__ __forceinline__ uint32_t encode8_rtn(const float* z, float r) {
 //   a < 0.5 (grid 0, 0.5): p * 65536 = a * 2^17, an exact float; compared
 //     with u as a float.
 // The hardware FP4 encode then maps each grid value to its code exactly.
-__device__ __forceinline__ float e2m1_sr_value(float v, uint32_t u) {
-  const float a = fminf(__builtin_fabsf(v), 6.0f);
-  const uint32_t bits = __float_as_uint(a);
+__host__ __device__ __forceinline__ float e2m1_sr_value(float v, uint32_t u) {
+  const float a = __builtin_fminf(__builtin_fabsf(v), 6.0f);
+  const uint32_t bits = f32_bits(a);
   const bool ge1 = bits >= 0x3F800000u;
   const uint32_t mask = ge1 ? 0x3FFFFFu : 0x7FFFFFu;
   const uint32_t u7 = u << 7;
@@ -199,7 +240,7 @@ __device__ __forceinline__ float e2m1_sr_value(float v, uint32_t u) {
   const uint32_t rounded = (bits + (mask - us)) & ~mask;
   const uint32_t small = ((float)u < a * 131072.0f) ? 0x3F000000u : 0u;
   const uint32_t mag = bits < 0x3F000000u ? small : rounded;
-  return __uint_as_float(mag | (__float_as_uint(v) & 0x80000000u));
+  return f32_from(mag | (f32_bits(v) & 0x80000000u));
 }
 
 // Stochastic rounding with the 8 16-bit halves of w (element j takes word
@@ -246,6 +287,7 @@ constexpr int kE4m3Codes = 128;
 
 struct ScaleCtx {
   float s_t, t6, rt6;  // tensor scale, 6 * s_t, and the rounded 1 / t6
+  bool divide;         // 1 / t6 overflowed (amax_t below ~1.3e-36): divide every block
   const float* rtab;
 };
 
@@ -256,6 +298,7 @@ __device__ __forceinline__ ScaleCtx scale_ctx(float amax_t, float* rtab, int slo
   c.s_t = tensor_scale_from_amax(amax_t);
   c.t6 = 6.0f * c.s_t;
   c.rt6 = 1.0f / c.t6;
+  c.divide = !(c.rt6 <= 3.40282347e38f);
   c.rtab = rtab;
   if (slot >= 0 && slot < kE4m3Codes) rtab[slot] = 1.0f / (e4m3_to_float((uint32_t)slot) * c.s_t);
   return c;
@@ -269,12 +312,14 @@ __device__ __forceinline__ ScaleCtx scale_ctx(float amax_t, float* rtab, int slo
 // 0x80000 above 2^-6 (3 significand bits kept) and 0 below it (the
 // subnormal steps of 2^-9 put the midpoints at odd multiples of 2^-10).  If
 // q' lies within 8 patterns of such a point (about one block in 2^16), the
-// quotient is taken by the correctly rounded division instead.
+// quotient is taken by the correctly rounded division instead.  So is every
+// block's when 1/t6 is not finite (a tensor amax below 448 / FLT_MAX): there
+// q' would be inf for every non-zero block and NaN for a zero one.
 __device__ __forceinline__ uint32_t scale_code(float amax_b, const ScaleCtx& c) {
   float q = amax_b * c.rt6;
   const uint32_t b = __float_as_uint(q);
   const uint32_t centre = b < 0x3C800000u ? 0u : 0x80000u;
-  if (((b - centre + 8u) & 0xFFFFFu) < 16u) q = amax_b / c.t6;
+  if (((b - centre + 8u) & 0xFFFFFu) < 16u || c.divide) q = amax_b / c.t6;
   return e4m3_code(q);
 }
 

@@ -15,15 +15,12 @@
 // accumulation, and the tensor scales are applied once in the epilogue.  (The
 // gfx950 scaled FP4 MFMA takes power-of-two E8M0 scales per 32 elements, so
 // it cannot apply an E4M3 scale per 16 exactly.)
+#include "gemm_decode.h"
+#include "gemm_tiles.h"
 #include "nvfp4_device.h"
 #include "nvfp4_kernels.h"
-#include "gemm_tiles.h"
 
 namespace nvfp4 {
-
-typedef _Float16 half8 __attribute__((ext_vector_type(8)));
-typedef _Float16 half2v __attribute__((ext_vector_type(2)));
-typedef float float16v __attribute__((ext_vector_type(16)));
 
 struct GemmArgs {
   GemmOperand a, b;
@@ -35,32 +32,6 @@ struct GemmArgs {
   int64_t full_tiles;  // tiles computed whole; tiles past them are cut by `tail`
   int tail;            // TailMode of the tiles past full_tiles
 };
-
-// Decoding.  The gfx950 FP4 -> FP16 convert multiplies by 2^floor(log2 s)
-// of its FP32 scale argument only (an E8M0-style scale; low nibble first),
-// which gives q * 2^e exactly.  One packed FP16 multiply by the E4M3
-// mantissa (1 + m/8) completes q * E exactly: 2 + 4 significant bits.
-struct BlockDec {
-  float e;       // E4M3 value as FP32 (the convert takes its exponent)
-  half2v mant;   // {mantissa, mantissa} in FP16
-};
-
-// Eight codes (one 32-bit word, element e in nibble e) -> eight FP16 values
-// q * E, element e in lane-vector slot e.
-__device__ __forceinline__ half8 decode8(uint32_t w, const BlockDec& d) {
-  half2v p0 = __builtin_amdgcn_cvt_scalef32_pk_f16_fp4(w, d.e, 0);
-  half2v p1 = __builtin_amdgcn_cvt_scalef32_pk_f16_fp4(w, d.e, 1);
-  half2v p2 = __builtin_amdgcn_cvt_scalef32_pk_f16_fp4(w, d.e, 2);
-  half2v p3 = __builtin_amdgcn_cvt_scalef32_pk_f16_fp4(w, d.e, 3);
-  p0 *= d.mant;
-  p1 *= d.mant;
-  p2 *= d.mant;
-  p3 *= d.mant;
-  half8 r;
-  r[0] = p0[0]; r[1] = p0[1]; r[2] = p1[0]; r[3] = p1[1];
-  r[4] = p2[0]; r[5] = p2[1]; r[6] = p3[0]; r[7] = p3[1];
-  return r;
-}
 
 constexpr uint32_t kBufFlags = 0x00020000u;  // raw 32-bit buffer descriptor word 3
 
@@ -137,31 +108,6 @@ __device__ __forceinline__ Slab load_slab(const OpView& v, uint32_t kbyte, uint3
     s.s1 = __builtin_amdgcn_raw_buffer_load_b8(v.scales, v.voff_scales + v.ss_k, sk, 0);
   }
   return s;
-}
-
-// Scale table: E4M3 code (0..127) -> {E as FP32, FP16 mantissa pair}, 1 KiB
-// of LDS filled once per workgroup (one 8-byte LDS read per block scale
-// costs less VALU than decoding the code).  The gfx950 FP8 -> FP32 convert
-// (OCP E4M3FN, subnormals included) gives E exactly; its FP32 mantissa bits
-// give the factor (1 + m/8).
-__device__ __forceinline__ v2u scale_entry(uint32_t code) {
-  const float e = __builtin_amdgcn_cvt_f32_fp8((int)code, 0);
-  const uint32_t mb = (__float_as_uint(e) >> 20) & 7u;
-  const uint32_t h = 0x3C00u | (mb << 7);
-  return v2u{__float_as_uint(e), h | (h << 16)};
-}
-
-// Decode the scale code in bits [pos, pos + 7) of w (the sign bit of an
-// E4M3 code is dropped: block scales are non-negative).
-__device__ __forceinline__ BlockDec scale_dec(const v2u* lut, uint32_t w, uint32_t pos) {
-  const v2u e = lut[__builtin_amdgcn_ubfe(w, pos, 7)];
-  // copy the lanes to scalars first: clang's __builtin_bit_cast of an
-  // ext-vector element expression reads element 0
-  const uint32_t ex = e.x, ey = e.y;
-  BlockDec d;
-  d.e = __uint_as_float(ex);
-  d.mant = __builtin_bit_cast(half2v, ey);
-  return d;
 }
 
 // ---------------------------------------------------------------------------
@@ -441,19 +387,6 @@ constexpr int kScBytes = kTile * kScRow;     // 4 KiB
 constexpr int vmcnt_imm(int n) { return (n & 15) | ((n >> 4) << 14) | (7 << 4) | (15 << 8); }
 
 typedef __attribute__((address_space(3))) void* lds_ptr_t;
-
-// E4M3 scale code in bits [pos, pos + 7) of w -> {E, mantissa pair} in ALU
-// (the table read of scale_dec would add an LDS wait next to the operand
-// reads).
-__device__ __forceinline__ BlockDec scale_alu(uint32_t w, uint32_t pos) {
-  const uint32_t code = __builtin_amdgcn_ubfe(w, pos, 7);
-  const float e = __builtin_amdgcn_cvt_f32_fp8((int)code, 0);
-  const uint32_t h = 0x3C00u | (__builtin_amdgcn_ubfe(__float_as_uint(e), 20, 3) << 7);
-  BlockDec d;
-  d.e = e;
-  d.mant = __builtin_bit_cast(half2v, h | (h << 16));
-  return d;
-}
 
 // Raw layout [row][4 chunks of 16 B], chunk c of row r at position
 // c ^ rg(r): the 16-byte reads of the A decode (8 rows x 2 chunks per 16

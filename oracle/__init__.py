@@ -68,6 +68,8 @@ def _load():
         "orc_amax": (ctypes.c_float, [_u16p, _i64, _i64]),
         "orc_amax_rht": (ctypes.c_float, [_u16p, _i64, _i64, _u64]),
         "orc_tensor_scale": (ctypes.c_float, [ctypes.c_float]),
+        "orc_block_scale": (ctypes.c_uint8, [ctypes.c_float, ctypes.c_float]),
+        "orc_block_recip": (ctypes.c_float, [ctypes.c_uint8, ctypes.c_float]),
         "orc_quantize": (ctypes.c_int, [_u16p, _i64, _i64, ctypes.c_int, ctypes.c_int, _u64,
                                         ctypes.c_int, _u64, _u32, ctypes.c_int, _f32p,
                                         _u8p, _u8p, _u8p, _f32p]),
@@ -153,6 +155,16 @@ def rht16(x: np.ndarray, signs: int) -> np.ndarray:
 
 def tensor_scale(amax: float) -> float:
     return float(_load().orc_tensor_scale(amax))
+
+
+def block_scale(amax_b: float, s_t: float) -> int:
+    """E4M3 code of a block with largest magnitude amax_b in a tensor of scale s_t."""
+    return int(_load().orc_block_scale(amax_b, s_t))
+
+
+def block_recip(code: int, s_t: float) -> float:
+    """Element scale 1 / (E * s_t) of a block with scale code E."""
+    return float(_load().orc_block_recip(code, s_t))
 
 
 # --------------------------------------------------------------------------- tensors

@@ -306,24 +306,36 @@ ORC_API float orc_tensor_scale(float amax_t) {
 /* ------------------------------------------------------------------ */
 /* One block: amax -> E4M3 scale -> E2M1 codes                          */
 /* ------------------------------------------------------------------ */
+/* Block scale: the E4M3 code of amax_b / (6 s_t), so that the block's
+ * largest magnitude lands on the largest E2M1 value, 6 ([BLOG] E4M3 scale
+ * factors; [PAPER] format paragraph: one E4M3 scale per 16 values). */
+ORC_API uint8_t orc_block_scale(float amax_b, float s_t) {
+  float t6 = 6.0f * s_t;
+  float e_f = amax_b / t6;
+  return orc_e4m3_encode(e_f);
+}
+
+/* Element scale of a block with scale code E: r = 1 / (E * s_t), once per
+ * block; the encode multiplies every element by it. */
+ORC_API float orc_block_recip(uint8_t E, float s_t) {
+  float d = orc_e4m3_decode(E) * s_t;
+  return 1.0f / d;
+}
+
 /* z[] holds the n (16 or 256) values of the block, idx[] their operand
  * indices (for the random bits).  Returns the E4M3 scale code. */
 static uint8_t quant_block(const float* z, const uint64_t* idx, int n, float s_t,
                            int use_sr, uint64_t seed, uint32_t stream_id, uint8_t* code) {
   float amax_b = 0.0f;
   for (int j = 0; j < n; ++j) { float a = fabsf(z[j]); if (a > amax_b) amax_b = a; }
-  float t6 = 6.0f * s_t;
-  float e_f = amax_b / t6;
-  uint8_t E = orc_e4m3_encode(e_f);
-  float Ef = orc_e4m3_decode(E);
+  uint8_t E = orc_block_scale(amax_b, s_t);
   if (E == 0) {
     /* the block's scale underflowed (or the block is all zero): every
        element becomes a signed zero */
     for (int j = 0; j < n; ++j) code[j] = (uint8_t)(signbit(z[j]) ? 8 : 0);
     return E;
   }
-  float d = Ef * s_t;
-  float r = 1.0f / d;
+  float r = orc_block_recip(E, s_t);
   for (int j = 0; j < n; ++j) {
     float v = z[j] * r;
     code[j] = use_sr ? orc_e2m1_sr(v, orc_sr_bits(seed, stream_id, idx[j])) : orc_e2m1_rtn(v);
