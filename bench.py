@@ -319,8 +319,10 @@ def quality(step: "Step"):
     out = {}
     yref = xf @ wt.float()
     out["Fprop recipe (X 1D, W 2D)"] = cmp(nv.gemm(nv.quantize_1d(x), nv.quantize_2d(w)), yref)
+    row = nv.NVFP4_ROWWISE
     out["Fprop RHT along K (X, W 1D)"] = cmp(
-        nv.gemm(nv.rht_quantize(xt, RHT_SEED), nv.rht_quantize(wt, RHT_SEED)), yref)
+        nv.gemm(nv.rht_quantize(x, RHT_SEED, axis=row), nv.rht_quantize(w, RHT_SEED, axis=row)),
+        yref)
     out["Fprop MXFP4"] = cmp(nv.mx_gemm(nv.mx_quantize(x), nv.mx_quantize(w)), yref)
     del yref
     g = torch.Generator(device=dy.device).manual_seed(7)
@@ -335,8 +337,8 @@ def quality(step: "Step"):
         out[f"Dgrad recipe (dY 1D SR){tag}"] = cmp(
             nv.gemm(nv.quantize_1d(d, sr_seed=SR_SEED), qw.t()), dxref)
         out[f"Dgrad RHT along K (dY SR, W 1D){tag}"] = cmp(
-            nv.gemm(nv.rht_quantize(dt, RHT_SEED, sr_seed=SR_SEED), nv.rht_quantize(w, RHT_SEED)),
-            dxref)
+            nv.gemm(nv.rht_quantize(d, RHT_SEED, sr_seed=SR_SEED, axis=row),
+                    nv.rht_quantize(w, RHT_SEED)), dxref)
         out[f"Dgrad MXFP4 SR{tag}"] = cmp(
             nv.mx_gemm(nv.mx_quantize(d, SR_SEED), nv.mx_quantize(wt)), dxref)
         del dxref, qw

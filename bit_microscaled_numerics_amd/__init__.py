@@ -34,7 +34,8 @@ EXPORTED = ("nvfp4_amax", "nvfp4_amax_rht", "nvfp4_quantize1d_rtn", "nvfp4_quant
             "nvfp4_dequantize", "nvfp4_gemm", "nvfp4_status_string", "nvfp4_last_error",
             "nvfp4_gemm_bf16", "mxfp4_quantize", "mxfp4_dequantize", "mxfp4_gemm",
             "nvfp4_probe_mfma", "nvfp4_probe_scratch_bytes", "nvfp4_amax_both",
-            "nvfp4_quantize_row_rht")
+            "nvfp4_quantize_row_rht", "nvfp4_amax_rht1d", "nvfp4_rht_quantize1d",
+            "nvfp4_probe_clock", "nvfp4_probe_clock_bytes")
 
 
 class NVFP4Error(RuntimeError):
@@ -82,6 +83,8 @@ def load_library(path: str = LIB_PATH) -> ctypes.CDLL:
         "nvfp4_quantize2d_rtn": [vp, i64, i64, vp, i32, vp, vp, vp, vp, vp, vp],
         "nvfp4_quantize2d_sr": [vp, i64, i64, vp, i32, u64, u32, vp, vp, vp, vp, vp, vp],
         "nvfp4_rht_quantize": [vp, i64, i64, u64, i32, u64, u32, vp, i32, vp, vp, vp, vp],
+        "nvfp4_amax_rht1d": [vp, i64, i64, i32, u64, vp, vp],
+        "nvfp4_rht_quantize1d": [vp, i64, i64, i32, u64, i32, u64, u32, vp, i32, vp, vp, vp, vp],
         "nvfp4_quantize_row_rht": [vp, i64, i64, u64, i32, u64, u32, u32, vp, vp, vp, vp, vp, vp,
                                    vp, vp, vp],
         "nvfp4_dequantize": [ctypes.POINTER(c_operand), vp, vp],
@@ -91,6 +94,7 @@ def load_library(path: str = LIB_PATH) -> ctypes.CDLL:
         "mxfp4_dequantize": [ctypes.POINTER(c_mx_operand), vp, vp],
         "mxfp4_gemm": [ctypes.POINTER(c_mx_operand), ctypes.POINTER(c_mx_operand), vp, i64, vp],
         "nvfp4_probe_mfma": [i32, i32, vp, i64, vp],
+        "nvfp4_probe_clock": [vp, i64, vp],
     }
     for name, args in sigs.items():
         fn = getattr(lib, name)
@@ -100,8 +104,9 @@ def load_library(path: str = LIB_PATH) -> ctypes.CDLL:
     lib.nvfp4_status_string.restype = ctypes.c_char_p
     lib.nvfp4_last_error.argtypes = []
     lib.nvfp4_last_error.restype = ctypes.c_char_p
-    lib.nvfp4_probe_scratch_bytes.argtypes = []
-    lib.nvfp4_probe_scratch_bytes.restype = ctypes.c_int64
+    for name in ("nvfp4_probe_scratch_bytes", "nvfp4_probe_clock_bytes"):
+        getattr(lib, name).argtypes = []
+        getattr(lib, name).restype = ctypes.c_int64
     _lib = lib
     return lib
 
@@ -186,6 +191,21 @@ def nvfp4_rht_quantize(x, rht_seed, use_sr, sr_seed, stream_id, amax_io, amax_mo
                                              _stream(stream)))
 
 
+def nvfp4_amax_rht1d(x, axis, rht_seed, amax_out, stream=None):
+    _dev_bf16(x, "x")
+    _check(load_library().nvfp4_amax_rht1d(_p(x), x.shape[0], x.shape[1], axis, rht_seed,
+                                           _p(amax_out), _stream(stream)))
+
+
+def nvfp4_rht_quantize1d(x, axis, rht_seed, use_sr, sr_seed, stream_id, amax_io, amax_mode, codes,
+                         scales, ts_out, stream=None):
+    _dev_bf16(x, "x")
+    _check(load_library().nvfp4_rht_quantize1d(_p(x), x.shape[0], x.shape[1], axis, rht_seed,
+                                               int(use_sr), sr_seed, stream_id, _p(amax_io),
+                                               amax_mode, _p(codes), _p(scales), _p(ts_out),
+                                               _stream(stream)))
+
+
 def nvfp4_quantize_row_rht(x, rht_seed, use_sr, sr_seed, stream_id_row, stream_id_rht, amax_row,
                            amax_rht, codes_row, scales_row, ts_row, codes_rht, scales_rht, ts_rht,
                            stream=None):
@@ -263,9 +283,11 @@ def amax(x: torch.Tensor) -> torch.Tensor:
     return out
 
 
-def amax_rht(x: torch.Tensor, rht_seed: int) -> torch.Tensor:
+def amax_rht(x: torch.Tensor, rht_seed: int, axis: int = NVFP4_COLWISE) -> torch.Tensor:
+    """max |RHT(x)| with the transform along the rows (COLWISE, the Wgrad
+    layout) or along each row (ROWWISE)."""
     out = torch.empty(1, dtype=torch.float32, device=x.device)
-    nvfp4_amax_rht(x, rht_seed, out)
+    nvfp4_amax_rht1d(x, axis, rht_seed, out)
     return out
 
 
@@ -310,15 +332,19 @@ def quantize_2d(w: torch.Tensor, sr_seed: Optional[int] = None, stream_id: int =
 
 
 def rht_quantize(x: torch.Tensor, rht_seed: int, sr_seed: Optional[int] = None,
-                 stream_id: int = 0, amax=None) -> NVFP4Tensor:
-    """Wgrad operand: quantized transpose of RHT(x) along the rows (tokens)."""
+                 stream_id: int = 0, amax=None, axis: int = NVFP4_COLWISE) -> NVFP4Tensor:
+    """1D quantization of the 16-point RHT of x.  COLWISE (the Wgrad operand):
+    the quantized transpose, transform along the rows (tokens).  ROWWISE
+    (Fprop / Dgrad operands with the transform along K): transform along
+    each row, codes [rows][cols/2]."""
     _dev_bf16(x, "x")
     R, C = x.shape
-    codes, scales, ts = _outputs(C, R, x.device, (C, R // 16))
+    I, K = (C, R) if axis == NVFP4_COLWISE else (R, C)
+    codes, scales, ts = _outputs(I, K, x.device, (I, K // 16))
     am, mode = _amax_arg(x, amax)
-    nvfp4_rht_quantize(x, rht_seed, sr_seed is not None, 0 if sr_seed is None else sr_seed,
-                       stream_id, am, mode, codes, scales, ts)
-    return NVFP4Tensor(codes, scales, ts, am, C, R, 1, R // 16, 1)
+    nvfp4_rht_quantize1d(x, axis, rht_seed, sr_seed is not None,
+                         0 if sr_seed is None else sr_seed, stream_id, am, mode, codes, scales, ts)
+    return NVFP4Tensor(codes, scales, ts, am, I, K, 1, K // 16, 1)
 
 
 def quantize_row_rht(x: torch.Tensor, rht_seed: int, sr_seed: Optional[int] = None,
@@ -444,3 +470,37 @@ def probe_mfma(mode: int, iters: int = 8000):
     secs = (max(r[3] for r in st) - min(r[2] for r in st)) * 1e-8
     flops = 2.0 * 32 * 32 * 16 * 16 * iters * 4 * wgs
     return flops / secs / 1e12, ghz
+
+
+class ClockStamps:
+    """Average shader clock of work enqueued between ``before()`` and
+    ``after()`` on the current stream (measurement support): per-XCD
+    differences of the shader-clock counter over the 100 MHz real-time
+    counter, averaged over the XCDs.  ``ghz()`` synchronizes."""
+
+    def __init__(self, device="cuda"):
+        lib = load_library()
+        n = int(lib.nvfp4_probe_clock_bytes())
+        self._n = n
+        self._buf = torch.empty(2, n // 8, dtype=torch.int64, device=device)
+
+    def _stamp(self, i: int, stream=None):
+        _check(load_library().nvfp4_probe_clock(self._buf[i].data_ptr(), self._n, _stream(stream)))
+
+    def before(self, stream=None):
+        self._stamp(0, stream)
+
+    def after(self, stream=None):
+        self._stamp(1, stream)
+
+    def ghz(self) -> float:
+        torch.cuda.synchronize()
+        st = self._buf.cpu().view(2, -1, 4).tolist()
+        first, last = {}, {}
+        for xcc, t, r, _ in st[0]:
+            first.setdefault(xcc, (t, r))
+        for xcc, t, r, _ in st[1]:
+            last[xcc] = (t, r)
+        rates = [(last[x][0] - first[x][0]) / (last[x][1] - first[x][1]) * 0.1
+                 for x in first if x in last and last[x][1] > first[x][1]]
+        return sum(rates) / len(rates) if rates else float("nan")

@@ -11,6 +11,9 @@
 // -- the GEMM fast path's MFMA pattern with no loads, decode or LDS.  Wave 0
 // of every workgroup reads the shader-clock counter (s_memtime) and the
 // 100 MHz real-time counter (s_memrealtime) around the loop.
+//
+// Also clock stamps for any work on a stream: taken before and after it, they
+// give the average shader clock the work ran at.
 #include "nvfp4_kernels.h"
 
 namespace nvfp4 {
@@ -82,7 +85,33 @@ __global__ __launch_bounds__(kProbeThreads, 1) void k_probe_mfma(const half8* sr
   }
 }
 
+// Clock stamps: each workgroup's first lane writes {XCC id, shader-clock
+// counter, 100 MHz real-time counter, 0}.  The shader-clock counters of the
+// XCDs are not synchronised with each other, so the host pairs a stamp taken
+// before some work with one taken after it on the same XCD; workgroups are
+// dealt to the XCDs in turn, so kStampWgs of them cover every XCD.
+constexpr int kStampWgs = 64;
+
+__global__ void k_clock_stamp(unsigned long long* out) {
+  if (threadIdx.x != 0) return;
+  const unsigned xcc = __builtin_amdgcn_s_getreg((3 << 11) | 20) & 0xFu;   // HW_REG_XCC_ID[3:0]
+  const unsigned long long t = __builtin_amdgcn_s_memtime();
+  const unsigned long long r = __builtin_amdgcn_s_memrealtime();
+  out[4 * blockIdx.x + 0] = xcc;
+  out[4 * blockIdx.x + 1] = t;
+  out[4 * blockIdx.x + 2] = r;
+  out[4 * blockIdx.x + 3] = 0;
+}
+
 }  // namespace
+
+int64_t clock_stamp_bytes() { return (int64_t)kStampWgs * 32; }
+
+hipError_t clock_stamp(void* out, hipStream_t s) {
+  hipLaunchKernelGGL(k_clock_stamp, dim3(kStampWgs), dim3(64), 0, s,
+                     static_cast<unsigned long long*>(out));
+  return hipGetLastError();
+}
 
 // Scratch layout: operands (kProbeWgs * 256 threads * 10 half8), the sink
 // (one float per thread), then the stamps (4 x uint64 per workgroup).

@@ -173,8 +173,8 @@ static int quantize1d(const void* x, int64_t rows, int64_t cols, int axis, float
     if (e != hipSuccess) return launched(e);
   }
   if (axis == NVFP4_ROWWISE)
-    return launched(nvfp4::launch_quant_row(x, rows, cols, amax_io, sr, seed, stream_id, codes,
-                                            scales, ts_out, s));
+    return launched(nvfp4::launch_quant_row(x, rows, cols, amax_io, false, 0, sr, seed, stream_id,
+                                            codes, scales, ts_out, s));
   return launched(nvfp4::launch_quant_col(x, rows, cols, amax_io, false, 0, sr, seed, stream_id,
                                           codes, scales, ts_out, s));
 }
@@ -242,6 +242,43 @@ int nvfp4_rht_quantize(const void* x, int64_t rows, int64_t cols, uint64_t rht_s
     if (e != hipSuccess) return launched(e);
   }
   return launched(nvfp4::launch_quant_col(x, rows, cols, amax_io, true, rht_seed, use_sr == 1,
+                                          sr_seed, stream_id, codes, scales, ts_out, s));
+}
+
+int nvfp4_amax_rht1d(const void* x, int64_t rows, int64_t cols, int axis, uint64_t rht_seed,
+                     float* amax_out, void* stream) {
+  if (axis != NVFP4_ROWWISE && axis != NVFP4_COLWISE)
+    return fail(NVFP4_ERR_ARG, "axis=%d is neither NVFP4_ROWWISE nor NVFP4_COLWISE", axis);
+  if (axis == NVFP4_COLWISE) return nvfp4_amax_rht(x, rows, cols, rht_seed, amax_out, stream);
+  int st = check_tensor(x, rows, cols, "x");
+  if (st) return st;
+  if (amax_out == nullptr) return fail(NVFP4_ERR_NULL, "amax_out is NULL");
+  if (!aligned(amax_out, 4)) return fail(NVFP4_ERR_ALIGN, "amax_out must be 4-byte aligned");
+  return launched(nvfp4::launch_amax_rht_row(x, rows * cols, rht_seed, amax_out,
+                                             as_stream(stream)));
+}
+
+int nvfp4_rht_quantize1d(const void* x, int64_t rows, int64_t cols, int axis, uint64_t rht_seed,
+                         int use_sr, uint64_t sr_seed, uint32_t stream_id, float* amax_io,
+                         int amax_mode, uint8_t* codes, uint8_t* scales, float* ts_out,
+                         void* stream) {
+  if (axis != NVFP4_ROWWISE && axis != NVFP4_COLWISE)
+    return fail(NVFP4_ERR_ARG, "axis=%d is neither NVFP4_ROWWISE nor NVFP4_COLWISE", axis);
+  if (axis == NVFP4_COLWISE)
+    return nvfp4_rht_quantize(x, rows, cols, rht_seed, use_sr, sr_seed, stream_id, amax_io,
+                              amax_mode, codes, scales, ts_out, stream);
+  int st = check_tensor(x, rows, cols, "x");
+  if (st) return st;
+  if ((st = check_outputs(codes, scales, amax_io, ts_out))) return st;
+  if (use_sr != 0 && use_sr != 1) return fail(NVFP4_ERR_ARG, "use_sr=%d must be 0 or 1", use_sr);
+  if (amax_mode != NVFP4_AMAX_COMPUTE && amax_mode != NVFP4_AMAX_GIVEN)
+    return fail(NVFP4_ERR_ARG, "amax_mode=%d out of range", amax_mode);
+  hipStream_t s = as_stream(stream);
+  if (amax_mode == NVFP4_AMAX_COMPUTE) {
+    hipError_t e = nvfp4::launch_amax_rht_row(x, rows * cols, rht_seed, amax_io, s);
+    if (e != hipSuccess) return launched(e);
+  }
+  return launched(nvfp4::launch_quant_row(x, rows, cols, amax_io, true, rht_seed, use_sr == 1,
                                           sr_seed, stream_id, codes, scales, ts_out, s));
 }
 
@@ -380,6 +417,17 @@ int nvfp4_probe_mfma(int mode, int iters, void* scratch, int64_t scratch_bytes, 
   if (mode < 0 || mode > 2) return fail(NVFP4_ERR_ARG, "mode=%d (0, 1 or 2)", mode);
   if (iters < 1 || iters > 1000000) return fail(NVFP4_ERR_ARG, "iters=%d (1 .. 1000000)", iters);
   return launched(nvfp4::probe_mfma(mode, iters, scratch, as_stream(stream)));
+}
+
+int64_t nvfp4_probe_clock_bytes(void) { return nvfp4::clock_stamp_bytes(); }
+
+int nvfp4_probe_clock(void* stamps, int64_t stamps_bytes, void* stream) {
+  if (stamps == nullptr) return fail(NVFP4_ERR_NULL, "stamps is NULL");
+  if (!aligned(stamps, 8)) return fail(NVFP4_ERR_ALIGN, "stamps must be 8-byte aligned");
+  if (stamps_bytes < nvfp4::clock_stamp_bytes())
+    return fail(NVFP4_ERR_SHAPE, "stamps_bytes=%lld < %lld", (long long)stamps_bytes,
+                (long long)nvfp4::clock_stamp_bytes());
+  return launched(nvfp4::clock_stamp(stamps, as_stream(stream)));
 }
 
 }  // extern "C"

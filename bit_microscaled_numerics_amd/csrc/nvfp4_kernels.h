@@ -13,9 +13,14 @@ hipError_t launch_amax(const void* x, int64_t n_elems, float* out, hipStream_t s
 // out_plain (nullable): also max |x| from the same read
 hipError_t launch_amax_rht(const void* x, int64_t rows, int64_t cols, uint64_t rht_seed,
                            float* out, hipStream_t s, float* out_plain = nullptr);
+// amax of the transform over every 16 consecutive columns of each row
+hipError_t launch_amax_rht_row(const void* x, int64_t n_elems, uint64_t rht_seed, float* out,
+                               hipStream_t s);
+// rowwise 1D; rht: each 16-block along the row transformed first
 hipError_t launch_quant_row(const void* x, int64_t rows, int64_t cols, const float* amax,
-                            bool sr, uint64_t seed, uint32_t stream_id, uint8_t* codes,
-                            uint8_t* scales, float* ts_out, hipStream_t s);
+                            bool rht, uint64_t rht_seed, bool sr, uint64_t seed,
+                            uint32_t stream_id, uint8_t* codes, uint8_t* scales, float* ts_out,
+                            hipStream_t s);
 hipError_t launch_quant_col(const void* x, int64_t rows, int64_t cols, const float* amax,
                             bool rht, uint64_t rht_seed, bool sr, uint64_t seed,
                             uint32_t stream_id, uint8_t* codes, uint8_t* scales, float* ts_out,
@@ -70,5 +75,8 @@ hipError_t launch_mx_gemm(const MxOperand& a, const MxOperand& b, int64_t K, flo
 // 1 decoded-NVFP4-like, 2 uniform FP16), clock stamps left in the scratch.
 int64_t probe_scratch_bytes();
 hipError_t probe_mfma(int mode, int iters, void* scratch, hipStream_t s);
+// Clock stamps {XCC id, shader clock, 100 MHz real time, 0} of 64 workgroups.
+int64_t clock_stamp_bytes();
+hipError_t clock_stamp(void* out, hipStream_t s);
 
 }  // namespace nvfp4

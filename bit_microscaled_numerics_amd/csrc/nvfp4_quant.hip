@@ -95,6 +95,42 @@ __global__ __launch_bounds__(kThreads) void k_amax(const v4u* __restrict__ x, in
   block_max_atomic(bf << 16, out);
 }
 
+// amax of the rowwise RHT of x (the transform over every 16 consecutive
+// columns of each row), with k_amax's chunked read.  A vector (8 elements) and
+// its partner (the other half of the 16-block, vector index ^ 1) sit in
+// adjacent lanes: chunks start at even vectors and the vector count is even.
+__device__ __forceinline__ float rht_row_amax(const v4u v, uint32_t signs, bool hi) {
+  float z[8] = {bf16_lo(v.x), bf16_hi(v.x), bf16_lo(v.y), bf16_hi(v.y),
+                bf16_lo(v.z), bf16_hi(v.z), bf16_lo(v.w), bf16_hi(v.w)};
+  rht16_pair(z, signs, hi);
+  float m = 0.0f;
+#pragma unroll
+  for (int j = 0; j < 8; ++j) m = fmaxf(m, __builtin_fabsf(z[j]));
+  return m;
+}
+
+__global__ __launch_bounds__(kThreads) void k_amax_rht_row(const v4u* __restrict__ x,
+                                                             int64_t nvec, uint64_t rht_seed,
+                                                             uint32_t* __restrict__ out) {
+  const uint32_t signs = rht_sign_bits(rht_seed);
+  const bool hi = threadIdx.x & 1;   // vector index parity (chunks start at even vectors)
+  float m = 0.0f;
+  for (int64_t c = (int64_t)blockIdx.x * kAmaxChunk; c < nvec;
+       c += (int64_t)gridDim.x * kAmaxChunk) {
+    if (c + kAmaxChunk <= nvec) {
+      v4u v[kAmaxU];
+#pragma unroll
+      for (int u = 0; u < kAmaxU; ++u) v[u] = ld_(&x[c + u * kThreads + threadIdx.x]);
+#pragma unroll
+      for (int u = 0; u < kAmaxU; ++u) m = fmaxf(m, rht_row_amax(v[u], signs, hi));
+    } else {
+      for (int64_t i = c + threadIdx.x; i < nvec; i += kThreads)
+        m = fmaxf(m, rht_row_amax(ld_(&x[i]), signs, hi));
+    }
+  }
+  block_max_atomic(__float_as_uint(m), out);
+}
+
 // Load a 16-row x 8-column bf16 micro-tile (one 16-byte chunk per row) and
 // return column j's 16 values as binary32.
 struct Tile16x8 { v4u row[16]; };
@@ -164,15 +200,18 @@ __global__ __launch_bounds__(kThreads) void k_amax_rht(const uint16_t* __restric
 constexpr int kRowU = 4;
 constexpr int64_t kRowChunk = (int64_t)kRowU * kThreads;
 
-template <bool SR>
+// RHT: each 16-block is first replaced by its 16-point transform (the two
+// lanes of the block exchange their halves for the last butterfly stage).
+template <bool SR, bool RHT>
 __global__ __launch_bounds__(kThreads) void k_quant_row(
     const v4u* __restrict__ x, int64_t nvec, const float* __restrict__ amax,
-    uint64_t seed, uint32_t stream_id, uint32_t* __restrict__ codes,
+    uint64_t rht_seed, uint64_t seed, uint32_t stream_id, uint32_t* __restrict__ codes,
     uint8_t* __restrict__ scales, float* __restrict__ ts_out) {
   __shared__ float rtab[kE4m3Codes];
   static_assert(kThreads >= kE4m3Codes, "one thread per table entry");
   const ScaleCtx sc = scale_ctx(*amax, rtab, threadIdx.x);
   if (blockIdx.x == 0 && threadIdx.x == 0) *ts_out = sc.s_t;
+  const uint32_t signs = RHT ? rht_sign_bits(rht_seed) : 0u;
   __syncthreads();
   for (int64_t c = (int64_t)blockIdx.x * kRowChunk; c < nvec;
        c += (int64_t)gridDim.x * kRowChunk) {
@@ -189,6 +228,7 @@ __global__ __launch_bounds__(kThreads) void k_quant_row(
       const v4u v = vs[u];
       float z[8] = {bf16_lo(v.x), bf16_hi(v.x), bf16_lo(v.y), bf16_hi(v.y),
                     bf16_lo(v.z), bf16_hi(v.z), bf16_lo(v.w), bf16_hi(v.w)};
+      if (RHT) rht16_pair(z, signs, i & 1);
       float m = 0.0f;
 #pragma unroll
       for (int j = 0; j < 8; ++j) m = fmaxf(m, __builtin_fabsf(z[j]));
@@ -528,20 +568,34 @@ hipError_t launch_amax_rht(const void* x, int64_t rows, int64_t cols, uint64_t r
   return hipGetLastError();
 }
 
+hipError_t launch_amax_rht_row(const void* x, int64_t n_elems, uint64_t rht_seed, float* out,
+                               hipStream_t s) {
+  uint32_t* o = reinterpret_cast<uint32_t*>(out);
+  hipLaunchKernelGGL(k_zero_u32, dim3(1), dim3(1), 0, s, o, nullptr);
+  const int64_t nvec = n_elems / 8;
+  const int64_t chunks = (nvec + kAmaxChunk - 1) / kAmaxChunk;
+  hipLaunchKernelGGL(k_amax_rht_row, dim3(balanced_grid(chunks, 8)), dim3(kThreads), 0, s,
+                     reinterpret_cast<const v4u*>(x), nvec, rht_seed, o);
+  return hipGetLastError();
+}
+
 hipError_t launch_quant_row(const void* x, int64_t rows, int64_t cols, const float* amax,
-                            bool sr, uint64_t seed, uint32_t stream_id, uint8_t* codes,
-                            uint8_t* scales, float* ts_out, hipStream_t s) {
+                            bool rht, uint64_t rht_seed, bool sr, uint64_t seed,
+                            uint32_t stream_id, uint8_t* codes, uint8_t* scales, float* ts_out,
+                            hipStream_t s) {
   const int64_t nvec = rows * cols / 8;
   const int64_t chunks = (nvec + kRowChunk - 1) / kRowChunk;
   const dim3 g(grid_for(chunks * kThreads, 8)), b(kThreads);
   const v4u* xv = reinterpret_cast<const v4u*>(x);
   uint32_t* cv = reinterpret_cast<uint32_t*>(codes);
-  if (sr)
-    hipLaunchKernelGGL(k_quant_row<true>, g, b, 0, s, xv, nvec, amax, seed, stream_id, cv,
-                       scales, ts_out);
-  else
-    hipLaunchKernelGGL(k_quant_row<false>, g, b, 0, s, xv, nvec, amax, seed, stream_id, cv,
-                       scales, ts_out);
+#define NVFP4_ROW(SRV, RHTV)                                                                  \
+  hipLaunchKernelGGL((k_quant_row<SRV, RHTV>), g, b, 0, s, xv, nvec, amax, rht_seed, seed,    \
+                     stream_id, cv, scales, ts_out)
+  if (sr && rht) NVFP4_ROW(true, true);
+  else if (sr) NVFP4_ROW(true, false);
+  else if (rht) NVFP4_ROW(false, true);
+  else NVFP4_ROW(false, false);
+#undef NVFP4_ROW
   return hipGetLastError();
 }
 

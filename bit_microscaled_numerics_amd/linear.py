@@ -16,6 +16,19 @@ GPU through the C ABI; there is no CPU path (CPU tensors are rejected).
 
 Random streams: one Philox key per call (seed + step); dY's rowwise SR uses
 stream 0, the Wgrad operand of dY stream 1; the RHT signs come from rht_seed.
+
+Opt-in variant (``rht_fprop_dgrad=True``): the 16-point RHT along K on Fprop
+and Dgrad as well -- the transform may be applied to the linear layers in the
+forward and the backward pass (NVIDIA blog, Hadamard-transforms section),
+though the recipe keeps it to Wgrad and leaves Fprop / Dgrad with it
+unvalidated ("Pretraining Large Language Models with NVFP4", summary page,
+limitations paragraph).  A transform along K mixes 16 weights of a row, which
+2D 16x16 weight scaling cannot follow, so W is then quantized 1D along the K
+of each GEMM:
+
+  Fprop  Y  = Q_RHT(X) Q_RHT(W)^T           both transformed along F (rows)
+  Dgrad  dX = Q_RHT,SR(dY) Q_RHT(W^T)^T     both along H (dY's rows, W's columns)
+  Wgrad  as above
 """
 from __future__ import annotations
 
@@ -23,7 +36,8 @@ from dataclasses import dataclass
 
 import torch
 
-from . import (NVFP4Tensor, dequantize, gemm, quantize_1d, quantize_2d, rht_quantize)
+from . import (NVFP4_ROWWISE, NVFP4Tensor, dequantize, gemm, quantize_1d, quantize_2d,
+               rht_quantize)
 
 
 @dataclass
@@ -50,16 +64,32 @@ def dgrad(dy: torch.Tensor, qw: NVFP4Tensor, sr_seed: int) -> torch.Tensor:
     return gemm(quantize_1d(dy, sr_seed=sr_seed, stream_id=0), qw.t())
 
 
+def fprop_rht(x: torch.Tensor, w: torch.Tensor, rht_seed: int) -> torch.Tensor:
+    """Y = Q_RHT(X) Q_RHT(W)^T in FP32, both transformed along F (their rows)."""
+    return gemm(rht_quantize(x, rht_seed, axis=NVFP4_ROWWISE),
+                rht_quantize(w, rht_seed, axis=NVFP4_ROWWISE))
+
+
+def dgrad_rht(dy: torch.Tensor, w: torch.Tensor, rht_seed: int, sr_seed: int) -> torch.Tensor:
+    """dX = Q_RHT,SR(dY) Q_RHT(W^T)^T in FP32, both transformed along H: dY
+    along its rows, W through its quantized transpose."""
+    return gemm(rht_quantize(dy, rht_seed, sr_seed=sr_seed, stream_id=0, axis=NVFP4_ROWWISE),
+                rht_quantize(w, rht_seed))
+
+
 def wgrad(dy: torch.Tensor, x: torch.Tensor, rht_seed: int, sr_seed: int) -> torch.Tensor:
     """dW = Q_RHT,SR(dY)^T Q_RHT(X) in FP32 (RHT along the tokens)."""
     return gemm(rht_quantize(dy, rht_seed, sr_seed=sr_seed, stream_id=1), rht_quantize(x, rht_seed))
 
 
-def linear_fwd_bwd(x, w, dy, rht_seed: int, sr_seed: int):
+def linear_fwd_bwd(x, w, dy, rht_seed: int, sr_seed: int, rht_fprop_dgrad: bool = False):
     """(Y, dX, dW) of one NVFP4 linear layer in FP32 (bf16 inputs)."""
     for t, n in ((x, "x"), (w, "w"), (dy, "dy")):
         _check(t, n)
     x, w, dy = x.contiguous(), w.contiguous(), dy.contiguous()
+    if rht_fprop_dgrad:
+        return (fprop_rht(x, w, rht_seed), dgrad_rht(dy, w, rht_seed, sr_seed),
+                wgrad(dy, x, rht_seed, sr_seed))
     y, qw = fprop(x, w)
     return y, dgrad(dy, qw, sr_seed), wgrad(dy, x, rht_seed, sr_seed)
 
@@ -69,25 +99,33 @@ class NVFP4LinearFunction(torch.autograd.Function):
     FP32.  Gradients are returned in bf16 (the input dtype)."""
 
     @staticmethod
-    def forward(ctx, x: torch.Tensor, w: torch.Tensor, rht_seed: int, sr_seed: int):
+    def forward(ctx, x: torch.Tensor, w: torch.Tensor, rht_seed: int, sr_seed: int,
+                rht_fprop_dgrad: bool = False):
         _check(x, "x")
         _check(w, "w")
         x, w = x.contiguous(), w.contiguous()
-        y, qw = fprop(x, w)
-        ctx.save_for_backward(x)
+        if rht_fprop_dgrad:
+            y, qw = fprop_rht(x, w, rht_seed), None
+            ctx.save_for_backward(x, w)
+        else:
+            y, qw = fprop(x, w)
+            ctx.save_for_backward(x)
         ctx.qw = qw
         ctx.seeds = (rht_seed, sr_seed)
+        ctx.rht_fprop_dgrad = rht_fprop_dgrad
         return y
 
     @staticmethod
     def backward(ctx, dy: torch.Tensor):
-        (x,) = ctx.saved_tensors
-        qw: NVFP4Tensor = ctx.qw
+        x = ctx.saved_tensors[0]
         rht_seed, sr_seed = ctx.seeds
         dy = dy.to(torch.bfloat16).contiguous()
-        dx = dgrad(dy, qw, sr_seed)
+        if ctx.rht_fprop_dgrad:
+            dx = dgrad_rht(dy, ctx.saved_tensors[1], rht_seed, sr_seed)
+        else:
+            dx = dgrad(dy, ctx.qw, sr_seed)
         dw = wgrad(dy, x, rht_seed, sr_seed)
-        return dx.to(torch.bfloat16), dw.to(torch.bfloat16), None, None
+        return dx.to(torch.bfloat16), dw.to(torch.bfloat16), None, None, None
 
 
 class NVFP4Linear(torch.nn.Module):
@@ -95,18 +133,19 @@ class NVFP4Linear(torch.nn.Module):
     call draws a fresh SR key (seeds.sr + call index)."""
 
     def __init__(self, in_features: int, out_features: int, seeds: Seeds | None = None,
-                 device=None):
+                 device=None, rht_fprop_dgrad: bool = False):
         super().__init__()
         self.weight = torch.nn.Parameter(
             torch.empty(out_features, in_features, dtype=torch.bfloat16, device=device))
         torch.nn.init.normal_(self.weight, std=0.02)
         self.seeds = seeds or Seeds()
+        self.rht_fprop_dgrad = rht_fprop_dgrad
         self.calls = 0
 
     def forward(self, x: torch.Tensor) -> torch.Tensor:
         sr = self.seeds.sr + self.calls
         self.calls += 1
-        return NVFP4LinearFunction.apply(x, self.weight, self.seeds.rht, sr)
+        return NVFP4LinearFunction.apply(x, self.weight, self.seeds.rht, sr, self.rht_fprop_dgrad)
 
 
 @dataclass
@@ -117,19 +156,27 @@ class QDQResult:
 
 
 def qdq_reference(x: torch.Tensor, w: torch.Tensor, dy: torch.Tensor, rht_seed: int,
-                  sr_seed: int) -> QDQResult:
+                  sr_seed: int, rht_fprop_dgrad: bool = False) -> QDQResult:
     """The same layer by fake quantization: the operands quantized exactly as
     NVFP4LinearFunction does (same seeds and streams), dequantized to FP32, and
     multiplied with FP32 matmul.  The RHT operands are dequantized in the
-    transformed domain; (H D / 4)^T (H D / 4) = I makes their product dY^T X."""
+    transformed domain; (H D / 4)^T (H D / 4) = I makes their product dY^T X
+    (and X W^T, dY W when the transform is on Fprop / Dgrad too)."""
     _check(x, "x")
     _check(w, "w")
     _check(dy, "dy")
     x, w, dy = x.contiguous(), w.contiguous(), dy.contiguous()
-    qx, qw = quantize_1d(x), quantize_2d(w)
-    y = dequantize(qx) @ dequantize(qw).t().contiguous()
-    qdy = quantize_1d(dy, sr_seed=sr_seed, stream_id=0)
-    dx = dequantize(qdy) @ dequantize(qw)
+    if rht_fprop_dgrad:
+        qx = rht_quantize(x, rht_seed, axis=NVFP4_ROWWISE)
+        qwr = rht_quantize(w, rht_seed, axis=NVFP4_ROWWISE)
+        y = dequantize(qx) @ dequantize(qwr).t().contiguous()
+        qdy = rht_quantize(dy, rht_seed, sr_seed=sr_seed, stream_id=0, axis=NVFP4_ROWWISE)
+        dx = dequantize(qdy) @ dequantize(rht_quantize(w, rht_seed)).t().contiguous()
+    else:
+        qx, qw = quantize_1d(x), quantize_2d(w)
+        y = dequantize(qx) @ dequantize(qw).t().contiguous()
+        qdy = quantize_1d(dy, sr_seed=sr_seed, stream_id=0)
+        dx = dequantize(qdy) @ dequantize(qw)
     qdy_t = rht_quantize(dy, rht_seed, sr_seed=sr_seed, stream_id=1)
     qx_t = rht_quantize(x, rht_seed)
     dw = dequantize(qdy_t) @ dequantize(qx_t).t().contiguous()

@@ -26,8 +26,9 @@
  *   6. (optional) z = 1/4 * H16 * D * x along K before step 1, D = +-1 signs
  *               from Philox(key = rht_seed, counter = (0,0,0,1)), word 0
  * The GPU output is bit-identical to the CPU reference for every finite
- * input with amax_t >= 2^-100 (outputs for NaN/Inf inputs are unspecified,
- * and never out of bounds).
+ * input with amax_t >= 2^-100, and for smaller amax_t wherever every non-zero
+ * block's element scale 1/(E_b*s_t) is finite (outputs for NaN/Inf inputs
+ * are unspecified, and never out of bounds).
  *
  * Conventions (all entry points):
  *  - Every pointer is DEVICE memory owned by the caller; the library never
@@ -143,6 +144,31 @@ int nvfp4_rht_quantize(const void* x_bf16, int64_t rows, int64_t cols, uint64_t 
                        float* amax_io, int amax_mode,
                        uint8_t* codes, uint8_t* scales_e4m3, float* tensor_scale_out,
                        void* stream);
+
+/* The 16-point RHT along either axis ("NVFP4 Trains with Precision of 16-Bit
+ * and Speed and Efficiency of 4-Bit", Hadamard-transforms section: the
+ * transform can be applied to the linear layers' inputs in the forward and
+ * the backward pass; "Pretraining Large Language Models with NVFP4", summary
+ * page, limitations paragraph: the recipe itself uses it on Wgrad only, and
+ * leaves Fprop / Dgrad with it unvalidated).  Fprop and Dgrad contract over
+ * the contiguous dimension of X, W and dY, so their transform runs along the
+ * rows of x:
+ *   axis NVFP4_ROWWISE: operand = x with every 16 consecutive columns of each
+ *     row transformed; I = rows, K = cols; codes [rows][cols/2], scales
+ *     [rows][cols/16]; SR element index n = r * cols + k.
+ *   axis NVFP4_COLWISE: exactly nvfp4_amax_rht / nvfp4_rht_quantize (the
+ *     quantized transpose, transform along the rows).
+ * Both GEMM operands of a product must use the same rht_seed so that the
+ * transforms cancel.  Other arguments, outputs and validation as in
+ * nvfp4_amax_rht and nvfp4_rht_quantize; *amax_io is max |RHT(x)| along the
+ * chosen axis. */
+int nvfp4_amax_rht1d(const void* x_bf16, int64_t rows, int64_t cols, int axis,
+                     uint64_t rht_seed, float* amax_out, void* stream);
+int nvfp4_rht_quantize1d(const void* x_bf16, int64_t rows, int64_t cols, int axis,
+                         uint64_t rht_seed, int use_sr, uint64_t sr_seed, uint32_t stream_id,
+                         float* amax_io, int amax_mode,
+                         uint8_t* codes, uint8_t* scales_e4m3, float* tensor_scale_out,
+                         void* stream);
 
 /* The two quantizations of one tensor that the recipe needs both of -- the
  * rowwise 1D operand (as nvfp4_quantize1d_*, axis NVFP4_ROWWISE) and the RHT
@@ -273,6 +299,16 @@ int mxfp4_gemm(const mxfp4_operand* a, const mxfp4_operand* b, float* c, int64_t
  * 100 MHz, and the run's duration is (max end - min start) real-time ticks. */
 int64_t nvfp4_probe_scratch_bytes(void);
 int nvfp4_probe_mfma(int mode, int iters, void* scratch, int64_t scratch_bytes, void* stream);
+
+/* Measurement support: clock stamps.  Enqueues on `stream` one small launch
+ * whose 64 workgroups each write 4 uint64 {XCC id, shader-clock counter,
+ * 100 MHz real-time counter, 0} into `stamps` (device memory of at least
+ * nvfp4_probe_clock_bytes() bytes, 8-byte aligned, caller-owned).  Stamps
+ * taken before and after other work on the same stream give, per XCD (the
+ * shader-clock counters of different XCDs are unrelated), d(shader) /
+ * d(real-time) * 100 MHz: the average clock that work ran at. */
+int64_t nvfp4_probe_clock_bytes(void);
+int nvfp4_probe_clock(void* stamps, int64_t stamps_bytes, void* stream);
 
 /* Human-readable name of a status code (static storage). */
 const char* nvfp4_status_string(int status);

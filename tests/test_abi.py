@@ -196,3 +196,33 @@ def test_quantize_row_rht_validation(lib):
     assert f(*a) == nv.NVFP4_ERR_ARG
     a = list(args); a[1] = 24      # rows not a multiple of 16
     assert f(*a) == nv.NVFP4_ERR_SHAPE
+
+
+def test_rht1d_validation(lib):
+    """Both axes of the RHT entry points validate before launching; the
+    COLWISE axis forwards to nvfp4_amax_rht / nvfp4_rht_quantize."""
+    a = lib.nvfp4_amax_rht1d
+    for axis in (0, 1):
+        assert a(None, 16, 16, axis, 1, FAKE, None) == nv.NVFP4_ERR_NULL
+        assert a(FAKE, 16, 24, axis, 1, FAKE, None) == nv.NVFP4_ERR_SHAPE
+        assert a(MIS, 16, 16, axis, 1, FAKE, None) == nv.NVFP4_ERR_ALIGN
+        assert a(FAKE, 16, 16, axis, 1, None, None) == nv.NVFP4_ERR_NULL
+    assert a(FAKE, 16, 16, 2, 1, FAKE, None) == nv.NVFP4_ERR_ARG
+    q = lib.nvfp4_rht_quantize1d
+    args = [FAKE, 32, 16, 0, 1, 0, 0, 0, FAKE, 0, FAKE, FAKE, FAKE, None]
+    for axis in (0, 1):
+        b = list(args); b[3] = axis
+        c = list(b); c[10] = None          # codes
+        assert q(*c) == nv.NVFP4_ERR_NULL
+        c = list(b); c[10] = MIS
+        assert q(*c) == nv.NVFP4_ERR_ALIGN
+        c = list(b); c[5] = 2              # use_sr
+        assert q(*c) == nv.NVFP4_ERR_ARG
+        c = list(b); c[9] = 2              # amax_mode
+        assert q(*c) == nv.NVFP4_ERR_ARG
+        c = list(b); c[2] = 8              # cols
+        assert q(*c) == nv.NVFP4_ERR_SHAPE
+        c = list(b); c[8] = None           # amax_io
+        assert q(*c) == nv.NVFP4_ERR_NULL
+    b = list(args); b[3] = -1
+    assert q(*b) == nv.NVFP4_ERR_ARG

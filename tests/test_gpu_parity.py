@@ -99,6 +99,26 @@ def test_rht_quantize(shape, kind, sr):
 @pytest.mark.parametrize("shape", SHAPES)
 @pytest.mark.parametrize("kind", KINDS)
 @pytest.mark.parametrize("sr", [False, True])
+def test_rht_quantize_rowwise(shape, kind, sr):
+    """The transform along each row (the Fprop / Dgrad operands' K): amax
+    computed and given, RTN and SR."""
+    x = _tensor(kind, *shape, seed=3)
+    kw = {"sr_seed": 0xABCD_0000_0077, "stream_id": 4} if sr else {}
+    say("rht_quantize rowwise", shape, kind, sr)
+    xd = x.cuda()
+    g = nv.rht_quantize(xd, 99, axis=nv.NVFP4_ROWWISE, **kw)
+    am = nv.amax_rht(xd, 99, nv.NVFP4_ROWWISE)
+    g2 = nv.rht_quantize(xd, 99, axis=nv.NVFP4_ROWWISE, amax=am, **kw)
+    torch.cuda.synchronize()
+    o = oracle.quantize(x, oracle.ROWWISE, rht_seed=99, **kw)
+    assert_operand_equal(g, o, f"rht rowwise {shape} {kind} sr={sr}")
+    assert_operand_equal(g2, o, f"rht rowwise, amax given {shape} {kind} sr={sr}")
+    assert float(am.cpu()[0]) == oracle.amax_rht(x.t().contiguous(), 99)
+
+
+@pytest.mark.parametrize("shape", SHAPES)
+@pytest.mark.parametrize("kind", KINDS)
+@pytest.mark.parametrize("sr", [False, True])
 def test_quantize_row_rht_one_read(shape, kind, sr):
     """Rowwise operand and RHT transpose from one read: each bit-exact with the
     oracle and byte-identical to the two single calls (same seeds, streams)."""

@@ -205,6 +205,33 @@ def test_rht_quantize_equals_quantize_of_transformed_input():
     assert q1.amax == oracle.amax_rht(x, seed) == float(np.abs(zt).max())
 
 
+def test_rowwise_rht_is_the_operand_of_the_transpose():
+    """The transform along K on the rowwise layout (Fprop / Dgrad operands)
+    quantizes the same K-contiguous operand as the transpose-quantize of x^T
+    with the transform along its rows: identical codes, scales, amax and
+    Philox indexing (both number the operand's elements r * K + k).  And for
+    integer inputs whose transform bf16 holds exactly, it equals quantizing
+    the explicitly transformed tensor."""
+    g = torch.Generator().manual_seed(17)
+    x = inputs.normal(g, 48, 96, 1.0, 0.01, 20.0)
+    xt = x.t().contiguous()
+    for kw in ({}, {"sr_seed": 5, "stream_id": 2}):
+        qr = oracle.quantize(x, oracle.ROWWISE, rht_seed=9, **kw)
+        qc = oracle.quantize(xt, oracle.COLWISE, rht_seed=9, **kw)
+        assert np.array_equal(qr.codes, qc.codes) and np.array_equal(qr.scales, qc.scales)
+        assert qr.amax == qc.amax == oracle.amax_rht(xt, 9)
+    rng = np.random.default_rng(18)
+    xi = rng.integers(-8, 9, size=(32, 32)).astype(np.float32)
+    s = oracle.rht_signs(4)
+    zr = np.stack([np.concatenate([oracle.rht16(xi[i, 16 * gg:16 * gg + 16], s)
+                                   for gg in range(2)]) for i in range(32)])
+    assert np.array_equal(bf16(zr).float().numpy(), zr)
+    q1 = oracle.quantize(bf16(xi), oracle.ROWWISE, rht_seed=4)
+    q2 = oracle.quantize(bf16(zr), oracle.ROWWISE)
+    assert np.array_equal(q1.codes, q2.codes) and np.array_equal(q1.scales, q2.scales)
+    assert q1.amax == float(np.abs(zr).max())
+
+
 def test_2d_tiles_codes_t_and_agreement_with_1d():
     g = torch.Generator().manual_seed(16)
     x = inputs.normal(g, 64, 96, 0.02)
