@@ -50,7 +50,7 @@ def log(*a):
     print("[bench]", *a, file=sys.stderr, flush=True)
 
 
-GEMM_SOURCES = ("nvfp4_gemm.hip", "gemm_tiles.h", "nvfp4_device.h")
+GEMM_SOURCES = ("nvfp4_gemm.hip", "gemm_tiles.h", "gemm_decode.h", "nvfp4_device.h")
 
 
 def gemm_traffic():
@@ -66,6 +66,38 @@ def gemm_traffic():
         with open(os.path.join(ROOT, "bit_microscaled_numerics_amd", "csrc", f), "rb") as fh:
             m.update(fh.read())
     return rec["traffic_bytes_per_launch"] if m.hexdigest() == rec["source_sha256"] else None
+
+
+class Flush:
+    """Evicts the 256 MB Infinity Cache (and the L2s) between timed launches:
+    a 1 GiB fill, outside the timed interval, so a kernel that re-reads a
+    tensor another kernel has just read (an encode after its amax) is timed
+    from HBM, not from the cache."""
+
+    def __init__(self, nbytes: int = 1 << 30):
+        self.buf = torch.empty(nbytes, dtype=torch.uint8, device="cuda")
+        self.k = 0
+
+    def __call__(self):
+        self.k ^= 1
+        self.buf.fill_(self.k)
+
+
+def copy_peak(reps: int = 10):
+    """HBM bandwidth of a plain device copy of 1 GiB (the library's probe
+    copy kernel, the read pattern of the amax and rowwise kernels; torch's
+    copy_ beside it): 2 GiB moved per launch; medians of `reps`."""
+    src = torch.empty(1 << 29, dtype=torch.bfloat16, device="cuda").fill_(1.0)
+    dst = torch.empty_like(src)
+    nbytes = 2.0 * src.numel() * 2
+    ms = _median_ms(lambda: nv.probe_copy(src, dst), reps)
+    ms_torch = _median_ms(lambda: dst.copy_(src), reps)
+    gbs = nbytes / (ms * 1e-3) / 1e9
+    del src, dst
+    torch.cuda.empty_cache()
+    return {"GB/s": round(gbs, 1), "frac": round(gbs / HBM_PEAK_GBS, 3), "bytes": int(nbytes),
+            "kernel": "nvfp4_probe_copy of 1 GiB (read + write)",
+            "torch_copy_GB/s": round(nbytes / (ms_torch * 1e-3) / 1e9, 1)}
 
 
 class Step:
@@ -128,6 +160,19 @@ class Step:
         if events is not None:
             events[len(self.ops)].record()
 
+    def run_cold(self, flush, events, stamps):
+        """Each launch on its own, the cache flushed before it, its own HIP
+        events around it, and clock stamps around every GEMM."""
+        for i, (_, kind, _, fn) in enumerate(self.ops):
+            flush()
+            if kind == "mfma":
+                stamps[i].before()
+            events[i][0].record()
+            fn()
+            events[i][1].record()
+            if kind == "mfma":
+                stamps[i].after()
+
     def run_overlapped(self, start=None, end=None):
         """The same launches with the independent chains on a second stream
         (default priority), in the order a forward + backward pass has them:
@@ -166,13 +211,18 @@ class Step:
             end.record(main)
 
 
-def cpu_baseline(x, w, dy, budget_s: float = 15.0):
-    """The oracle, as it stands, on a bounded sample of the same step: a slice
-    of rows of every quantization and a set of entries of every GEMM, timed
-    and extrapolated linearly to the full step."""
+def cpu_baseline(x, w, dy, c5=None, gpu_c5_us=None):
+    """The oracle, as it stands, on the same host bytes as the GPU:
+      * the step: a slice of rows of every quantization and a set of exact
+        entries of every GEMM, timed on all threads and extrapolated linearly
+        to the whole step (the `value`, in the metric's unit);
+      * the 32768x8192 quantize (1D RTN including its amax, the first sweep
+        tensor, whole) on all threads and on one thread, its codes compared
+        with the GPU's."""
     import oracle
     T, F = x.shape
     H = w.shape[0]
+    threads = oracle.num_threads()
     rows = 64   # sampled rows / columns of each quantized tensor
     t_quant = 0.0
     full_quant = 0.0
@@ -192,7 +242,7 @@ def cpu_baseline(x, w, dy, budget_s: float = 15.0):
         dt = time.perf_counter() - t0
         t_quant += dt
         full_quant += dt / frac
-    # GEMM entries: pick n entries per GEMM so the sample is ~budget seconds
+    # GEMM entries: pick n entries per GEMM so the sample is ~8 seconds
     ox = oracle.quantize(x[:256].contiguous(), oracle.ROWWISE)
     ow = oracle.quantize(w[:256].contiguous(), oracle.TWO_D)
     rng = np.random.default_rng(0)
@@ -202,9 +252,7 @@ def cpu_baseline(x, w, dy, budget_s: float = 15.0):
     t0 = time.perf_counter()
     oracle.gemm_entries(ox, ow, ms, ns)
     dt = time.perf_counter() - t0
-    per_mac = dt / (n * F)
-    # scale the sample up until it costs about the budget, then re-time
-    n2 = int(min(2_000_000, max(n, n * (budget_s - t_quant) / max(dt, 1e-6) * 0.8)))
+    n2 = int(min(2_000_000, max(n, n * 8.0 / max(dt, 1e-6))))
     ms = rng.integers(0, 256, n2)
     ns = rng.integers(0, 256, n2)
     t0 = time.perf_counter()
@@ -214,53 +262,90 @@ def cpu_baseline(x, w, dy, budget_s: float = 15.0):
     macs_step = 3.0 * T * H * F
     full = full_quant + per_mac * macs_step
     flops = 2.0 * macs_step
-    return {"value": flops / full / 1e12, "unit": "TFLOP/s", "cores": oracle.num_threads(),
-            "kind": "oracle",
-            "sample": (f"oracle quantize of {rows} rows/cols of each of the 5 operands "
-                       f"({t_quant:.2f} s) + {n2} exact GEMM entries at K={F} ({dt:.2f} s), "
-                       f"extrapolated to one full step ({full:.0f} s)")}
+    out = {"value": flops / full / 1e12, "unit": "TFLOP/s", "cores": threads, "kind": "oracle",
+           "sample": (f"oracle quantize of {rows} rows/cols of each of the 5 operands "
+                      f"({t_quant:.2f} s) + {n2} exact GEMM entries at K={F} ({dt:.2f} s), "
+                      f"{threads} threads, extrapolated to one full step ({full:.0f} s)")}
+    if c5 is not None:
+        xc5, gpu_codes, gpu_scales = c5
+        nbytes = 4.5625 * xc5.numel()
+        rec = {"workload": "1D RTN quantize incl. amax, 32768x8192 bf16 N(0,1), whole tensor"}
+        for th in (threads, 1):
+            oracle.set_num_threads(th)
+            t0 = time.perf_counter()
+            q = oracle.quantize(xc5, oracle.ROWWISE)
+            dt = time.perf_counter() - t0
+            rec[f"s_{th}_threads"] = round(dt, 3)
+            rec[f"GB/s_{th}_threads"] = round(nbytes / dt / 1e9, 3)
+        oracle.set_num_threads(threads)
+        rec["codes_equal_gpu"] = bool(np.array_equal(q.codes, gpu_codes) and
+                                      np.array_equal(q.scales, gpu_scales))
+        if gpu_c5_us:
+            rec["gpu_us"] = gpu_c5_us
+            rec["gpu_speedup_vs_all_threads"] = round(rec[f"s_{threads}_threads"] /
+                                                      (gpu_c5_us * 1e-6), 1)
+        out["quantize_32768x8192"] = rec
+    return out
 
 
-def quant_sweep(steps: int = 10):
-    """Quantize-only bandwidth on 32768x8192 tensors (N(0,1) and Student-t):
-    1D / 2D x RTN / SR, RHT on / off.  Returns GB/s per variant."""
-    dev = torch.device("cuda")
-    g = torch.Generator(device=dev).manual_seed(0)
-    R, C = 32768, 8192
+def quant_sweep(flush, steps: int = 10, keep_first=False):
+    """Quantize-only bandwidth on 32768x8192 tensors (N(0,1) and Student-t,
+    generated on the host from seed 0 and copied over): 1D / 2D / colwise
+    x RTN / SR, RHT along either axis, with and without the amax pass, and
+    MXFP4.  The cache is flushed before every timed launch.  Returns GB/s per
+    variant (and, with keep_first, the N(0,1) tensor on the host with the
+    GPU's 1D RTN codes and scales, for the oracle's timing on the same bytes)."""
+    wl = inputs.sweep_tensors(0)
     out = {}
+    kept = None
     for dist in ["normal", "t3"]:
-        if dist == "normal":
-            x = torch.randn(R, C, generator=g, device=dev).to(torch.bfloat16)
-        else:
-            z = torch.randn(4, R, C, generator=g, device=dev)
-            x = (z[0] / torch.sqrt((z[1] ** 2 + z[2] ** 2 + z[3] ** 2) / 3)).to(torch.bfloat16)
-            del z
+        xh = wl.tensors.pop(dist)
+        x = xh.cuda()
         n = x.numel()
         q1 = nv.quantize_1d(x)
         q2 = nv.quantize_2d(x)
         qc = nv.quantize_1d(x, nv.NVFP4_COLWISE)
+        qr = nv.rht_quantize(x, 1, axis=nv.NVFP4_ROWWISE)
         qm = nv.mx_quantize(x)
-        G = nv.NVFP4_AMAX_GIVEN
+        torch.cuda.synchronize()
+        if keep_first and kept is None:
+            kept = (xh, q1.codes.cpu().numpy(), q1.scales.cpu().numpy())
+        del xh
+        G, CMP, ROW = nv.NVFP4_AMAX_GIVEN, nv.NVFP4_AMAX_COMPUTE, nv.NVFP4_ROWWISE
         variants = [
             ("amax", 2 * n, lambda: nv.nvfp4_amax(x, q1.amax)),
             ("1d RTN encode", 2.5625 * n, lambda: nv.nvfp4_quantize1d_rtn(
                 x, 0, q1.amax, G, q1.codes, q1.scales, q1.tensor_scale)),
             ("1d SR encode", 2.5625 * n, lambda: nv.nvfp4_quantize1d_sr(
                 x, 0, q1.amax, G, 7, 0, q1.codes, q1.scales, q1.tensor_scale)),
+            ("1d RTN incl. amax", 4.5625 * n, lambda: nv.nvfp4_quantize1d_rtn(
+                x, 0, q1.amax, CMP, q1.codes, q1.scales, q1.tensor_scale)),
+            ("1d SR incl. amax", 4.5625 * n, lambda: nv.nvfp4_quantize1d_sr(
+                x, 0, q1.amax, CMP, 7, 0, q1.codes, q1.scales, q1.tensor_scale)),
             ("2d RTN encode", 2.50390625 * n, lambda: nv.nvfp4_quantize2d_rtn(
                 x, q2.amax, G, q2.codes, None, q2.scales, None, q2.tensor_scale)),
             ("2d RTN encode +transposed", 3.0078125 * n, lambda: nv.nvfp4_quantize2d_rtn(
                 x, q2.amax, G, q2.codes, q2.codes_t, q2.scales, q2.scales_t, q2.tensor_scale)),
+            ("2d RTN incl. amax", 4.50390625 * n, lambda: nv.nvfp4_quantize2d_rtn(
+                x, q2.amax, CMP, q2.codes, None, q2.scales, None, q2.tensor_scale)),
             ("col RTN encode", 2.5625 * n, lambda: nv.nvfp4_quantize1d_rtn(
                 x, 1, qc.amax, G, qc.codes, qc.scales, qc.tensor_scale)),
-            ("amax RHT", 2 * n, lambda: nv.nvfp4_amax_rht(x, 1, qc.amax)),
+            ("amax RHT col", 2 * n, lambda: nv.nvfp4_amax_rht(x, 1, qc.amax)),
+            ("col RHT RTN encode", 2.5625 * n, lambda: nv.nvfp4_rht_quantize(
+                x, 1, 0, 0, 0, qc.amax, G, qc.codes, qc.scales, qc.tensor_scale)),
             ("col RHT SR encode", 2.5625 * n, lambda: nv.nvfp4_rht_quantize(
                 x, 1, 1, 7, 0, qc.amax, G, qc.codes, qc.scales, qc.tensor_scale)),
-            ("1d RTN incl. amax", 4.5625 * n, lambda: nv.nvfp4_quantize1d_rtn(
-                x, 0, q1.amax, nv.NVFP4_AMAX_COMPUTE, q1.codes, q1.scales, q1.tensor_scale)),
-            ("RHT SR incl. amax", 4.5625 * n, lambda: nv.nvfp4_rht_quantize(
-                x, 1, 1, 7, 0, qc.amax, nv.NVFP4_AMAX_COMPUTE, qc.codes, qc.scales,
-                qc.tensor_scale)),
+            ("col RHT RTN incl. amax", 4.5625 * n, lambda: nv.nvfp4_rht_quantize(
+                x, 1, 0, 0, 0, qc.amax, CMP, qc.codes, qc.scales, qc.tensor_scale)),
+            ("col RHT SR incl. amax", 4.5625 * n, lambda: nv.nvfp4_rht_quantize(
+                x, 1, 1, 7, 0, qc.amax, CMP, qc.codes, qc.scales, qc.tensor_scale)),
+            ("amax RHT row", 2 * n, lambda: nv.nvfp4_amax_rht1d(x, ROW, 1, qr.amax)),
+            ("row RHT RTN encode", 2.5625 * n, lambda: nv.nvfp4_rht_quantize1d(
+                x, ROW, 1, 0, 0, 0, qr.amax, G, qr.codes, qr.scales, qr.tensor_scale)),
+            ("row RHT SR encode", 2.5625 * n, lambda: nv.nvfp4_rht_quantize1d(
+                x, ROW, 1, 1, 7, 0, qr.amax, G, qr.codes, qr.scales, qr.tensor_scale)),
+            ("row RHT SR incl. amax", 4.5625 * n, lambda: nv.nvfp4_rht_quantize1d(
+                x, ROW, 1, 1, 7, 0, qr.amax, CMP, qr.codes, qr.scales, qr.tensor_scale)),
             ("MXFP4 RTN (single pass)", 2.53125 * n, lambda: nv.mxfp4_quantize(
                 x, 0, 0, 0, qm.codes, qm.scales)),
             ("MXFP4 SR (single pass)", 2.53125 * n, lambda: nv.mxfp4_quantize(
@@ -269,20 +354,21 @@ def quant_sweep(steps: int = 10):
         s = torch.cuda.current_stream()
         for name, nbytes, fn in variants:
             fn()
-            ev = [torch.cuda.Event(enable_timing=True) for _ in range(steps + 1)]
-            s.synchronize()
-            for i in range(steps):
-                ev[i].record(s)
+            ev = [(torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True))
+                  for _ in range(steps)]
+            for a, b in ev:
+                flush()
+                a.record(s)
                 fn()
-            ev[steps].record(s)
+                b.record(s)
             s.synchronize()
-            ms = float(np.median([ev[i].elapsed_time(ev[i + 1]) for i in range(steps)]))
+            ms = float(np.median([a.elapsed_time(b) for a, b in ev]))
             out[f"{dist} {name}"] = {"us": round(ms * 1e3, 1),
                                      "GB/s": round(nbytes / (ms * 1e-3) / 1e9, 1),
                                      "frac": round(nbytes / (ms * 1e-3) / 1e9 / HBM_PEAK_GBS, 3)}
-        del x, q1, q2, qc, qm
+        del x, q1, q2, qc, qr, qm
         torch.cuda.empty_cache()
-    return out
+    return (out, kept) if keep_first else out
 
 
 def _median_ms(fn, reps: int) -> float:
@@ -442,8 +528,8 @@ def main():
                          "profiler runs over the quantizer kernels on large tensors)")
     ap.add_argument("--seed", type=int, default=0)
     ap.add_argument("--copy-calibration", action="store_true",
-                    help="first run a plain 1 GiB device copy (3 launches), the reference "
-                         "for scaling HBM byte counters")
+                    help="first run the plain 1 GiB device copy k_copy (3 launches), the "
+                         "reference for scaling HBM byte counters")
     args = ap.parse_args()
     if args.step_only:
         args.no_mx = args.no_quality = args.no_sweep = args.no_cpu_baseline = True
@@ -460,13 +546,14 @@ def main():
         src = torch.empty(1 << 29, dtype=torch.bfloat16, device="cuda").fill_(1.0)
         dst = torch.empty_like(src)
         for _ in range(3):
-            dst.copy_(src)
+            nv.probe_copy(src, dst)
         torch.cuda.synchronize()
-        log("copy calibration: 3 x copy of 1 GiB (read 1 GiB + write 1 GiB each)")
+        log("copy calibration: 3 x k_copy of 1 GiB (read 1 GiB + write 1 GiB each)")
         del src, dst
     if args.sweep_only:
         log("quantize sweep 32768x8192")
-        print(json.dumps({"quantize_sweep_32768x8192": quant_sweep(max(args.steps, 2))}),
+        print(json.dumps({"quantize_sweep_32768x8192": quant_sweep(Flush(),
+                                                                    max(args.steps, 2))}),
               flush=True)
         return
 
@@ -476,7 +563,10 @@ def main():
     dev = torch.device("cuda")
     x, w, dy = xh.to(dev), wh.to(dev), dyh.to(dev)
     step = Step(x, w, dy)
-    stream = torch.cuda.current_stream()
+
+    flush = Flush()
+    log("hbm copy peak")
+    hbm_copy = copy_peak()
 
     log(f"warmup {args.warmup}")
     for _ in range(args.warmup):
@@ -484,18 +574,32 @@ def main():
     torch.cuda.synchronize()
 
     nops = len(step.ops)
+    # serial pass: the launches back to back, events between them (warm caches)
     evs = [[torch.cuda.Event(enable_timing=True) for _ in range(nops + 1)]
            for _ in range(args.steps)]
-    log(f"timing {args.steps} steps")
+    log(f"timing {args.steps} serial steps")
     torch.cuda.synchronize()
-    t0 = time.perf_counter()
     for k in range(args.steps):
         step.run(evs[k])
     torch.cuda.synchronize()
-    wall = time.perf_counter() - t0
-    per_op = np.array([[evs[k][i].elapsed_time(evs[k][i + 1]) for i in range(nops)]
+    per_op_warm = np.array([[evs[k][i].elapsed_time(evs[k][i + 1]) for i in range(nops)]
+                            for k in range(args.steps)])  # ms
+    serial_ms = float(np.median([evs[k][0].elapsed_time(evs[k][nops])
+                                 for k in range(args.steps)]))
+    # cold pass: every launch timed on its own after a cache flush, GEMM clocks
+    log(f"timing {args.steps} cold-cache passes")
+    gemm_idx = [i for i, o in enumerate(step.ops) if o[1] == "mfma"]
+    stamps = {i: nv.ClockStamps() for i in gemm_idx}
+    clocks = {i: [] for i in gemm_idx}
+    cev = [[(torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True))
+            for _ in range(nops)] for _ in range(args.steps)]
+    for k in range(args.steps):
+        step.run_cold(flush, cev[k], stamps)
+        for i in gemm_idx:
+            clocks[i].append(stamps[i].ghz())
+    torch.cuda.synchronize()
+    per_op = np.array([[cev[k][i][0].elapsed_time(cev[k][i][1]) for i in range(nops)]
                        for k in range(args.steps)])  # ms
-    serial_ms = float(np.mean([evs[k][0].elapsed_time(evs[k][nops]) for k in range(args.steps)]))
     # the step as a framework would run it: independent chains on two streams
     log(f"timing {args.steps} overlapped steps")
     for _ in range(max(args.warmup, 1)):
@@ -508,30 +612,35 @@ def main():
         step.run_overlapped(*oev[k])
     torch.cuda.synchronize()
     wall = time.perf_counter() - t0
-    step_ms = float(np.mean([a.elapsed_time(b) for a, b in oev]))
+    step_ms = float(np.median([a.elapsed_time(b) for a, b in oev]))
     gemm_flops = sum(a for (_, kind, a, _) in step.ops if kind == "mfma")
     value = gemm_flops / (step_ms * 1e-3) / 1e12
 
     kernels = {}
     for i, (name, kind, amount, _) in enumerate(step.ops):
-        ms = float(per_op[:, i].mean())
+        ms = float(np.median(per_op[:, i]))
+        rec = {"us": round(ms * 1e3, 1), "us_warm": round(float(np.median(per_op_warm[:, i])) * 1e3, 1)}
         if kind == "hbm":
             gbs = amount / (ms * 1e-3) / 1e9
-            kernels[name] = {"us": round(ms * 1e3, 1), "GB/s": round(gbs, 1),
-                             "frac_hbm": round(gbs / HBM_PEAK_GBS, 3)}
+            rec.update({"GB/s": round(gbs, 1), "frac_hbm": round(gbs / HBM_PEAK_GBS, 3),
+                        "frac_copy": round(gbs / hbm_copy["GB/s"], 3)})
         else:
             tf = amount / (ms * 1e-3) / 1e12
-            kernels[name] = {"us": round(ms * 1e3, 1), "TFLOP/s": round(tf, 1),
-                             "frac_mfma": round(tf / MFMA_F16_PEAK_TFLOPS, 3)}
-    gemm_idx = [i for i, o in enumerate(step.ops) if o[1] == "mfma"]
-    gemm_ms = float(per_op[:, gemm_idx].mean())
+            rec.update({"TFLOP/s": round(tf, 1), "frac_mfma": round(tf / MFMA_F16_PEAK_TFLOPS, 3),
+                        "clock_GHz": round(float(np.median(clocks[i])), 3)})
+        kernels[name] = rec
+    gemm_ms_mean = float(per_op[:, gemm_idx].mean())
     gemm_flops_launch = gemm_flops / len(gemm_idx)
-    achieved = gemm_flops_launch / (gemm_ms * 1e-3) / 1e12
+    achieved = gemm_flops_launch / (gemm_ms_mean * 1e-3) / 1e12
     roofline = {"bound": "mfma", "kernel": "k_gemm_dma (Fprop, Dgrad, Wgrad launches)",
                 "achieved": round(achieved, 1), "peak": MFMA_F16_PEAK_TFLOPS,
                 "unit": "TFLOP/s", "frac": round(achieved / MFMA_F16_PEAK_TFLOPS, 4),
-                "traffic": gemm_traffic()}
-    quant_ms = float(per_op[:, [i for i in range(nops) if i not in gemm_idx]].sum(axis=1).mean())
+                "traffic": gemm_traffic(),
+                "launch_us_mean": round(gemm_ms_mean * 1e3, 1),
+                "clock_GHz_median": round(float(np.median([c for i in gemm_idx
+                                                           for c in clocks[i]])), 3)}
+    quant_idx = [i for i in range(nops) if i not in gemm_idx]
+    quant_ms = float(np.median(per_op[:, quant_idx].sum(axis=1)))
     quant_bytes = sum(a for (_, kind, a, _) in step.ops if kind == "hbm")
 
     result = {
@@ -547,9 +656,14 @@ def main():
                             "Wgrad 5120x20480x8192",
                    "quantization": "X 1D RTN, W 2D RTN, dY 1D SR, Wgrad inputs RHT16 "
                                    "(dY SR, X RTN)"},
+        "timing": "medians of HIP events on the launch stream; `value` and ms_per_step from the "
+                  "overlapped step (warm caches, as in training); per-kernel us / GB/s from "
+                  "launches timed one by one after a 1 GiB cache-flush write (us_warm: the "
+                  "serial pass without the flush); roofline.achieved from the mean GEMM launch",
         "gemm_tflops": round(achieved, 1),
         "quantize_gbs": round(quant_bytes / (quant_ms * 1e-3) / 1e9, 1),
         "quantize_ms_per_step": round(quant_ms, 4),
+        "hbm_copy_peak": hbm_copy,
         "kernels": kernels,
         "roofline": roofline,
         "wall_s_timed": round(wall, 4),
@@ -572,12 +686,18 @@ def main():
     if not args.no_quality:
         log("quality (cosine vs FP32 products)")
         result["quality"] = quality(step)
+    c5 = None
     if not args.no_sweep:
         log("quantize sweep 32768x8192")
-        result["quantize_sweep_32768x8192"] = quant_sweep()
+        del step, x, w, dy
+        torch.cuda.empty_cache()
+        sweep, c5 = quant_sweep(flush, keep_first=not args.no_cpu_baseline)
+        result["quantize_sweep_32768x8192"] = sweep
     if not args.no_cpu_baseline:
-        log("cpu baseline (oracle) on a bounded sample")
-        result["cpu_baseline"] = cpu_baseline(xh, wh, dyh)
+        log("cpu baseline (oracle) on the same host bytes")
+        gpu_us = result.get("quantize_sweep_32768x8192", {}).get(
+            "normal 1d RTN incl. amax", {}).get("us")
+        result["cpu_baseline"] = cpu_baseline(xh, wh, dyh, c5, gpu_us)
     print(json.dumps(result), flush=True)
 
 

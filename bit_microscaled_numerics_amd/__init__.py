@@ -35,7 +35,7 @@ EXPORTED = ("nvfp4_amax", "nvfp4_amax_rht", "nvfp4_quantize1d_rtn", "nvfp4_quant
             "nvfp4_gemm_bf16", "mxfp4_quantize", "mxfp4_dequantize", "mxfp4_gemm",
             "nvfp4_probe_mfma", "nvfp4_probe_scratch_bytes", "nvfp4_amax_both",
             "nvfp4_quantize_row_rht", "nvfp4_amax_rht1d", "nvfp4_rht_quantize1d",
-            "nvfp4_probe_clock", "nvfp4_probe_clock_bytes")
+            "nvfp4_probe_clock", "nvfp4_probe_clock_bytes", "nvfp4_probe_copy")
 
 
 class NVFP4Error(RuntimeError):
@@ -95,6 +95,7 @@ def load_library(path: str = LIB_PATH) -> ctypes.CDLL:
         "mxfp4_gemm": [ctypes.POINTER(c_mx_operand), ctypes.POINTER(c_mx_operand), vp, i64, vp],
         "nvfp4_probe_mfma": [i32, i32, vp, i64, vp],
         "nvfp4_probe_clock": [vp, i64, vp],
+        "nvfp4_probe_copy": [vp, vp, i64, vp],
     }
     for name, args in sigs.items():
         fn = getattr(lib, name)
@@ -125,6 +126,12 @@ def _p(t: Optional[torch.Tensor]):
 def _stream(stream=None):
     s = torch.cuda.current_stream() if stream is None else stream
     return s.cuda_stream
+
+
+def _empty(*shape, dtype, device) -> torch.Tensor:
+    """Every output buffer of the allocating functions below comes from here
+    (one place to replace the allocator, e.g. with guard-banded buffers)."""
+    return torch.empty(*shape, dtype=dtype, device=device)
 
 
 def _dev_bf16(x: torch.Tensor, name: str):
@@ -263,22 +270,22 @@ class NVFP4Tensor:
 
 
 def _outputs(I, K, dev, scale_shape):
-    codes = torch.empty(I, K // 2, dtype=torch.uint8, device=dev)
-    scales = torch.empty(*scale_shape, dtype=torch.uint8, device=dev)
-    ts = torch.empty(1, dtype=torch.float32, device=dev)
+    codes = _empty(I, K // 2, dtype=torch.uint8, device=dev)
+    scales = _empty(*scale_shape, dtype=torch.uint8, device=dev)
+    ts = _empty(1, dtype=torch.float32, device=dev)
     return codes, scales, ts
 
 
 def _amax_arg(x, amax):
     if amax is None:
-        return torch.empty(1, dtype=torch.float32, device=x.device), NVFP4_AMAX_COMPUTE
+        return _empty(1, dtype=torch.float32, device=x.device), NVFP4_AMAX_COMPUTE
     if isinstance(amax, torch.Tensor):
         return amax, NVFP4_AMAX_GIVEN
     return torch.tensor([float(amax)], dtype=torch.float32, device=x.device), NVFP4_AMAX_GIVEN
 
 
 def amax(x: torch.Tensor) -> torch.Tensor:
-    out = torch.empty(1, dtype=torch.float32, device=x.device)
+    out = _empty(1, dtype=torch.float32, device=x.device)
     nvfp4_amax(x, out)
     return out
 
@@ -286,14 +293,14 @@ def amax(x: torch.Tensor) -> torch.Tensor:
 def amax_rht(x: torch.Tensor, rht_seed: int, axis: int = NVFP4_COLWISE) -> torch.Tensor:
     """max |RHT(x)| with the transform along the rows (COLWISE, the Wgrad
     layout) or along each row (ROWWISE)."""
-    out = torch.empty(1, dtype=torch.float32, device=x.device)
+    out = _empty(1, dtype=torch.float32, device=x.device)
     nvfp4_amax_rht1d(x, axis, rht_seed, out)
     return out
 
 
 def amax_both(x: torch.Tensor, rht_seed: int):
     """(max |x|, max |RHT(x^T)|) from one read of x, as two 1-element tensors."""
-    out = torch.empty(2, dtype=torch.float32, device=x.device)
+    out = _empty(2, dtype=torch.float32, device=x.device)
     nvfp4_amax_both(x, rht_seed, out[0:1], out[1:2])
     return out[0:1], out[1:2]
 
@@ -321,8 +328,8 @@ def quantize_2d(w: torch.Tensor, sr_seed: Optional[int] = None, stream_id: int =
     codes, scales, ts = _outputs(R, C, w.device, (R // 16, C // 16))
     codes_t = scales_t = None
     if with_codes_t:
-        codes_t = torch.empty(C, R // 2, dtype=torch.uint8, device=w.device)
-        scales_t = torch.empty(C // 16, R // 16, dtype=torch.uint8, device=w.device)
+        codes_t = _empty(C, R // 2, dtype=torch.uint8, device=w.device)
+        scales_t = _empty(C // 16, R // 16, dtype=torch.uint8, device=w.device)
     am, mode = _amax_arg(w, amax)
     if sr_seed is None:
         nvfp4_quantize2d_rtn(w, am, mode, codes, codes_t, scales, scales_t, ts)
@@ -365,7 +372,7 @@ def quantize_row_rht(x: torch.Tensor, rht_seed: int, sr_seed: Optional[int] = No
 
 
 def dequantize(q: NVFP4Tensor) -> torch.Tensor:
-    out = torch.empty(q.rows, q.k, dtype=torch.float32, device=q.codes.device)
+    out = _empty(q.rows, q.k, dtype=torch.float32, device=q.codes.device)
     nvfp4_dequantize(q, out)
     return out
 
@@ -381,8 +388,8 @@ def gemm_bf16(a: NVFP4Tensor, b: NVFP4Tensor, out: Optional[torch.Tensor] = None
     """C = s_a s_b A B^T rounded to BF16, and (with_amax) max |C| as a device
     float, ready to pass as the given amax of C's quantization."""
     if out is None:
-        out = torch.empty(a.rows, b.rows, dtype=torch.bfloat16, device=a.codes.device)
-    amax = torch.empty(1, dtype=torch.float32, device=a.codes.device) if with_amax else None
+        out = _empty(a.rows, b.rows, dtype=torch.bfloat16, device=a.codes.device)
+    amax = _empty(1, dtype=torch.float32, device=a.codes.device) if with_amax else None
     nvfp4_gemm_bf16(a, b, out, out.stride(0), amax)
     return out, amax
 
@@ -390,7 +397,7 @@ def gemm_bf16(a: NVFP4Tensor, b: NVFP4Tensor, out: Optional[torch.Tensor] = None
 def gemm(a: NVFP4Tensor, b: NVFP4Tensor, out: Optional[torch.Tensor] = None) -> torch.Tensor:
     """C = s_a s_b A B^T in FP32, A [M][K], B [N][K]."""
     if out is None:
-        out = torch.empty(a.rows, b.rows, dtype=torch.float32, device=a.codes.device)
+        out = _empty(a.rows, b.rows, dtype=torch.float32, device=a.codes.device)
     nvfp4_gemm(a, b, out, out.stride(0))
     return out
 
@@ -430,15 +437,15 @@ def mx_quantize(x: torch.Tensor, sr_seed: Optional[int] = None, stream_id: int =
     """Rowwise MXFP4 quantization of bf16 x [rows][cols] (cols % 32 == 0)."""
     _dev_bf16(x, "x")
     R, C = x.shape
-    codes = torch.empty(R, C // 2, dtype=torch.uint8, device=x.device)
-    scales = torch.empty(R, C // 32, dtype=torch.uint8, device=x.device)
+    codes = _empty(R, C // 2, dtype=torch.uint8, device=x.device)
+    scales = _empty(R, C // 32, dtype=torch.uint8, device=x.device)
     mxfp4_quantize(x, sr_seed is not None, 0 if sr_seed is None else sr_seed, stream_id, codes,
                    scales)
     return MXFP4Tensor(codes, scales, R, C)
 
 
 def mx_dequantize(q: MXFP4Tensor) -> torch.Tensor:
-    out = torch.empty(q.rows, q.k, dtype=torch.float32, device=q.codes.device)
+    out = _empty(q.rows, q.k, dtype=torch.float32, device=q.codes.device)
     mxfp4_dequantize(q, out)
     return out
 
@@ -446,7 +453,7 @@ def mx_dequantize(q: MXFP4Tensor) -> torch.Tensor:
 def mx_gemm(a: MXFP4Tensor, b: MXFP4Tensor, out: Optional[torch.Tensor] = None) -> torch.Tensor:
     """C = A B^T in FP32, A [M][K], B [N][K] MXFP4."""
     if out is None:
-        out = torch.empty(a.rows, b.rows, dtype=torch.float32, device=a.codes.device)
+        out = _empty(a.rows, b.rows, dtype=torch.float32, device=a.codes.device)
     mxfp4_gemm(a, b, out, out.stride(0))
     return out
 
@@ -470,6 +477,14 @@ def probe_mfma(mode: int, iters: int = 8000):
     secs = (max(r[3] for r in st) - min(r[2] for r in st)) * 1e-8
     flops = 2.0 * 32 * 32 * 16 * 16 * iters * 4 * wgs
     return flops / secs / 1e12, ghz
+
+
+def probe_copy(src: torch.Tensor, dst: torch.Tensor, stream=None):
+    """Plain device copy of src's bytes into dst (measurement support)."""
+    n = src.numel() * src.element_size()
+    if dst.numel() * dst.element_size() < n:
+        raise ValueError("dst is smaller than src")
+    _check(load_library().nvfp4_probe_copy(_p(src), _p(dst), n, _stream(stream)))
 
 
 class ClockStamps:

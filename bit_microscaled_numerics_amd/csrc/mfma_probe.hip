@@ -13,7 +13,10 @@
 // 100 MHz real-time counter (s_memrealtime) around the loop.
 //
 // Also clock stamps for any work on a stream: taken before and after it, they
-// give the average shader clock the work ran at.
+// give the average shader clock the work ran at; and a plain device copy, the
+// achievable HBM bandwidth of a read + write stream.
+#include <hip/hip_runtime.h>
+
 #include "nvfp4_kernels.h"
 
 namespace nvfp4 {
@@ -103,7 +106,45 @@ __global__ void k_clock_stamp(unsigned long long* out) {
   out[4 * blockIdx.x + 3] = 0;
 }
 
+// Plain device copy: the achievable HBM bandwidth of a read + write stream,
+// the reference the quantizers' bandwidth fractions and the byte counters are
+// read against.  The access pattern of the amax and rowwise kernels: each
+// workgroup takes whole chunks of 8 x 16-byte vectors per thread, loads them
+// all, then stores them; chunks dealt to the workgroups in turn.
+constexpr int kCopyU = 8, kCopyThreads = 256;
+typedef uint32_t v4u_ __attribute__((ext_vector_type(4)));
+
+__global__ __launch_bounds__(kCopyThreads) void k_copy(const v4u_* __restrict__ src,
+                                                        v4u_* __restrict__ dst, int64_t nvec) {
+  const int64_t chunk = (int64_t)kCopyU * kCopyThreads;
+  for (int64_t c = (int64_t)blockIdx.x * chunk; c < nvec; c += (int64_t)gridDim.x * chunk) {
+    if (c + chunk <= nvec) {
+      v4u_ v[kCopyU];
+#pragma unroll
+      for (int u = 0; u < kCopyU; ++u)
+        v[u] = __builtin_nontemporal_load(&src[c + u * kCopyThreads + threadIdx.x]);
+#pragma unroll
+      for (int u = 0; u < kCopyU; ++u)
+        __builtin_nontemporal_store(v[u], &dst[c + u * kCopyThreads + threadIdx.x]);
+    } else {
+      for (int64_t i = c + threadIdx.x; i < nvec; i += kCopyThreads)
+        __builtin_nontemporal_store(__builtin_nontemporal_load(&src[i]), &dst[i]);
+    }
+  }
+}
+
 }  // namespace
+
+hipError_t copy_bytes(const void* src, void* dst, int64_t bytes, hipStream_t s) {
+  const int64_t nvec = bytes / 16, chunk = (int64_t)kCopyU * kCopyThreads;
+  int64_t chunks = (nvec + chunk - 1) / chunk;
+  const int64_t cap = (int64_t)num_cus() * 8;
+  const int64_t trips = (chunks + cap - 1) / cap;
+  const int64_t grid = trips > 0 ? (chunks + trips - 1) / trips : 1;
+  hipLaunchKernelGGL(k_copy, dim3((unsigned)(grid < 1 ? 1 : grid)), dim3(kCopyThreads), 0, s,
+                     static_cast<const v4u_*>(src), static_cast<v4u_*>(dst), nvec);
+  return hipGetLastError();
+}
 
 int64_t clock_stamp_bytes() { return (int64_t)kStampWgs * 32; }
 

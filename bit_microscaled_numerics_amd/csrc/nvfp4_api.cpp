@@ -3,7 +3,7 @@
 // here allocates, frees or synchronises.
 #include "../../include/nvfp4.h"
 
-#include <hip/hip_runtime.h>
+#include <hip/hip_runtime_api.h>
 
 #include <atomic>
 #include <cstdarg>
@@ -16,6 +16,12 @@
 namespace {
 
 thread_local char g_last_error[256] = "";
+
+// No tensor or buffer the library touches may exceed 2^40 elements or bytes
+// (far beyond the 288 GB of one MI355X): with that bound every size, offset
+// and grid computation here and in the launchers stays within int64 (and the
+// grids within their 32-bit dimensions).
+constexpr int64_t kMaxElems = int64_t(1) << 40;
 
 int fail(int status, const char* fmt, ...) {
   va_list ap;
@@ -34,6 +40,8 @@ int check_tensor(const void* x, int64_t rows, int64_t cols, const char* name) {
                 (long long)rows, (long long)cols);
   if (cols > (int64_t(1) << 28))
     return fail(NVFP4_ERR_SHAPE, "%s: cols=%lld exceeds 2^28", name, (long long)cols);
+  if (rows > kMaxElems / cols)
+    return fail(NVFP4_ERR_SHAPE, "%s: rows*cols exceeds 2^40 elements", name);
   if (!aligned(x, 16)) return fail(NVFP4_ERR_ALIGN, "%s must be 16-byte aligned", name);
   return NVFP4_OK;
 }
@@ -74,6 +82,18 @@ int check_operand(const nvfp4_operand* q, const char* name) {
   if (q->blk_rows != 1 && q->blk_rows != 16)
     return fail(NVFP4_ERR_ARG, "%s: blk_rows must be 1 or 16", name);
   if (q->ss_row < 0 || q->ss_k < 0) return fail(NVFP4_ERR_ARG, "%s: negative scale stride", name);
+  if (q->ld_codes > kMaxElems || q->rows > kMaxElems / q->ld_codes)
+    return fail(NVFP4_ERR_SHAPE, "%s: rows*ld_codes exceeds 2^40 bytes", name);
+  const int64_t rb = (q->rows - 1) / q->blk_rows, kb = (q->k - 1) / 16;
+  if ((q->ss_row > 0 && rb > kMaxElems / q->ss_row) || (q->ss_k > 0 && kb > kMaxElems / q->ss_k))
+    return fail(NVFP4_ERR_SHAPE, "%s: scale index span exceeds 2^40", name);
+  return NVFP4_OK;
+}
+
+// C [M][ldc] (elements) must stay within the size bound.
+int check_ldc(int64_t ldc, int64_t m, const char* name) {
+  if (ldc > kMaxElems / m)
+    return fail(NVFP4_ERR_SHAPE, "%s: M*ldc exceeds 2^40 elements", name);
   return NVFP4_OK;
 }
 
@@ -322,6 +342,7 @@ int nvfp4_gemm(const nvfp4_operand* a, const nvfp4_operand* b, float* c, int64_t
   if (!aligned(c, 4)) return fail(NVFP4_ERR_ALIGN, "c must be 4-byte aligned");
   if (ldc < b->rows) return fail(NVFP4_ERR_SHAPE, "ldc=%lld < N=%lld", (long long)ldc,
                                  (long long)b->rows);
+  if ((st = check_ldc(ldc, a->rows, "c"))) return st;
   return launched(nvfp4::launch_gemm(to_kernel(a), to_kernel(b), a->k, c, ldc,
                                      as_stream(stream)));
 }
@@ -341,6 +362,7 @@ int nvfp4_gemm_bf16(const nvfp4_operand* a, const nvfp4_operand* b, uint16_t* c,
     return fail(NVFP4_ERR_ALIGN, "amax_out must be 4-byte aligned");
   if (ldc < b->rows) return fail(NVFP4_ERR_SHAPE, "ldc=%lld < N=%lld", (long long)ldc,
                                  (long long)b->rows);
+  if ((st = check_ldc(ldc, a->rows, "c"))) return st;
   return launched(nvfp4::launch_gemm_bf16(to_kernel(a), to_kernel(b), a->k, c, ldc, amax_out,
                                           as_stream(stream)));
 }
@@ -354,6 +376,8 @@ int mxfp4_quantize(const void* x, int64_t rows, int64_t cols, int use_sr, uint64
   if (rows <= 0 || cols <= 0 || cols % 32)
     return fail(NVFP4_ERR_SHAPE, "rows=%lld cols=%lld: rows > 0, cols a positive multiple of 32",
                 (long long)rows, (long long)cols);
+  if (cols > kMaxElems || rows > kMaxElems / cols)
+    return fail(NVFP4_ERR_SHAPE, "rows*cols exceeds 2^40 elements");
   if (!aligned(x, 16)) return fail(NVFP4_ERR_ALIGN, "x must be 16-byte aligned");
   if (!aligned(codes, 4)) return fail(NVFP4_ERR_ALIGN, "codes must be 4-byte aligned");
   if (use_sr != 0 && use_sr != 1) return fail(NVFP4_ERR_ARG, "use_sr=%d must be 0 or 1", use_sr);
@@ -370,6 +394,9 @@ static int check_mx_operand(const mxfp4_operand* q, const char* name, int64_t co
                 name, (long long)q->rows, (long long)q->k);
   if (q->ld_codes < q->k / 2 || q->ld_scales < q->k / 32)
     return fail(NVFP4_ERR_SHAPE, "%s: ld_codes >= k/2 and ld_scales >= k/32 required", name);
+  if (q->ld_codes > kMaxElems || q->rows > kMaxElems / q->ld_codes ||
+      q->rows > kMaxElems / q->ld_scales)
+    return fail(NVFP4_ERR_SHAPE, "%s: rows*ld_codes or rows*ld_scales exceeds 2^40", name);
   if (q->ld_codes % code_align || !aligned(q->codes, (uintptr_t)code_align))
     return fail(NVFP4_ERR_ALIGN, "%s: codes and ld_codes must be %lld-byte aligned", name,
                 (long long)code_align);
@@ -402,6 +429,7 @@ int mxfp4_gemm(const mxfp4_operand* a, const mxfp4_operand* b, float* c, int64_t
   if (!aligned(c, 4)) return fail(NVFP4_ERR_ALIGN, "c must be 4-byte aligned");
   if (ldc < b->rows) return fail(NVFP4_ERR_SHAPE, "ldc=%lld < N=%lld", (long long)ldc,
                                  (long long)b->rows);
+  if ((st = check_ldc(ldc, a->rows, "c"))) return st;
   return launched(nvfp4::launch_mx_gemm(mx_kernel(a), mx_kernel(b), a->k, c, ldc,
                                         as_stream(stream)));
 }
@@ -417,6 +445,16 @@ int nvfp4_probe_mfma(int mode, int iters, void* scratch, int64_t scratch_bytes, 
   if (mode < 0 || mode > 2) return fail(NVFP4_ERR_ARG, "mode=%d (0, 1 or 2)", mode);
   if (iters < 1 || iters > 1000000) return fail(NVFP4_ERR_ARG, "iters=%d (1 .. 1000000)", iters);
   return launched(nvfp4::probe_mfma(mode, iters, scratch, as_stream(stream)));
+}
+
+int nvfp4_probe_copy(const void* src, void* dst, int64_t bytes, void* stream) {
+  if (src == nullptr || dst == nullptr) return fail(NVFP4_ERR_NULL, "src / dst is NULL");
+  if (!aligned(src, 16) || !aligned(dst, 16))
+    return fail(NVFP4_ERR_ALIGN, "src and dst must be 16-byte aligned");
+  if (bytes <= 0 || bytes % 16 || bytes > kMaxElems)
+    return fail(NVFP4_ERR_SHAPE, "bytes=%lld must be a positive multiple of 16, at most 2^40",
+                (long long)bytes);
+  return launched(nvfp4::copy_bytes(src, dst, bytes, as_stream(stream)));
 }
 
 int64_t nvfp4_probe_clock_bytes(void) { return nvfp4::clock_stamp_bytes(); }

@@ -2,7 +2,7 @@
 // libnvfp4.so; the public interface is include/nvfp4.h).
 #pragma once
 
-#include <hip/hip_runtime.h>
+#include <hip/hip_runtime_api.h>
 #include <stdint.h>
 
 namespace nvfp4 {
@@ -78,5 +78,7 @@ hipError_t probe_mfma(int mode, int iters, void* scratch, hipStream_t s);
 // Clock stamps {XCC id, shader clock, 100 MHz real time, 0} of 64 workgroups.
 int64_t clock_stamp_bytes();
 hipError_t clock_stamp(void* out, hipStream_t s);
+// Plain device copy of `bytes` (a multiple of 16, 16-byte aligned pointers).
+hipError_t copy_bytes(const void* src, void* dst, int64_t bytes, hipStream_t s);
 
 }  // namespace nvfp4

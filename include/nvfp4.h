@@ -310,6 +310,14 @@ int nvfp4_probe_mfma(int mode, int iters, void* scratch, int64_t scratch_bytes, 
 int64_t nvfp4_probe_clock_bytes(void);
 int nvfp4_probe_clock(void* stamps, int64_t stamps_bytes, void* stream);
 
+/* Measurement support: a plain device copy of `bytes` (a positive multiple of
+ * 16) from src to dst (device memory, 16-byte aligned, not overlapping),
+ * with the read pattern of the amax and rowwise kernels (whole chunks of
+ * 8 x 16-byte vectors per thread, non-temporal).  Its bandwidth is the
+ * achievable HBM rate of a read + write stream, the reference for the
+ * quantizers' bandwidth and for scaling HBM byte counters. */
+int nvfp4_probe_copy(const void* src, void* dst, int64_t bytes, void* stream);
+
 /* Human-readable name of a status code (static storage). */
 const char* nvfp4_status_string(int status);
 

@@ -17,7 +17,9 @@ from dataclasses import dataclass
 import numpy as np
 
 _HERE = os.path.dirname(os.path.abspath(__file__))
-_LIB_PATH = os.path.join(_HERE, "liboracle.so")
+# NVFP4_ORACLE_LIB selects another build of the same sources (the sanitizer
+# build the tests run the oracle's own suite against).
+_LIB_PATH = os.environ.get("NVFP4_ORACLE_LIB", os.path.join(_HERE, "liboracle.so"))
 _lib = None
 
 ROWWISE, COLWISE, TWO_D = 0, 1, 2
@@ -78,6 +80,7 @@ def _load():
         "orc_gemm_entries": (ctypes.c_int, _OPERAND + _OPERAND + [_i64, _i64p, _i64p, _i64,
                                                                   _f64p, _f64p]),
         "orc_num_threads": (ctypes.c_int, []),
+        "orc_set_num_threads": (None, [ctypes.c_int]),
     }
     for name, (res, args) in sig.items():
         fn = getattr(lib, name)
@@ -94,6 +97,11 @@ def _ptr(a: np.ndarray, typ):
 
 def num_threads() -> int:
     return int(_load().orc_num_threads())
+
+
+def set_num_threads(n: int) -> None:
+    """Threads of the reference's parallel loops from now on (timing only)."""
+    _load().orc_set_num_threads(int(n))
 
 
 # --------------------------------------------------------------------------- scalars

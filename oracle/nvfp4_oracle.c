@@ -506,6 +506,16 @@ ORC_API int orc_gemm_entries(ORC_OPERAND_ARGS(a), ORC_OPERAND_ARGS(b), int64_t K
   return 0;
 }
 
+/* Thread count of the OpenMP loops from here on (for timing the reference
+ * single-threaded and on all cores); n <= 0 leaves it unchanged. */
+ORC_API void orc_set_num_threads(int n) {
+#ifdef _OPENMP
+  if (n > 0) omp_set_num_threads(n);
+#else
+  (void)n;
+#endif
+}
+
 ORC_API int orc_num_threads(void) {
 #ifdef _OPENMP
   return omp_get_max_threads();

@@ -19,3 +19,15 @@ def _oracle_built():
     if not os.path.exists(oracle_build.LIB):
         oracle_build.build()
     yield
+
+
+@pytest.fixture(autouse=True)
+def _guard_bands(request):
+    """Every output the binding allocates in a GPU test is guard-banded and
+    the guards are checked after the test (tests/parity.py)."""
+    if request.node.get_closest_marker("gpu") is None:
+        yield
+        return
+    import parity
+    with parity.guard_bands():
+        yield

@@ -2,6 +2,8 @@
 device, run the HIP path, and compare its outputs with the CPU oracle's."""
 from __future__ import annotations
 
+import contextlib
+import math
 import sys
 
 import numpy as np
@@ -55,3 +57,50 @@ def assert_gemm_close(c_gpu: np.ndarray, c_ref: np.ndarray, t_ref: np.ndarray, n
                            f"{bad[:3].tolist()} err={err[tuple(bad[0])]:.3e} "
                            f"lim={lim[tuple(bad[0])]:.3e}")
     return float(np.max(err / np.maximum(t_ref, 1e-300)))
+
+
+# ---------------------------------------------------------------- guard bands
+GUARD_BYTES = 4096
+GUARD_FILL = 0xA5
+
+
+class GuardBands:
+    """A replacement for the binding's output allocator: every buffer sits
+    inside a larger allocation with GUARD_BYTES of a sentinel byte on both
+    sides, so a kernel that writes past either end of an output is caught
+    (an exact-size torch.empty buffer would let such a write land silently in
+    whatever the caching allocator put next to it)."""
+
+    def __init__(self):
+        self.bufs = []
+
+    def empty(self, *shape, dtype, device):
+        item = torch.empty(0, dtype=dtype).element_size()
+        n = math.prod(shape) * item
+        raw = torch.empty(n + 2 * GUARD_BYTES, dtype=torch.uint8, device=device)
+        raw.fill_(GUARD_FILL)
+        self.bufs.append((raw, n))
+        return raw[GUARD_BYTES:GUARD_BYTES + n].view(dtype).view(*shape)
+
+    def check(self):
+        torch.cuda.synchronize()
+        for raw, n in self.bufs:
+            for part in (raw[:GUARD_BYTES], raw[GUARD_BYTES + n:]):
+                bad = torch.nonzero(part != GUARD_FILL)
+                assert bad.numel() == 0, (f"write outside an output buffer of {n} bytes: "
+                                          f"{bad.numel()} guard bytes changed")
+        self.bufs.clear()
+
+
+@contextlib.contextmanager
+def guard_bands():
+    """Route the binding's output allocations through GuardBands for the
+    duration, then check every guard."""
+    g = GuardBands()
+    saved = nv._empty
+    nv._empty = g.empty
+    try:
+        yield g
+    finally:
+        nv._empty = saved
+    g.check()

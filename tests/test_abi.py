@@ -226,3 +226,31 @@ def test_rht1d_validation(lib):
         assert q(*c) == nv.NVFP4_ERR_NULL
     b = list(args); b[3] = -1
     assert q(*b) == nv.NVFP4_ERR_ARG
+
+
+def test_measurement_probe_validation(lib):
+    assert lib.nvfp4_probe_clock_bytes() >= 64 * 32
+    c = lib.nvfp4_probe_clock
+    assert c(None, 4096, None) == nv.NVFP4_ERR_NULL
+    assert c(FAKE + 4, 4096, None) == nv.NVFP4_ERR_ALIGN
+    assert c(FAKE, 16, None) == nv.NVFP4_ERR_SHAPE
+    p = lib.nvfp4_probe_copy
+    assert p(None, FAKE, 16, None) == nv.NVFP4_ERR_NULL
+    assert p(FAKE, MIS, 16, None) == nv.NVFP4_ERR_ALIGN
+    assert p(FAKE, FAKE + 4096, 24, None) == nv.NVFP4_ERR_SHAPE
+    assert p(FAKE, FAKE + 4096, 0, None) == nv.NVFP4_ERR_SHAPE
+    assert p(FAKE, FAKE + 4096, (1 << 40) + 16, None) == nv.NVFP4_ERR_SHAPE
+
+
+def test_sizes_beyond_2_pow_40_are_rejected(lib):
+    """Dimensions that are multiples of 16 but whose products overflow the
+    library's size bound are rejected before any arithmetic on them."""
+    big = 1 << 62
+    assert lib.nvfp4_amax(FAKE, big, 1 << 28, FAKE, None) == nv.NVFP4_ERR_SHAPE
+    assert lib.nvfp4_quantize1d_rtn(FAKE, big, 1 << 20, 0, FAKE, 0, FAKE, FAKE, FAKE,
+                                    None) == nv.NVFP4_ERR_SHAPE
+    g = lib.nvfp4_gemm
+    ok = _op()
+    assert g(ctypes.byref(_op(rows=big)), ctypes.byref(ok), FAKE, 16, None) == nv.NVFP4_ERR_SHAPE
+    assert g(ctypes.byref(_op(ss_row=big)), ctypes.byref(ok), FAKE, 16, None) == nv.NVFP4_ERR_SHAPE
+    assert g(ctypes.byref(ok), ctypes.byref(ok), FAKE, big, None) == nv.NVFP4_ERR_SHAPE
