@@ -233,11 +233,16 @@ __device__ __forceinline__ uint32_t encode8_rtn(const float* z, float r) {
 __host__ __device__ __forceinline__ float e2m1_sr_value(float v, uint32_t u) {
   const float a = __builtin_fminf(__builtin_fabsf(v), 6.0f);
   const uint32_t bits = f32_bits(a);
-  const bool ge1 = bits >= 0x3F800000u;
-  const uint32_t mask = ge1 ? 0x3FFFFFu : 0x7FFFFFu;
-  const uint32_t u7 = u << 7;
-  const uint32_t us = ge1 ? (u7 >> 1) : u7;
-  const uint32_t rounded = (bits + (mask - us)) & ~mask;
+  // g = 1 for a >= 1 (22 dropped bits), 0 in [0.5, 1) (23): the top bit of
+  // bits + (2^31 - 1.0f's pattern) -- no compare, so no mask register
+  const uint32_t g = (bits + 0x40800000u) >> 31;
+  // the 23-bit form of the addend, 2^23 - 1 - u * 2^7; shifted right by g it
+  // is the 22-bit one (2^22 - 1 - u * 2^6) exactly, its low bit being 1.
+  // Adding it to bits shifted left by g puts the carry at bit 23 in both
+  // binades; clearing bits 0..22 and shifting back leaves the grid value.
+  const uint32_t t7 = 0x7FFFFFu - (u << 7);
+  const uint32_t rounded = (((bits << g) + t7) & 0xFF800000u) >> g;
+  // a < 0.5 (grid 0, 0.5): up iff u < a * 2^17, an exact float compare
   const uint32_t small = ((float)u < a * 131072.0f) ? 0x3F000000u : 0u;
   const uint32_t mag = bits < 0x3F000000u ? small : rounded;
   return f32_from(mag | (f32_bits(v) & 0x80000000u));
@@ -258,19 +263,6 @@ __device__ __forceinline__ uint32_t encode8_sr(const float* z, float r, u32x4 w)
   return out;
 }
 
-// Sign-only codes for a block whose scale is zero.
-__device__ __forceinline__ uint32_t encode8_zero(const float* z) {
-  uint32_t out = 0;
-#pragma unroll
-  for (int j = 0; j < 8; ++j) out |= ((__float_as_uint(z[j]) >> 31) << 3) << (4 * j);
-  return out;
-}
-
-// A block whose scale is zero encodes as signed zeros (sign-only codes).
-__device__ __forceinline__ uint32_t select_zero_block(uint32_t code, uint32_t q, const float* z) {
-  return code == 0u ? encode8_zero(z) : q;
-}
-
 __device__ __forceinline__ float tensor_scale_from_amax(float amax_t) {
   return amax_t > 0.0f ? amax_t / kScaleDen : 1.0f;
 }
@@ -279,10 +271,13 @@ __device__ __forceinline__ float tensor_scale_from_amax(float amax_t) {
 struct BlockScale { uint32_t code; float r; };
 
 // Per-tensor constants of the block-scale step.  rtab (LDS) holds the
-// reciprocals r = 1 / (float(E) * s_t) of the E4M3 codes 0 .. 0x7E (and of
+// reciprocals r = 1 / (float(E) * s_t) of the E4M3 codes 1 .. 0x7E (and of
 // 0x7F, which no scale takes: a 7-bit code always indexes the table), each
 // computed exactly as the per-block formula would, so a lookup returns the
-// same binary32 as the division it replaces.
+// same binary32 as the division it replaces.  Code 0 (a block whose scale
+// underflows, or an all-zero block) gets r = 0: every element then scales to
+// a zero with its own sign, which both encodes turn into the sign-only code
+// such a block takes -- no separate path for zero blocks.
 constexpr int kE4m3Codes = 128;
 
 struct ScaleCtx {
@@ -300,7 +295,8 @@ __device__ __forceinline__ ScaleCtx scale_ctx(float amax_t, float* rtab, int slo
   c.rt6 = 1.0f / c.t6;
   c.divide = !(c.rt6 <= 3.40282347e38f);
   c.rtab = rtab;
-  if (slot >= 0 && slot < kE4m3Codes) rtab[slot] = 1.0f / (e4m3_to_float((uint32_t)slot) * c.s_t);
+  if (slot >= 0 && slot < kE4m3Codes)
+    rtab[slot] = slot == 0 ? 0.0f : 1.0f / (e4m3_to_float((uint32_t)slot) * c.s_t);
   return c;
 }
 
@@ -319,7 +315,9 @@ __device__ __forceinline__ uint32_t scale_code(float amax_b, const ScaleCtx& c) 
   float q = amax_b * c.rt6;
   const uint32_t b = __float_as_uint(q);
   const uint32_t centre = b < 0x3C800000u ? 0u : 0x80000u;
-  if (((b - centre + 8u) & 0xFFFFFu) < 16u || c.divide) q = amax_b / c.t6;
+  // a real branch (the division is rare): if-converted, its ~10 instructions
+  // would run for every block
+  if (__builtin_expect(((b - centre + 8u) & 0xFFFFFu) < 16u || c.divide, 0)) q = amax_b / c.t6;
   return e4m3_code(q);
 }
 

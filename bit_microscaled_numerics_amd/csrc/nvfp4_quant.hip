@@ -234,11 +234,8 @@ __global__ __launch_bounds__(kThreads) void k_quant_row(
       for (int j = 0; j < 8; ++j) m = fmaxf(m, __builtin_fabsf(z[j]));
       m = fmaxf(m, __shfl_xor(m, 1, 64));
       const BlockScale b = block_scale(m, sc);
-      // computed for every block (a zero scale gives inf/NaN here, discarded
-      // by the select), which keeps the lanes of a wave on one path
-      uint32_t q = SR ? encode8_sr(z, b.r, sr_words(seed, stream_id, (uint64_t)i * 8u))
+      const uint32_t q = SR ? encode8_sr(z, b.r, sr_words(seed, stream_id, (uint64_t)i * 8u))
                       : encode8_rtn(z, b.r);
-      q = select_zero_block(b.code, q, z);
       st_(q, &codes[i]);
       if ((i & 1) == 0) scales[i >> 1] = (uint8_t)b.code;
     }
@@ -334,10 +331,9 @@ __global__ __launch_bounds__(kThreads) void k_quant_col(
         for (int j = 0; j < 8; ++j) m = fmaxf(m, __builtin_fabsf(z[j]));
         m = fmaxf(m, __shfl_xor(m, 1, 64));
         const BlockScale b = block_scale(m, sr_ctx);
-        uint32_t q = SR ? encode8_sr(z, b.r, sr_words(seed, ro.stream_id,
+        const uint32_t q = SR ? encode8_sr(z, b.r, sr_words(seed, ro.stream_id,
                                                       n_row0 + (uint64_t)i * (uint64_t)cols))
                         : encode8_rtn(z, b.r);
-        q = select_zero_block(b.code, q, z);
         *reinterpret_cast<uint32_t*>(rcodes + i * pc) = q;
         if ((cg & 1) == 0) rscales[i * ps] = (uint8_t)b.code;
       }
@@ -361,8 +357,6 @@ __global__ __launch_bounds__(kThreads) void k_quant_col(
         q0 = encode8_rtn(v, b.r);
         q1 = encode8_rtn(v + 8, b.r);
       }
-      q0 = select_zero_block(b.code, q0, v);
-      q1 = select_zero_block(b.code, q1, v + 8);
       lds_codes[8 * cg + c][rg] = v2u{q0, q1};
       lds_scales[8 * cg + c][rg] = (uint8_t)b.code;
     }
@@ -463,7 +457,6 @@ __global__ __launch_bounds__(kThreads) void k_quant_2d(
       q[i] = SR ? encode8_sr(z, b.r, sr_words(seed, stream_id,
                                                n_row0 + (uint64_t)i * (uint64_t)cols))
                 : encode8_rtn(z, b.r);
-      q[i] = select_zero_block(b.code, q[i], z);
       *reinterpret_cast<uint32_t*>(rcodes + i * pc) = q[i];
     }
     if ((cg & 1) == 0) {
