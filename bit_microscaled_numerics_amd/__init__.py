@@ -489,9 +489,10 @@ def probe_copy(src: torch.Tensor, dst: torch.Tensor, stream=None):
 
 class ClockStamps:
     """Average shader clock of work enqueued between ``before()`` and
-    ``after()`` on the current stream (measurement support): per-XCD
-    differences of the shader-clock counter over the 100 MHz real-time
-    counter, averaged over the XCDs.  ``ghz()`` synchronizes."""
+    ``after()`` on the current stream (measurement support): per compute
+    unit, the difference of its shader-clock counter over that of the
+    100 MHz real-time counter; the median over the CUs stamped both times.
+    ``ghz()`` synchronizes."""
 
     def __init__(self, device="cuda"):
         lib = load_library()
@@ -512,10 +513,10 @@ class ClockStamps:
         torch.cuda.synchronize()
         st = self._buf.cpu().view(2, -1, 4).tolist()
         first, last = {}, {}
-        for xcc, t, r, _ in st[0]:
-            first.setdefault(xcc, (t, r))
-        for xcc, t, r, _ in st[1]:
-            last[xcc] = (t, r)
-        rates = [(last[x][0] - first[x][0]) / (last[x][1] - first[x][1]) * 0.1
-                 for x in first if x in last and last[x][1] > first[x][1]]
-        return sum(rates) / len(rates) if rates else float("nan")
+        for xcc, hw, t, r in st[0]:
+            first.setdefault((xcc, hw & 0xFF00), (t, r))
+        for xcc, hw, t, r in st[1]:
+            last[(xcc, hw & 0xFF00)] = (t, r)
+        rates = sorted((last[k][0] - first[k][0]) / (last[k][1] - first[k][1]) * 0.1
+                       for k in first if k in last and last[k][1] > first[k][1])
+        return rates[len(rates) // 2] if rates else float("nan")

@@ -88,22 +88,25 @@ __global__ __launch_bounds__(kProbeThreads, 1) void k_probe_mfma(const half8* sr
   }
 }
 
-// Clock stamps: each workgroup's first lane writes {XCC id, shader-clock
-// counter, 100 MHz real-time counter, 0}.  The shader-clock counters of the
-// XCDs are not synchronised with each other, so the host pairs a stamp taken
-// before some work with one taken after it on the same XCD; workgroups are
-// dealt to the XCDs in turn, so kStampWgs of them cover every XCD.
-constexpr int kStampWgs = 64;
+// Clock stamps: each workgroup's first lane writes {XCC id, HW_ID (its
+// wave, SIMD, CU, shader-array and engine fields), shader-clock counter,
+// 100 MHz real-time counter}.  Shader-clock counters of different compute
+// units are not synchronised with each other, so the host pairs a stamp
+// taken before some work with one taken after it on the same compute unit
+// (same XCC and same CU / shader-array / engine fields); one workgroup per
+// CU covers the chip.
+constexpr int kStampWgs = 256;
 
 __global__ void k_clock_stamp(unsigned long long* out) {
   if (threadIdx.x != 0) return;
   const unsigned xcc = __builtin_amdgcn_s_getreg((3 << 11) | 20) & 0xFu;   // HW_REG_XCC_ID[3:0]
+  const unsigned hw = __builtin_amdgcn_s_getreg((31 << 11) | 4);         // HW_REG_HW_ID
   const unsigned long long t = __builtin_amdgcn_s_memtime();
   const unsigned long long r = __builtin_amdgcn_s_memrealtime();
   out[4 * blockIdx.x + 0] = xcc;
-  out[4 * blockIdx.x + 1] = t;
-  out[4 * blockIdx.x + 2] = r;
-  out[4 * blockIdx.x + 3] = 0;
+  out[4 * blockIdx.x + 1] = hw;
+  out[4 * blockIdx.x + 2] = t;
+  out[4 * blockIdx.x + 3] = r;
 }
 
 // Plain device copy: the achievable HBM bandwidth of a read + write stream,

@@ -75,7 +75,7 @@ hipError_t launch_mx_gemm(const MxOperand& a, const MxOperand& b, int64_t K, flo
 // 1 decoded-NVFP4-like, 2 uniform FP16), clock stamps left in the scratch.
 int64_t probe_scratch_bytes();
 hipError_t probe_mfma(int mode, int iters, void* scratch, hipStream_t s);
-// Clock stamps {XCC id, shader clock, 100 MHz real time, 0} of 64 workgroups.
+// Clock stamps {XCC id, HW_ID, shader clock, 100 MHz real time} of 256 workgroups.
 int64_t clock_stamp_bytes();
 hipError_t clock_stamp(void* out, hipStream_t s);
 // Plain device copy of `bytes` (a multiple of 16, 16-byte aligned pointers).

@@ -259,12 +259,18 @@ constexpr int kColTileR = 256, kColTileC = 128;
 // colwise ones, 64-byte rowwise code pieces); this way the pieces meet in
 // one L2 while both tiles are resident rather than reaching HBM as separate
 // partial-line writes.
+// COLS_FIRST: bands of 8 tile-columns, columns fastest instead -- for the
+// kernel that also writes the rowwise operand (row-major like its input),
+// whose concurrent tiles then write contiguous pieces of the same rows
+// (measured: 5% faster there; 11% slower for the plain transpose).
+template <bool COLS_FIRST = false>
 __device__ __forceinline__ void quant_tile(int64_t rows, int64_t cols, int64_t& r0, int64_t& c0) {
   const int64_t gy = (rows + kColTileR - 1) / kColTileR, gx = (cols + kColTileC - 1) / kColTileC;
   const int64_t n = gx * gy, b = blockIdx.x, per = n / kXcds;
   const int64_t t = b < per * kXcds ? (b % kXcds) * per + b / kXcds : b;
   int64_t ty, tx;
-  grouped(t, gy, gx, ty, tx);
+  if (COLS_FIRST) grouped(t, gx, gy, tx, ty);
+  else grouped(t, gy, gx, ty, tx);
   r0 = ty * kColTileR;
   c0 = tx * kColTileC;
 }
@@ -306,7 +312,7 @@ __global__ __launch_bounds__(kThreads) void k_quant_col(
   __syncthreads();
   const uint32_t signs = RHT ? rht_sign_bits(rht_seed) : 0u;
   int64_t r0, c0;
-  quant_tile(rows, cols, r0, c0);
+  quant_tile<ROW>(rows, cols, r0, c0);
   const int cg = threadIdx.x & 15, rg = threadIdx.x >> 4;
   const int64_t rr = r0 + 16 * rg, cc = c0 + 8 * cg;
   if (rr < rows && cc < cols) {

@@ -301,11 +301,13 @@ int64_t nvfp4_probe_scratch_bytes(void);
 int nvfp4_probe_mfma(int mode, int iters, void* scratch, int64_t scratch_bytes, void* stream);
 
 /* Measurement support: clock stamps.  Enqueues on `stream` one small launch
- * whose 64 workgroups each write 4 uint64 {XCC id, shader-clock counter,
- * 100 MHz real-time counter, 0} into `stamps` (device memory of at least
+ * whose 256 workgroups each write 4 uint64 {XCC id, HW_ID register (wave,
+ * SIMD, CU, shader-array, engine fields), shader-clock counter, 100 MHz
+ * real-time counter} into `stamps` (device memory of at least
  * nvfp4_probe_clock_bytes() bytes, 8-byte aligned, caller-owned).  Stamps
- * taken before and after other work on the same stream give, per XCD (the
- * shader-clock counters of different XCDs are unrelated), d(shader) /
+ * taken before and after other work on the same stream give, per compute
+ * unit (the shader-clock counters of different CUs are unrelated: pair
+ * stamps with equal XCC id and equal HW_ID bits 8..15), d(shader) /
  * d(real-time) * 100 MHz: the average clock that work ran at. */
 int64_t nvfp4_probe_clock_bytes(void);
 int nvfp4_probe_clock(void* stamps, int64_t stamps_bytes, void* stream);

@@ -74,7 +74,7 @@ hipError_t launch_mx_gemm(const MxOperand&, const MxOperand&, int64_t, float*, i
 }
 int64_t probe_scratch_bytes() { return 1 << 20; }
 hipError_t probe_mfma(int, int, void*, hipStream_t) { return ok(); }
-int64_t clock_stamp_bytes() { return 2048; }
+int64_t clock_stamp_bytes() { return 8192; }
 hipError_t clock_stamp(void*, hipStream_t) { return ok(); }
 hipError_t copy_bytes(const void*, void*, int64_t, hipStream_t) { return ok(); }
 }  // namespace nvfp4

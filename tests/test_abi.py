@@ -229,11 +229,12 @@ def test_rht1d_validation(lib):
 
 
 def test_measurement_probe_validation(lib):
-    assert lib.nvfp4_probe_clock_bytes() >= 64 * 32
+    assert lib.nvfp4_probe_clock_bytes() >= 256 * 32
     c = lib.nvfp4_probe_clock
     assert c(None, 4096, None) == nv.NVFP4_ERR_NULL
     assert c(FAKE + 4, 4096, None) == nv.NVFP4_ERR_ALIGN
     assert c(FAKE, 16, None) == nv.NVFP4_ERR_SHAPE
+    assert c(FAKE, 256 * 32 - 8, None) == nv.NVFP4_ERR_SHAPE
     p = lib.nvfp4_probe_copy
     assert p(None, FAKE, 16, None) == nv.NVFP4_ERR_NULL
     assert p(FAKE, MIS, 16, None) == nv.NVFP4_ERR_ALIGN
