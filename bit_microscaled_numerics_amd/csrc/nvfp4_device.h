@@ -203,8 +203,9 @@ __device__ __forceinline__ void rht16_pair(float (&v)[8], uint32_t signs, bool h
 // gfx950 FP4 encode (scale 1.0: no scaling) rounds a binary32 to the nearest
 // E2M1 value with ties to the even code, saturates beyond 6 and keeps the
 // sign of zero -- the same decision as e2m1_rtn_index, taken on the same
-// binary32 v = z * r (checked over millions of inputs around every decision
-// point); it packs two codes per byte, first operand in the low nibble.
+// binary32 v = z * r (compared on MI355X with the nearest-value definition
+// on every binary32 in [-8, 8]); it packs two codes per byte, first operand
+// in the low nibble.
 __device__ __forceinline__ uint32_t encode8_rtn(const float* z, float r) {
   uint32_t out = 0;
   out = __builtin_amdgcn_cvt_scalef32_pk_fp4_f32(out, z[0] * r, z[1] * r, 1.0f, 0);
