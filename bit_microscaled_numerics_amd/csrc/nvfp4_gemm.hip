@@ -31,6 +31,7 @@ struct GemmArgs {
   int64_t ldc;
   int64_t full_tiles;  // tiles computed whole; tiles past them are cut by `tail`
   int tail;            // TailMode of the tiles past full_tiles
+  int vec_out;         // output rows take 16-byte stores (ldc and base aligned)
 };
 
 constexpr uint32_t kBufFlags = 0x00020000u;  // raw 32-bit buffer descriptor word 3
@@ -519,6 +520,84 @@ __device__ __forceinline__ void interleave16() {
   }
 }
 
+// Epilogue of a whole fast-path tile through LDS.  The accumulator layout
+// gives each lane one column of 4-row runs, so written straight out every
+// store instruction carries 4 bytes per lane, and a wave can keep only 63
+// of them in flight: the store phase then took 16 us per tile, about 12%
+// of a short-K GEMM.  Here each wave transposes its 32 x 32 blocks in its
+// own 16 KiB of the decoded-A stages (free after the K loop) and writes
+// 16-byte pieces of rows: 4 FP32 or 8 BF16 values per lane and store.
+// Physical LDS row of block row r: r ^ ((r >> 2) & 1).  A wave's 2- or
+// 4-byte writes touch rows r and r + 4 (r % 8 < 4), which this puts in
+// different bank groups; its 16-byte reads cover whole consecutive rows.
+// Values, rounding and the amax are those of store_c.
+template <bool BF16, int NB>
+__device__ __forceinline__ void store_c_lds(const GemmArgs& g, float16v (&acc)[kMB][NB],
+                                            int64_t m0, int64_t n0, uint8_t* smem, int wave) {
+  const int lane = threadIdx.x & 63, lrow = lane & 31, lk = lane >> 5;
+  const float alpha = (*g.a.ts) * (*g.b.ts);
+  uint8_t* region = smem + wave * 16384;
+  constexpr int kBlockBytes = BF16 ? 2048 : 4096;   // one 32 x 32 block
+  constexpr int kPer = 16384 / kBlockBytes;          // blocks per pass
+  constexpr int kBlocks = kMB * NB;
+  uint32_t mag = 0u;
+#pragma unroll
+  for (int pass = 0; pass < kBlocks / kPer; ++pass) {
+#pragma unroll
+    for (int b = 0; b < kPer; ++b) {
+      const int idx = pass * kPer + b, i = idx / NB, j = idx % NB;
+#pragma unroll
+      for (int v = 0; v < 16; ++v) {
+        const int r = (v & 3) + 8 * (v >> 2) + 4 * lk;
+        const int pr = r ^ ((r >> 2) & 1);
+        const float val = acc[i][j][v] * alpha;
+        if (BF16) {
+          const uint32_t u = __float_as_uint(val);
+          const uint32_t h = (u + 0x7FFFu + ((u >> 16) & 1u)) >> 16;
+          reinterpret_cast<uint16_t*>(region + b * kBlockBytes)[pr * 32 + lrow] = (uint16_t)h;
+        } else {
+          reinterpret_cast<float*>(region + b * kBlockBytes)[pr * 32 + lrow] = val;
+        }
+      }
+    }
+    __builtin_amdgcn_s_waitcnt(0xC07F);   // lgkmcnt(0): the wave's writes are done
+    __builtin_amdgcn_wave_barrier();
+#pragma unroll
+    for (int b = 0; b < kPer; ++b) {
+      const int idx = pass * kPer + b, i = idx / NB, j = idx % NB;
+      // 16-byte pieces per block row: 8 (FP32) or 4 (BF16); lane -> (row, piece)
+      constexpr int kPieces = BF16 ? 4 : 8, kRowsPer = 64 / kPieces;
+      constexpr int kRowB = BF16 ? 64 : 128, kVals = BF16 ? 8 : 4;
+#pragma unroll
+      for (int q = 0; q < 32 / kRowsPer; ++q) {
+        const int r = lane / kPieces + kRowsPer * q, c = lane % kPieces;
+        const int pr = r ^ ((r >> 2) & 1);
+        const v4u val = *reinterpret_cast<const v4u*>(region + b * kBlockBytes + pr * kRowB + 16 * c);
+        const int64_t row = m0 + 32 * i + r;
+        const int64_t col = n0 + 32 * j + c * kVals;
+        // N is a multiple of 16 (operand rows are), so a piece that starts
+        // inside the output ends inside it
+        if (row >= g.M || col >= g.N) continue;
+        if (BF16) {
+#pragma unroll
+          for (int e = 0; e < 4; ++e)
+            mag = max(mag, max(val[e] & 0x7FFFu, (val[e] >> 16) & 0x7FFFu));
+        }
+        void* dst = BF16 ? static_cast<void*>(&g.cb[row * g.ldc + col])
+                         : static_cast<void*>(&g.c[row * g.ldc + col]);
+        __builtin_nontemporal_store(val, reinterpret_cast<v4u*>(dst));
+      }
+    }
+    __builtin_amdgcn_s_waitcnt(0xC07F);   // reads done before the next pass overwrites
+    __builtin_amdgcn_wave_barrier();
+  }
+  if (BF16 && g.amax != nullptr) {
+#pragma unroll
+    for (int off = 32; off > 0; off >>= 1) mag = max(mag, (uint32_t)__shfl_xor((int)mag, off, 64));
+    if (lane == 0) atomicMax(g.amax, mag << 16);
+  }
+}
+
 // One tile (or half-width tail tile) of the fast path: A rows tm * 256 ..
 // +255, B rows b_row0 .. + 64 NB * 4 - 1 (NB blocks of 32 per wave: 2 for
 // a whole 256-wide tile, 1 for a half-width one), K part `part`.
@@ -666,7 +745,12 @@ __device__ __forceinline__ void gemm_dma_tile(const GemmArgs& g, int64_t tm, int
   }
   __builtin_amdgcn_s_waitcnt(0);   // loads of the groups past the end
 
-  store_c<BF16, kMB, NB>(g, acc, tm * kTile, b_row0 + bw, part);
+  if (part < 0 && g.vec_out) {
+    __syncthreads();   // every wave is done with the decoded-A stages
+    store_c_lds<BF16, NB>(g, acc, tm * kTile, b_row0 + bw, smem, wave);
+  } else {
+    store_c<BF16, kMB, NB>(g, acc, tm * kTile, b_row0 + bw, part);
+  }
 }
 
 template <bool BF16>
@@ -749,7 +833,10 @@ static hipError_t launch_gemm_any(const GemmOperand& a, const GemmOperand& b, in
                                   float* c, uint16_t* cb, uint32_t* amax, int64_t ldc,
                                   hipStream_t s) {
   const bool bf16 = cb != nullptr;
-  GemmArgs g{a, b, a.rows, b.rows, K, c, cb, amax, ldc, 0, kTailWhole};
+  // 16-byte output stores: 4 FP32 or 8 BF16 values of a row per store
+  const uintptr_t cbase = bf16 ? reinterpret_cast<uintptr_t>(cb) : reinterpret_cast<uintptr_t>(c);
+  const int vec_out = (ldc % (bf16 ? 8 : 4)) == 0 && (cbase & 15) == 0;
+  GemmArgs g{a, b, a.rows, b.rows, K, c, cb, amax, ldc, 0, kTailWhole, vec_out};
   if (bf16 && amax != nullptr) {
     hipLaunchKernelGGL(k_zero_word, dim3(1), dim3(1), 0, s, amax);
     const hipError_t e = hipGetLastError();

@@ -99,3 +99,58 @@ def test_half_width_tail_tiles_bf16():
     err = np.abs(y[ms, ns] - ref)
     lim = GEMM_TOL * t + 2.0 ** -8 * np.abs(ref)
     assert np.all(err <= lim), float(np.max(err / np.maximum(lim, 1e-300)))
+
+
+# Output layouts of the fast-path epilogue: 16-byte pieces of rows (4 FP32 /
+# 8 BF16 values) when ldc and the base allow them, else 4- or 2-byte stores.
+# Each case writes into a sentinel-filled buffer: the pitch padding past N
+# and the bytes around the output must stay untouched.
+def _ops_1d(M, N, K, seed):
+    g = torch.Generator().manual_seed(seed)
+    x = inputs.normal(g, M, K, 1.0, 0.001, 50.0)
+    w = inputs.normal(g, N, K, 0.02)
+    return nv.quantize_1d(x.cuda()), nv.quantize_1d(w.cuda()), x, w
+
+
+@pytest.mark.parametrize("case", [(272, 400, 512, 404, 0),    # 16-byte rows, padded pitch
+                                  (272, 400, 512, 402, 0),    # pitch not a multiple of 4
+                                  (272, 400, 512, 400, 1),    # base 4 bytes off 16
+                                  (48, 80, 256, 84, 0)])      # one partial tile
+def test_fp32_output_layouts(case):
+    M, N, K, ldc, off = case
+    qa, qb, x, w = _ops_1d(M, N, K, M + N + K + ldc)
+    say("gemm fp32 layout", case)
+    buf = torch.full((off + M * ldc + 64,), 7.0, device="cuda")
+    nv.nvfp4_gemm(qa, qb, buf[off:], ldc)
+    torch.cuda.synchronize()
+    got = buf.cpu().numpy()
+    rows = got[off:off + M * ldc].reshape(M, ldc)
+    ox, ow = oracle.quantize(x, oracle.ROWWISE), oracle.quantize(w, oracle.ROWWISE)
+    c, t = oracle.gemm(ox, ow)
+    err = np.abs(rows[:, :N].astype(np.float64) - c)
+    assert np.all(err <= GEMM_TOL * t), float(np.max(err / np.maximum(GEMM_TOL * t, 1e-300)))
+    assert np.all(rows[:, N:] == 7.0)
+    assert np.all(got[:off] == 7.0) and np.all(got[off + M * ldc:] == 7.0)
+
+
+@pytest.mark.parametrize("case", [(272, 304, 512, 312, 0),    # 16-byte rows, padded pitch
+                                  (272, 304, 512, 306, 0),    # pitch not a multiple of 8
+                                  (272, 304, 512, 304, 4),    # base 8 bytes off 16
+                                  (48, 80, 256, 88, 0)])      # one partial tile
+def test_bf16_output_layouts(case):
+    M, N, K, ldc, off = case
+    qa, qb, _, _ = _ops_1d(M, N, K, M + N + K + ldc)
+    say("gemm bf16 layout", case)
+    c32 = nv.gemm(qa, qb)
+    sentinel = 0x7E57
+    buf = torch.full((off + M * ldc + 64,), sentinel, dtype=torch.int16, device="cuda")
+    amax = torch.empty(1, dtype=torch.float32, device="cuda")
+    nv.nvfp4_gemm_bf16(qa, qb, buf[off:], ldc, amax)
+    torch.cuda.synchronize()
+    got = buf.cpu().numpy().view(np.uint16)
+    rows = got[off:off + M * ldc].reshape(M, ldc)
+    assert np.array_equal(rows[:, :N], rne_bf16_bits(c32.cpu().numpy()))
+    assert np.all(rows[:, N:] == sentinel)
+    assert np.all(got[:off] == sentinel) and np.all(got[off + M * ldc:] == sentinel)
+    mag = (rows[:, :N] & 0x7FFF).astype(np.uint32) << 16
+    assert float(amax.cpu()[0]) == float(mag.max().view(np.float32))
