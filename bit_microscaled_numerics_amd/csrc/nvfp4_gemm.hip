@@ -31,10 +31,11 @@ struct GemmArgs {
   int64_t ldc;
   int64_t full_tiles;  // tiles computed whole; tiles past them are cut by `tail`
   int tail;            // TailMode of the tiles past full_tiles
-  int vec_out;         // output rows take 16-byte stores (ldc and base aligned)
+  int vec_out;         // 16-byte output stores: ldc and base aligned, 256 rows < 2^31 B
 };
 
 constexpr uint32_t kBufFlags = 0x00020000u;  // raw 32-bit buffer descriptor word 3
+constexpr int kNontemporal = 2;               // buffer store cache policy: non-temporal
 
 // Buffer view of one operand for one workgroup: codes and scales of the
 // 256-row slab starting at row0.  Loads take this thread's row part of the
@@ -524,22 +525,45 @@ __device__ __forceinline__ void interleave16() {
 // gives each lane one column of 4-row runs, so written straight out every
 // store instruction carries 4 bytes per lane, and a wave can keep only 63
 // of them in flight: the store phase then took 16 us per tile, about 12%
-// of a short-K GEMM.  Here each wave transposes its 32 x 32 blocks in its
-// own 16 KiB of the decoded-A stages (free after the K loop) and writes
-// 16-byte pieces of rows: 4 FP32 or 8 BF16 values per lane and store.
-// Physical LDS row of block row r: r ^ ((r >> 2) & 1).  A wave's 2- or
-// 4-byte writes touch rows r and r + 4 (r % 8 < 4), which this puts in
-// different bank groups; its 16-byte reads cover whole consecutive rows.
-// Values, rounding and the amax are those of store_c.
+// of a short-K GEMM.  Here each wave writes its accumulators times the
+// tensor scales (FP32, or rounded to BF16) into its own 16 KiB of the
+// decoded-A stages (free after the K loop), 4 (FP32) or 8 (BF16) 32 x 32
+// blocks at a time, reads them back as 16-byte pieces of rows (4 FP32 or
+// 8 BF16 values) and stores those.  Physical LDS row of block row r:
+// r ^ ((r >> 2) & 1).  A wave's 2- or 4-byte writes touch rows r and r + 4
+// (r % 8 < 4), which this puts in different bank groups; its 16-byte reads
+// cover consecutive rows.  Stores go through a buffer resource based at the
+// wave's first output element: rows at or past M lie past num_records and a
+// piece at or past column N gets an offset of 2^31, so both are dropped with
+// no branch (the accumulators there are zero, as operand rows past M and N
+// read as zero, so the BF16 amax may take them in).  Needs 256 rows of C
+// within 2^31 bytes (checked on the host).  Values, rounding and the amax
+// are those of store_c.
 template <bool BF16, int NB>
 __device__ __forceinline__ void store_c_lds(const GemmArgs& g, float16v (&acc)[kMB][NB],
                                             int64_t m0, int64_t n0, uint8_t* smem, int wave) {
   const int lane = threadIdx.x & 63, lrow = lane & 31, lk = lane >> 5;
   const float alpha = (*g.a.ts) * (*g.b.ts);
   uint8_t* region = smem + wave * 16384;
-  constexpr int kBlockBytes = BF16 ? 2048 : 4096;   // one 32 x 32 block
-  constexpr int kPer = 16384 / kBlockBytes;          // blocks per pass
+  constexpr int kEs = BF16 ? 2 : 4;                  // output element bytes
+  constexpr int kRowB = 32 * kEs;                    // bytes of a block row in LDS
+  constexpr int kBlockB = 32 * kRowB;                // bytes of a block in LDS
+  constexpr int kPer = 16384 / kBlockB;              // blocks per pass
+  constexpr int kVals = 16 / kEs;                    // values per 16-byte piece
+  constexpr int kPieces = 32 / kVals;                // pieces per block row
+  constexpr int kRowsPer = 64 / kPieces;             // block rows per store instruction
   constexpr int kBlocks = kMB * NB;
+  uint8_t* obase = BF16 ? reinterpret_cast<uint8_t*>(g.cb + m0 * g.ldc + n0)
+                        : reinterpret_cast<uint8_t*>(g.c + m0 * g.ldc + n0);
+  const int64_t span = (g.M - m0) * g.ldc * kEs;
+  const __amdgpu_buffer_rsrc_t out = __builtin_amdgcn_make_buffer_rsrc(
+      obase, (short)0, (int)(span < 0x7FFFFFFF ? span : 0x7FFFFFFF), (int)kBufFlags);
+  const int pr_row = lane / kPieces, pc = lane % kPieces;
+  const uint32_t lane_off = (uint32_t)(pr_row * g.ldc + pc * kVals) * kEs;
+  uint32_t voff[NB];
+#pragma unroll
+  for (int j = 0; j < NB; ++j)
+    voff[j] = lane_off + (n0 + 32 * j + pc * kVals < g.N ? 0u : 0x80000000u);
   uint32_t mag = 0u;
 #pragma unroll
   for (int pass = 0; pass < kBlocks / kPer; ++pass) {
@@ -549,14 +573,13 @@ __device__ __forceinline__ void store_c_lds(const GemmArgs& g, float16v (&acc)[k
 #pragma unroll
       for (int v = 0; v < 16; ++v) {
         const int r = (v & 3) + 8 * (v >> 2) + 4 * lk;
-        const int pr = r ^ ((r >> 2) & 1);
+        uint8_t* dst = region + b * kBlockB + (r ^ ((r >> 2) & 1)) * kRowB + lrow * kEs;
         const float val = acc[i][j][v] * alpha;
         if (BF16) {
           const uint32_t u = __float_as_uint(val);
-          const uint32_t h = (u + 0x7FFFu + ((u >> 16) & 1u)) >> 16;
-          reinterpret_cast<uint16_t*>(region + b * kBlockBytes)[pr * 32 + lrow] = (uint16_t)h;
+          *reinterpret_cast<uint16_t*>(dst) = (uint16_t)((u + 0x7FFFu + ((u >> 16) & 1u)) >> 16);
         } else {
-          reinterpret_cast<float*>(region + b * kBlockBytes)[pr * 32 + lrow] = val;
+          *reinterpret_cast<float*>(dst) = val;
         }
       }
     }
@@ -565,27 +588,18 @@ __device__ __forceinline__ void store_c_lds(const GemmArgs& g, float16v (&acc)[k
 #pragma unroll
     for (int b = 0; b < kPer; ++b) {
       const int idx = pass * kPer + b, i = idx / NB, j = idx % NB;
-      // 16-byte pieces per block row: 8 (FP32) or 4 (BF16); lane -> (row, piece)
-      constexpr int kPieces = BF16 ? 4 : 8, kRowsPer = 64 / kPieces;
-      constexpr int kRowB = BF16 ? 64 : 128, kVals = BF16 ? 8 : 4;
 #pragma unroll
       for (int q = 0; q < 32 / kRowsPer; ++q) {
-        const int r = lane / kPieces + kRowsPer * q, c = lane % kPieces;
-        const int pr = r ^ ((r >> 2) & 1);
-        const v4u val = *reinterpret_cast<const v4u*>(region + b * kBlockBytes + pr * kRowB + 16 * c);
-        const int64_t row = m0 + 32 * i + r;
-        const int64_t col = n0 + 32 * j + c * kVals;
-        // N is a multiple of 16 (operand rows are), so a piece that starts
-        // inside the output ends inside it
-        if (row >= g.M || col >= g.N) continue;
+        const int r = pr_row + kRowsPer * q;
+        const v4u val = *reinterpret_cast<const v4u*>(region + b * kBlockB +
+                                                      (r ^ ((r >> 2) & 1)) * kRowB + 16 * pc);
         if (BF16) {
 #pragma unroll
           for (int e = 0; e < 4; ++e)
             mag = max(mag, max(val[e] & 0x7FFFu, (val[e] >> 16) & 0x7FFFu));
         }
-        void* dst = BF16 ? static_cast<void*>(&g.cb[row * g.ldc + col])
-                         : static_cast<void*>(&g.c[row * g.ldc + col]);
-        __builtin_nontemporal_store(val, reinterpret_cast<v4u*>(dst));
+        const uint32_t soff = (uint32_t)(((32 * i + kRowsPer * q) * g.ldc + 32 * j) * kEs);
+        __builtin_amdgcn_raw_buffer_store_b128(val, out, voff[j], soff, kNontemporal);
       }
     }
     __builtin_amdgcn_s_waitcnt(0xC07F);   // reads done before the next pass overwrites
@@ -835,7 +849,8 @@ static hipError_t launch_gemm_any(const GemmOperand& a, const GemmOperand& b, in
   const bool bf16 = cb != nullptr;
   // 16-byte output stores: 4 FP32 or 8 BF16 values of a row per store
   const uintptr_t cbase = bf16 ? reinterpret_cast<uintptr_t>(cb) : reinterpret_cast<uintptr_t>(c);
-  const int vec_out = (ldc % (bf16 ? 8 : 4)) == 0 && (cbase & 15) == 0;
+  const int vec_out = (ldc % (bf16 ? 8 : 4)) == 0 && (cbase & 15) == 0 &&
+                      ldc * kTile * (bf16 ? 2 : 4) < ((int64_t)1 << 31);
   GemmArgs g{a, b, a.rows, b.rows, K, c, cb, amax, ldc, 0, kTailWhole, vec_out};
   if (bf16 && amax != nullptr) {
     hipLaunchKernelGGL(k_zero_word, dim3(1), dim3(1), 0, s, amax);
