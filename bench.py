@@ -211,14 +211,52 @@ class Step:
             end.record(main)
 
 
-def cpu_baseline(x, w, dy, c5=None, gpu_c5_us=None):
+C5_SR_SEED, C5_RHT_SEED = 7, 1   # seeds of the whole-tensor oracle comparisons
+
+
+def oracle_c5(c5, threads, gpu_us):
+    """The oracle on the whole 32768x8192 N(0,1) sweep tensor, each
+    quantization including its amax pass: 1D RTN on all threads and on one
+    thread, 1D SR, 2D RTN and the colwise RHT (RTN) on all threads; codes and
+    scales compared with the GPU's, times against the GPU's (cold) ones."""
+    import oracle
+    x = c5["x"]
+    n = x.numel()
+    runs = [("1D RTN", 4.5625, (threads, 1), oracle.ROWWISE, {}, "normal 1d RTN incl. amax"),
+            ("1D SR", 4.5625, (threads,), oracle.ROWWISE, {"sr_seed": C5_SR_SEED},
+             "normal 1d SR incl. amax"),
+            ("2D RTN", 4.50390625, (threads,), oracle.TWO_D, {}, "normal 2d RTN incl. amax"),
+            ("colwise RHT RTN", 4.5625, (threads,), oracle.COLWISE, {"rht_seed": C5_RHT_SEED},
+             "normal col RHT RTN incl. amax")]
+    rec = {"workload": "32768x8192 bf16 N(0,1), whole tensor, each quantization incl. its amax",
+           "threads": threads}
+    for name, bpe, ths, mode, kw, gkey in runs:
+        r = {}
+        for th in ths:
+            oracle.set_num_threads(th)
+            t0 = time.perf_counter()
+            q = oracle.quantize(x, mode, **kw)
+            dt = time.perf_counter() - t0
+            r[f"s_{th}_threads"] = round(dt, 3)
+            r[f"GB/s_{th}_threads"] = round(bpe * n / dt / 1e9, 3)
+        oracle.set_num_threads(threads)
+        gc, gs = c5["gpu"][name]
+        r["codes_equal_gpu"] = bool(np.array_equal(q.codes, gc) and np.array_equal(q.scales, gs))
+        us = gpu_us.get(gkey, {}).get("us")
+        if us:
+            r["gpu_us"] = us
+            r["gpu_speedup_vs_all_threads"] = round(r[f"s_{threads}_threads"] / (us * 1e-6), 1)
+        rec[name] = r
+        del q
+    return rec
+
+
+def cpu_baseline(x, w, dy, c5=None, gpu_us=None):
     """The oracle, as it stands, on the same host bytes as the GPU:
       * the step: a slice of rows of every quantization and a set of exact
         entries of every GEMM, timed on all threads and extrapolated linearly
         to the whole step (the `value`, in the metric's unit);
-      * the 32768x8192 quantize (1D RTN including its amax, the first sweep
-        tensor, whole) on all threads and on one thread, its codes compared
-        with the GPU's."""
+      * the 32768x8192 quantizations (oracle_c5)."""
     import oracle
     T, F = x.shape
     H = w.shape[0]
@@ -267,24 +305,7 @@ def cpu_baseline(x, w, dy, c5=None, gpu_c5_us=None):
                       f"({t_quant:.2f} s) + {n2} exact GEMM entries at K={F} ({dt:.2f} s), "
                       f"{threads} threads, extrapolated to one full step ({full:.0f} s)")}
     if c5 is not None:
-        xc5, gpu_codes, gpu_scales = c5
-        nbytes = 4.5625 * xc5.numel()
-        rec = {"workload": "1D RTN quantize incl. amax, 32768x8192 bf16 N(0,1), whole tensor"}
-        for th in (threads, 1):
-            oracle.set_num_threads(th)
-            t0 = time.perf_counter()
-            q = oracle.quantize(xc5, oracle.ROWWISE)
-            dt = time.perf_counter() - t0
-            rec[f"s_{th}_threads"] = round(dt, 3)
-            rec[f"GB/s_{th}_threads"] = round(nbytes / dt / 1e9, 3)
-        oracle.set_num_threads(threads)
-        rec["codes_equal_gpu"] = bool(np.array_equal(q.codes, gpu_codes) and
-                                      np.array_equal(q.scales, gpu_scales))
-        if gpu_c5_us:
-            rec["gpu_us"] = gpu_c5_us
-            rec["gpu_speedup_vs_all_threads"] = round(rec[f"s_{threads}_threads"] /
-                                                      (gpu_c5_us * 1e-6), 1)
-        out["quantize_32768x8192"] = rec
+        out["quantize_32768x8192"] = oracle_c5(c5, threads, gpu_us or {})
     return out
 
 
@@ -309,7 +330,16 @@ def quant_sweep(flush, steps: int = 10, keep_first=False):
         qm = nv.mx_quantize(x)
         torch.cuda.synchronize()
         if keep_first and kept is None:
-            kept = (xh, q1.codes.cpu().numpy(), q1.scales.cpu().numpy())
+            # the GPU's outputs of the whole-tensor quantizations the oracle
+            # repeats on the same host bytes (before the timed variants
+            # overwrite q1 .. qr)
+            qs = nv.quantize_1d(x, sr_seed=C5_SR_SEED)
+            qt = nv.rht_quantize(x, C5_RHT_SEED)
+            torch.cuda.synchronize()
+            host = lambda q: (q.codes.cpu().numpy(), q.scales.cpu().numpy())
+            kept = {"x": xh, "gpu": {"1D RTN": host(q1), "1D SR": host(qs), "2D RTN": host(q2),
+                                     "colwise RHT RTN": host(qt)}}
+            del qs, qt
         del xh
         G, CMP, ROW = nv.NVFP4_AMAX_GIVEN, nv.NVFP4_AMAX_COMPUTE, nv.NVFP4_ROWWISE
         variants = [
@@ -695,9 +725,8 @@ def main():
         result["quantize_sweep_32768x8192"] = sweep
     if not args.no_cpu_baseline:
         log("cpu baseline (oracle) on the same host bytes")
-        gpu_us = result.get("quantize_sweep_32768x8192", {}).get(
-            "normal 1d RTN incl. amax", {}).get("us")
-        result["cpu_baseline"] = cpu_baseline(xh, wh, dyh, c5, gpu_us)
+        result["cpu_baseline"] = cpu_baseline(xh, wh, dyh, c5,
+                                              result.get("quantize_sweep_32768x8192", {}))
     print(json.dumps(result), flush=True)
 
 
