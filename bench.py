@@ -53,19 +53,29 @@ def log(*a):
 GEMM_SOURCES = ("nvfp4_gemm.hip", "gemm_tiles.h", "gemm_decode.h", "nvfp4_device.h")
 
 
+def gemm_source_digest() -> str:
+    """SHA-256 of the GEMM sources with comments and blank lines removed, so
+    that the record below goes stale when the code changes, not its comments."""
+    import hashlib
+    import re
+    m = hashlib.sha256()
+    for f in GEMM_SOURCES:
+        with open(os.path.join(ROOT, "bit_microscaled_numerics_amd", "csrc", f)) as fh:
+            text = fh.read()
+        text = re.sub(r"/\*.*?\*/", "", text, flags=re.S)
+        lines = (re.sub(r"//.*", "", ln).rstrip() for ln in text.splitlines())
+        m.update("\n".join(ln for ln in lines if ln).encode())
+    return m.hexdigest()
+
+
 def gemm_traffic():
     """HBM bytes per GEMM launch from the committed rocprofv3 FETCH_SIZE /
-    WRITE_SIZE record, or None when the GEMM source changed since."""
-    import hashlib
+    WRITE_SIZE record, or None when the GEMM code changed since."""
     path = os.path.join(ROOT, "profiles", "gemm_traffic.json")
     if not os.path.exists(path):
         return None
     rec = json.load(open(path))
-    m = hashlib.sha256()
-    for f in GEMM_SOURCES:
-        with open(os.path.join(ROOT, "bit_microscaled_numerics_amd", "csrc", f), "rb") as fh:
-            m.update(fh.read())
-    return rec["traffic_bytes_per_launch"] if m.hexdigest() == rec["source_sha256"] else None
+    return rec["traffic_bytes_per_launch"] if gemm_source_digest() == rec["source_sha256"] else None
 
 
 class Flush:

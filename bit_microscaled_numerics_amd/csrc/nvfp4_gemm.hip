@@ -220,8 +220,9 @@ __device__ __forceinline__ void interleave() {
   }
 }
 
-// Shared epilogue of both kernels: this lane's accumulators of WM x WN
-// blocks starting at (m0, n0).  Lane l holds column (l % 32) of each 32x32
+// Epilogue straight from the accumulators (the general kernel; on the fast
+// path the split tiles and outputs that cannot take 16-byte stores): this
+// lane's accumulators of WM x WN blocks starting at (m0, n0).  Lane l holds column (l % 32) of each 32x32
 // block; accumulator slot v is row (v % 4) + 8 (v / 4) + 4 (l / 32).  A split
 // tile adds its half into the zeroed output: with exactly two addends onto
 // zero the sum does not depend on their order (fp32 addition commutes), so
