@@ -511,6 +511,36 @@ __device__ __forceinline__ void mfma16(float16v (&acc)[kMB][NB], const OpsA& a, 
       acc[i][j] = __builtin_amdgcn_mfma_f32_32x32x16_f16(a.a[i], b.b[j], acc[i][j], 0, 0, 0);
 }
 
+// The MFMAs of a sub-step from linear block index FROM on (block m is
+// i = m / NB, j = m % NB, the order of mfma16).
+template <int NB, int FROM>
+__device__ __forceinline__ void mfma_from(float16v (&acc)[kMB][NB], const OpsA& a, const OpsB& b) {
+#pragma unroll
+  for (int m = FROM; m < kMB * NB; ++m)
+    acc[m / NB][m % NB] =
+        __builtin_amdgcn_mfma_f32_32x32x16_f16(a.a[m / NB], b.b[m % NB], acc[m / NB][m % NB], 0, 0, 0);
+}
+
+// The last sub-step of a K step, after the workgroup barrier: the LDS reads
+// of the next step's operands go out first (they wait only on the LDS), then
+// the sub-step's MFMAs -- whose operands are already in registers -- with
+// the NQ code loads of a slot refill between the first ones and the next
+// step's first B decode (VALU, waiting on those reads) from the fourth on.
+// The four waves leave the barrier together and share the compute unit's
+// load unit and LDS: issued back to back before any MFMA, the loads and
+// the read-decode chain left the matrix cores idle for about a tenth of
+// the K loop (measured).
+template <int NQ>
+__device__ __forceinline__ void interleave_boundary() {
+  __builtin_amdgcn_sched_group_barrier(0x100, 14, 0);   // DS read
+#pragma unroll
+  for (int m = 0; m < 16; ++m) {
+    __builtin_amdgcn_sched_group_barrier(0x008, 1, 0);   // MFMA
+    if (m < NQ) __builtin_amdgcn_sched_group_barrier(0x010, 1, 0);   // VMEM
+    if (m >= 3) __builtin_amdgcn_sched_group_barrier(0x002, 3, 0);   // VALU
+  }
+}
+
 // 16 x {1 MFMA, 3 VALU}, with the LDS reads and writes spread in between.
 __device__ __forceinline__ void interleave16() {
 #pragma unroll
@@ -729,28 +759,33 @@ __device__ __forceinline__ void gemm_dma_tile(const GemmArgs& g, int64_t tm, int
           // memory fence, which would also wait for the raw loads in flight
           asm volatile("s_waitcnt lgkmcnt(0)\n\ts_barrier" ::: "memory");
           __builtin_amdgcn_sched_barrier(0);
-          if ((h & 1) == 0) dma_codes<4>(va, (h >> 1) ? rawA1 : rawA0, a_crow, x + 4, last);
-          else dma_codes<2 * NB>(vb, (h >> 1) ? rawB1 : rawB0, b_crow, x + 3, last);
           // per trip the loads go A codes (4), B codes (2 NB), A codes + A
-          // scales, B codes + B scales (scales after the reads)
-          if (h == 0) __builtin_amdgcn_s_waitcnt(vmcnt_imm(2 * NB + 6));
-          else if (h == 2) __builtin_amdgcn_s_waitcnt(vmcnt_imm(2 * NB + 4));
-          else __builtin_amdgcn_s_waitcnt(vmcnt_imm(2 * NB + 5));
+          // scales, B codes + B scales; the waits below come before this
+          // step's code loads, so they allow that many fewer in flight
+          if (h == 0) __builtin_amdgcn_s_waitcnt(vmcnt_imm(2 * NB + 2));
+          else if (h == 2) __builtin_amdgcn_s_waitcnt(vmcnt_imm(2 * NB));
+          else __builtin_amdgcn_s_waitcnt(vmcnt_imm(5));
           __builtin_amdgcn_sched_barrier(0);
-          read_a(anxt, oth, lrow, lk, 0);
+          // a new 4-step scale group first: read_raw takes its scale dwords
+          // from these registers (at h = 3 B(x + 1) starts the next group)
           if (h == 2) read_sg(sa, scA, a_sidx);
           if (h == 3) read_sg(sb, scB, b_sidx);
-          read_raw(ra, a2 ? rawA1 : rawA0, sa, ar0, ar1, ah, h & 1, (h + 2) & 3);
           read_raw(rb, b1 ? rawB1 : rawB0, sb, br0, br1, lk, (h + 1) & 1, (h + 1) & 3);
+          read_a(anxt, oth, lrow, lk, 0);
+          read_raw(ra, a2 ? rawA1 : rawA0, sa, ar0, ar1, ah, h & 1, (h + 2) & 3);
+          if ((h & 1) == 0) dma_codes<4>(va, (h >> 1) ? rawA1 : rawA0, a_crow, x + 4, last);
+          else dma_codes<2 * NB>(vb, (h >> 1) ? rawB1 : rawB0, b_crow, x + 3, last);
           dec_b<NB>(bnxt, rb, 0, bpos0, bpos1);
+          mfma16<NB>(acc, acur, bcur);
+          if ((h & 1) == 0) interleave_boundary<4>();
+          else interleave_boundary<2 * NB>();
           if (h >= 2) {
+            __builtin_amdgcn_sched_barrier(0);
             __builtin_amdgcn_s_waitcnt(0xC07F);   // lgkmcnt(0): slot read before its reload
             __builtin_amdgcn_sched_barrier(0);
             if (h == 2) dma_scales(va, scA, wave, it + 8, last);
             else dma_scales(vb, scB, wave, it + 8, last);
           }
-          mfma16<NB>(acc, acur, bcur);
-          interleave16();
           acur = anxt;
           bcur = bnxt;
           __builtin_amdgcn_sched_barrier(0);
