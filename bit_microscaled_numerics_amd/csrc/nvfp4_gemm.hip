@@ -521,23 +521,26 @@ __device__ __forceinline__ void mfma_from(float16v (&acc)[kMB][NB], const OpsA& 
         __builtin_amdgcn_mfma_f32_32x32x16_f16(a.a[m / NB], b.b[m % NB], acc[m / NB][m % NB], 0, 0, 0);
 }
 
-// The last sub-step of a K step, after the workgroup barrier: the LDS reads
-// of the next step's operands go out first (they wait only on the LDS), then
-// the sub-step's MFMAs -- whose operands are already in registers -- with
-// the NQ code loads of a slot refill between the first ones and the next
-// step's first B decode (VALU, waiting on those reads) from the fourth on.
-// The four waves leave the barrier together and share the compute unit's
-// load unit and LDS: issued back to back before any MFMA, the loads and
-// the read-decode chain left the matrix cores idle for about a tenth of
-// the K loop (measured).
-template <int NQ>
-__device__ __forceinline__ void interleave_boundary() {
-  __builtin_amdgcn_sched_group_barrier(0x100, 14, 0);   // DS read
+// The first 4 MFMAs of the last sub-step of a K step, after the workgroup
+// barrier, with the NQ code loads of a slot refill (steps x0, x0 + 1, as
+// dma_codes) issued one after each.  The four waves leave the barrier
+// together and share the compute unit's load unit: issued back to back, the
+// loads stalled each wave at issue while its matrix core had nothing queued;
+// between MFMAs whose operands are already in registers the wait overlaps
+// the matrix-core work.
+template <int NB, int NQ>
+__device__ __forceinline__ void mfma4_dma(float16v (&acc)[kMB][NB], const OpsA& a, const OpsB& b,
+                                          const DmaOp& v, uint8_t* raw, const int (&crow)[4],
+                                          int x0, int last) {
+  const uint32_t kb = (uint32_t)((x0 < last ? x0 : last) * 32);
 #pragma unroll
-  for (int m = 0; m < 16; ++m) {
-    __builtin_amdgcn_sched_group_barrier(0x008, 1, 0);   // MFMA
-    if (m < NQ) __builtin_amdgcn_sched_group_barrier(0x010, 1, 0);   // VMEM
-    if (m >= 3) __builtin_amdgcn_sched_group_barrier(0x002, 3, 0);   // VALU
+  for (int m = 0; m < 4; ++m) {
+    acc[m / NB][m % NB] =
+        __builtin_amdgcn_mfma_f32_32x32x16_f16(a.a[m / NB], b.b[m % NB], acc[m / NB][m % NB], 0, 0, 0);
+    if (m < NQ)
+      __builtin_amdgcn_raw_ptr_buffer_load_lds(v.codes, (lds_ptr_t)(raw + crow[m] * kRawRow), 16,
+                                               v.voff_c[m], kb, 0, 0);
+    __builtin_amdgcn_sched_barrier(0);
   }
 }
 
@@ -757,11 +760,13 @@ __device__ __forceinline__ void gemm_dma_tile(const GemmArgs& g, int64_t tm, int
         } else {
           // this wave's decode writes done, then the workgroup barrier; no
           // memory fence, which would also wait for the raw loads in flight
-          asm volatile("s_waitcnt lgkmcnt(0)\n\ts_barrier" ::: "memory");
-          __builtin_amdgcn_sched_barrier(0);
-          // per trip the loads go A codes (4), B codes (2 NB), A codes + A
-          // scales, B codes + B scales; the waits below come before this
-          // step's code loads, so they allow that many fewer in flight
+          // This wave's own raw data for the next steps first (its code and
+          // scale slots are private to it): the load wait and the raw reads,
+          // whose latency then passes at the barrier; after it only the
+          // shared decoded-A reads remain.  Per trip the loads go A codes (4),
+          // B codes (2 NB), A codes + A scales, B codes + B scales; the waits
+          // come before this step's loads, so they allow that many fewer in
+          // flight.
           if (h == 0) __builtin_amdgcn_s_waitcnt(vmcnt_imm(2 * NB + 2));
           else if (h == 2) __builtin_amdgcn_s_waitcnt(vmcnt_imm(2 * NB));
           else __builtin_amdgcn_s_waitcnt(vmcnt_imm(5));
@@ -771,17 +776,24 @@ __device__ __forceinline__ void gemm_dma_tile(const GemmArgs& g, int64_t tm, int
           if (h == 2) read_sg(sa, scA, a_sidx);
           if (h == 3) read_sg(sb, scB, b_sidx);
           read_raw(rb, b1 ? rawB1 : rawB0, sb, br0, br1, lk, (h + 1) & 1, (h + 1) & 3);
-          read_a(anxt, oth, lrow, lk, 0);
           read_raw(ra, a2 ? rawA1 : rawA0, sa, ar0, ar1, ah, h & 1, (h + 2) & 3);
-          if ((h & 1) == 0) dma_codes<4>(va, (h >> 1) ? rawA1 : rawA0, a_crow, x + 4, last);
-          else dma_codes<2 * NB>(vb, (h >> 1) ? rawB1 : rawB0, b_crow, x + 3, last);
+          // this wave's decode writes and reads done, then the workgroup
+          // barrier; no memory fence, which would also wait for the raw loads
+          // in flight
+          asm volatile("s_waitcnt lgkmcnt(0)\n\ts_barrier" ::: "memory");
+          __builtin_amdgcn_sched_barrier(0);
+          read_a(anxt, oth, lrow, lk, 0);
+          __builtin_amdgcn_sched_barrier(0);
+          if ((h & 1) == 0)
+            mfma4_dma<NB, 4>(acc, acur, bcur, va, (h >> 1) ? rawA1 : rawA0, a_crow, x + 4, last);
+          else
+            mfma4_dma<NB, 2 * NB>(acc, acur, bcur, vb, (h >> 1) ? rawB1 : rawB0, b_crow, x + 3, last);
           dec_b<NB>(bnxt, rb, 0, bpos0, bpos1);
-          mfma16<NB>(acc, acur, bcur);
-          if ((h & 1) == 0) interleave_boundary<4>();
-          else interleave_boundary<2 * NB>();
+          mfma_from<NB, 4>(acc, acur, bcur);
+          interleave16();
           if (h >= 2) {
-            __builtin_amdgcn_sched_barrier(0);
-            __builtin_amdgcn_s_waitcnt(0xC07F);   // lgkmcnt(0): slot read before its reload
+            // the scale slot refill after the code loads (the load waits
+            // count them in this order); the slot was read before the barrier
             __builtin_amdgcn_sched_barrier(0);
             if (h == 2) dma_scales(va, scA, wave, it + 8, last);
             else dma_scales(vb, scB, wave, it + 8, last);
