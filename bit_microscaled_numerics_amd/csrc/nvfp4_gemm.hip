@@ -758,8 +758,6 @@ __device__ __forceinline__ void gemm_dma_tile(const GemmArgs& g, int64_t tm, int
           acur = anxt;
           bcur = bnxt;
         } else {
-          // this wave's decode writes done, then the workgroup barrier; no
-          // memory fence, which would also wait for the raw loads in flight
           // This wave's own raw data for the next steps first (its code and
           // scale slots are private to it): the load wait and the raw reads,
           // whose latency then passes at the barrier; after it only the
