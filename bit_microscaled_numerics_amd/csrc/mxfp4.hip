@@ -55,11 +55,11 @@ __global__ __launch_bounds__(kQThreads) void k_mx_quant_row(
     float m = 0.0f;
 #pragma unroll
     for (int j = 0; j < 8; ++j) m = fmaxf(m, __builtin_fabsf(z[j]));
-    m = fmaxf(m, __shfl_xor(m, 1, 64));
-    m = fmaxf(m, __shfl_xor(m, 2, 64));
+    m = quad_xor_max<1>(m);
+    m = quad_xor_max<2>(m);
     const uint32_t byte = e8m0_from_amax(m);
     const float inv = e8m0_inverse(byte);
-    const uint32_t q = SR ? encode8_sr(z, inv, sr_words(seed, stream_id, (uint64_t)i * 8u))
+    const uint32_t q = SR ? encode8_sr(z, inv, sr_words_g(seed, stream_id, (uint64_t)i))
                           : encode8_rtn(z, inv);
     st_(q, &codes[i]);
     if ((i & 3) == 0) scales[i >> 2] = (uint8_t)byte;

@@ -100,13 +100,13 @@ __global__ __launch_bounds__(kThreads) void k_amax(const v4u* __restrict__ x, in
 // its partner (the other half of the 16-block, vector index ^ 1) sit in
 // adjacent lanes: chunks start at even vectors and the vector count is even.
 __device__ __forceinline__ float rht_row_amax(const v4u v, uint32_t signs, bool hi) {
-  float z[8] = {bf16_lo(v.x), bf16_hi(v.x), bf16_lo(v.y), bf16_hi(v.y),
-                bf16_lo(v.z), bf16_hi(v.z), bf16_lo(v.w), bf16_hi(v.w)};
-  rht16_pair(z, signs, hi);
+  float z[8];
+  unpack8_flip(v, hi ? signs >> 8 : signs, z);
+  rht16_pair_butterflies<false>(z, hi);   // 4 * the transform
   float m = 0.0f;
 #pragma unroll
   for (int j = 0; j < 8; ++j) m = fmaxf(m, __builtin_fabsf(z[j]));
-  return m;
+  return m;   // 4 * the amax, exactly
 }
 
 __global__ __launch_bounds__(kThreads) void k_amax_rht_row(const v4u* __restrict__ x,
@@ -128,7 +128,7 @@ __global__ __launch_bounds__(kThreads) void k_amax_rht_row(const v4u* __restrict
         m = fmaxf(m, rht_row_amax(ld_(&x[i]), signs, hi));
     }
   }
-  block_max_atomic(__float_as_uint(m), out);
+  block_max_atomic(__float_as_uint(m * 0.25f), out);
 }
 
 // Load a 16-row x 8-column bf16 micro-tile (one 16-byte chunk per row) and
@@ -143,12 +143,15 @@ __device__ __forceinline__ void tile_load(Tile16x8& t, const uint16_t* __restric
         reinterpret_cast<const v4u*>(x + (r0 + j) * cols + c0));
 }
 
-__device__ __forceinline__ void tile_column(const Tile16x8& t, int c, float (&v)[16]) {
+// The sign of element j is flipped where bit j of signs is set (the RHT's
+// sign flips; 0 for none).
+__device__ __forceinline__ void tile_column(const Tile16x8& t, int c, float (&v)[16],
+                                            uint32_t signs = 0u) {
 #pragma unroll
   for (int j = 0; j < 16; ++j) {
     uint32_t w = (c >> 1) == 0 ? t.row[j].x : (c >> 1) == 1 ? t.row[j].y
                : (c >> 1) == 2 ? t.row[j].z : t.row[j].w;
-    v[j] = (c & 1) ? bf16_hi(w) : bf16_lo(w);
+    v[j] = (c & 1) ? bf16_hi_flip(w, flip_bit(signs, j)) : bf16_lo_flip(w, flip_bit(signs, j));
   }
 }
 
@@ -172,17 +175,17 @@ __global__ __launch_bounds__(kThreads) void k_amax_rht(const uint16_t* __restric
 #pragma unroll
     for (int c = 0; c < 8; ++c) {
       float v[16];
-      tile_column(t, c, v);
+      tile_column(t, c, v, signs);   // |v| is unaffected by the flips
       if (PLAIN) {
 #pragma unroll
         for (int j = 0; j < 16; ++j) p = fmaxf(p, __builtin_fabsf(v[j]));
       }
-      rht16(v, signs);
+      rht16_butterflies<false>(v);   // 4 * the transform; the 1/4 is taken on the max
 #pragma unroll
       for (int j = 0; j < 16; ++j) m = fmaxf(m, __builtin_fabsf(v[j]));
     }
   }
-  block_max_atomic(__float_as_uint(m), out);
+  block_max_atomic(__float_as_uint(m * 0.25f), out);
   if (PLAIN) {
     __syncthreads();   // the reduction slots are reused
     block_max_atomic(__float_as_uint(p), out_plain);
@@ -226,16 +229,22 @@ __global__ __launch_bounds__(kThreads) void k_quant_row(
       const int64_t i = c + u * kThreads + threadIdx.x;
       if (i >= nvec) continue;
       const v4u v = vs[u];
-      float z[8] = {bf16_lo(v.x), bf16_hi(v.x), bf16_lo(v.y), bf16_hi(v.y),
-                    bf16_lo(v.z), bf16_hi(v.z), bf16_lo(v.w), bf16_hi(v.w)};
-      if (RHT) rht16_pair(z, signs, i & 1);
+      float z[8];
+      if (RHT) {
+        unpack8_flip(v, (i & 1) ? signs >> 8 : signs, z);
+        rht16_pair_butterflies<false>(z, i & 1);   // 4 * the transform
+      } else {
+        unpack8_flip(v, 0u, z);
+      }
       float m = 0.0f;
 #pragma unroll
       for (int j = 0; j < 8; ++j) m = fmaxf(m, __builtin_fabsf(z[j]));
-      m = fmaxf(m, __shfl_xor(m, 1, 64));
+      m = quad_xor_max<1>(m);
+      if (RHT) m *= 0.25f;
       const BlockScale b = block_scale(m, sc);
-      const uint32_t q = SR ? encode8_sr(z, b.r, sr_words(seed, stream_id, (uint64_t)i * 8u))
-                      : encode8_rtn(z, b.r);
+      const float r = RHT ? quarter_fold(z, b.r, sc) : b.r;
+      const uint32_t q = SR ? encode8_sr(z, r, sr_words_g(seed, stream_id, (uint64_t)i))
+                      : encode8_rtn(z, r);
       st_(q, &codes[i]);
       if ((i & 1) == 0) scales[i >> 1] = (uint8_t)b.code;
     }
@@ -326,7 +335,8 @@ __global__ __launch_bounds__(kThreads) void k_quant_col(
       uint8_t* const rcodes = ro.codes + rr * (cols / 2) + cc / 2;
       uint8_t* const rscales = ro.scales + rr * (cols / 16) + cc / 16;
       const uint32_t pc = (uint32_t)(cols / 2), ps = (uint32_t)(cols / 16);  // 16 rows < 2^32
-      const uint64_t n_row0 = (uint64_t)rr * (uint64_t)cols + (uint64_t)cc;
+      // Philox counter of row rr's 8-element group at column cc (cc is a multiple of 8)
+      const uint64_t g_row0 = ((uint64_t)rr * (uint64_t)cols + (uint64_t)cc) >> 3;
 #pragma unroll
       for (int i = 0; i < 16; ++i) {
         const v4u w = t.row[i];
@@ -335,33 +345,38 @@ __global__ __launch_bounds__(kThreads) void k_quant_col(
         float m = 0.0f;
 #pragma unroll
         for (int j = 0; j < 8; ++j) m = fmaxf(m, __builtin_fabsf(z[j]));
-        m = fmaxf(m, __shfl_xor(m, 1, 64));
+        m = quad_xor_max<1>(m);
         const BlockScale b = block_scale(m, sr_ctx);
-        const uint32_t q = SR ? encode8_sr(z, b.r, sr_words(seed, ro.stream_id,
-                                                      n_row0 + (uint64_t)i * (uint64_t)cols))
+        const uint32_t q = SR ? encode8_sr(z, b.r, sr_words_g(seed, ro.stream_id,
+                                                        g_row0 + (uint64_t)i * (uint64_t)(cols >> 3)))
                         : encode8_rtn(z, b.r);
         *reinterpret_cast<uint32_t*>(rcodes + i * pc) = q;
         if ((cg & 1) == 0) rscales[i * ps] = (uint8_t)b.code;
       }
     }
-    const uint64_t n_col0 = (uint64_t)cc * (uint64_t)rows + (uint64_t)rr;
+    // output index of (column cc, row rr) over 8: the Philox counter of its
+    // 8-element group (rr and rows are multiples of 16)
+    const uint64_t g_col0 = ((uint64_t)cc * (uint64_t)rows + (uint64_t)rr) >> 3;
 #pragma unroll
     for (int c = 0; c < 8; ++c) {
       float v[16];
-      tile_column(t, c, v);
-      if (RHT) rht16(v, signs);
+      tile_column(t, c, v, RHT ? signs : 0u);
+      if (RHT) rht16_butterflies<false>(v);   // 4 * the transform
       float m = 0.0f;
 #pragma unroll
       for (int j = 0; j < 16; ++j) m = fmaxf(m, __builtin_fabsf(v[j]));
+      if (RHT) m *= 0.25f;
       const BlockScale b = block_scale(m, sc);
+      const float r = RHT ? quarter_fold(v, b.r, sc) : b.r;
       uint32_t q0, q1;
       if (SR) {
-        const uint64_t n0 = n_col0 + (uint64_t)c * (uint64_t)rows;
-        q0 = encode8_sr(v, b.r, sr_words(seed, stream_id, n0));
-        q1 = encode8_sr(v + 8, b.r, sr_words(seed, stream_id, n0 + 8));
+        // counters of the column's two 8-element groups (n0 / 8 and n0 / 8 + 1)
+        const uint64_t g0 = g_col0 + (uint64_t)c * (uint64_t)(rows >> 3);
+        q0 = encode8_sr(v, r, sr_words_g(seed, stream_id, g0));
+        q1 = encode8_sr(v + 8, r, sr_words_g(seed, stream_id, g0 + 1));
       } else {
-        q0 = encode8_rtn(v, b.r);
-        q1 = encode8_rtn(v + 8, b.r);
+        q0 = encode8_rtn(v, r);
+        q1 = encode8_rtn(v + 8, r);
       }
       lds_codes[8 * cg + c][rg] = v2u{q0, q1};
       lds_scales[8 * cg + c][rg] = (uint8_t)b.code;
@@ -448,20 +463,21 @@ __global__ __launch_bounds__(kThreads) void k_quant_2d(
       mp = pk_max_u16(mp, t.row[i].w & 0x7FFF7FFFu);
     }
     float m = fmaxf(bf16_lo(mp), bf16_hi(mp));
-    m = fmaxf(m, __shfl_xor(m, 1, 64));
+    m = quad_xor_max<1>(m);
     const BlockScale b = block_scale(m, sc);
     uint32_t q[16];
     // row i's codes sit at a uniform offset i * pitch from row rr's
     uint8_t* const rcodes = codes + rr * (cols / 2) + cc / 2;
     const uint32_t pc = (uint32_t)(cols / 2);  // 16 rows of codes span < 2^32 bytes
-    const uint64_t n_row0 = (uint64_t)rr * (uint64_t)cols + (uint64_t)cc;
+    // Philox counter of row rr's 8-element group at column cc (cc is a multiple of 8)
+    const uint64_t g_row0 = ((uint64_t)rr * (uint64_t)cols + (uint64_t)cc) >> 3;
 #pragma unroll
     for (int i = 0; i < 16; ++i) {
       const v4u w = t.row[i];
       float z[8] = {bf16_lo(w.x), bf16_hi(w.x), bf16_lo(w.y), bf16_hi(w.y),
                     bf16_lo(w.z), bf16_hi(w.z), bf16_lo(w.w), bf16_hi(w.w)};
-      q[i] = SR ? encode8_sr(z, b.r, sr_words(seed, stream_id,
-                                               n_row0 + (uint64_t)i * (uint64_t)cols))
+      q[i] = SR ? encode8_sr(z, b.r, sr_words_g(seed, stream_id,
+                                                 g_row0 + (uint64_t)i * (uint64_t)(cols >> 3)))
                 : encode8_rtn(z, b.r);
       *reinterpret_cast<uint32_t*>(rcodes + i * pc) = q[i];
     }
@@ -584,7 +600,13 @@ hipError_t launch_quant_row(const void* x, int64_t rows, int64_t cols, const flo
                             hipStream_t s) {
   const int64_t nvec = rows * cols / 8;
   const int64_t chunks = (nvec + kRowChunk - 1) / kRowChunk;
-  const dim3 g(grid_for(chunks * kThreads, 8)), b(kThreads);
+  // 8 workgroups per compute unit, or more where that would leave a
+  // workgroup more than 4 chunks: the extra workgroups queue, and the
+  // dispatcher hands them to whichever units finish first, which evens out
+  // the units' progress on large tensors (measured: 1D SR encode of a
+  // 32768x8192 tensor -10% against 16 chunks per workgroup)
+  const int64_t wg = std::min<int64_t>(chunks, std::max<int64_t>((int64_t)num_cus() * 8, (chunks + 3) / 4));
+  const dim3 g((unsigned)std::max<int64_t>(wg, 1)), b(kThreads);
   const v4u* xv = reinterpret_cast<const v4u*>(x);
   uint32_t* cv = reinterpret_cast<uint32_t*>(codes);
 #define NVFP4_ROW(SRV, RHTV)                                                                  \

@@ -150,7 +150,7 @@ int devtest_gemm_decode(const uint32_t* w, const uint8_t* sc, uint16_t* out_alu,
 // Host: the stochastic-rounding decision of the encodes (the E2M1 grid value
 // chosen for v with random bits u), compiled for the CPU from the same source.
 void devtest_sr_value_host(const float* v, const uint16_t* u, float* out, int64_t n) {
-  for (int64_t i = 0; i < n; ++i) out[i] = e2m1_sr_value(v[i], u[i]);
+  for (int64_t i = 0; i < n; ++i) out[i] = 0.5f * e2m1_sr_twice(v[i], u[i]);  // exact halving
 }
 
 }  // extern "C"

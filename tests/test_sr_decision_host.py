@@ -1,11 +1,13 @@
 """The stochastic-rounding decision of the HIP encoders, compiled for the CPU
-from the kernels' own source (e2m1_sr_value in nvfp4_device.h), against the
+from the kernels' own source (e2m1_sr_twice in nvfp4_device.h, which returns
+twice the chosen value for the FP4 encode's scale of 2; halved here), against the
 CPU reference's definition: between the neighbouring E2M1 values lo <= |v| <
 hi, round away from zero iff the 16 random bits u < (|v| - lo)/(hi - lo) *
 65536 ("NVFP4 Trains with Precision of 16-Bit and Speed and Efficiency of
 4-Bit", stochastic-rounding section: the larger neighbour with probability
 given by the distance).  The kernels take the decision as an add-and-carry on
-the binary32 bits above 0.5 and as a float compare below it; the values here
+the binary32 bits from 1 up and as a ceiling of a fused multiply-add below
+1, where the grid step is uniform; the values here
 are every binary32 within 16 patterns of every grid value and midpoint (and
 of 0, 0.125, 8) with all 65536 random values, and every 4099th binary32 in
 [0, 8] with every 97th random value.  CPU only."""
