@@ -51,15 +51,23 @@ def log(*a):
 
 
 GEMM_SOURCES = ("nvfp4_gemm.hip", "gemm_tiles.h", "gemm_decode.h", "nvfp4_device.h")
+QUANT_SOURCES = ("nvfp4_quant.hip", "mxfp4.hip", "nvfp4_device.h", "gemm_tiles.h")
+# VALU issue peak in lane-instructions per second: 1024 SIMDs, a wave64
+# instruction every 4 cycles per SIMD (16 lanes a cycle), 2.4 GHz
+VALU_LANE_OPS_PER_S = 1024 * 64 / 4 * 2.4e9
 
 
 def gemm_source_digest() -> str:
     """SHA-256 of the GEMM sources with comments and blank lines removed, so
     that the record below goes stale when the code changes, not its comments."""
+    return source_digest(GEMM_SOURCES)
+
+
+def source_digest(files) -> str:
     import hashlib
     import re
     m = hashlib.sha256()
-    for f in GEMM_SOURCES:
+    for f in files:
         with open(os.path.join(ROOT, "bit_microscaled_numerics_amd", "csrc", f)) as fh:
             text = fh.read()
         text = re.sub(r"/\*.*?\*/", "", text, flags=re.S)
@@ -76,6 +84,24 @@ def gemm_traffic():
         return None
     rec = json.load(open(path))
     return rec["traffic_bytes_per_launch"] if gemm_source_digest() == rec["source_sha256"] else None
+
+
+# the sweep's stochastic-rounding encodes and the kernel each one launches
+SR_SWEEP_KERNELS = {"1d SR encode": "k_quant_row<true, false>",
+                    "row RHT SR encode": "k_quant_row<true, true>",
+                    "col RHT SR encode": "k_quant_col<true, true, false>",
+                    "MXFP4 SR (single pass)": "k_mx_quant_row<true>"}
+
+
+def quant_valu():
+    """VALU lane-instructions per 8 elements of the quantizer kernels, from the
+    committed rocprofv3 SQ_INSTS_VALU record, or None when the quantizer code
+    changed since."""
+    path = os.path.join(ROOT, "profiles", "quantize_valu.json")
+    if not os.path.exists(path):
+        return None
+    rec = json.load(open(path))
+    return rec["valu_per_8_elements"] if source_digest(QUANT_SOURCES) == rec["source_sha256"] else None
 
 
 class Flush:
@@ -329,6 +355,7 @@ def quant_sweep(flush, steps: int = 10, keep_first=False):
     wl = inputs.sweep_tensors(0)
     out = {}
     kept = None
+    valu = quant_valu()
     for dist in ["normal", "t3"]:
         xh = wl.tensors.pop(dist)
         x = xh.cuda()
@@ -403,9 +430,17 @@ def quant_sweep(flush, steps: int = 10, keep_first=False):
                 b.record(s)
             s.synchronize()
             ms = float(np.median([a.elapsed_time(b) for a, b in ev]))
-            out[f"{dist} {name}"] = {"us": round(ms * 1e3, 1),
-                                     "GB/s": round(nbytes / (ms * 1e-3) / 1e9, 1),
-                                     "frac": round(nbytes / (ms * 1e-3) / 1e9 / HBM_PEAK_GBS, 3)}
+            rec = {"us": round(ms * 1e3, 1), "GB/s": round(nbytes / (ms * 1e-3) / 1e9, 1),
+                   "frac": round(nbytes / (ms * 1e-3) / 1e9 / HBM_PEAK_GBS, 3)}
+            if name in SR_SWEEP_KERNELS:
+                # bound by VALU issue: the time the kernel's VALU instructions
+                # take at the issue peak, over the measured time (null when the
+                # instruction record is stale)
+                v8 = (valu or {}).get(SR_SWEEP_KERNELS[name])
+                rec["bound"] = "valu"
+                rec["valu_frac"] = (round(n * v8 / 8 / VALU_LANE_OPS_PER_S / (ms * 1e-3), 3)
+                                    if v8 else None)
+            out[f"{dist} {name}"] = rec
         del x, q1, q2, qc, qr, qm
         torch.cuda.empty_cache()
     return (out, kept) if keep_first else out
@@ -733,6 +768,12 @@ def main():
         torch.cuda.empty_cache()
         sweep, c5 = quant_sweep(flush, keep_first=not args.no_cpu_baseline)
         result["quantize_sweep_32768x8192"] = sweep
+        result["quantize_sweep_bounds"] = {
+            "hbm": "frac = algorithmic bytes / time / 8 TB/s",
+            "valu": "SR encodes: valu_frac = VALU lane-instructions (rocprofv3 SQ_INSTS_VALU "
+                    "per 8 elements, profiles/quantize_valu.json) / time / peak; peak "
+                    f"{VALU_LANE_OPS_PER_S:.4g} lane-instructions/s = 1024 SIMDs x 16 lanes a "
+                    "cycle x 2.4 GHz"}
     if not args.no_cpu_baseline:
         log("cpu baseline (oracle) on the same host bytes")
         result["cpu_baseline"] = cpu_baseline(xh, wh, dyh, c5,
