@@ -409,8 +409,12 @@ hipError_t launch_mx_gemm(const MxOperand& a, const MxOperand& b, int64_t K, flo
     const hipError_t e = zero_split_tiles(plan, c, ldc, g.M, g.N, s);
     if (e != hipSuccess) return e;
   }
+  // 4-byte scale loads only where every dword is either wholly inside K or
+  // wholly past it (K / 32 a multiple of 4): a dword straddling the end of a
+  // row's blocks would bring in bytes past K (padding or the next row)
   auto sb4 = [&](const MxOperand& o) {
-    return o.ld_scales % 4 == 0 && (reinterpret_cast<uintptr_t>(o.scales) & 3) == 0;
+    return o.ld_scales % 4 == 0 && (reinterpret_cast<uintptr_t>(o.scales) & 3) == 0 &&
+           (K / 32) % 4 == 0;
   };
 #define NVFP4_MX_LAUNCH(SB)                                                                 \
   do {                                                                                       \

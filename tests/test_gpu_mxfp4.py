@@ -66,8 +66,12 @@ def _operands(M, N, K, seed):
     return a, b
 
 
+# (300, 260, 768) and (520, 264, 1280) are ragged in M and N with whole
+# 256-K stages (3 and 5 of them: odd counts); (272, 144, 544) and
+# (520, 264, 1312) end in a partial stage
 @pytest.mark.parametrize("mnk", [(32, 32, 32), (64, 96, 64), (256, 256, 256), (300, 260, 96),
-                                 (272, 144, 544), (512, 768, 1024), (520, 264, 1312)])
+                                 (272, 144, 544), (512, 768, 1024), (520, 264, 1312),
+                                 (300, 260, 768), (520, 264, 1280)])
 def test_gemm_matches_exact_product(mnk):
     M, N, K = mnk
     a, b = _operands(M, N, K, M + N + K)
@@ -97,6 +101,47 @@ def test_gemm_split_last_round_and_determinism():
     ns = np.concatenate([rng.integers(0, N, 3000), rng.integers(0, N, 256)])
     ref, t = oracle.mx_gemm_entries(oa, ob, ms, ns)
     assert_gemm_close(c1.cpu().numpy()[ms, ns], ref, t, "mx gemm split")
+
+
+def test_gemm_split_odd_stages():
+    """17 x 16 tiles at K = 768 (3 stages): the split last round's halves have
+    2 and 1 stages."""
+    M, N, K = 17 * 256, 16 * 256, 768
+    a, b = _operands(M, N, K, 6)
+    say("mx gemm split odd", (M, N, K))
+    qa, qb = nv.mx_quantize(a.cuda()), nv.mx_quantize(b.cuda())
+    c = nv.mx_gemm(qa, qb)
+    torch.cuda.synchronize()
+    oa, ob = oracle.mx_quantize(a), oracle.mx_quantize(b)
+    rng = np.random.default_rng(2)
+    ms = np.concatenate([rng.integers(0, M, 3000), np.arange(M - 256, M)])
+    ns = np.concatenate([rng.integers(0, N, 3000), rng.integers(0, N, 256)])
+    ref, t = oracle.mx_gemm_entries(oa, ob, ms, ns)
+    assert_gemm_close(c.cpu().numpy()[ms, ns], ref, t, "mx gemm split odd")
+
+
+def test_gemm_padded_scale_rows():
+    """Scale rows padded to a multiple of 4 bytes (K / 32 = 3 blocks, 4 bytes
+    per row) with 0xFF (the E8M0 NaN) in the padding: the padding is never
+    read as a block scale."""
+    M, N, K = 64, 96, 96
+    a, b = _operands(M, N, K, 7)
+    say("mx gemm padded scale rows", (M, N, K))
+    qa, qb = nv.mx_quantize(a.cuda()), nv.mx_quantize(b.cuda())
+
+    def padded(q):
+        sc = torch.full((q.rows, 4), 0xFF, dtype=torch.uint8, device="cuda")
+        sc[:, :K // 32] = q.scales
+        return nv.MXFP4Tensor(q.codes, sc, q.rows, q.k)
+
+    c = torch.empty(M, N, dtype=torch.float32, device="cuda")
+    nv.mxfp4_gemm(padded(qa), padded(qb), c, N)
+    torch.cuda.synchronize()
+    oa, ob = oracle.mx_quantize(a), oracle.mx_quantize(b)
+    ref, t = oracle.mx_gemm(oa, ob)
+    cc = c.cpu().numpy()
+    assert np.all(np.isfinite(cc))
+    assert_gemm_close(cc, ref, t, "mx gemm padded scale rows")
 
 
 def test_gemm_fprop_shape_sampled():
