@@ -841,19 +841,35 @@ __global__ __launch_bounds__(kThreads4, 1) void k_gemm_dma(GemmArgs g) {
 
 __global__ void k_zero_word(uint32_t* p) { *p = 0u; }
 
-// Zero the output tiles that split workgroups add into: one workgroup per
-// tile, same tile order as the GEMM.
+// Zero the output tiles that split workgroups add into, same tile order as
+// the GEMM: 16 workgroups per tile, 16 rows each; with VEC (N and ldc
+// multiples of 4, 16-byte aligned base, so a store never straddles N) a
+// thread clears 4 columns of 4 rows with 16-byte stores, else one column of
+// its 16 rows.
+constexpr int kZeroSlabs = kTile / 16;
+template <bool VEC>
 __global__ __launch_bounds__(256) void k_zero_tiles(float* __restrict__ c, int64_t ldc,
                                                     int64_t M, int64_t N, int64_t tiles_m,
                                                     int64_t tiles_n, int64_t first) {
   int64_t tm, tn;
-  grouped(first + blockIdx.x, tiles_m, tiles_n, tm, tn);
-  const int64_t col = tn * kTile + threadIdx.x;
-  if (col >= N) return;
-  for (int64_t r = 0; r < kTile; ++r) {
-    const int64_t row = tm * kTile + r;
-    if (row >= M) break;
-    c[row * ldc + col] = 0.0f;
+  grouped(first + blockIdx.x / kZeroSlabs, tiles_m, tiles_n, tm, tn);
+  const int64_t row0 = tm * kTile + 16 * (blockIdx.x % kZeroSlabs);
+  if (VEC) {
+    const int64_t col = tn * kTile + 4 * (threadIdx.x & 63);
+    if (col >= N) return;
+#pragma unroll
+    for (int k = 0; k < 4; ++k) {
+      const int64_t row = row0 + (threadIdx.x >> 6) + 4 * k;
+      if (row < M) *reinterpret_cast<v4f*>(&c[row * ldc + col]) = v4f{0.0f, 0.0f, 0.0f, 0.0f};
+    }
+  } else {
+    const int64_t col = tn * kTile + threadIdx.x;
+    if (col >= N) return;
+    for (int r = 0; r < 16; ++r) {
+      const int64_t row = row0 + r;
+      if (row >= M) break;
+      c[row * ldc + col] = 0.0f;
+    }
   }
 }
 
@@ -884,8 +900,13 @@ TilePlan plan_tiles(int64_t M, int64_t N, int64_t steps, bool allow_split, bool 
 hipError_t zero_split_tiles(const TilePlan& p, float* c, int64_t ldc, int64_t M, int64_t N,
                             hipStream_t s) {
   if (!p.split) return hipSuccess;
-  hipLaunchKernelGGL(k_zero_tiles, dim3((unsigned)p.rem), dim3(256), 0, s, c, ldc, M, N,
-                     p.tiles_m, p.tiles_n, p.full_tiles);
+  const dim3 grid((unsigned)(p.rem * kZeroSlabs));
+  if (N % 4 == 0 && ldc % 4 == 0 && (reinterpret_cast<uintptr_t>(c) & 15) == 0)
+    hipLaunchKernelGGL(k_zero_tiles<true>, grid, dim3(256), 0, s, c, ldc, M, N, p.tiles_m,
+                       p.tiles_n, p.full_tiles);
+  else
+    hipLaunchKernelGGL(k_zero_tiles<false>, grid, dim3(256), 0, s, c, ldc, M, N, p.tiles_m,
+                       p.tiles_n, p.full_tiles);
   return hipGetLastError();
 }
 
