@@ -521,25 +521,28 @@ def quality(step: "Step"):
 def fused_epilogue(step: "Step", reps: int):
     """The fused BF16 + amax epilogue vs the FP32 GEMM followed by the separate
     amax read of C that the next layer's quantization needs, at the Fprop and
-    Dgrad shapes.  The BF16 path computes every tile whole (its output cannot
-    take the two FP32 addends of a split tile), so it wins where the tiles fill
-    whole rounds of the CUs (Dgrad: 2560 tiles) and loses the tail split where
-    they do not (Fprop: 640)."""
+    Dgrad shapes.  With its workspace the BF16 path cuts the last round's tiles
+    along K as the FP32 path does (Fprop: 640 tiles, 2.5 rounds); "no workspace"
+    times it with half-width tiles there instead."""
     out = {}
     for name, qa, qb, c32 in [("Fprop", step.qx, step.qw, step.y),
                               ("Dgrad", step.qdy, step.qw.t(), step.dx)]:
         cb = torch.empty(qa.rows, qb.rows, dtype=torch.bfloat16, device=step.x.device)
         am = torch.empty(1, dtype=torch.float32, device=step.x.device)
-        fused = _median_ms(lambda: nv.nvfp4_gemm_bf16(qa, qb, cb, cb.stride(0), am), reps)
+        ws = nv.gemm_bf16_workspace(qa.rows, qb.rows, qa.k, step.x.device)
+        fused = _median_ms(lambda: nv.nvfp4_gemm_bf16(qa, qb, cb, cb.stride(0), am, ws), reps)
+        no_ws = (_median_ms(lambda: nv.nvfp4_gemm_bf16(qa, qb, cb, cb.stride(0), am), reps)
+                 if ws is not None else fused)
         plain = _median_ms(lambda: nv.gemm(qa, qb, c32), reps)
         scan = _median_ms(lambda: nv.nvfp4_amax(cb, am), reps)
         fl = 2.0 * qa.rows * qb.rows * qa.k
         out[name] = {"fused bf16 + amax us": round(fused * 1e3, 1),
+                     "fused, no workspace us": round(no_ws * 1e3, 1),
                      "fp32 gemm us": round(plain * 1e3, 1),
                      "separate amax of C us": round(scan * 1e3, 1),
                      "fused TFLOP/s": round(fl / (fused * 1e-3) / 1e12, 1),
                      "saved us": round((plain + scan - fused) * 1e3, 1)}
-        del cb
+        del cb, ws
     return out
 
 

@@ -17,7 +17,7 @@ from __future__ import annotations
 import ctypes
 import os
 from dataclasses import dataclass
-from typing import Optional
+from typing import Optional, Union
 
 import torch
 
@@ -32,7 +32,8 @@ NVFP4_ROWWISE, NVFP4_COLWISE = 0, 1
 EXPORTED = ("nvfp4_amax", "nvfp4_amax_rht", "nvfp4_quantize1d_rtn", "nvfp4_quantize1d_sr",
             "nvfp4_quantize2d_rtn", "nvfp4_quantize2d_sr", "nvfp4_rht_quantize",
             "nvfp4_dequantize", "nvfp4_gemm", "nvfp4_status_string", "nvfp4_last_error",
-            "nvfp4_gemm_bf16", "mxfp4_quantize", "mxfp4_dequantize", "mxfp4_gemm",
+            "nvfp4_gemm_bf16", "nvfp4_gemm_bf16_workspace_bytes", "mxfp4_quantize",
+            "mxfp4_dequantize", "mxfp4_gemm",
             "nvfp4_probe_mfma", "nvfp4_probe_scratch_bytes", "nvfp4_amax_both",
             "nvfp4_quantize_row_rht", "nvfp4_amax_rht1d", "nvfp4_rht_quantize1d",
             "nvfp4_probe_clock", "nvfp4_probe_clock_bytes", "nvfp4_probe_copy")
@@ -89,7 +90,8 @@ def load_library(path: str = LIB_PATH) -> ctypes.CDLL:
                                    vp, vp, vp],
         "nvfp4_dequantize": [ctypes.POINTER(c_operand), vp, vp],
         "nvfp4_gemm": [ctypes.POINTER(c_operand), ctypes.POINTER(c_operand), vp, i64, vp],
-        "nvfp4_gemm_bf16": [ctypes.POINTER(c_operand), ctypes.POINTER(c_operand), vp, i64, vp, vp],
+        "nvfp4_gemm_bf16": [ctypes.POINTER(c_operand), ctypes.POINTER(c_operand), vp, i64, vp, vp,
+                            i64, vp],
         "mxfp4_quantize": [vp, i64, i64, i32, u64, u32, vp, vp, vp],
         "mxfp4_dequantize": [ctypes.POINTER(c_mx_operand), vp, vp],
         "mxfp4_gemm": [ctypes.POINTER(c_mx_operand), ctypes.POINTER(c_mx_operand), vp, i64, vp],
@@ -108,6 +110,8 @@ def load_library(path: str = LIB_PATH) -> ctypes.CDLL:
     for name in ("nvfp4_probe_scratch_bytes", "nvfp4_probe_clock_bytes"):
         getattr(lib, name).argtypes = []
         getattr(lib, name).restype = ctypes.c_int64
+    lib.nvfp4_gemm_bf16_workspace_bytes.argtypes = [i64, i64, i64]
+    lib.nvfp4_gemm_bf16_workspace_bytes.restype = ctypes.c_int64
     _lib = lib
     return lib
 
@@ -377,20 +381,47 @@ def dequantize(q: NVFP4Tensor) -> torch.Tensor:
     return out
 
 
-def nvfp4_gemm_bf16(a: "NVFP4Tensor", b: "NVFP4Tensor", c, ldc: int, amax_out=None, stream=None):
+def nvfp4_gemm_bf16(a: "NVFP4Tensor", b: "NVFP4Tensor", c, ldc: int, amax_out=None,
+                    workspace: Optional[torch.Tensor] = None, stream=None):
     oa, ob = a.c_struct(), b.c_struct()
+    nbytes = 0 if workspace is None else workspace.numel() * workspace.element_size()
     _check(load_library().nvfp4_gemm_bf16(ctypes.byref(oa), ctypes.byref(ob), _p(c), ldc,
-                                          _p(amax_out), _stream(stream)))
+                                          _p(amax_out), _p(workspace), nbytes, _stream(stream)))
+
+
+def nvfp4_gemm_bf16_workspace_bytes(M: int, N: int, K: int) -> int:
+    n = int(load_library().nvfp4_gemm_bf16_workspace_bytes(M, N, K))
+    if n < 0:
+        _check(n)
+    return n
+
+
+def gemm_bf16_workspace(M: int, N: int, K: int, device) -> Optional[torch.Tensor]:
+    """The workspace nvfp4_gemm_bf16 takes for an M x N x K product (None when
+    it needs none); reusable by any later call of the same or smaller need on
+    the same stream."""
+    n = nvfp4_gemm_bf16_workspace_bytes(M, N, K)
+    if n == 0:
+        return None
+    ws = torch.empty(n, dtype=torch.uint8, device=device)
+    assert ws.data_ptr() % 256 == 0
+    return ws
 
 
 def gemm_bf16(a: NVFP4Tensor, b: NVFP4Tensor, out: Optional[torch.Tensor] = None,
-              with_amax: bool = True):
+              with_amax: bool = True, workspace: Union[torch.Tensor, None, bool] = True):
     """C = s_a s_b A B^T rounded to BF16, and (with_amax) max |C| as a device
-    float, ready to pass as the given amax of C's quantization."""
+    float, ready to pass as the given amax of C's quantization.  workspace:
+    True allocates the K-split workspace (every entry then equals the FP32
+    GEMM's, rounded), a tensor supplies it, None/False runs without one."""
     if out is None:
         out = _empty(a.rows, b.rows, dtype=torch.bfloat16, device=a.codes.device)
     amax = _empty(1, dtype=torch.float32, device=a.codes.device) if with_amax else None
-    nvfp4_gemm_bf16(a, b, out, out.stride(0), amax)
+    if workspace is True:
+        workspace = gemm_bf16_workspace(a.rows, b.rows, a.k, a.codes.device)
+    elif workspace is False:
+        workspace = None
+    nvfp4_gemm_bf16(a, b, out, out.stride(0), amax, workspace)
     return out, amax
 
 

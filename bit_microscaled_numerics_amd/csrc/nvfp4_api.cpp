@@ -347,8 +347,9 @@ int nvfp4_gemm(const nvfp4_operand* a, const nvfp4_operand* b, float* c, int64_t
                                      as_stream(stream)));
 }
 
-int nvfp4_gemm_bf16(const nvfp4_operand* a, const nvfp4_operand* b, uint16_t* c, int64_t ldc,
-                    float* amax_out, void* stream) {
+// The operand and output checks shared by the two BF16-output GEMM entries.
+static int check_gemm_bf16(const nvfp4_operand* a, const nvfp4_operand* b, const uint16_t* c,
+                           int64_t ldc, const float* amax_out) {
   int st = check_operand(a, "a");
   if (st) return st;
   if ((st = check_operand(b, "b"))) return st;
@@ -362,10 +363,35 @@ int nvfp4_gemm_bf16(const nvfp4_operand* a, const nvfp4_operand* b, uint16_t* c,
     return fail(NVFP4_ERR_ALIGN, "amax_out must be 4-byte aligned");
   if (ldc < b->rows) return fail(NVFP4_ERR_SHAPE, "ldc=%lld < N=%lld", (long long)ldc,
                                  (long long)b->rows);
-  if ((st = check_ldc(ldc, a->rows, "c"))) return st;
-  return launched(nvfp4::launch_gemm_bf16(to_kernel(a), to_kernel(b), a->k, c, ldc, amax_out,
-                                          as_stream(stream)));
+  return check_ldc(ldc, a->rows, "c");
 }
+
+int64_t nvfp4_gemm_bf16_workspace_bytes(int64_t M, int64_t N, int64_t K) {
+  if (M <= 0 || N <= 0 || K <= 0)
+    return fail(NVFP4_ERR_SHAPE, "M=%lld N=%lld K=%lld must be positive", (long long)M,
+                (long long)N, (long long)K);
+  return nvfp4::gemm_bf16_workspace_bytes(M, N, K);
+}
+
+int nvfp4_gemm_bf16(const nvfp4_operand* a, const nvfp4_operand* b, uint16_t* c, int64_t ldc,
+                    float* amax_out, void* workspace, int64_t workspace_bytes, void* stream) {
+  int st = check_gemm_bf16(a, b, c, ldc, amax_out);
+  if (st) return st;
+  if (workspace == nullptr) {
+    if (workspace_bytes != 0)
+      return fail(NVFP4_ERR_ARG, "workspace is NULL but workspace_bytes=%lld",
+                  (long long)workspace_bytes);
+  } else {
+    if (!aligned(workspace, 256)) return fail(NVFP4_ERR_ALIGN, "workspace must be 256-byte aligned");
+    const int64_t need = nvfp4::gemm_bf16_workspace_bytes(a->rows, b->rows, a->k);
+    if (workspace_bytes < need)
+      return fail(NVFP4_ERR_ARG, "workspace_bytes=%lld < %lld (nvfp4_gemm_bf16_workspace_bytes)",
+                  (long long)workspace_bytes, (long long)need);
+  }
+  return launched(nvfp4::launch_gemm_bf16(to_kernel(a), to_kernel(b), a->k, c, ldc, amax_out,
+                                          workspace, workspace_bytes, as_stream(stream)));
+}
+
 
 // ---------------------------------------------------------------- MXFP4
 

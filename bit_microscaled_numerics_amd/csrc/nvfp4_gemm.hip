@@ -32,6 +32,10 @@ struct GemmArgs {
   int64_t full_tiles;  // tiles computed whole; tiles past them are cut by `tail`
   int tail;            // TailMode of the tiles past full_tiles
   int vec_out;         // 16-byte output stores: ldc and base aligned, 256 rows < 2^31 B
+  // BF16 epilogue with K-split tail tiles: per split slot two FP32 partial
+  // buffers (one per K half, kSplitSlotFloats each) and one ticket word
+  float* ws;
+  uint32_t* ws_tickets;
 };
 
 constexpr uint32_t kBufFlags = 0x00020000u;  // raw 32-bit buffer descriptor word 3
@@ -234,9 +238,8 @@ __device__ __forceinline__ void interleave() {
 // the next quantization of C can take its amax as given.
 template <bool BF16, int WM, int WN>
 __device__ __forceinline__ void store_c(const GemmArgs& g, float16v (&acc)[WM][WN], int64_t m0,
-                                        int64_t n0, int part) {
+                                        int64_t n0, int part, float alpha) {
   const int lane = threadIdx.x & 63, lrow = lane & 31, lk = lane >> 5;
-  const float alpha = (*g.a.ts) * (*g.b.ts);
   uint32_t mag = 0u;   // largest |bf16| bits seen by this lane
 #pragma unroll
   for (int i = 0; i < WM; ++i)
@@ -348,7 +351,8 @@ __global__ __launch_bounds__(kThreads, 1) void k_gemm(GemmArgs g) {
     }
   }
 
-  store_c<BF16, kWM, kWN>(g, acc, tm * kTile + wm * 128, tn * kTile + wn * 64, part);
+  store_c<BF16, kWM, kWN>(g, acc, tm * kTile + wm * 128, tn * kTile + wn * 64, part,
+                          (*g.a.ts) * (*g.b.ts));
 }
 
 // ---------------------------------------------------------------------------
@@ -575,9 +579,9 @@ __device__ __forceinline__ void interleave16() {
 // are those of store_c.
 template <bool BF16, int NB>
 __device__ __forceinline__ void store_c_lds(const GemmArgs& g, float16v (&acc)[kMB][NB],
-                                            int64_t m0, int64_t n0, uint8_t* smem, int wave) {
+                                            int64_t m0, int64_t n0, uint8_t* smem, int wave,
+                                            float alpha) {
   const int lane = threadIdx.x & 63, lrow = lane & 31, lk = lane >> 5;
-  const float alpha = (*g.a.ts) * (*g.b.ts);
   uint8_t* region = smem + wave * 16384;
   constexpr int kEs = BF16 ? 2 : 4;                  // output element bytes
   constexpr int kRowB = 32 * kEs;                    // bytes of a block row in LDS
@@ -646,12 +650,67 @@ __device__ __forceinline__ void store_c_lds(const GemmArgs& g, float16v (&acc)[k
   }
 }
 
+// K-split tail tiles with the BF16 epilogue.  The two K halves of a tile
+// compute partial accumulators P0 and P1; FP32 output adds alpha P0 and
+// alpha P1 into a zeroed C, fl(alpha P0 + alpha P1) whatever their order.
+// The BF16 output is that sum rounded, so the halves meet in a workspace
+// instead: each stores its scaled partial (in register order: for each
+// block and accumulator slot, 64 lanes' consecutive words), makes it visible
+// device-wide (the halves usually run on different XCDs), and takes a ticket
+// with one atomic add on the slot's counter.  The half that draws ticket 1
+// finishes second: the other partial is complete, so it adds it to its own
+// (the same commutative sum) and writes the tile; the first half returns
+// without writing anything.  No workgroup waits for another.  The partial
+// words move with agent-scope atomic loads and stores, which bypass the
+// per-XCD caches.
+constexpr int64_t kSplitSlotFloats = 4 * kMB * 2 * 16 * 64;   // one K half of a 256 x 256 tile
+
+template <int NB>
+__device__ __forceinline__ bool bf16_split_exchange(const GemmArgs& g, float16v (&acc)[kMB][NB],
+                                                    int part, int64_t slot, int wave,
+                                                    float alpha, uint8_t* smem) {
+  const int lane = threadIdx.x & 63;
+  const int64_t wave_off = (int64_t)wave * (kMB * NB * 16 * 64) + lane;
+  float* mine = g.ws + (2 * slot + part) * kSplitSlotFloats + wave_off;
+  const float* other = g.ws + (2 * slot + (part ^ 1)) * kSplitSlotFloats + wave_off;
+#pragma unroll
+  for (int i = 0; i < kMB; ++i)
+#pragma unroll
+    for (int j = 0; j < NB; ++j)
+#pragma unroll
+      for (int v = 0; v < 16; ++v)
+        __hip_atomic_store(mine + ((i * NB + j) * 16 + v) * 64, acc[i][j][v] * alpha,
+                           __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
+  __threadfence();     // this thread's partial is visible before the ticket
+  __syncthreads();     // ... and every thread's; the decoded-A stages are free
+  int* ticket = reinterpret_cast<int*>(smem);
+  if (threadIdx.x == 0) *ticket = (int)atomicAdd(g.ws_tickets + slot, 1u);
+  __syncthreads();
+  const bool last = *ticket == 1;
+  __syncthreads();     // the ticket is read before the epilogue reuses the stages
+  if (!last) return false;
+  __threadfence();     // the other half's partial, stored before its ticket
+#pragma unroll
+  for (int i = 0; i < kMB; ++i)
+#pragma unroll
+    for (int j = 0; j < NB; ++j)
+#pragma unroll
+      for (int v = 0; v < 16; ++v)
+        // (0 + other) + own: the FP32 path's two adds onto a zero, also for
+        // two partials of -0 (which it turns into +0)
+        acc[i][j][v] = (0.0f + __hip_atomic_load(other + ((i * NB + j) * 16 + v) * 64,
+                                                 __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT)) +
+                       acc[i][j][v] * alpha;
+  return true;
+}
+
 // One tile (or half-width tail tile) of the fast path: A rows tm * 256 ..
 // +255, B rows b_row0 .. + 64 NB * 4 - 1 (NB blocks of 32 per wave: 2 for
 // a whole 256-wide tile, 1 for a half-width one), K part `part`.
 template <bool BF16, int NB>
 __device__ __forceinline__ void gemm_dma_tile(const GemmArgs& g, int64_t tm, int64_t b_row0,
-                                              int part, int wave, uint8_t* smem, uint8_t* rawA0,
+                                              int part, int64_t slot, int wave, uint8_t* smem,
+                                              uint8_t* rawA0,
                                               uint8_t* rawA1, uint8_t* rawB0, uint8_t* rawB1,
                                               uint8_t* scA, uint8_t* scB) {
   const int t = threadIdx.x, lane = t & 63;
@@ -805,11 +864,19 @@ __device__ __forceinline__ void gemm_dma_tile(const GemmArgs& g, int64_t tm, int
   }
   __builtin_amdgcn_s_waitcnt(0);   // loads of the groups past the end
 
+  float alpha = (*g.a.ts) * (*g.b.ts);
+  if (BF16 && part >= 0) {
+    // a K half of a BF16 tail tile: the workgroup that finishes second writes
+    // the tile from both halves' partials, already scaled (alpha 1)
+    if (!bf16_split_exchange<NB>(g, acc, part, slot, wave, alpha, smem)) return;
+    alpha = 1.0f;
+    part = -1;
+  }
   if (part < 0 && g.vec_out) {
     __syncthreads();   // every wave is done with the decoded-A stages
-    store_c_lds<BF16, NB>(g, acc, tm * kTile, b_row0 + bw, smem, wave);
+    store_c_lds<BF16, NB>(g, acc, tm * kTile, b_row0 + bw, smem, wave, alpha);
   } else {
-    store_c<BF16, kMB, NB>(g, acc, tm * kTile, b_row0 + bw, part);
+    store_c<BF16, kMB, NB>(g, acc, tm * kTile, b_row0 + bw, part, alpha);
   }
 }
 
@@ -831,12 +898,17 @@ __global__ __launch_bounds__(kThreads4, 1) void k_gemm_dma(GemmArgs g) {
   tn = __builtin_amdgcn_readfirstlane((int)tn);
   part = __builtin_amdgcn_readfirstlane(part);
   nh = __builtin_amdgcn_readfirstlane(nh);
+  // split slot of a K half (BF16 epilogue): tail tile, and its N half
+  const int pieces = g.tail == kTailNK ? 4 : 2;
+  const int64_t slot = part < 0 ? 0
+                                : ((int64_t)blockIdx.x - g.full_tiles) / pieces *
+                                          (g.tail == kTailNK ? 2 : 1) + (nh < 0 ? 0 : nh);
   if (nh < 0)
-    gemm_dma_tile<BF16, 2>(g, tm, tn * kTile, part, wave, smem, rawA0, rawA1, rawB0, rawB1, scA,
-                           scB);
+    gemm_dma_tile<BF16, 2>(g, tm, tn * kTile, part, slot, wave, smem, rawA0, rawA1, rawB0, rawB1,
+                           scA, scB);
   else
-    gemm_dma_tile<BF16, 1>(g, tm, tn * kTile + 128 * nh, part, wave, smem, rawA0, rawA1, rawB0,
-                           rawB1, scA, scB);
+    gemm_dma_tile<BF16, 1>(g, tm, tn * kTile + 128 * nh, part, slot, wave, smem, rawA0, rawA1,
+                           rawB0, rawB1, scA, scB);
 }
 
 __global__ void k_zero_word(uint32_t* p) { *p = 0u; }
@@ -910,9 +982,31 @@ hipError_t zero_split_tiles(const TilePlan& p, float* c, int64_t ldc, int64_t M,
   return hipGetLastError();
 }
 
+// The BF16 epilogue's K-split workspace: per split slot (a tail tile, or
+// one N half of it) two partial buffers, then one ticket word per slot.
+static int64_t split_slots(const TilePlan& p) {
+  return p.split ? p.rem * (p.tail == kTailNK ? 2 : 1) : 0;
+}
+static int64_t split_partial_bytes(int64_t slots) {
+  return slots * 2 * kSplitSlotFloats * (int64_t)sizeof(float);
+}
+static int64_t split_ws_bytes(int64_t slots) {
+  return slots == 0 ? 0 : split_partial_bytes(slots) + ((slots * 4 + 255) & ~(int64_t)255);
+}
+
+int64_t gemm_bf16_workspace_bytes(int64_t M, int64_t N, int64_t K) {
+  // the plan a fast-path launch with a workspace makes (plan_tiles below)
+  return split_ws_bytes(split_slots(plan_tiles(M, N, (K + kBK - 1) / kBK, true, true)));
+}
+
+__global__ __launch_bounds__(256) void k_zero_words(uint32_t* __restrict__ p, int64_t n) {
+  for (int64_t i = (int64_t)blockIdx.x * 256 + threadIdx.x; i < n; i += (int64_t)gridDim.x * 256)
+    p[i] = 0u;
+}
+
 static hipError_t launch_gemm_any(const GemmOperand& a, const GemmOperand& b, int64_t K,
                                   float* c, uint16_t* cb, uint32_t* amax, int64_t ldc,
-                                  hipStream_t s) {
+                                  void* ws, int64_t ws_bytes, hipStream_t s) {
   const bool bf16 = cb != nullptr;
   // 16-byte output stores: 4 FP32 or 8 BF16 values of a row per store
   const uintptr_t cbase = bf16 ? reinterpret_cast<uintptr_t>(cb) : reinterpret_cast<uintptr_t>(c);
@@ -942,12 +1036,22 @@ static hipError_t launch_gemm_any(const GemmOperand& a, const GemmOperand& b, in
   // The tail plan: K halves need an FP32 output (two addends onto zero) and,
   // on the fast path, whole 4-step trips per half; half-width tail tiles
   // exist on the fast path only.
-  const TilePlan plan = plan_tiles(g.M, g.N, (K + kBK - 1) / kBK, !bf16 && (!dma || steps % 8 == 0),
-                                   dma);
+  // With a BF16 output the K halves meet in the workspace (bf16_split_exchange),
+  // so they need one, and the fast path.
+  const bool split_ok = bf16 ? (ws != nullptr && dma && steps % 8 == 0) : (!dma || steps % 8 == 0);
+  const TilePlan plan = plan_tiles(g.M, g.N, (K + kBK - 1) / kBK, split_ok, dma);
   g.full_tiles = plan.full_tiles;
   g.tail = plan.tail;
   const dim3 grid((unsigned)plan.grid);
-  {
+  if (bf16 && plan.split) {
+    const int64_t slots = split_slots(plan);
+    if (split_ws_bytes(slots) > ws_bytes) return hipErrorInvalidValue;
+    g.ws = static_cast<float*>(ws);
+    g.ws_tickets = reinterpret_cast<uint32_t*>(static_cast<uint8_t*>(ws) + split_partial_bytes(slots));
+    hipLaunchKernelGGL(k_zero_words, dim3(1), dim3(256), 0, s, g.ws_tickets, slots);
+    const hipError_t e = hipGetLastError();
+    if (e != hipSuccess) return e;
+  } else if (!bf16) {
     const hipError_t e = zero_split_tiles(plan, c, ldc, g.M, g.N, s);
     if (e != hipSuccess) return e;
   }
@@ -988,12 +1092,14 @@ static hipError_t launch_gemm_any(const GemmOperand& a, const GemmOperand& b, in
 
 hipError_t launch_gemm(const GemmOperand& a, const GemmOperand& b, int64_t K, float* c,
                        int64_t ldc, hipStream_t s) {
-  return launch_gemm_any(a, b, K, c, nullptr, nullptr, ldc, s);
+  return launch_gemm_any(a, b, K, c, nullptr, nullptr, ldc, nullptr, 0, s);
 }
 
 hipError_t launch_gemm_bf16(const GemmOperand& a, const GemmOperand& b, int64_t K, uint16_t* c,
-                            int64_t ldc, float* amax, hipStream_t s) {
-  return launch_gemm_any(a, b, K, nullptr, c, reinterpret_cast<uint32_t*>(amax), ldc, s);
+                            int64_t ldc, float* amax, void* ws, int64_t ws_bytes, hipStream_t s) {
+  return launch_gemm_any(a, b, K, nullptr, c, reinterpret_cast<uint32_t*>(amax), ldc, ws, ws_bytes,
+                         s);
 }
+
 
 }  // namespace nvfp4

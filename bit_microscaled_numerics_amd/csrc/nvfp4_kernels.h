@@ -52,8 +52,11 @@ struct GemmOperand {
 
 hipError_t launch_gemm(const GemmOperand& a, const GemmOperand& b, int64_t K, float* c,
                        int64_t ldc, hipStream_t s);
+// BF16 output (+ max |C|); ws (nullable) of ws_bytes >= gemm_bf16_workspace_bytes
+// lets the tail tiles split along K, exactly as the FP32 path's do.
 hipError_t launch_gemm_bf16(const GemmOperand& a, const GemmOperand& b, int64_t K, uint16_t* c,
-                            int64_t ldc, float* amax, hipStream_t s);
+                            int64_t ldc, float* amax, void* ws, int64_t ws_bytes, hipStream_t s);
+int64_t gemm_bf16_workspace_bytes(int64_t M, int64_t N, int64_t K);
 
 // MXFP4 (comparison format): rowwise, 32-element blocks, E8M0 scales.
 struct MxOperand {

@@ -230,9 +230,25 @@ int nvfp4_gemm(const nvfp4_operand* a, const nvfp4_operand* b, float* c, int64_t
  * over the BF16 values -- the tensor amax the next layer's quantization of C
  * needs, without its separate full read of C (the cost named in "Pretraining
  * Large Language Models with NVFP4", summary page, limitations paragraph).
- * Pass it with NVFP4_AMAX_GIVEN.  Same operands and validation as nvfp4_gemm. */
+ * Pass it with NVFP4_AMAX_GIVEN.  Same operands and validation as nvfp4_gemm.
+ *
+ * workspace: caller-owned device memory, 256-byte aligned, of workspace_bytes
+ * >= nvfp4_gemm_bf16_workspace_bytes(M, N, K) bytes, or NULL with 0.  With it
+ * the last round's tiles may be cut along K as in the FP32 GEMM: the two
+ * halves' FP32 partials meet in the workspace, and every BF16 entry is then
+ * exactly the FP32 GEMM's entry rounded (ties to even).  Without it those
+ * tiles run as half-width tiles over the whole K (same rounding of their own
+ * FP32 sums).  The workspace content on entry does not matter; calls that use
+ * one workspace at the same time race.  NVFP4_ERR_ARG: workspace_bytes too
+ * small; NVFP4_ERR_ALIGN: workspace not 256-byte aligned. */
 int nvfp4_gemm_bf16(const nvfp4_operand* a, const nvfp4_operand* b, uint16_t* c_bf16, int64_t ldc,
-                    float* amax_out, void* stream);
+                    float* amax_out, void* workspace, int64_t workspace_bytes, void* stream);
+
+/* Workspace bytes nvfp4_gemm_bf16 needs for an M x N x K product on the
+ * current device (0 when its tiles are never cut along K); a negative
+ * NVFP4_ERR_* status for M, N or K not positive. */
+int64_t nvfp4_gemm_bf16_workspace_bytes(int64_t M, int64_t N, int64_t K);
+
 
 /* ------------------------------------------------------------------------
  * MXFP4, the format NVFP4 is measured against: 32-element blocks along K, a

@@ -77,7 +77,18 @@ int main() {
   nvfp4_operand b{B, 16, B, 2, 1, 1, F, 512, 32};
   EXPECT(nvfp4_dequantize(&a, F, nullptr), OK);
   EXPECT(nvfp4_gemm(&a, &b, F, 512, nullptr), OK);
-  EXPECT(nvfp4_gemm_bf16(&a, &b, reinterpret_cast<uint16_t*>(F), 512, F, nullptr), OK);
+  EXPECT(nvfp4_gemm_bf16(&a, &b, reinterpret_cast<uint16_t*>(F), 512, F, nullptr, 0, nullptr), OK);
+  // the stub workspace need is 4096 bytes
+  EXPECT(nvfp4_gemm_bf16(&a, &b, reinterpret_cast<uint16_t*>(F), 512, F, dev + 4096, 4096,
+                         nullptr), OK);
+  EXPECT(nvfp4_gemm_bf16(&a, &b, reinterpret_cast<uint16_t*>(F), 512, F, dev + 4096, 4095,
+                         nullptr), EARG);
+  EXPECT(nvfp4_gemm_bf16(&a, &b, reinterpret_cast<uint16_t*>(F), 512, F, dev + 4100, 4096,
+                         nullptr), EALIGN);
+  EXPECT(nvfp4_gemm_bf16(&a, &b, reinterpret_cast<uint16_t*>(F), 512, F, nullptr, 16, nullptr),
+         EARG);
+  EXPECT(nvfp4_gemm_bf16_workspace_bytes(256, 512, 32), 4096);
+  EXPECT(nvfp4_gemm_bf16_workspace_bytes(0, 512, 32), ESHAPE);
   nvfp4_operand huge = a;
   huge.rows = BIG;
   EXPECT(nvfp4_dequantize(&huge, F, nullptr), ESHAPE);

@@ -155,11 +155,22 @@ def test_linear_rejects_cpu_tensors():
 def test_gemm_bf16_validation(lib):
     g = lib.nvfp4_gemm_bf16
     ok = _op()
-    assert g(ctypes.byref(ok), ctypes.byref(ok), None, 16, None, None) == nv.NVFP4_ERR_NULL
-    assert g(ctypes.byref(ok), ctypes.byref(ok), MIS, 16, None, None) == nv.NVFP4_ERR_ALIGN
-    assert g(ctypes.byref(ok), ctypes.byref(ok), FAKE, 16, MIS, None) == nv.NVFP4_ERR_ALIGN
-    assert g(ctypes.byref(ok), ctypes.byref(ok), FAKE, 8, None, None) == nv.NVFP4_ERR_SHAPE
-    assert g(ctypes.byref(ok), ctypes.byref(_op(k=48)), FAKE, 16, None, None) == nv.NVFP4_ERR_SHAPE
+    r = ctypes.byref
+    assert g(r(ok), r(ok), None, 16, None, None, 0, None) == nv.NVFP4_ERR_NULL
+    assert g(r(ok), r(ok), MIS, 16, None, None, 0, None) == nv.NVFP4_ERR_ALIGN
+    assert g(r(ok), r(ok), FAKE, 16, MIS, None, 0, None) == nv.NVFP4_ERR_ALIGN
+    assert g(r(ok), r(ok), FAKE, 8, None, None, 0, None) == nv.NVFP4_ERR_SHAPE
+    assert g(r(ok), r(_op(k=48)), FAKE, 16, None, None, 0, None) == nv.NVFP4_ERR_SHAPE
+    # a workspace size without a workspace; a workspace off 256-byte alignment
+    assert g(r(ok), r(ok), FAKE, 16, None, None, 4096, None) == nv.NVFP4_ERR_ARG
+    assert g(r(ok), r(ok), FAKE, 16, None, FAKE + 16, 4096, None) == nv.NVFP4_ERR_ALIGN
+
+
+def test_gemm_bf16_workspace_query(lib):
+    """The workspace query refuses empty shapes."""
+    w = lib.nvfp4_gemm_bf16_workspace_bytes
+    assert w(0, 16, 16) == nv.NVFP4_ERR_SHAPE
+    assert w(16, -16, 16) == nv.NVFP4_ERR_SHAPE
 
 
 def test_probe_mfma_validation(lib):

@@ -1,9 +1,12 @@
-"""The fused GEMM epilogue (BF16 output + max |C|): on shapes where the FP32
-path computes every tile whole, the BF16 output is exactly the FP32 output
-rounded to nearest-even; the amax is exactly max |C| over the written BF16
-values; quantizing C with that amax given equals quantizing it with a computed
-amax byte for byte; at the benchmark's Fprop shape the BF16 output matches the
-oracle's exact product within the GEMM tolerance plus BF16 rounding."""
+"""The fused GEMM epilogue (BF16 output + max |C|): the BF16 output is exactly
+the FP32 output rounded to nearest-even -- on every shape when the K-split
+workspace is given (the last round's tiles then split along K as in the FP32
+path, both halves' partials meeting in the workspace), and where the FP32 path
+computes every tile whole without it; the amax is exactly max |C| over the
+written BF16 values; quantizing C with that amax given equals quantizing it
+with a computed amax byte for byte; at the benchmark's Fprop shape the BF16
+output matches the oracle's exact product within the GEMM tolerance plus BF16
+rounding."""
 import numpy as np
 import pytest
 import torch
@@ -42,6 +45,30 @@ def test_bf16_is_rounded_fp32_and_amax_exact(mnk):
     assert float(amax.cpu()[0]) == float(mag.max().view(np.float32))
 
 
+@pytest.mark.parametrize("mnk", [(22 * 256, 16 * 256, 512),     # 352 tiles: 96 cut in K halves
+                                 (17 * 256, 16 * 256, 1024)])   # 272 tiles: 16 cut in 4 pieces
+def test_bf16_split_tail_is_rounded_fp32(mnk):
+    """Tail tiles cut along K (and N): both halves' FP32 partials meet in the
+    workspace, so every entry is the FP32 path's sum rounded; twice, bit for
+    bit (the workspace is reused as it comes)."""
+    M, N, K = mnk
+    qa, qb, _, _ = _ops(M, N, K, M + K)
+    say("gemm bf16 split tail", mnk)
+    ws = nv.gemm_bf16_workspace(M, N, K, "cuda")
+    assert ws is not None and ws.numel() == nv.nvfp4_gemm_bf16_workspace_bytes(M, N, K)
+    c32 = nv.gemm(qa, qb)
+    cb1, amax = nv.gemm_bf16(qa, qb, workspace=ws)
+    cb2, _ = nv.gemm_bf16(qa, qb, workspace=ws)
+    torch.cuda.synchronize()
+    assert torch.equal(cb1, cb2)
+    got = cb1.cpu().view(torch.int16).numpy().view(np.uint16)
+    want = rne_bf16_bits(c32.cpu().numpy())
+    bad = np.argwhere(got != want)
+    assert bad.size == 0, (len(bad), bad[:4].tolist())
+    mag = (got & 0x7FFF).astype(np.uint32) << 16
+    assert float(amax.cpu()[0]) == float(mag.max().view(np.float32))
+
+
 def test_given_amax_feeds_the_next_quantization():
     qa, qb, _, _ = _ops(256, 512, 256, 3)
     cb, amax = nv.gemm_bf16(qa, qb)
@@ -59,7 +86,12 @@ def test_fprop_shape_against_oracle():
     say("gemm bf16 fprop 8192x5120x20480")
     qx, qw = nv.quantize_1d(X.cuda()), nv.quantize_2d(W.cuda())
     cb, amax = nv.gemm_bf16(qx, qw)
+    c32 = nv.gemm(qx, qw)
     torch.cuda.synchronize()
+    # 640 tiles: the last 128 are cut along K; every entry is the FP32 one rounded
+    got = cb.cpu().view(torch.int16).numpy().view(np.uint16)
+    assert np.array_equal(got, rne_bf16_bits(c32.cpu().numpy()))
+    del c32
     y = cb.float().cpu().numpy().astype(np.float64)
     assert np.all(np.isfinite(y))
     assert float(amax.cpu()[0]) == float(np.abs(y).max())
@@ -75,16 +107,17 @@ def test_fprop_shape_against_oracle():
 
 
 def test_half_width_tail_tiles_bf16():
-    """17 x 16 tiles leave a last round of 16 tiles; with a BF16 output they
-    run as 32 half-width (256 x 128) workgroups over the whole K.  Those tiles
+    """17 x 16 tiles leave a last round of 16 tiles; with a BF16 output and
+    no workspace they run as 32 half-width (256 x 128) workgroups over the
+    whole K.  Those tiles
     (the last tile-row) are checked densely against the oracle within the GEMM
     tolerance plus BF16 rounding, the amax against the written values, and two
     runs bit for bit."""
     M, N, K = 17 * 256, 16 * 256, 1024
     qa, qb, x, w = _ops(M, N, K, 41)
     say("gemm bf16 half-width tail", (M, N, K))
-    cb1, amax = nv.gemm_bf16(qa, qb)
-    cb2, _ = nv.gemm_bf16(qa, qb)
+    cb1, amax = nv.gemm_bf16(qa, qb, workspace=None)
+    cb2, _ = nv.gemm_bf16(qa, qb, workspace=None)
     torch.cuda.synchronize()
     assert torch.equal(cb1, cb2)
     y = cb1.float().cpu().numpy().astype(np.float64)
