@@ -681,15 +681,20 @@ __device__ __forceinline__ bool bf16_split_exchange(const GemmArgs& g, float16v 
       for (int v = 0; v < 16; ++v)
         __hip_atomic_store(mine + ((i * NB + j) * 16 + v) * 64, acc[i][j][v] * alpha,
                            __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
-  __threadfence();     // this thread's partial is visible before the ticket
-  __syncthreads();     // ... and every thread's; the decoded-A stages are free
+  // Every wave's partial stores happen before thread 0's ticket (barrier),
+  // which releases them at agent scope and acquires the other half's; the
+  // barrier after it carries that to every wave.  Only thread 0 fences: an
+  // agent-scope fence writes back and invalidates this XCD's whole L2, which
+  // the workgroups still streaming operands there would pay for.
+  __syncthreads();     // also: the decoded-A stages are free
   int* ticket = reinterpret_cast<int*>(smem);
-  if (threadIdx.x == 0) *ticket = (int)atomicAdd(g.ws_tickets + slot, 1u);
+  if (threadIdx.x == 0)
+    *ticket = (int)__hip_atomic_fetch_add(g.ws_tickets + slot, 1u, __ATOMIC_ACQ_REL,
+                                          __HIP_MEMORY_SCOPE_AGENT);
   __syncthreads();
   const bool last = *ticket == 1;
   __syncthreads();     // the ticket is read before the epilogue reuses the stages
   if (!last) return false;
-  __threadfence();     // the other half's partial, stored before its ticket
 #pragma unroll
   for (int i = 0; i < kMB; ++i)
 #pragma unroll
