@@ -32,8 +32,8 @@ NVFP4_ROWWISE, NVFP4_COLWISE = 0, 1
 EXPORTED = ("nvfp4_amax", "nvfp4_amax_rht", "nvfp4_quantize1d_rtn", "nvfp4_quantize1d_sr",
             "nvfp4_quantize2d_rtn", "nvfp4_quantize2d_sr", "nvfp4_rht_quantize",
             "nvfp4_dequantize", "nvfp4_gemm", "nvfp4_status_string", "nvfp4_last_error",
-            "nvfp4_gemm_bf16", "nvfp4_gemm_bf16_workspace_bytes", "mxfp4_quantize",
-            "mxfp4_dequantize", "mxfp4_gemm",
+            "nvfp4_gemm_bf16", "nvfp4_gemm_bf16_workspace_bytes", "nvfp4_gemm_bf16_noalloc",
+            "nvfp4_gemm_bf16_noalloc_max_bytes", "mxfp4_quantize", "mxfp4_dequantize", "mxfp4_gemm",
             "nvfp4_probe_mfma", "nvfp4_probe_scratch_bytes", "nvfp4_amax_both",
             "nvfp4_quantize_row_rht", "nvfp4_amax_rht1d", "nvfp4_rht_quantize1d",
             "nvfp4_probe_clock", "nvfp4_probe_clock_bytes", "nvfp4_probe_copy")
@@ -92,6 +92,8 @@ def load_library(path: str = LIB_PATH) -> ctypes.CDLL:
         "nvfp4_gemm": [ctypes.POINTER(c_operand), ctypes.POINTER(c_operand), vp, i64, vp],
         "nvfp4_gemm_bf16": [ctypes.POINTER(c_operand), ctypes.POINTER(c_operand), vp, i64, vp, vp,
                             i64, vp],
+        "nvfp4_gemm_bf16_noalloc": [ctypes.POINTER(c_operand), ctypes.POINTER(c_operand), vp, i64,
+                                    vp, vp],
         "mxfp4_quantize": [vp, i64, i64, i32, u64, u32, vp, vp, vp],
         "mxfp4_dequantize": [ctypes.POINTER(c_mx_operand), vp, vp],
         "mxfp4_gemm": [ctypes.POINTER(c_mx_operand), ctypes.POINTER(c_mx_operand), vp, i64, vp],
@@ -107,7 +109,8 @@ def load_library(path: str = LIB_PATH) -> ctypes.CDLL:
     lib.nvfp4_status_string.restype = ctypes.c_char_p
     lib.nvfp4_last_error.argtypes = []
     lib.nvfp4_last_error.restype = ctypes.c_char_p
-    for name in ("nvfp4_probe_scratch_bytes", "nvfp4_probe_clock_bytes"):
+    for name in ("nvfp4_probe_scratch_bytes", "nvfp4_probe_clock_bytes",
+                 "nvfp4_gemm_bf16_noalloc_max_bytes"):
         getattr(lib, name).argtypes = []
         getattr(lib, name).restype = ctypes.c_int64
     lib.nvfp4_gemm_bf16_workspace_bytes.argtypes = [i64, i64, i64]
@@ -394,6 +397,13 @@ def nvfp4_gemm_bf16_workspace_bytes(M: int, N: int, K: int) -> int:
     if n < 0:
         _check(n)
     return n
+
+
+def nvfp4_gemm_bf16_noalloc(a: "NVFP4Tensor", b: "NVFP4Tensor", c, ldc: int, amax_out=None,
+                            stream=None):
+    oa, ob = a.c_struct(), b.c_struct()
+    _check(load_library().nvfp4_gemm_bf16_noalloc(ctypes.byref(oa), ctypes.byref(ob), _p(c), ldc,
+                                                  _p(amax_out), _stream(stream)))
 
 
 def gemm_bf16_workspace(M: int, N: int, K: int, device) -> Optional[torch.Tensor]:

@@ -392,6 +392,20 @@ int nvfp4_gemm_bf16(const nvfp4_operand* a, const nvfp4_operand* b, uint16_t* c,
                                           workspace, workspace_bytes, as_stream(stream)));
 }
 
+int64_t nvfp4_gemm_bf16_noalloc_max_bytes(void) { return nvfp4::gemm_bf16_noalloc_max_bytes(); }
+
+int nvfp4_gemm_bf16_noalloc(const nvfp4_operand* a, const nvfp4_operand* b, uint16_t* c,
+                            int64_t ldc, float* amax_out, void* stream) {
+  int st = check_gemm_bf16(a, b, c, ldc, amax_out);
+  if (st) return st;
+  const int64_t need = nvfp4::gemm_bf16_workspace_bytes(a->rows, b->rows, a->k);
+  if (need > nvfp4::gemm_bf16_noalloc_max_bytes())
+    return fail(NVFP4_ERR_SHAPE, "M=%lld N=%lld K=%lld needs %lld workspace bytes, above the "
+                "%lld this entry point holds", (long long)a->rows, (long long)b->rows,
+                (long long)a->k, (long long)need, (long long)nvfp4::gemm_bf16_noalloc_max_bytes());
+  return launched(nvfp4::launch_gemm_bf16_noalloc(to_kernel(a), to_kernel(b), a->k, c, ldc,
+                                                  amax_out, as_stream(stream)));
+}
 
 // ---------------------------------------------------------------- MXFP4
 

@@ -15,6 +15,8 @@
 // accumulation, and the tensor scales are applied once in the epilogue.  (The
 // gfx950 scaled FP4 MFMA takes power-of-two E8M0 scales per 32 elements, so
 // it cannot apply an E4M3 scale per 16 exactly.)
+#include <mutex>
+
 #include "gemm_decode.h"
 #include "gemm_tiles.h"
 #include "nvfp4_device.h"
@@ -1106,5 +1108,44 @@ hipError_t launch_gemm_bf16(const GemmOperand& a, const GemmOperand& b, int64_t 
                          s);
 }
 
+// The allocation-free BF16 GEMM's workspace: a file-scope device array, one
+// per GPU, held for the life of the process.  Its size covers every split
+// plan on a 256-CU device (at most 128 slots: 2 x rem <= 256 for K halves,
+// 4 x rem <= 256 with N halves).  The host uses its device address (looked
+// up once per device), never the symbol itself.
+constexpr int64_t kNoAllocSlots = 128;
+constexpr int64_t kNoAllocBytes = kNoAllocSlots * 2 * kSplitSlotFloats * 4 + kNoAllocSlots * 4;
+static __device__ __align__(256) uint8_t scratch[kNoAllocBytes];
+
+static hipError_t scratch_address(void** out) {
+  constexpr int kMaxDevices = 64;
+  static std::mutex mu;
+  static void* addr[kMaxDevices] = {};
+  int dev = 0;
+  hipError_t e = hipGetDevice(&dev);
+  if (e != hipSuccess) return e;
+  if (dev < 0 || dev >= kMaxDevices) return hipErrorInvalidDevice;
+  std::lock_guard<std::mutex> lock(mu);
+  if (addr[dev] == nullptr) {
+    void* p = nullptr;
+    e = hipGetSymbolAddress(&p, HIP_SYMBOL(scratch));
+    if (e != hipSuccess) return e;
+    addr[dev] = p;
+  }
+  *out = addr[dev];
+  return hipSuccess;
+}
+
+int64_t gemm_bf16_noalloc_max_bytes() { return kNoAllocBytes; }
+
+hipError_t launch_gemm_bf16_noalloc(const GemmOperand& a, const GemmOperand& b, int64_t K,
+                                    uint16_t* c, int64_t ldc, float* amax, hipStream_t s) {
+  if (gemm_bf16_workspace_bytes(a.rows, b.rows, K) > kNoAllocBytes) return hipErrorInvalidValue;
+  void* ws = nullptr;
+  const hipError_t e = scratch_address(&ws);
+  if (e != hipSuccess) return e;
+  return launch_gemm_any(a, b, K, nullptr, c, reinterpret_cast<uint32_t*>(amax), ldc, ws,
+                         kNoAllocBytes, s);
+}
 
 }  // namespace nvfp4

@@ -57,6 +57,11 @@ hipError_t launch_gemm(const GemmOperand& a, const GemmOperand& b, int64_t K, fl
 hipError_t launch_gemm_bf16(const GemmOperand& a, const GemmOperand& b, int64_t K, uint16_t* c,
                             int64_t ldc, float* amax, void* ws, int64_t ws_bytes, hipStream_t s);
 int64_t gemm_bf16_workspace_bytes(int64_t M, int64_t N, int64_t K);
+// The same with the library's own per-device workspace (no allocation, no
+// workspace argument), for shapes needing at most gemm_bf16_noalloc_max_bytes().
+hipError_t launch_gemm_bf16_noalloc(const GemmOperand& a, const GemmOperand& b, int64_t K,
+                                    uint16_t* c, int64_t ldc, float* amax, hipStream_t s);
+int64_t gemm_bf16_noalloc_max_bytes();
 
 // MXFP4 (comparison format): rowwise, 32-element blocks, E8M0 scales.
 struct MxOperand {

@@ -249,6 +249,17 @@ int nvfp4_gemm_bf16(const nvfp4_operand* a, const nvfp4_operand* b, uint16_t* c_
  * NVFP4_ERR_* status for M, N or K not positive. */
 int64_t nvfp4_gemm_bf16_workspace_bytes(int64_t M, int64_t N, int64_t K);
 
+/* nvfp4_gemm_bf16 for callers that cannot allocate device memory (code under
+ * HIP graph capture, tight serving loops, harnesses that forbid allocation):
+ * no workspace argument and no allocation; the K-split partials go to a
+ * fixed array of nvfp4_gemm_bf16_noalloc_max_bytes() bytes (64 MiB + 512 B)
+ * in each GPU's memory, held by the library until the process ends.  Shapes
+ * whose workspace need exceeds it are rejected (NVFP4_ERR_SHAPE; every shape
+ * on a 256-CU MI355X fits).  All calls on one GPU share that array: calls
+ * that overlap on one GPU race. */
+int nvfp4_gemm_bf16_noalloc(const nvfp4_operand* a, const nvfp4_operand* b, uint16_t* c_bf16,
+                            int64_t ldc, float* amax_out, void* stream);
+int64_t nvfp4_gemm_bf16_noalloc_max_bytes(void);
 
 /* ------------------------------------------------------------------------
  * MXFP4, the format NVFP4 is measured against: 32-element blocks along K, a

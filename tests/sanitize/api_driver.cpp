@@ -87,6 +87,10 @@ int main() {
                          nullptr), EALIGN);
   EXPECT(nvfp4_gemm_bf16(&a, &b, reinterpret_cast<uint16_t*>(F), 512, F, nullptr, 16, nullptr),
          EARG);
+  EXPECT(nvfp4_gemm_bf16_noalloc(&a, &b, reinterpret_cast<uint16_t*>(F), 512, F, nullptr), OK);
+  EXPECT(nvfp4_gemm_bf16_noalloc(&a, &b, reinterpret_cast<uint16_t*>(F), 256, F, nullptr),
+         ESHAPE);
+  EXPECT(nvfp4_gemm_bf16_noalloc_max_bytes(), 8192);
   EXPECT(nvfp4_gemm_bf16_workspace_bytes(256, 512, 32), 4096);
   EXPECT(nvfp4_gemm_bf16_workspace_bytes(0, 512, 32), ESHAPE);
   nvfp4_operand huge = a;

@@ -64,6 +64,11 @@ hipError_t launch_gemm_bf16(const GemmOperand&, const GemmOperand&, int64_t, uin
   return ok();
 }
 int64_t gemm_bf16_workspace_bytes(int64_t, int64_t, int64_t) { return 4096; }
+hipError_t launch_gemm_bf16_noalloc(const GemmOperand&, const GemmOperand&, int64_t, uint16_t*,
+                                    int64_t, float*, hipStream_t) {
+  return ok();
+}
+int64_t gemm_bf16_noalloc_max_bytes() { return 8192; }
 hipError_t launch_mx_quant_row(const void*, int64_t, int64_t, bool, uint64_t, uint32_t, uint8_t*,
                                uint8_t*, hipStream_t) {
   return ok();

@@ -166,8 +166,18 @@ def test_gemm_bf16_validation(lib):
     assert g(r(ok), r(ok), FAKE, 16, None, FAKE + 16, 4096, None) == nv.NVFP4_ERR_ALIGN
 
 
-def test_gemm_bf16_workspace_query(lib):
-    """The workspace query refuses empty shapes."""
+def test_gemm_bf16_noalloc_validation(lib):
+    """The allocation-free variant: the same argument checks, its fixed
+    workspace size, and the workspace query's refusal of empty shapes."""
+    g = lib.nvfp4_gemm_bf16_noalloc
+    ok = _op()
+    r = ctypes.byref
+    assert g(r(ok), r(ok), None, 16, None, None) == nv.NVFP4_ERR_NULL
+    assert g(r(ok), r(ok), MIS, 16, None, None) == nv.NVFP4_ERR_ALIGN
+    assert g(r(ok), r(ok), FAKE, 16, MIS, None) == nv.NVFP4_ERR_ALIGN
+    assert g(r(ok), r(ok), FAKE, 8, None, None) == nv.NVFP4_ERR_SHAPE
+    assert g(r(ok), r(_op(k=48)), FAKE, 16, None, None) == nv.NVFP4_ERR_SHAPE
+    assert lib.nvfp4_gemm_bf16_noalloc_max_bytes() == 128 * 2 * 65536 * 4 + 128 * 4
     w = lib.nvfp4_gemm_bf16_workspace_bytes
     assert w(0, 16, 16) == nv.NVFP4_ERR_SHAPE
     assert w(16, -16, 16) == nv.NVFP4_ERR_SHAPE
