@@ -175,8 +175,10 @@ class Step:
             ("gemm Fprop", "mfma", 2.0 * T * H * F, lambda: nv.gemm(q.qx, q.qw, q.y)),
             ("amax dY + RHT dY", "hbm", 2 * n_dy,
              lambda: nv.nvfp4_amax_both(dy, RHT_SEED, q.qdy.amax, q.qdy_t.amax)),
-            # dY's two SR encodes stay separate launches: SR is bound by the
-            # Philox arithmetic, not by the read a shared pass would save
+            # dY's two SR encodes stay separate launches: one shared pass
+            # (nvfp4_quantize_row_rht with SR) saves only ~5 us of ~70 here,
+            # and in the overlapped step the RHT encode runs beside Dgrad, so
+            # the step takes the same time either way
             ("quant dY rowwise SR", "hbm", 2.5625 * n_dy,
              lambda: nv.nvfp4_quantize1d_sr(dy, 0, q.qdy.amax, G, SR_SEED, 0, q.qdy.codes,
                                             q.qdy.scales, q.qdy.tensor_scale)),

@@ -77,4 +77,34 @@ __device__ __forceinline__ BlockDec scale_alu(uint32_t w, uint32_t pos) {
   return d;
 }
 
+// The fast path's form.  A lane's two blocks of a K step have their scale
+// codes in bytes 0 and 1 of w (after a shift by the lane's K half): one
+// packed FP8 -> FP32 convert gives both E values (scale codes are 0x00..0x7E
+// by contract, so the sign bit is left unmasked).
+typedef float float2v __attribute__((ext_vector_type(2)));
+__device__ __forceinline__ float2v scale_pair(uint32_t w) {
+  return __builtin_amdgcn_cvt_pk_f32_fp8((int)w, false);
+}
+
+// decode8 from E as FP32: the convert takes E's exponent; the FP16 factor
+// (1 + m/8) is built from E's top three mantissa bits (subnormal E included,
+// whose FP32 form is normalised) as one half that the packed multiply
+// broadcasts.  Same products as decode8(w, scale_alu(...)).
+__device__ __forceinline__ half8 decode8e(uint32_t w, float e) {
+  const uint16_t h = (uint16_t)(((__float_as_uint(e) >> 13) & 0x380u) | 0x3C00u);
+  const _Float16 m = __builtin_bit_cast(_Float16, h);
+  half2v p0 = __builtin_amdgcn_cvt_scalef32_pk_f16_fp4(w, e, 0);
+  half2v p1 = __builtin_amdgcn_cvt_scalef32_pk_f16_fp4(w, e, 1);
+  half2v p2 = __builtin_amdgcn_cvt_scalef32_pk_f16_fp4(w, e, 2);
+  half2v p3 = __builtin_amdgcn_cvt_scalef32_pk_f16_fp4(w, e, 3);
+  p0 *= m;
+  p1 *= m;
+  p2 *= m;
+  p3 *= m;
+  half8 r;
+  r[0] = p0[0]; r[1] = p0[1]; r[2] = p1[0]; r[3] = p1[1];
+  r[4] = p2[0]; r[5] = p2[1]; r[6] = p3[0]; r[7] = p3[1];
+  return r;
+}
+
 }  // namespace nvfp4

@@ -482,11 +482,13 @@ __device__ __forceinline__ void read_sg(v4u (&sg)[2], const uint8_t* sc, int idx
 }
 
 // Decode word p of A row (t / 2) + 128 q into a stage (chunk 4 (t % 2) + p).
+// pos0: bit offset of the thread's first block scale in the step's dword.
 __device__ __forceinline__ void store_a(uint8_t* stage, const RawRegs& r, int q, int p,
-                                        uint32_t pos0, uint32_t pos1) {
+                                        uint32_t pos0) {
   const int row = (threadIdx.x >> 1) + 128 * q, h = threadIdx.x & 1;
-  const BlockDec d = scale_alu(r.sc[q], p < 2 ? pos0 : pos1);
-  *reinterpret_cast<half8*>(stage + lds_off(row, 4 * h + p)) = decode8(r.codes[q][p], d);
+  const float2v e = scale_pair(r.sc[q] >> pos0);
+  *reinterpret_cast<half8*>(stage + lds_off(row, 4 * h + p)) =
+      decode8e(r.codes[q][p], p < 2 ? e.x : e.y);
 }
 
 struct OpsA { half8 a[kMB]; };
@@ -494,11 +496,12 @@ struct OpsB { half8 b[kNB]; };
 
 // B fragments of sub-step s: word s of each of the NB blocks' chunks.
 template <int NB>
-__device__ __forceinline__ void dec_b(OpsB& o, const RawRegs& r, int s, uint32_t pos0,
-                                      uint32_t pos1) {
+__device__ __forceinline__ void dec_b(OpsB& o, const RawRegs& r, int s, uint32_t pos0) {
 #pragma unroll
-  for (int j = 0; j < NB; ++j)
-    o.b[j] = decode8(r.codes[j][s], scale_alu(r.sc[j], s < 2 ? pos0 : pos1));
+  for (int j = 0; j < NB; ++j) {
+    const float2v e = scale_pair(r.sc[j] >> pos0);
+    o.b[j] = decode8e(r.codes[j][s], s < 2 ? e.x : e.y);
+  }
 }
 
 // A fragments of sub-step s (chunk 4 lk + s of rows 32 i + lane % 32).
@@ -738,8 +741,8 @@ __device__ __forceinline__ void gemm_dma_tile(const GemmArgs& g, int64_t tm, int
   const int br0 = bw + lrow, br1 = NB == 2 ? br0 + 32 : br0;
   const int a_sidx = 64 * wave + (lane >> 1), b_sidx = 64 * wave + lrow;
   // bit positions of the step's two block scales in a scale dword
-  const uint32_t apos0 = 16u * ah, apos1 = apos0 + 8u;
-  const uint32_t bpos0 = 16u * lk, bpos1 = bpos0 + 8u;
+  const uint32_t apos0 = 16u * ah;   // bit offsets of the first block scale of a K half
+  const uint32_t bpos0 = 16u * lk;
 
   float16v acc[kMB][NB];
 #pragma unroll
@@ -774,11 +777,11 @@ __device__ __forceinline__ void gemm_dma_tile(const GemmArgs& g, int64_t tm, int
 #pragma unroll
   for (int q = 0; q < 2; ++q)
 #pragma unroll
-    for (int p = 0; p < 4; ++p) store_a(smem, ra, q, p, apos0, apos1);
+    for (int p = 0; p < 4; ++p) store_a(smem, ra, q, p, apos0);
   read_raw(ra, rawA0, sa, ar0, ar1, ah, 1, 1);
   read_raw(rb, rawB0, sb, br0, br1, lk, 0, 0);
   OpsB bcur, bnxt;
-  dec_b<NB>(bcur, rb, 0, bpos0, bpos1);
+  dec_b<NB>(bcur, rb, 0, bpos0);
   __syncthreads();
   OpsA acur, anxt;
   read_a(acur, smem, lrow, lk, 0);
@@ -806,18 +809,18 @@ __device__ __forceinline__ void gemm_dma_tile(const GemmArgs& g, int64_t tm, int
       for (int s = 0; s < 4; ++s) {
         if (s < 3) {
           read_a(anxt, cur, lrow, lk, s + 1);
-          dec_b<NB>(bnxt, rb, s + 1, bpos0, bpos1);
+          dec_b<NB>(bnxt, rb, s + 1, bpos0);
           if (s == 0) {
-            store_a(oth, ra, 0, 0, apos0, apos1);
-            store_a(oth, ra, 0, 1, apos0, apos1);
-            store_a(oth, ra, 0, 2, apos0, apos1);
+            store_a(oth, ra, 0, 0, apos0);
+            store_a(oth, ra, 0, 1, apos0);
+            store_a(oth, ra, 0, 2, apos0);
           } else if (s == 1) {
-            store_a(oth, ra, 0, 3, apos0, apos1);
-            store_a(oth, ra, 1, 0, apos0, apos1);
-            store_a(oth, ra, 1, 1, apos0, apos1);
+            store_a(oth, ra, 0, 3, apos0);
+            store_a(oth, ra, 1, 0, apos0);
+            store_a(oth, ra, 1, 1, apos0);
           } else {
-            store_a(oth, ra, 1, 2, apos0, apos1);
-            store_a(oth, ra, 1, 3, apos0, apos1);
+            store_a(oth, ra, 1, 2, apos0);
+            store_a(oth, ra, 1, 3, apos0);
           }
           mfma16<NB>(acc, acur, bcur);
           interleave16();
@@ -852,7 +855,7 @@ __device__ __forceinline__ void gemm_dma_tile(const GemmArgs& g, int64_t tm, int
             mfma4_dma<NB, 4>(acc, acur, bcur, va, (h >> 1) ? rawA1 : rawA0, a_crow, x + 4, last);
           else
             mfma4_dma<NB, 2 * NB>(acc, acur, bcur, vb, (h >> 1) ? rawB1 : rawB0, b_crow, x + 3, last);
-          dec_b<NB>(bnxt, rb, 0, bpos0, bpos1);
+          dec_b<NB>(bnxt, rb, 0, bpos0);
           mfma_from<NB, 4>(acc, acur, bcur);
           interleave16();
           if (h >= 2) {

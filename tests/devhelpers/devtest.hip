@@ -75,10 +75,13 @@ __global__ void k_block_scale(const float* __restrict__ amax_b, int64_t n, float
 }
 
 // one 32-bit word of 8 codes and one E4M3 scale code per item -> 8 FP16
-// values q * E through the GEMM's ALU scale decode and its table decode
+// values q * E through the GEMM's ALU scale decode, its table decode and
+// the fast path's pair decode.  For the pair decode the code sits in byte
+// b = i % 2 of half h = (i / 2) % 2 of a dword whose other bytes hold other
+// codes, shifted by 16 h as the fast path shifts a lane's K half.
 __global__ void k_gemm_decode(const uint32_t* __restrict__ w, const uint8_t* __restrict__ sc,
                               half8* __restrict__ out_alu, half8* __restrict__ out_lut,
-                              int64_t n) {
+                              half8* __restrict__ out_pair, int64_t n) {
   __shared__ v2u lut[128];
   if (threadIdx.x < 128) lut[threadIdx.x] = scale_entry(threadIdx.x);
   __syncthreads();
@@ -87,6 +90,12 @@ __global__ void k_gemm_decode(const uint32_t* __restrict__ w, const uint8_t* __r
     const uint32_t s = sc[i];
     out_alu[i] = decode8(w[i], scale_alu(s << 8, 8));
     out_lut[i] = decode8(w[i], scale_dec(lut, s << 16, 16));
+    const uint32_t b = (uint32_t)i & 1u, h = ((uint32_t)i >> 1) & 1u;
+    const uint32_t other = (s + 37u) % 127u;   // a different finite code
+    const uint32_t word = (other * 0x01010101u & ~(0xFFu << (8u * (b + 2u * h)))) |
+                          (s << (8u * (b + 2u * h)));
+    const float2v e = scale_pair(word >> (16u * h));
+    out_pair[i] = decode8e(w[i], b ? e.y : e.x);
   }
 }
 
@@ -138,12 +147,14 @@ int devtest_block_scale(const float* amax_b, int64_t n, float amax_t, uint8_t* c
 // (0 .. 0x7E), by the fast-path ALU decode (out_alu) and the table decode
 // (out_lut), 8 per item, element e of the word in slot e.
 int devtest_gemm_decode(const uint32_t* w, const uint8_t* sc, uint16_t* out_alu,
-                        uint16_t* out_lut, int64_t n, void* stream) {
-  if (w == nullptr || sc == nullptr || out_alu == nullptr || out_lut == nullptr || n < 0)
+                        uint16_t* out_lut, uint16_t* out_pair, int64_t n, void* stream) {
+  if (w == nullptr || sc == nullptr || out_alu == nullptr || out_lut == nullptr ||
+      out_pair == nullptr || n < 0)
     return -1;
   if (n == 0) return 0;
   hipLaunchKernelGGL(k_gemm_decode, dim3(grid_for(n)), dim3(kThreads), 0, (hipStream_t)stream, w,
-                     sc, reinterpret_cast<half8*>(out_alu), reinterpret_cast<half8*>(out_lut), n);
+                     sc, reinterpret_cast<half8*>(out_alu), reinterpret_cast<half8*>(out_lut),
+                     reinterpret_cast<half8*>(out_pair), n);
   return done();
 }
 

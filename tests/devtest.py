@@ -27,7 +27,7 @@ def load() -> ctypes.CDLL:
                        "devtest_encode_rtn": [vp, vp, i64, vp],
                        "devtest_encode_sr": [vp, vp, vp, i64, vp],
                        "devtest_block_scale": [vp, i64, ctypes.c_float, vp, vp, vp],
-                       "devtest_gemm_decode": [vp, vp, vp, vp, i64, vp]}.items():
+                       "devtest_gemm_decode": [vp, vp, vp, vp, vp, i64, vp]}.items():
         fn = getattr(lib, name)
         fn.argtypes, fn.restype = args, ctypes.c_int
     lib.devtest_sr_value_host.argtypes = [vp, vp, vp, i64]

@@ -19,7 +19,8 @@ with the CPU reference's bit-level definitions:
     E4M3 midpoint +-64 patterns, and random block amaxes;
   * the GEMM's operand decode (FP4 -> FP16 convert scaled by 2^floor(log2
     E), times E's mantissa) for every scale code and every code at every
-    nibble position, by both its ALU and table forms.
+    nibble position, by its ALU, table and pair forms (the pair form takes
+    the code from either byte of either half of a scale dword).
 
 The helpers are compiled from the kernels' own headers into a test-only
 library (tests/devhelpers)."""
@@ -198,13 +199,15 @@ def test_gemm_operand_decode_every_scale_and_code():
     wd, sd = torch.from_numpy(w.view(np.int32)).cuda(), torch.from_numpy(sc).cuda()
     alu = torch.empty(w.size * 8, dtype=torch.int16, device="cuda")
     lut = torch.empty(w.size * 8, dtype=torch.int16, device="cuda")
+    pair = torch.empty(w.size * 8, dtype=torch.int16, device="cuda")
     assert devtest.load().devtest_gemm_decode(wd.data_ptr(), sd.data_ptr(), alu.data_ptr(),
-                                              lut.data_ptr(), w.size, _stream()) == 0
+                                              lut.data_ptr(), pair.data_ptr(), w.size,
+                                              _stream()) == 0
     nib = ((w[:, None] >> (4 * np.arange(8, dtype=np.uint32))[None, :]) & 0xF).astype(np.uint8)
     E = np.array([oracle.e4m3_decode(c) for c in range(127)], np.float32)
     want = (E2M1[nib] * E[sc][:, None]).astype(np.float16).ravel()
     assert np.array_equal(want.astype(np.float32), E2M1[nib].ravel() * np.repeat(E[sc], 8))
-    for name, got in (("alu", alu), ("table", lut)):
+    for name, got in (("alu", alu), ("table", lut), ("pair", pair)):
         g = got.cpu().numpy().view(np.float16)
         bad = np.flatnonzero(g != want)     # +-0 compare equal: a zero scale may give either sign
         assert bad.size == 0, (name, bad.size, int(sc[bad[0] // 8]), hex(int(w[bad[0] // 8])),
