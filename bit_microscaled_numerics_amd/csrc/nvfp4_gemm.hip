@@ -743,6 +743,10 @@ __device__ __forceinline__ void gemm_dma_tile(const GemmArgs& g, int64_t tm, int
   // bit positions of the step's two block scales in a scale dword
   const uint32_t apos0 = 16u * ah;   // bit offsets of the first block scale of a K half
   const uint32_t bpos0 = 16u * lk;
+  // alpha = s_a s_b, read now so that its latency hides under the prologue's
+  // loads instead of following the K loop (uniform: kept in a scalar register)
+  float alpha = __uint_as_float(__builtin_amdgcn_readfirstlane(
+      __float_as_uint((*g.a.ts) * (*g.b.ts))));
 
   float16v acc[kMB][NB];
 #pragma unroll
@@ -874,7 +878,6 @@ __device__ __forceinline__ void gemm_dma_tile(const GemmArgs& g, int64_t tm, int
   }
   __builtin_amdgcn_s_waitcnt(0);   // loads of the groups past the end
 
-  float alpha = (*g.a.ts) * (*g.b.ts);
   if (BF16 && part >= 0) {
     // a K half of a BF16 tail tile: the workgroup that finishes second writes
     // the tile from both halves' partials, already scaled (alpha 1)
