@@ -659,38 +659,49 @@ __device__ __forceinline__ void store_c_lds(const GemmArgs& g, float16v (&acc)[k
 // compute partial accumulators P0 and P1; FP32 output adds alpha P0 and
 // alpha P1 into a zeroed C, fl(alpha P0 + alpha P1) whatever their order.
 // The BF16 output is that sum rounded, so the halves meet in a workspace
-// instead: each stores its scaled partial (in register order: for each
-// block and accumulator slot, 64 lanes' consecutive words), makes it visible
-// device-wide (the halves usually run on different XCDs), and takes a ticket
-// with one atomic add on the slot's counter.  The half that draws ticket 1
-// finishes second: the other partial is complete, so it adds it to its own
-// (the same commutative sum) and writes the tile; the first half returns
-// without writing anything.  No workgroup waits for another.  The partial
-// words move with agent-scope atomic loads and stores, which bypass the
-// per-XCD caches.
+// instead: each stores its scaled partial, and thread 0 takes a ticket with
+// one acquire-release atomic add on the slot's counter.  The half that draws
+// ticket 1 finishes second: the other partial is complete, so it adds it to
+// its own (the same commutative sum) and writes the tile; the first half
+// returns without writing anything.  No workgroup waits for another.
+// Layout: per wave, 16-byte pieces of four consecutive accumulator slots,
+// 64 lanes' pieces side by side (1 KiB per wave instruction).
 constexpr int64_t kSplitSlotFloats = 4 * kMB * 2 * 16 * 64;   // one K half of a 256 x 256 tile
+constexpr int kAgentScope = 16;   // buffer cache policy sc1: coherent across the XCDs
 
 template <int NB>
 __device__ __forceinline__ bool bf16_split_exchange(const GemmArgs& g, float16v (&acc)[kMB][NB],
                                                     int part, int64_t slot, int wave,
                                                     float alpha, uint8_t* smem) {
   const int lane = threadIdx.x & 63;
-  const int64_t wave_off = (int64_t)wave * (kMB * NB * 16 * 64) + lane;
-  float* mine = g.ws + (2 * slot + part) * kSplitSlotFloats + wave_off;
-  const float* other = g.ws + (2 * slot + (part ^ 1)) * kSplitSlotFloats + wave_off;
+  // the slot's two partials; this lane's pieces at voff + 1024 c in each
+  const __amdgpu_buffer_rsrc_t ws = __builtin_amdgcn_make_buffer_rsrc(
+      g.ws + 2 * slot * kSplitSlotFloats, (short)0, (int)(2 * kSplitSlotFloats * 4),
+      (int)kBufFlags);
+  const uint32_t voff = (uint32_t)(wave * (kMB * NB * 4 * 64) + lane) * 16u;
+  const uint32_t mine = (uint32_t)(part * kSplitSlotFloats * 4);
+  const uint32_t other = (uint32_t)((part ^ 1) * kSplitSlotFloats * 4);
 #pragma unroll
   for (int i = 0; i < kMB; ++i)
 #pragma unroll
     for (int j = 0; j < NB; ++j)
 #pragma unroll
-      for (int v = 0; v < 16; ++v)
-        __hip_atomic_store(mine + ((i * NB + j) * 16 + v) * 64, acc[i][j][v] * alpha,
-                           __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
-  // Every wave's partial stores happen before thread 0's ticket (barrier),
-  // which releases them at agent scope and acquires the other half's; the
-  // barrier after it carries that to every wave.  Only thread 0 fences: an
-  // agent-scope fence writes back and invalidates this XCD's whole L2, which
-  // the workgroups still streaming operands there would pay for.
+      for (int q = 0; q < 4; ++q)
+        __builtin_amdgcn_raw_buffer_store_b128(
+            __builtin_bit_cast(v4u, v4f{acc[i][j][4 * q] * alpha, acc[i][j][4 * q + 1] * alpha,
+                                        acc[i][j][4 * q + 2] * alpha,
+                                        acc[i][j][4 * q + 3] * alpha}),
+            ws, voff, mine + (uint32_t)(((i * NB + j) * 4 + q) * 1024), kAgentScope);
+  // The partial words move with agent-scope (sc1) stores and loads, which
+  // write through and read past the per-XCD caches (the halves usually run
+  // on different XCDs); each wave waits until its stores are complete before
+  // the barrier.  Thread 0's ticket then orders them formally: every wave's
+  // stores happen before it (barrier), it releases them at agent scope and
+  // acquires the other half's, and the barrier after it carries that to
+  // every wave's loads.  Only thread 0 fences: an agent-scope fence writes
+  // back and invalidates this XCD's whole L2, which the workgroups still
+  // streaming operands there would pay for.
+  __builtin_amdgcn_s_waitcnt(vmcnt_imm(0));
   __syncthreads();     // also: the decoded-A stages are free
   int* ticket = reinterpret_cast<int*>(smem);
   if (threadIdx.x == 0)
@@ -705,12 +716,16 @@ __device__ __forceinline__ bool bf16_split_exchange(const GemmArgs& g, float16v 
 #pragma unroll
     for (int j = 0; j < NB; ++j)
 #pragma unroll
-      for (int v = 0; v < 16; ++v)
+      for (int q = 0; q < 4; ++q) {
+        const v4f o = __builtin_bit_cast(
+            v4f, __builtin_amdgcn_raw_buffer_load_b128(
+                     ws, voff, other + (uint32_t)(((i * NB + j) * 4 + q) * 1024), kAgentScope));
         // (0 + other) + own: the FP32 path's two adds onto a zero, also for
         // two partials of -0 (which it turns into +0)
-        acc[i][j][v] = (0.0f + __hip_atomic_load(other + ((i * NB + j) * 16 + v) * 64,
-                                                 __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT)) +
-                       acc[i][j][v] * alpha;
+#pragma unroll
+        for (int k = 0; k < 4; ++k)
+          acc[i][j][4 * q + k] = (0.0f + o[k]) + acc[i][j][4 * q + k] * alpha;
+      }
   return true;
 }
 
