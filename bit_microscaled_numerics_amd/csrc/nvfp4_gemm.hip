@@ -939,7 +939,6 @@ __global__ __launch_bounds__(kThreads4, 1) void k_gemm_dma(GemmArgs g) {
                            rawB0, rawB1, scA, scB);
 }
 
-__global__ void k_zero_word(uint32_t* p) { *p = 0u; }
 
 // Zero the output tiles that split workgroups add into, same tile order as
 // the GEMM: 16 workgroups per tile, 16 rows each; with VEC (N and ldc
@@ -1027,7 +1026,11 @@ int64_t gemm_bf16_workspace_bytes(int64_t M, int64_t N, int64_t K) {
   return split_ws_bytes(split_slots(plan_tiles(M, N, (K + kBK - 1) / kBK, true, true)));
 }
 
-__global__ __launch_bounds__(256) void k_zero_words(uint32_t* __restrict__ p, int64_t n) {
+// The BF16 epilogue's start: its amax word (when given) and the n split
+// tickets cleared in one launch (a kernel, not a memset: capture-safe).
+__global__ __launch_bounds__(256) void k_zero_words(uint32_t* __restrict__ amax,
+                                                    uint32_t* __restrict__ p, int64_t n) {
+  if (amax != nullptr && blockIdx.x == 0 && threadIdx.x == 0) *amax = 0u;
   for (int64_t i = (int64_t)blockIdx.x * 256 + threadIdx.x; i < n; i += (int64_t)gridDim.x * 256)
     p[i] = 0u;
 }
@@ -1041,11 +1044,6 @@ static hipError_t launch_gemm_any(const GemmOperand& a, const GemmOperand& b, in
   const int vec_out = (ldc % (bf16 ? 8 : 4)) == 0 && (cbase & 15) == 0 &&
                       ldc * kTile * (bf16 ? 2 : 4) < ((int64_t)1 << 31);
   GemmArgs g{a, b, a.rows, b.rows, K, c, cb, amax, ldc, 0, kTailWhole, vec_out};
-  if (bf16 && amax != nullptr) {
-    hipLaunchKernelGGL(k_zero_word, dim3(1), dim3(1), 0, s, amax);
-    const hipError_t e = hipGetLastError();
-    if (e != hipSuccess) return e;
-  }
   const bool ld16 = (a.ld % 16 == 0) && (b.ld % 16 == 0);
   const bool checked = (K % 64) != 0;
   // dword scales: scales contiguous along K, every row's scales 4-byte
@@ -1071,15 +1069,21 @@ static hipError_t launch_gemm_any(const GemmOperand& a, const GemmOperand& b, in
   g.full_tiles = plan.full_tiles;
   g.tail = plan.tail;
   const dim3 grid((unsigned)plan.grid);
-  if (bf16 && plan.split) {
-    const int64_t slots = split_slots(plan);
-    if (split_ws_bytes(slots) > ws_bytes) return hipErrorInvalidValue;
-    g.ws = static_cast<float*>(ws);
-    g.ws_tickets = reinterpret_cast<uint32_t*>(static_cast<uint8_t*>(ws) + split_partial_bytes(slots));
-    hipLaunchKernelGGL(k_zero_words, dim3(1), dim3(256), 0, s, g.ws_tickets, slots);
-    const hipError_t e = hipGetLastError();
-    if (e != hipSuccess) return e;
-  } else if (!bf16) {
+  if (bf16) {
+    int64_t slots = 0;
+    if (plan.split) {
+      slots = split_slots(plan);
+      if (split_ws_bytes(slots) > ws_bytes) return hipErrorInvalidValue;
+      g.ws = static_cast<float*>(ws);
+      g.ws_tickets =
+          reinterpret_cast<uint32_t*>(static_cast<uint8_t*>(ws) + split_partial_bytes(slots));
+    }
+    if (amax != nullptr || slots > 0) {
+      hipLaunchKernelGGL(k_zero_words, dim3(1), dim3(256), 0, s, amax, g.ws_tickets, slots);
+      const hipError_t e = hipGetLastError();
+      if (e != hipSuccess) return e;
+    }
+  } else {
     const hipError_t e = zero_split_tiles(plan, c, ldc, g.M, g.N, s);
     if (e != hipSuccess) return e;
   }
