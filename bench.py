@@ -461,6 +461,25 @@ def _median_ms(fn, reps: int) -> float:
     return float(np.median([ev[i].elapsed_time(ev[i + 1]) for i in range(reps)]))
 
 
+def _medians_interleaved(fns: dict, reps: int) -> dict:
+    """Median ms of each callable, timed in turn within every repetition so
+    that clock drift (the chip warming or cooling after earlier work) weighs
+    on all of them alike."""
+    s = torch.cuda.current_stream()
+    for fn in fns.values():
+        fn()
+    ev = {k: [(torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True))
+              for _ in range(reps)] for k in fns}
+    s.synchronize()
+    for i in range(reps):
+        for k, fn in fns.items():
+            ev[k][i][0].record(s)
+            fn()
+            ev[k][i][1].record(s)
+    s.synchronize()
+    return {k: float(np.median([a.elapsed_time(b) for a, b in ev[k]])) for k in fns}
+
+
 def quality(step: "Step"):
     """How closely each quantized GEMM tracks the unquantized FP32 product at
     the step's shapes: cosine similarity and relative Frobenius error
@@ -525,18 +544,22 @@ def fused_epilogue(step: "Step", reps: int):
     amax read of C that the next layer's quantization needs, at the Fprop and
     Dgrad shapes.  With its workspace the BF16 path cuts the last round's tiles
     along K as the FP32 path does (Fprop: 640 tiles, 2.5 rounds); "no workspace"
-    times it with half-width tiles there instead."""
+    times it with half-width tiles there instead.  The variants are timed in
+    turn within each repetition."""
     out = {}
     for name, qa, qb, c32 in [("Fprop", step.qx, step.qw, step.y),
                               ("Dgrad", step.qdy, step.qw.t(), step.dx)]:
         cb = torch.empty(qa.rows, qb.rows, dtype=torch.bfloat16, device=step.x.device)
         am = torch.empty(1, dtype=torch.float32, device=step.x.device)
         ws = nv.gemm_bf16_workspace(qa.rows, qb.rows, qa.k, step.x.device)
-        fused = _median_ms(lambda: nv.nvfp4_gemm_bf16(qa, qb, cb, cb.stride(0), am, ws), reps)
-        no_ws = (_median_ms(lambda: nv.nvfp4_gemm_bf16(qa, qb, cb, cb.stride(0), am), reps)
-                 if ws is not None else fused)
-        plain = _median_ms(lambda: nv.gemm(qa, qb, c32), reps)
-        scan = _median_ms(lambda: nv.nvfp4_amax(cb, am), reps)
+        fns = {"fused": lambda: nv.nvfp4_gemm_bf16(qa, qb, cb, cb.stride(0), am, ws),
+               "plain": lambda: nv.gemm(qa, qb, c32),
+               "scan": lambda: nv.nvfp4_amax(cb, am)}
+        if ws is not None:
+            fns["no_ws"] = lambda: nv.nvfp4_gemm_bf16(qa, qb, cb, cb.stride(0), am)
+        t = _medians_interleaved(fns, reps)
+        fused, plain, scan = t["fused"], t["plain"], t["scan"]
+        no_ws = t.get("no_ws", fused)
         fl = 2.0 * qa.rows * qb.rows * qa.k
         out[name] = {"fused bf16 + amax us": round(fused * 1e3, 1),
                      "fused, no workspace us": round(no_ws * 1e3, 1),
