@@ -4,7 +4,9 @@ TEST INFRASTRUCTURE ONLY: the plain, slow reference the GPU library is checked
 against.  Only the tests, the smoke check and the benchmark's CPU-baseline leg
 may import it.  It shares no code with the HIP library and imports nothing
 from it.  The arithmetic lives in ``nvfp4_oracle.c`` (binary32, no FMA
-contraction, exact int64 GEMM) and, for the MXFP4 comparison format,
+contraction, exact int64 GEMM; ``gemm_f64`` is its float64 form for whole
+full-size products, a float64 library matmul of the exactly decoded operands)
+and, for the MXFP4 comparison format,
 ``mxfp4_oracle.c``; this module is ctypes marshalling over numpy arrays.
 ``oracle.model`` is a second, pure-numpy model for tiny inputs.
 """
@@ -77,6 +79,7 @@ def _load():
                                         _u8p, _u8p, _u8p, _f32p]),
         "orc_dequantize": (None, [_u8p, _i64, _u8p, _i64, _i64, _i32, _f32, _i64, _i64, _f32p]),
         "orc_gemm": (ctypes.c_int, _OPERAND + _OPERAND + [_i64, _f64p, _f64p]),
+        "orc_decode_exact": (ctypes.c_int, _OPERAND + [_i64, _f64p]),
         "orc_gemm_entries": (ctypes.c_int, _OPERAND + _OPERAND + [_i64, _i64p, _i64p, _i64,
                                                                   _f64p, _f64p]),
         "orc_num_threads": (ctypes.c_int, []),
@@ -281,6 +284,34 @@ def gemm(a: Operand, b: Operand, with_bound: bool = True):
     if rc != 0:
         raise ValueError(f"oracle gemm rejected the arguments (status {rc})")
     return (c, t) if with_bound else c
+
+
+def decode_exact(q: Operand) -> np.ndarray:
+    """q * E of every element (without the tensor scale) as float64 [rows][k]
+    (exact; zeros as +0)."""
+    out = np.empty((q.rows, q.k), np.float64)
+    args, _keep = _operand_args(q)
+    rc = _load().orc_decode_exact(*args, q.k, _ptr(out, _f64p))
+    if rc != 0:
+        raise ValueError(f"oracle decode rejected the arguments (status {rc})")
+    return out
+
+
+def gemm_f64(a: Operand, b: Operand, with_bound: bool = True):
+    """The GEMM of ``gemm`` through a float64 matrix product of the exactly
+    decoded operands (the product is a library routine; summation error at
+    most about K * 2^-53 * T), then times s_a * s_b; also T = sum_k |A*B|
+    the same way when with_bound.  Fast enough for whole full-size products."""
+    assert a.k == b.k
+    da, db = decode_exact(a), decode_exact(b)
+    s = float(np.float64(a.tensor_scale) * np.float64(b.tensor_scale))
+    c = (da @ db.T) * s
+    if not with_bound:
+        return c
+    np.abs(da, out=da)
+    np.abs(db, out=db)
+    t = (da @ db.T) * abs(s)
+    return c, t
 
 
 def gemm_entries(a: Operand, b: Operand, ms: np.ndarray, ns: np.ndarray):

@@ -123,3 +123,73 @@ def test_gemm_entries_equal_full_product():
     ns = np.array([47, 0, 5, 33])
     ce, te = oracle.gemm_entries(a, b, ms, ns)
     assert np.array_equal(ce, c[ms, ns]) and np.array_equal(te, t[ms, ns])
+
+
+# ---------------------------------------------------------------------------
+# The float64 form (decode_exact + a float64 library matmul): the fast form of
+# the GEMM for whole full-size products.
+# ---------------------------------------------------------------------------
+
+def _wide_range(g, rows, cols, seed_scale=1.0):
+    """Rows scaled by 2^0 .. 2^-30 so that the block scales run from the top of
+    E4M3 down through its subnormal codes (and to zero) within one tensor."""
+    x = inputs.normal(g, rows, cols, seed_scale).float()
+    x = x * torch.pow(2.0, -(torch.arange(rows) % 31).float())[:, None]
+    return x.to(torch.bfloat16)
+
+
+def test_decode_exact_equals_independent_decode_every_layout():
+    g = torch.Generator().manual_seed(35)
+    x = _wide_range(g, 64, 128)
+    w = _wide_range(g, 96, 128)
+    qs = [oracle.quantize(x, oracle.ROWWISE),
+          oracle.quantize(x, oracle.ROWWISE, sr_seed=5),
+          oracle.quantize(w, oracle.TWO_D, with_codes_t=True),
+          oracle.quantize(x, oracle.COLWISE, rht_seed=3),
+          oracle.quantize(x, oracle.COLWISE)]
+    qs.append(qs[2].transposed())
+    codes_seen = set()
+    for q in qs:
+        d = oracle.decode_exact(q)
+        assert d.shape == (q.rows, q.k) and d.dtype == np.float64
+        assert np.array_equal(d, decoded_f64(q))       # values (its zeros are +0)
+        codes_seen |= set(np.unique(q.scales).tolist())
+    # the scales reached the subnormal E4M3 codes and zero as well as normal ones
+    assert {0} | set(range(1, 8)) <= codes_seen and max(codes_seen) >= 0x70
+
+
+def test_gemm_f64_k16_equals_exact_rational():
+    """One block along K: every float64 sum is exact, so the float64 form
+    equals the rational result exactly."""
+    g = torch.Generator().manual_seed(30)
+    a = oracle.quantize(inputs.normal(g, 16, 16), oracle.ROWWISE)
+    b = oracle.quantize(inputs.normal(g, 16, 16, 0.02), oracle.TWO_D)
+    c, t = oracle.gemm_f64(a, b)
+    ce, te = oracle.gemm(a, b)          # itself pinned by the fractions test above
+    assert np.array_equal(c, ce) and np.array_equal(t, te)
+
+
+def test_gemm_f64_within_its_bound_of_the_exact_path():
+    """Every mapping, a long K and a wide scale range: |C_f64 - C_exact| is
+    inside the float64 summation bound K * 2^-52 * T (far inside 1e-5 * T)."""
+    g = torch.Generator().manual_seed(36)
+    T_, H, F = 256, 64, 96                     # tokens, in-features, out-features
+    X = _wide_range(g, T_, H)
+    W = inputs.normal(g, F, H, 0.02)
+    dY = inputs.normal(g, T_, F, 1e-3)
+    qx = oracle.quantize(X, oracle.ROWWISE)
+    qw = oracle.quantize(W, oracle.TWO_D, with_codes_t=True)
+    qdy = oracle.quantize(dY, oracle.ROWWISE, sr_seed=1)
+    qdy_t = oracle.quantize(dY, oracle.COLWISE, rht_seed=7, sr_seed=1, stream_id=0)
+    qx_t = oracle.quantize(X, oracle.COLWISE, rht_seed=7)
+    long_a = oracle.quantize(inputs.normal(g, 32, 4096), oracle.ROWWISE, sr_seed=2)
+    long_b = oracle.quantize(inputs.normal(g, 48, 4096, 0.05), oracle.ROWWISE)
+    for a, b in [(qx, qw), (qdy, qw.transposed()), (qdy_t, qx_t), (long_a, long_b)]:
+        c, t = oracle.gemm_f64(a, b)
+        ce, te = oracle.gemm(a, b)
+        bound = a.k * 2.0 ** -52 * te
+        assert np.all(np.abs(c - ce) <= bound)
+        assert np.all(np.abs(t - te) <= bound)
+        assert np.all(t >= np.abs(c) * (1 - 1e-12))
+        # and without the bound the product is the same array
+        assert np.array_equal(oracle.gemm_f64(a, b, with_bound=False), c)
