@@ -289,59 +289,61 @@ def oracle_c5(c5, threads, gpu_us):
     return rec
 
 
+def _blas_threads() -> int:
+    try:
+        from threadpoolctl import threadpool_info
+        n = [i["num_threads"] for i in threadpool_info() if i.get("user_api") == "blas"]
+        return max(n) if n else 0
+    except Exception:       # threadpoolctl missing: report the OpenMP count only
+        return 0
+
+
 def cpu_baseline(x, w, dy, c5=None, gpu_us=None):
     """The oracle, as it stands, on the same host bytes as the GPU:
-      * the step: a slice of rows of every quantization and a set of exact
-        entries of every GEMM, timed on all threads and extrapolated linearly
-        to the whole step (the `value`, in the metric's unit);
+      * the whole step, timed (the `value`, in the metric's unit): the five
+        quantizations of the full tensors, then the three GEMMs through the
+        oracle's float64 form (exact decode, float64 library matmul);
+      * beside it, the exact int64 GEMM path on a sample of entries (its
+        rate, for reference);
       * the 32768x8192 quantizations (oracle_c5)."""
     import oracle
     T, F = x.shape
     H = w.shape[0]
     threads = oracle.num_threads()
-    rows = 64   # sampled rows / columns of each quantized tensor
-    t_quant = 0.0
-    full_quant = 0.0
-    for name, t, mode, kw in [("X", x, oracle.ROWWISE, {}), ("W", w, oracle.TWO_D, {}),
-                              ("dY", dy, oracle.ROWWISE, {"sr_seed": SR_SEED}),
-                              ("dY^T", dy, oracle.COLWISE, {"rht_seed": RHT_SEED, "sr_seed": 1}),
-                              ("X^T", x, oracle.COLWISE, {"rht_seed": RHT_SEED})]:
-        if mode == oracle.COLWISE:
-            sl = t[:, :rows].contiguous()       # `rows` output rows of the transpose
-            frac = rows / t.shape[1]
-        else:
-            sl = t[:rows].contiguous()
-            frac = rows / t.shape[0]
-        extra = {"with_codes_t": True} if mode == oracle.TWO_D else {}
-        t0 = time.perf_counter()
-        oracle.quantize(sl, mode, **kw, **extra)
-        dt = time.perf_counter() - t0
-        t_quant += dt
-        full_quant += dt / frac
-    # GEMM entries: pick n entries per GEMM so the sample is ~8 seconds
-    ox = oracle.quantize(x[:256].contiguous(), oracle.ROWWISE)
-    ow = oracle.quantize(w[:256].contiguous(), oracle.TWO_D)
+    blas = _blas_threads()
+    t0 = time.perf_counter()
+    ox = oracle.quantize(x, oracle.ROWWISE)
+    ox_t = oracle.quantize(x, oracle.COLWISE, rht_seed=RHT_SEED)
+    ow = oracle.quantize(w, oracle.TWO_D, with_codes_t=True)
+    ody = oracle.quantize(dy, oracle.ROWWISE, sr_seed=SR_SEED)
+    ody_t = oracle.quantize(dy, oracle.COLWISE, rht_seed=RHT_SEED, sr_seed=SR_SEED, stream_id=1)
+    t_quant = time.perf_counter() - t0
+    t1 = time.perf_counter()
+    for a, b in [(ox, ow), (ody, ow.transposed()), (ody_t, ox_t)]:
+        c = oracle.gemm_f64(a, b, with_bound=False)
+        del c
+    t_gemm = time.perf_counter() - t1
+    full = t_quant + t_gemm
+    flops = 3 * 2.0 * T * H * F
+    # the exact path's rate on ~3 s of entries
     rng = np.random.default_rng(0)
-    n = 2048
-    ms = rng.integers(0, 256, n)
-    ns = rng.integers(0, 256, n)
-    t0 = time.perf_counter()
-    oracle.gemm_entries(ox, ow, ms, ns)
-    dt = time.perf_counter() - t0
-    n2 = int(min(2_000_000, max(n, n * 8.0 / max(dt, 1e-6))))
-    ms = rng.integers(0, 256, n2)
-    ns = rng.integers(0, 256, n2)
-    t0 = time.perf_counter()
-    oracle.gemm_entries(ox, ow, ms, ns)
-    dt = time.perf_counter() - t0
-    per_mac = dt / (n2 * F)
-    macs_step = 3.0 * T * H * F
-    full = full_quant + per_mac * macs_step
-    flops = 2.0 * macs_step
-    out = {"value": flops / full / 1e12, "unit": "TFLOP/s", "cores": threads, "kind": "oracle",
-           "sample": (f"oracle quantize of {rows} rows/cols of each of the 5 operands "
-                      f"({t_quant:.2f} s) + {n2} exact GEMM entries at K={F} ({dt:.2f} s), "
-                      f"{threads} threads, extrapolated to one full step ({full:.0f} s)")}
+    n = 4096
+    t2 = time.perf_counter()
+    oracle.gemm_entries(ox, ow, rng.integers(0, T, n), rng.integers(0, H, n))
+    dt = time.perf_counter() - t2
+    n2 = int(min(1_000_000, max(n, n * 3.0 / max(dt, 1e-6))))
+    t2 = time.perf_counter()
+    oracle.gemm_entries(ox, ow, rng.integers(0, T, n2), rng.integers(0, H, n2))
+    dt = time.perf_counter() - t2
+    del ox, ox_t, ow, ody, ody_t
+    out = {"value": flops / full / 1e12, "unit": "TFLOP/s", "cores": max(threads, blas),
+           "kind": "oracle",
+           "sample": (f"the whole step on the oracle, timed: the 5 quantizations of the full "
+                      f"tensors ({t_quant:.1f} s, {threads} OpenMP threads) and the 3 GEMMs "
+                      f"through its float64 form ({t_gemm:.1f} s, {blas or threads} BLAS "
+                      f"threads); {full:.1f} s per step"),
+           "exact_gemm_path": {"TFLOP/s": round(2.0 * n2 * F / dt / 1e12, 5),
+                               "sample": f"{n2} exact int64 entries at K={F} ({dt:.1f} s)"}}
     if c5 is not None:
         out["quantize_32768x8192"] = oracle_c5(c5, threads, gpu_us or {})
     return out

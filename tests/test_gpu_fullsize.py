@@ -1,8 +1,9 @@
 """Parity at the full workload sizes, in the launch configuration bench.py
 times: every quantized tensor is compared byte for byte with the oracle over
 the whole tensor; GEMM outputs are compared with the oracle's exact product on
-sampled entries (all tile corners plus random ones), and the full product is
-checked for finiteness.  Workloads: the 12B hybrid's FFN up-projection
+sampled entries (all tile corners plus random ones), and every entry with its
+float64 form (oracle.gemm_f64, whose own error of about K * 2^-53 * T is far
+inside the 1e-5 * T tolerance).  Workloads: the 12B hybrid's FFN up-projection
 (Fprop + Dgrad), the FFN down-projection triple (Fprop, Dgrad, Wgrad with
 RHT + SR), the 4096-token Wgrad with RHT + SR on heavy-tailed gradients
 (full product), and the 32768 x 8192 quantize sweep."""
@@ -33,7 +34,10 @@ def check_gemm_sampled(c_dev: torch.Tensor, oa, ob, name):
     assert np.all(np.isfinite(c)), f"{name}: non-finite outputs"
     ms, ns = sample_entries(*c.shape)
     ref, t = oracle.gemm_entries(oa, ob, ms, ns)
-    assert_gemm_close(c[ms, ns], ref, t, name)
+    assert_gemm_close(c[ms, ns], ref, t, name + " (exact path, sampled entries)")
+    say(name, "every entry")
+    ref, t = oracle.gemm_f64(oa, ob)
+    assert_gemm_close(c, ref, t, name + " (float64 form, every entry)")
 
 
 def test_ffn_up_fprop_dgrad():
