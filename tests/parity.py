@@ -59,6 +59,19 @@ def assert_gemm_close(c_gpu: np.ndarray, c_ref: np.ndarray, t_ref: np.ndarray, n
     return float(np.max(err / np.maximum(t_ref, 1e-300)))
 
 
+def assert_gemm_every_entry(c_gpu: np.ndarray, oa, ob, name: str = "", rel: float = 0.0):
+    """Every entry of a GPU product against the oracle's float64 form (its own
+    error, about K * 2^-53 * T, is far inside the tolerance); rel adds a
+    relative allowance (2^-8 for a BF16 output's rounding)."""
+    ref, t = oracle.gemm_f64(oa, ob)
+    err = np.abs(c_gpu.astype(np.float64) - ref)
+    lim = GEMM_TOL * t + rel * np.abs(ref)
+    bad = np.argwhere(err > lim)
+    assert bad.size == 0, (f"{name}: {len(bad)} of {err.size} entries beyond tolerance; first "
+                           f"{bad[:3].tolist()} err={err[tuple(bad[0])]:.3e} "
+                           f"lim={lim[tuple(bad[0])]:.3e}")
+
+
 # ---------------------------------------------------------------- guard bands
 GUARD_BYTES = 4096
 GUARD_FILL = 0xA5

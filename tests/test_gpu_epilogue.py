@@ -14,7 +14,7 @@ import torch
 import oracle
 import bit_microscaled_numerics_amd as nv
 from bit_microscaled_numerics_amd import inputs
-from parity import GEMM_TOL, say
+from parity import GEMM_TOL, assert_gemm_every_entry, say
 
 pytestmark = pytest.mark.gpu
 
@@ -104,6 +104,7 @@ def test_fprop_shape_against_oracle():
     err = np.abs(y[ms, ns] - ref)
     lim = GEMM_TOL * t + 2.0 ** -8 * np.abs(ref)
     assert np.all(err <= lim), float(np.max(err / np.maximum(lim, 1e-300)))
+    assert_gemm_every_entry(y, ox, ow, "bf16 fprop, every entry", rel=2.0 ** -8)
 
 
 def test_half_width_tail_tiles_bf16():
@@ -132,6 +133,7 @@ def test_half_width_tail_tiles_bf16():
     err = np.abs(y[ms, ns] - ref)
     lim = GEMM_TOL * t + 2.0 ** -8 * np.abs(ref)
     assert np.all(err <= lim), float(np.max(err / np.maximum(lim, 1e-300)))
+    assert_gemm_every_entry(y, ox, ow, "half-width tail, every entry", rel=2.0 ** -8)
 
 
 # Output layouts of the fast-path epilogue: 16-byte pieces of rows (4 FP32 /

@@ -14,7 +14,7 @@ import torch
 import oracle
 import bit_microscaled_numerics_amd as nv
 from bit_microscaled_numerics_amd import inputs
-from parity import assert_gemm_close, assert_operand_equal, say
+from parity import assert_gemm_close, assert_gemm_every_entry, assert_operand_equal, say
 
 pytestmark = pytest.mark.gpu
 
@@ -379,3 +379,4 @@ def test_gemm_split_last_round_is_exact_and_deterministic(K):
     ms, ns = np.meshgrid(rows, cols, indexing="ij")
     ref, t = oracle.gemm_entries(ox, ow, ms.ravel(), ns.ravel())
     assert_gemm_close(c1[ms.ravel(), ns.ravel()], ref, t, "split tail")
+    assert_gemm_every_entry(c1, ox, ow, "split tail, every entry")
