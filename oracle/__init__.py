@@ -67,6 +67,7 @@ def _load():
         "orc_mx_quantize": (ctypes.c_int, [_u16p, _i64, _i64, ctypes.c_int, _u64, _u32, _u8p, _u8p]),
         "orc_mx_dequantize": (None, [_u8p, _u8p, _i64, _i64, _f32p]),
         "orc_mx_gemm": (ctypes.c_int, [_u8p, _u8p, _i64, _u8p, _u8p, _i64, _i64, _f64p, _f64p]),
+        "orc_mx_decode_exact": (ctypes.c_int, [_u8p, _u8p, _i64, _i64, _f64p]),
         "orc_mx_gemm_entries": (ctypes.c_int, [_u8p, _u8p, _u8p, _u8p, _i64, _i64p, _i64p, _i64,
                                                _f64p, _f64p]),
         "orc_amax": (ctypes.c_float, [_u16p, _i64, _i64]),
@@ -390,6 +391,29 @@ def mx_gemm(a: MXOperand, b: MXOperand):
     if rc != 0:
         raise ValueError(f"oracle mx_gemm rejected the arguments (status {rc})")
     return c, t
+
+
+def mx_decode_exact(q: MXOperand) -> np.ndarray:
+    """Every decoded MXFP4 value as float64 [rows][k] (exact)."""
+    out = np.empty((q.rows, q.k), np.float64)
+    codes, scales = np.ascontiguousarray(q.codes), np.ascontiguousarray(q.scales)
+    rc = _load().orc_mx_decode_exact(_ptr(codes, _u8p), _ptr(scales, _u8p), q.rows, q.k,
+                                     _ptr(out, _f64p))
+    if rc != 0:
+        raise ValueError(f"oracle mx decode rejected the arguments (status {rc})")
+    return out
+
+
+def mx_gemm_f64(a: MXOperand, b: MXOperand):
+    """mx_gemm through one float64 library matmul of the exactly decoded
+    operands (and T from their magnitudes): the same float64 arithmetic in
+    another summation order, fast enough for whole full-size products."""
+    assert a.k == b.k
+    da, db = mx_decode_exact(a), mx_decode_exact(b)
+    c = da @ db.T
+    np.abs(da, out=da)
+    np.abs(db, out=db)
+    return c, da @ db.T
 
 
 def mx_gemm_entries(a: MXOperand, b: MXOperand, ms: np.ndarray, ns: np.ndarray):

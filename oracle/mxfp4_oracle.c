@@ -128,6 +128,18 @@ static void mx_one(const uint8_t* ac, const uint8_t* as, const uint8_t* bc, cons
   if (t) *t = abs_acc;
 }
 
+/* Every decoded value q * 2^(e - 127) as double, [rows][K] row-major
+ * (exact: a power of two times a value with two significant bits).  A
+ * float64 matrix product of these is the fast form of the GEMM below. */
+ORC_API int orc_mx_decode_exact(const uint8_t* codes, const uint8_t* scales, int64_t rows,
+                                int64_t K, double* out) {
+  if (K <= 0 || K % 32) return -2;
+#pragma omp parallel for schedule(static)
+  for (int64_t r = 0; r < rows; ++r)
+    for (int64_t k = 0; k < K; ++k) out[r * K + k] = mx_value(codes, scales, K, r, k);
+  return 0;
+}
+
 /* C[m][n] = sum_k A[m,k] * B[n,k]; A [M][K], B [N][K] MXFP4 (rowwise);
  * c, t [M][N] (t nullable). */
 ORC_API int orc_mx_gemm(const uint8_t* ac, const uint8_t* as, int64_t M, const uint8_t* bc,

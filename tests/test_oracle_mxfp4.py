@@ -273,3 +273,35 @@ def test_gemm_one_hot_selects_an_element():
 def test_rejects_bad_shapes():
     with pytest.raises(ValueError):
         oracle.mx_quantize(torch.zeros(4, 48, dtype=torch.bfloat16))
+
+
+def test_decode_exact_is_the_exact_product_wide_scales():
+    """Every element, across a range of E8M0 exponents far beyond binary32's
+    comfortable range for products (rows scaled by 2^-60 .. 2^60)."""
+    g = torch.Generator().manual_seed(8)
+    x = torch.randn(64, 128, generator=g) * torch.pow(2.0, torch.arange(64).float() * 2 - 60)[:, None]
+    q = oracle.mx_quantize(x.to(torch.bfloat16))
+    d = oracle.mx_decode_exact(q)
+    expect = E2M1[unpack(q.codes)] * np.repeat(np.ldexp(1.0, q.scales.astype(np.int64) - 127), 32, axis=1)
+    assert d.dtype == np.float64 and np.array_equal(d, expect)
+    assert q.scales.min() < 100 and q.scales.max() > 160
+
+
+def test_gemm_f64_k32_equals_exact_rational():
+    """One block along K: every float64 sum is exact, so the matmul form
+    equals mx_gemm (pinned by the rational test above) exactly."""
+    a, b = _random_mx(3, 32, 1), _random_mx(4, 32, 2)
+    c, t = oracle.mx_gemm_f64(a, b)
+    ce, te = oracle.mx_gemm(a, b)
+    assert np.array_equal(c, ce) and np.array_equal(t, te)
+
+
+def test_gemm_f64_within_float64_bound_of_the_loop():
+    """Two float64 summation orders of the same exact products: within
+    2 K 2^-53 T of each other."""
+    for rows_a, rows_b, k, sa, sb in [(40, 24, 256, 3, 4), (16, 48, 4096, 5, 6)]:
+        a, b = _random_mx(rows_a, k, sa), _random_mx(rows_b, k, sb)
+        c, t = oracle.mx_gemm_f64(a, b)
+        ce, te = oracle.mx_gemm(a, b)
+        bound = 2 * k * 2.0 ** -53 * te
+        assert np.all(np.abs(c - ce) <= bound) and np.all(np.abs(t - te) <= bound)
