@@ -101,6 +101,8 @@ def test_gemm_split_last_round_and_determinism():
     ns = np.concatenate([rng.integers(0, N, 3000), rng.integers(0, N, 256)])
     ref, t = oracle.mx_gemm_entries(oa, ob, ms, ns)
     assert_gemm_close(c1.cpu().numpy()[ms, ns], ref, t, "mx gemm split")
+    ref, t = oracle.mx_gemm_f64(oa, ob)
+    assert_gemm_close(c1.cpu().numpy(), ref, t, "mx gemm split, every entry")
 
 
 def test_gemm_split_odd_stages():
@@ -118,6 +120,8 @@ def test_gemm_split_odd_stages():
     ns = np.concatenate([rng.integers(0, N, 3000), rng.integers(0, N, 256)])
     ref, t = oracle.mx_gemm_entries(oa, ob, ms, ns)
     assert_gemm_close(c.cpu().numpy()[ms, ns], ref, t, "mx gemm split odd")
+    ref, t = oracle.mx_gemm_f64(oa, ob)
+    assert_gemm_close(c.cpu().numpy(), ref, t, "mx gemm split odd, every entry")
 
 
 def test_gemm_padded_scale_rows():
@@ -146,7 +150,8 @@ def test_gemm_padded_scale_rows():
 
 def test_gemm_fprop_shape_sampled():
     """The benchmark's Fprop shape, 8192 x 5120 x 20480, from the FFN
-    down-projection tensors quantized as MXFP4; sampled entries."""
+    down-projection tensors quantized as MXFP4; sampled entries on the
+    oracle's loop and every entry on its float64 matmul form."""
     wl = inputs.ffn_down(0)
     X, W = wl.tensors["X"], wl.tensors["W"]
     say("mx gemm fprop 8192x5120x20480")
@@ -163,3 +168,6 @@ def test_gemm_fprop_shape_sampled():
     yc = y.cpu().numpy()
     assert np.all(np.isfinite(yc))
     assert_gemm_close(yc[ms, ns], ref, t, "mx fprop")
+    say("mx gemm fprop, every entry")
+    ref, t = oracle.mx_gemm_f64(ox, ow)
+    assert_gemm_close(yc, ref, t, "mx fprop, every entry")
