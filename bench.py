@@ -335,7 +335,22 @@ def cpu_baseline(x, w, dy, c5=None, gpu_us=None):
     t2 = time.perf_counter()
     oracle.gemm_entries(ox, ow, rng.integers(0, T, n2), rng.integers(0, H, n2))
     dt = time.perf_counter() - t2
-    del ox, ox_t, ow, ody, ody_t
+    # one thread: the Fprop's float64 form on its first 512 rows of X
+    rows1 = 512
+    ox1 = oracle.quantize(x[:rows1].contiguous(), oracle.ROWWISE)
+    t1_thread = None
+    try:
+        from threadpoolctl import threadpool_limits
+        oracle.set_num_threads(1)
+        with threadpool_limits(limits=1):
+            t3 = time.perf_counter()
+            oracle.gemm_f64(ox1, ow, with_bound=False)
+            t1_thread = time.perf_counter() - t3
+    except ImportError:
+        pass
+    finally:
+        oracle.set_num_threads(threads)
+    del ox, ox_t, ow, ody, ody_t, ox1
     out = {"value": flops / full / 1e12, "unit": "TFLOP/s", "cores": max(threads, blas),
            "kind": "oracle",
            "sample": (f"the whole step on the oracle, timed: the 5 quantizations of the full "
@@ -344,6 +359,10 @@ def cpu_baseline(x, w, dy, c5=None, gpu_us=None):
                       f"threads); {full:.1f} s per step"),
            "exact_gemm_path": {"TFLOP/s": round(2.0 * n2 * F / dt / 1e12, 5),
                                "sample": f"{n2} exact int64 entries at K={F} ({dt:.1f} s)"}}
+    if t1_thread is not None:
+        out["gemm_f64_1_thread"] = {
+            "TFLOP/s": round(2.0 * rows1 * H * F / t1_thread / 1e12, 4),
+            "sample": f"Fprop on the first {rows1} of {T} rows ({t1_thread:.1f} s, 1 thread)"}
     if c5 is not None:
         out["quantize_32768x8192"] = oracle_c5(c5, threads, gpu_us or {})
     return out
