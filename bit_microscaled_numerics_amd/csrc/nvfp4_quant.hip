@@ -311,6 +311,15 @@ __global__ __launch_bounds__(kThreads) void k_quant_col(
   __shared__ uint8_t lds_scales[kColTileC][kColTileR / 16];
   __shared__ float rtab[kE4m3Codes], rtab_row[ROW ? kE4m3Codes : 1];
   static_assert(kThreads >= 2 * kE4m3Codes, "threads 0..127 fill rtab, 128..255 rtab_row");
+  int64_t r0, c0;
+  quant_tile<ROW>(rows, cols, r0, c0);
+  const int cg = threadIdx.x & 15, rg = threadIdx.x >> 4;
+  const int64_t rr = r0 + 16 * rg, cc = c0 + 8 * cg;
+  const bool in = rr < rows && cc < cols;
+  // the tile's loads go out first: their latency then hides the scale
+  // tables' set-up and the sign draw
+  Tile16x8 t;
+  if (in) tile_load(t, x, cols, rr, cc);
   const ScaleCtx sc = scale_ctx(*amax, rtab, threadIdx.x);
   if (blockIdx.x == 0 && threadIdx.x == 0) *ts_out = sc.s_t;
   ScaleCtx sr_ctx;
@@ -320,13 +329,7 @@ __global__ __launch_bounds__(kThreads) void k_quant_col(
   }
   __syncthreads();
   const uint32_t signs = RHT ? rht_sign_bits(rht_seed) : 0u;
-  int64_t r0, c0;
-  quant_tile<ROW>(rows, cols, r0, c0);
-  const int cg = threadIdx.x & 15, rg = threadIdx.x >> 4;
-  const int64_t rr = r0 + 16 * rg, cc = c0 + 8 * cg;
-  if (rr < rows && cc < cols) {
-    Tile16x8 t;
-    tile_load(t, x, cols, rr, cc);
+  if (in) {
     if (ROW) {
       // rows rr .. rr+15, columns cc .. cc+7: half of a 16-wide block each;
       // the partner lane (cg ^ 1) holds the other half (cols % 16 == 0, so
@@ -441,17 +444,18 @@ __global__ __launch_bounds__(kThreads) void k_quant_2d(
     uint8_t* __restrict__ scales_t, float* __restrict__ ts_out) {
   __shared__ v2u lds_codes[kColTileC][kColTileR / 16];   // [column][row group]
   __shared__ float rtab[kE4m3Codes];
-  const ScaleCtx sc = scale_ctx(*amax, rtab, threadIdx.x);
-  if (blockIdx.x == 0 && threadIdx.x == 0) *ts_out = sc.s_t;
-  __syncthreads();
   int64_t r0, c0;
   quant_tile(rows, cols, r0, c0);
   const int cg = threadIdx.x & 15, rg = threadIdx.x >> 4;
   const int64_t rr = r0 + 16 * rg, cc = c0 + 8 * cg;
   // rows and cols are multiples of 16: a lane pair is in range together
-  if (rr < rows && cc < cols) {
-    Tile16x8 t;
-    tile_load(t, x, cols, rr, cc);
+  const bool in = rr < rows && cc < cols;
+  Tile16x8 t;   // loaded first: the latency hides the scale table's set-up
+  if (in) tile_load(t, x, cols, rr, cc);
+  const ScaleCtx sc = scale_ctx(*amax, rtab, threadIdx.x);
+  if (blockIdx.x == 0 && threadIdx.x == 0) *ts_out = sc.s_t;
+  __syncthreads();
+  if (in) {
     // block amax on the bf16 magnitudes (their bit patterns order like the
     // values), two per 32-bit lane op, then the partner lane's half
     uint32_t mp = 0;
