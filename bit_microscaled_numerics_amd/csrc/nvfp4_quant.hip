@@ -212,17 +212,33 @@ __global__ __launch_bounds__(kThreads) void k_quant_row(
     uint8_t* __restrict__ scales, float* __restrict__ ts_out) {
   __shared__ float rtab[kE4m3Codes];
   static_assert(kThreads >= kE4m3Codes, "one thread per table entry");
+  auto load_chunk = [&](v4u (&v)[kRowU], int64_t c) {
+#pragma unroll
+    for (int u = 0; u < kRowU; ++u) {
+      const int64_t i = c + u * kThreads + threadIdx.x;
+      if (i < nvec) v[u] = ld_(&x[i]);
+    }
+  };
+  // The SR encodes load one chunk ahead (the first one before the table
+  // set-up), so that their rounding arithmetic covers the next chunk's
+  // loads; the RTN encodes, with little arithmetic per element, run at a
+  // higher occupancy without the extra registers.
+  constexpr bool kAhead = SR;
+  const int64_t stride = (int64_t)gridDim.x * kRowChunk;
+  v4u nxt[kRowU];
+  if (kAhead) load_chunk(nxt, (int64_t)blockIdx.x * kRowChunk);
   const ScaleCtx sc = scale_ctx(*amax, rtab, threadIdx.x);
   if (blockIdx.x == 0 && threadIdx.x == 0) *ts_out = sc.s_t;
   const uint32_t signs = RHT ? rht_sign_bits(rht_seed) : 0u;
   __syncthreads();
-  for (int64_t c = (int64_t)blockIdx.x * kRowChunk; c < nvec;
-       c += (int64_t)gridDim.x * kRowChunk) {
+  for (int64_t c = (int64_t)blockIdx.x * kRowChunk; c < nvec; c += stride) {
     v4u vs[kRowU];
+    if (kAhead) {
 #pragma unroll
-    for (int u = 0; u < kRowU; ++u) {
-      const int64_t i = c + u * kThreads + threadIdx.x;
-      if (i < nvec) vs[u] = ld_(&x[i]);
+      for (int u = 0; u < kRowU; ++u) vs[u] = nxt[u];
+      load_chunk(nxt, c + stride);
+    } else {
+      load_chunk(vs, c);
     }
 #pragma unroll
     for (int u = 0; u < kRowU; ++u) {
