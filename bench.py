@@ -402,6 +402,7 @@ def quant_sweep(flush, steps: int = 10, keep_first=False):
             del qs, qt
         del xh
         G, CMP, ROW = nv.NVFP4_AMAX_GIVEN, nv.NVFP4_AMAX_COMPUTE, nv.NVFP4_ROWWISE
+        deq = torch.empty(x.shape, dtype=torch.float32, device=x.device)
         variants = [
             ("amax", 2 * n, lambda: nv.nvfp4_amax(x, q1.amax)),
             ("1d RTN encode", 2.5625 * n, lambda: nv.nvfp4_quantize1d_rtn(
@@ -440,6 +441,8 @@ def quant_sweep(flush, steps: int = 10, keep_first=False):
                 x, 0, 0, 0, qm.codes, qm.scales)),
             ("MXFP4 SR (single pass)", 2.53125 * n, lambda: nv.mxfp4_quantize(
                 x, 1, 7, 0, qm.codes, qm.scales)),
+            # codes + scales in, FP32 out
+            ("dequantize 1d (FP32 out)", 4.5625 * n, lambda: nv.nvfp4_dequantize(q1, deq)),
         ]
         s = torch.cuda.current_stream()
         for name, nbytes, fn in variants:
@@ -464,7 +467,7 @@ def quant_sweep(flush, steps: int = 10, keep_first=False):
                 rec["valu_frac"] = (round(n * v8 / 8 / VALU_LANE_OPS_PER_S / (ms * 1e-3), 3)
                                     if v8 else None)
             out[f"{dist} {name}"] = rec
-        del x, q1, q2, qc, qr, qm
+        del x, q1, q2, qc, qr, qm, deq
         torch.cuda.empty_cache()
     return (out, kept) if keep_first else out
 

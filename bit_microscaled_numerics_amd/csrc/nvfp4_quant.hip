@@ -531,29 +531,52 @@ __global__ __launch_bounds__(kThreads) void k_quant_2d(
 // ---------------------------------------------------------------------------
 // dequantize: out = (E2M1 * E4M3) * s_t
 // ---------------------------------------------------------------------------
+// Each workgroup iteration takes a piece of one row: kDeqU groups of 4
+// elements per thread (one 16-bit code load, one 16-byte store: a wave's
+// store covers 1 KiB of the row without gaps); the row index is one uniform
+// division per piece.  One group per thread keeps the pieces small, so the
+// workgroups in flight write one narrow window of the output (4 KiB pieces:
+// 0.49 of HBM peak at 32768 x 8192; 0.44 with a 32-byte run per thread and
+// 0.47 with 32 KiB pieces).
+constexpr int kDeqU = 1;
 __global__ __launch_bounds__(kThreads) void k_dequant(
     const uint8_t* __restrict__ codes, int64_t ld_codes, const uint8_t* __restrict__ scales,
     int64_t ss_row, int64_t ss_k, int32_t blk_rows, const float* __restrict__ ts,
     int64_t rows, int64_t k, float* __restrict__ out) {
   const float s_t = *ts;
-  const int64_t kv = k / 8, items = rows * kv;
-  for (int64_t it = (int64_t)blockIdx.x * kThreads + threadIdx.x; it < items;
-       it += (int64_t)gridDim.x * kThreads) {
-    const int64_t r = it / kv, c8 = (it - r * kv) * 8;
-    const uint32_t q = *reinterpret_cast<const uint32_t*>(codes + r * ld_codes + c8 / 2);
-    const float E = e4m3_to_float(scales[(r / blk_rows) * ss_row + (c8 / 16) * ss_k]);
-    float o[8];
+  const int64_t kv = k / 4;                                     // 4-element groups per row
+  constexpr int64_t kPiece = (int64_t)kThreads * kDeqU;         // groups per piece
+  const int64_t per_row = (kv + kPiece - 1) / kPiece, pieces = rows * per_row;
+  for (int64_t p = blockIdx.x; p < pieces; p += gridDim.x) {
+    const int64_t r = p / per_row, g0 = (p - r * per_row) * kPiece;
+    const uint8_t* const crow = codes + r * ld_codes;
+    const uint8_t* const srow = scales + (r / blk_rows) * ss_row;
+    uint32_t q[kDeqU];
+    uint8_t sc[kDeqU];
 #pragma unroll
-    for (int j = 0; j < 8; ++j) {
-      const uint32_t c = (q >> (4 * j)) & 0xFu;
-      const uint32_t i = c & 7u;
-      float mag = i < 4u ? 0.5f * (float)i : (i < 7u ? (float)i - 2.0f : 6.0f);
-      float v = (c & 8u) ? -mag : mag;
-      o[j] = (v * E) * s_t;
+    for (int u = 0; u < kDeqU; ++u) {
+      const int64_t g = g0 + u * kThreads + threadIdx.x;
+      if (g < kv) {
+        q[u] = *reinterpret_cast<const uint16_t*>(crow + g * 2);
+        sc[u] = srow[(g >> 2) * ss_k];                          // 16-element block g / 4
+      }
     }
-    v4f* dst = reinterpret_cast<v4f*>(out + r * k + c8);
-    st_(v4f{o[0], o[1], o[2], o[3]}, dst);
-    st_(v4f{o[4], o[5], o[6], o[7]}, dst + 1);
+#pragma unroll
+    for (int u = 0; u < kDeqU; ++u) {
+      const int64_t g = g0 + u * kThreads + threadIdx.x;
+      if (g >= kv) continue;
+      const float E = e4m3_to_float(sc[u]);
+      float o[4];
+#pragma unroll
+      for (int j = 0; j < 4; ++j) {
+        const uint32_t c = (q[u] >> (4 * j)) & 0xFu;
+        const uint32_t i = c & 7u;
+        float mag = i < 4u ? 0.5f * (float)i : (i < 7u ? (float)i - 2.0f : 6.0f);
+        float v = (c & 8u) ? -mag : mag;
+        o[j] = (v * E) * s_t;
+      }
+      st_(v4f{o[0], o[1], o[2], o[3]}, reinterpret_cast<v4f*>(out + r * k + g * 4));
+    }
   }
 }
 
@@ -691,8 +714,11 @@ hipError_t launch_quant_2d(const void* x, int64_t rows, int64_t cols, const floa
 hipError_t launch_dequant(const uint8_t* codes, int64_t ld_codes, const uint8_t* scales,
                           int64_t ss_row, int64_t ss_k, int32_t blk_rows, const float* ts,
                           int64_t rows, int64_t k, float* out, hipStream_t s) {
-  const int64_t items = rows * (k / 8);
-  hipLaunchKernelGGL(k_dequant, dim3(grid_for(items, 16)), dim3(kThreads), 0, s, codes,
+  const int64_t piece = (int64_t)kThreads * kDeqU;
+  const int64_t pieces = rows * ((k / 4 + piece - 1) / piece);
+  const int64_t cap = (int64_t)num_cus() * 8;
+  const int grid = (int)(pieces < cap ? (pieces < 1 ? 1 : pieces) : cap);
+  hipLaunchKernelGGL(k_dequant, dim3(grid), dim3(kThreads), 0, s, codes,
                      ld_codes, scales, ss_row, ss_k, blk_rows, ts, rows, k, out);
   return hipGetLastError();
 }
