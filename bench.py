@@ -290,12 +290,13 @@ def oracle_c5(c5, threads, gpu_us):
 
 
 def _blas_threads() -> int:
+    """Threads of the BLAS the oracle's float64 matmul runs on (0 if unknown)."""
     try:
         from threadpoolctl import threadpool_info
-        n = [i["num_threads"] for i in threadpool_info() if i.get("user_api") == "blas"]
-        return max(n) if n else 0
-    except Exception:       # threadpoolctl missing: report the OpenMP count only
+    except ImportError:     # threadpoolctl missing: report the OpenMP count only
         return 0
+    n = [i["num_threads"] for i in threadpool_info() if i.get("user_api") == "blas"]
+    return max(n) if n else 0
 
 
 def cpu_baseline(x, w, dy, c5=None, gpu_us=None):
