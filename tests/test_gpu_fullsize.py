@@ -143,5 +143,19 @@ def test_sweep_32768x8192(dist):
         say("sweep", dist, name)
         gq = gpu()
         torch.cuda.synchronize()
-        assert_operand_equal(gq, orc(), f"{dist} {name}")
-        del gq
+        oq = orc()
+        assert_operand_equal(gq, oq, f"{dist} {name}")
+        if name in ("1d RTN", "2d RTN"):
+            # the whole tensor dequantized, bit for bit (2D also through its
+            # transposed view)
+            say("sweep", dist, name, "dequantize")
+            views = [(gq, oq)] + ([(gq.t(), oq.transposed())] if name == "2d RTN" else [])
+            for gv, ov in views:
+                d = nv.dequantize(gv)
+                torch.cuda.synchronize()
+                got = d.cpu().numpy()
+                del d
+                want = oracle.dequantize(ov)
+                assert np.array_equal(got.view(np.uint32), want.view(np.uint32)), \
+                    f"{dist} {name} dequantize: {int(np.sum(got.view(np.uint32) != want.view(np.uint32)))} differ"
+        del gq, oq
