@@ -593,6 +593,11 @@ static int balanced_grid(int64_t chunks, int per_cu) {
   return (int)((chunks + trips - 1) / trips);
 }
 
+// The amax reductions finish with one atomic max per workgroup, all on one
+// address and mostly at the end of the launch, where they serialize: two
+// workgroups per CU keep the read stream as fast and that tail short.
+constexpr int kAmaxPerCu = 2;
+
 static int grid_for(int64_t items, int per_cu) {
   int64_t g = (items + kThreads - 1) / kThreads;
   int64_t cap = (int64_t)num_cus() * per_cu;
@@ -605,7 +610,7 @@ hipError_t launch_amax(const void* x, int64_t n_elems, float* out, hipStream_t s
   hipLaunchKernelGGL(k_zero_u32, dim3(1), dim3(1), 0, s, o, nullptr);
   const int64_t nvec = n_elems / 8;
   const int64_t chunks = (nvec + kAmaxChunk - 1) / kAmaxChunk;
-  hipLaunchKernelGGL(k_amax, dim3(balanced_grid(chunks, 8)), dim3(kThreads), 0, s,
+  hipLaunchKernelGGL(k_amax, dim3(balanced_grid(chunks, kAmaxPerCu)), dim3(kThreads), 0, s,
                      reinterpret_cast<const v4u*>(x), nvec, o);
   return hipGetLastError();
 }
@@ -617,12 +622,13 @@ hipError_t launch_amax_rht(const void* x, int64_t rows, int64_t cols, uint64_t r
   hipLaunchKernelGGL(k_zero_u32, dim3(1), dim3(1), 0, s, o, op);
   const int64_t items = (rows / 16) * (cols / 8);
   const uint16_t* xh = reinterpret_cast<const uint16_t*>(x);
+  const dim3 grid(balanced_grid((items + kThreads - 1) / kThreads, kAmaxPerCu));
   if (op != nullptr)
-    hipLaunchKernelGGL(k_amax_rht<true>, dim3(balanced_grid((items + kThreads - 1) / kThreads, 8)), dim3(kThreads), 0, s, xh, rows,
-                       cols, rht_seed, o, op);
+    hipLaunchKernelGGL(k_amax_rht<true>, grid, dim3(kThreads), 0, s, xh, rows, cols, rht_seed, o,
+                       op);
   else
-    hipLaunchKernelGGL(k_amax_rht<false>, dim3(balanced_grid((items + kThreads - 1) / kThreads, 8)), dim3(kThreads), 0, s, xh, rows,
-                       cols, rht_seed, o, nullptr);
+    hipLaunchKernelGGL(k_amax_rht<false>, grid, dim3(kThreads), 0, s, xh, rows, cols, rht_seed, o,
+                       nullptr);
   return hipGetLastError();
 }
 
@@ -632,7 +638,7 @@ hipError_t launch_amax_rht_row(const void* x, int64_t n_elems, uint64_t rht_seed
   hipLaunchKernelGGL(k_zero_u32, dim3(1), dim3(1), 0, s, o, nullptr);
   const int64_t nvec = n_elems / 8;
   const int64_t chunks = (nvec + kAmaxChunk - 1) / kAmaxChunk;
-  hipLaunchKernelGGL(k_amax_rht_row, dim3(balanced_grid(chunks, 8)), dim3(kThreads), 0, s,
+  hipLaunchKernelGGL(k_amax_rht_row, dim3(balanced_grid(chunks, kAmaxPerCu)), dim3(kThreads), 0, s,
                      reinterpret_cast<const v4u*>(x), nvec, rht_seed, o);
   return hipGetLastError();
 }
