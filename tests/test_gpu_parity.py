@@ -69,6 +69,31 @@ def test_amax(shape, kind):
     assert float(rht.cpu()[0]) == oracle.amax_rht(x, 1234)
 
 
+@pytest.mark.parametrize("where", ["first", "mid", "last"])
+def test_amax_several_trips(where):
+    """A tensor past the amax kernels' grid cap, so that workgroups take
+    several pieces and the last piece is partial.  On 256 CUs 8208x2064 is
+    1035 chunks of 16384 elements for the plain and rowwise-RHT scans (three
+    per workgroup, the last one 256 elements long) and 132354 micro-tiles for
+    the colwise RHT scan (two per thread).  The largest magnitude is planted
+    at the start, in chunk 345 (the first workgroup's second chunk there), or
+    at the last element."""
+    rows, cols = 8208, 2064
+    x = inputs.normal(torch.Generator().manual_seed(11), rows, cols).float()
+    x[{"first": (0, 0), "mid": (2739, 100), "last": (rows - 1, cols - 1)}[where]] = -900.0
+    x = x.to(torch.bfloat16)
+    xd = x.cuda()
+    say("amax several trips", where)
+    plain = nv.amax(xd)
+    both = nv.amax_both(xd, 77)
+    row = nv.amax_rht(xd, 77, nv.NVFP4_ROWWISE)
+    torch.cuda.synchronize()
+    assert float(plain.cpu()[0]) == oracle.amax(x) == 900.0
+    assert float(both[0].cpu()[0]) == 900.0
+    assert float(both[1].cpu()[0]) == oracle.amax_rht(x, 77)
+    assert float(row.cpu()[0]) == oracle.amax_rht(x.t().contiguous(), 77)
+
+
 @pytest.mark.parametrize("shape", SHAPES)
 @pytest.mark.parametrize("kind", KINDS)
 @pytest.mark.parametrize("axis", [nv.NVFP4_ROWWISE, nv.NVFP4_COLWISE])
